@@ -1,0 +1,40 @@
+"""CPU oracle for the shared-prefix beam-decode step -- TEST INFRASTRUCTURE.
+
+This package is a plain, slow, obviously-correct NumPy implementation of what
+the decode step computes.  It is test infrastructure only: the tests, the smoke
+check and the benchmark's CPU-baseline leg may import it; the product library
+(the HIP kernels behind the C ABI and its Python binding) never does, and it
+shares no code, table or helper with that path.
+
+Precision: inputs are float32 arrays (bf16 workloads hold bf16-representable
+values); every dot product, softmax and sum is evaluated in float64 and the
+results are rounded to float32 where a stored tensor is produced (attention
+outputs, candidate scores).  Selections are decided on those float32 scores,
+the same precision the GPU path decides in.
+
+Modules:
+  trie       append-only record arena with parent indices; ancestor chains
+  attention  attention of each beam over the shared prompt plus its own chain,
+             in three independent formulations (materialised, explicit mask,
+             split prefix/suffix with a log-sum-exp merge)
+  beam       codebook logits, log-softmax, prior add, exact top-k, the whole
+             decode step, chained decoding, scalar scoring
+
+Pins: every function here is checked in tests/test_oracle_*.py against closed
+forms, library special cases, invariants and brute force (see the docstrings
+of those tests).  Parity of the absolute values to the pages is unpinned: the
+pages print no worked example of this computation.
+"""
+from .trie import trie_append, chain, TrieError, new_arena
+from .attention import (attend_materialized, attend_masked, attend_split,
+                        prefix_attn)
+from .beam import (codebook_logits, log_softmax, candidate_scores,
+                   select_topk, decode_step, scalar_scores, beam_topk,
+                   run_chained)
+
+__all__ = [
+    "trie_append", "chain", "TrieError", "new_arena", "attend_materialized",
+    "attend_masked", "attend_split", "prefix_attn", "codebook_logits",
+    "log_softmax", "candidate_scores", "select_topk", "decode_step",
+    "scalar_scores", "beam_topk", "run_chained",
+]

@@ -1,0 +1,159 @@
+"""ctypes binding of libgrbeam.so (the C ABI in include/gr_beam.h).
+
+Argument marshalling only: every function here forwards device pointers,
+sizes and the current HIP stream to the C entry point of the same name and
+raises GrError on a nonzero status.  No computation happens in Python, and
+there is no fallback: if the library is missing, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+# torch ships its own HIP runtime (same soname as /opt/rocm's).  Loading torch
+# first makes libgrbeam.so bind to that already-loaded runtime, so the tensors
+# torch allocates and the kernels launched here share one HIP runtime; loading
+# the library first would bring in a second runtime instance.
+import torch  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgrbeam.so")
+
+GR_OK, GR_ERR_NULL, GR_ERR_SHAPE, GR_ERR_UNSUPPORTED = 0, 1, 2, 3
+GR_ERR_CAPACITY, GR_ERR_K_TOO_LARGE, GR_ERR_WORKSPACE, GR_ERR_HIP = 4, 5, 6, 7
+GR_F32, GR_BF16 = 0, 1
+GR_DEVERR_PARENT_RANGE, GR_DEVERR_PARENT_ORDER = 1, 2
+GR_DEVERR_DEPTH, GR_DEVERR_BEAM_RANGE = 4, 8
+GR_TOPK_LOG_SOFTMAX = 1
+GR_MAX_DEPTH, GR_MAX_K = 8, 2048
+
+EXPORTED = ["gr_trie_append", "gr_prefix_attn", "gr_beam_topk", "gr_decode_step",
+            "gr_attn_workspace_size", "gr_topk_workspace_size",
+            "gr_decode_workspace_size", "gr_status_string"]
+
+
+class GrError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+class Shape(ctypes.Structure):
+    """gr_shape: R requests, H heads of head_dim, prompt_len prompt rows,
+    window (0 = all), dtype (GR_BF16 / GR_F32), scale (0 = 1/sqrt(head_dim))."""
+    _fields_ = [("R", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("prompt_len", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+class Trie(ctypes.Structure):
+    """gr_trie: arena k, v [R][capacity][H][head_dim], parent [R][capacity]."""
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("parent", ctypes.c_void_p), ("capacity", ctypes.c_int32),
+                ("max_depth", ctypes.c_int32)]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m "
+        "generative_recommendation_beam_amd.build` (there is no fallback path)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_S = ctypes.c_size_t
+_sig = {
+    "gr_trie_append": [ctypes.POINTER(Shape), ctypes.POINTER(Trie), _I, _I, _P, _P, _P, _P, _I, _P, _P, _P],
+    "gr_prefix_attn": [ctypes.POINTER(Shape), _P, _P, _P, _I, ctypes.POINTER(Trie), _P, _P, _P, _S, _P, _P],
+    "gr_beam_topk": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P],
+    "gr_decode_step": [ctypes.POINTER(Shape), _P, _P, _P, _I, ctypes.POINTER(Trie), _P, _P, _I, _P, _I, _I,
+                       _P, _P, _P, _P, _P, _P, _S, _P, _P],
+    "gr_attn_workspace_size": [ctypes.POINTER(Shape), _I],
+    "gr_topk_workspace_size": [_I, _I, _I, _I],
+    "gr_decode_workspace_size": [ctypes.POINTER(Shape), _I, _I, _I],
+    "gr_status_string": [_I],
+}
+for _name, _args in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = ctypes.c_int32
+for _name in ("gr_attn_workspace_size", "gr_topk_workspace_size", "gr_decode_workspace_size"):
+    getattr(_lib, _name).restype = ctypes.c_size_t
+_lib.gr_status_string.restype = ctypes.c_char_p
+
+
+def status_string(status: int) -> str:
+    return _lib.gr_status_string(int(status)).decode()
+
+
+def _ptr(t) -> Optional[int]:
+    """Device (or host) address of a tensor, an int address, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(st: int, where: str) -> None:
+    if st != GR_OK:
+        raise GrError(st, where)
+
+
+def _shape_ref(shape):
+    return None if shape is None else ctypes.byref(shape)
+
+
+def gr_trie_append(shape, trie, base, n_new, k_new, v_new, parent_beam, prev_nodes, n_prev,
+                   node_out, dev_err, stream=None):
+    _check(_lib.gr_trie_append(_shape_ref(shape), None if trie is None else ctypes.byref(trie),
+                               int(base), int(n_new), _ptr(k_new), _ptr(v_new), _ptr(parent_beam),
+                               _ptr(prev_nodes), int(n_prev), _ptr(node_out), _ptr(dev_err),
+                               _stream(stream)), "gr_trie_append")
+
+
+def gr_prefix_attn(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, out, ws, ws_bytes,
+                   dev_err, stream=None):
+    _check(_lib.gr_prefix_attn(_shape_ref(shape), _ptr(prompt_k), _ptr(prompt_v), _ptr(q), int(n_beams),
+                               None if trie is None else ctypes.byref(trie), _ptr(beam_node), _ptr(out),
+                               _ptr(ws), int(ws_bytes), _ptr(dev_err), _stream(stream)), "gr_prefix_attn")
+
+
+def gr_beam_topk(R, n_in, vocab, k, flags, logits, prior, out_score, out_token, out_parent, cand_out,
+                 ws, ws_bytes, stream=None):
+    _check(_lib.gr_beam_topk(int(R), int(n_in), int(vocab), int(k), int(flags), _ptr(logits), _ptr(prior),
+                             _ptr(out_score), _ptr(out_token), _ptr(out_parent), _ptr(cand_out), _ptr(ws),
+                             int(ws_bytes), _stream(stream)), "gr_beam_topk")
+
+
+def gr_decode_step(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, W, vocab, prior, beam_width,
+                   flags, out_score, out_token, out_parent, attn_out, cand_out, ws, ws_bytes, dev_err,
+                   stream=None):
+    _check(_lib.gr_decode_step(_shape_ref(shape), _ptr(prompt_k), _ptr(prompt_v), _ptr(q), int(n_beams),
+                               None if trie is None else ctypes.byref(trie), _ptr(beam_node), _ptr(W),
+                               int(vocab), _ptr(prior), int(beam_width), int(flags), _ptr(out_score),
+                               _ptr(out_token), _ptr(out_parent), _ptr(attn_out), _ptr(cand_out), _ptr(ws),
+                               int(ws_bytes), _ptr(dev_err), _stream(stream)), "gr_decode_step")
+
+
+def gr_attn_workspace_size(shape, n_beams) -> int:
+    return int(_lib.gr_attn_workspace_size(_shape_ref(shape), int(n_beams)))
+
+
+def gr_topk_workspace_size(R, n_in, vocab, k) -> int:
+    return int(_lib.gr_topk_workspace_size(int(R), int(n_in), int(vocab), int(k)))
+
+
+def gr_decode_workspace_size(shape, n_beams, vocab, k) -> int:
+    return int(_lib.gr_decode_workspace_size(_shape_ref(shape), int(n_beams), int(vocab), int(k)))

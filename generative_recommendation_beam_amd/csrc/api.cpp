@@ -1,0 +1,350 @@
+// C ABI of the decode step: host-side validation, workspace layout, launches.
+//
+// Every check here runs before anything is enqueued, so a nonzero status
+// means no device work was issued (except GR_ERR_HIP, which reports a failed
+// launch).  No allocation, no synchronisation, no global state.
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gr_beam.h"
+#include "gr_launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline int elem_bytes(int dtype) { return dtype == GR_BF16 ? 2 : 4; }
+
+gr_status check_shape(const gr_shape *s) {
+  if (!s) return GR_ERR_NULL;
+  if (s->R <= 0 || s->H <= 0 || s->prompt_len <= 0 || s->window < 0) return GR_ERR_SHAPE;
+  if (s->dtype != GR_BF16 && s->dtype != GR_F32) return GR_ERR_UNSUPPORTED;
+  if (s->head_dim != 32 && s->head_dim != 64) return GR_ERR_UNSUPPORTED;
+  if (!(s->scale >= 0.f) || !isfinite(s->scale)) return GR_ERR_SHAPE;
+  // every tensor index must fit comfortably in 63 bits and grids in 31 bits
+  const long long D = (long long)s->H * s->head_dim;
+  if (D > 4096 || (long long)s->R * s->prompt_len * D > (1ll << 40)) return GR_ERR_SHAPE;
+  return GR_OK;
+}
+
+gr_status check_trie(const gr_shape *s, const gr_trie *t, bool need) {
+  if (!need) return GR_OK;
+  if (!t || !t->k || !t->v || !t->parent) return GR_ERR_NULL;
+  if (t->capacity <= 0) return GR_ERR_SHAPE;
+  if (t->max_depth < 1 || t->max_depth > GR_MAX_DEPTH) return GR_ERR_UNSUPPORTED;
+  if (!aligned16(t->k) || !aligned16(t->v)) return GR_ERR_UNSUPPORTED;
+  const long long D = (long long)s->H * s->head_dim;
+  if ((long long)s->R * t->capacity * D > (1ll << 40)) return GR_ERR_SHAPE;
+  return GR_OK;
+}
+
+int prompt_window(const gr_shape *s) {
+  return (s->window <= 0 || s->window >= s->prompt_len) ? s->prompt_len : s->window;
+}
+float eff_scale(const gr_shape *s) {
+  return s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
+}
+
+// partial-list geometry of a selection over n_in x vocab candidates
+struct SelGeo {
+  int n_groups, kk;
+  size_t bytes;  // partial lists (0 with a single group)
+};
+SelGeo sel_geo(int R, int n_in, int vocab, int k) {
+  SelGeo g;
+  g.n_groups = gr::select_groups(n_in, vocab);
+  g.kk = k < gr::kGroupPositions ? k : gr::kGroupPositions;
+  g.bytes = g.n_groups > 1 ? align_up((size_t)R * g.n_groups * g.kk * sizeof(uint64_t)) : 0;
+  return g;
+}
+
+gr_status check_select(int R, int n_in, int vocab, int k, int flags) {
+  if (R <= 0 || n_in <= 0 || k <= 0) return GR_ERR_SHAPE;
+  if (vocab != 1 && vocab != 256) return GR_ERR_UNSUPPORTED;
+  if (flags & ~GR_TOPK_LOG_SOFTMAX) return GR_ERR_UNSUPPORTED;
+  if (vocab == 1 && flags) return GR_ERR_UNSUPPORTED;   // a 1-way softmax is constant
+  if ((long long)n_in * vocab > (1ll << 30)) return GR_ERR_SHAPE;
+  if (k > GR_MAX_K || (long long)k > (long long)n_in * vocab) return GR_ERR_K_TOO_LARGE;
+  const SelGeo g = sel_geo(R, n_in, vocab, k);
+  if (g.n_groups > 1 && (long long)g.n_groups * g.kk > gr::kMergeCapacity) return GR_ERR_UNSUPPORTED;
+  return GR_OK;
+}
+
+struct DecodeLayout {
+  size_t o_off, o_bytes, z_off, z_bytes, part_off, part_bytes, total;
+};
+DecodeLayout decode_layout(const gr_shape *s, int n_beams, int vocab, int k) {
+  DecodeLayout L;
+  const size_t rows = (size_t)s->R * n_beams;
+  const size_t D = (size_t)s->H * s->head_dim;
+  const bool mfma_logits = s->dtype == GR_BF16 && vocab == 256;
+  // bf16 codebook path feeds the MFMA projection with a bf16 copy of o; the
+  // other paths keep o in fp32 and write logits / scalar scores to z.
+  L.o_bytes = align_up(rows * D * (mfma_logits ? 2 : 4));
+  L.z_bytes = mfma_logits ? 0 : align_up(rows * (size_t)vocab * sizeof(float));
+  const SelGeo g = sel_geo(s->R, n_beams, vocab, k);
+  L.part_bytes = g.bytes;
+  L.o_off = 0;
+  L.z_off = L.o_off + L.o_bytes;
+  L.part_off = L.z_off + L.z_bytes;
+  L.total = L.part_off + L.part_bytes + kAlign;  // slack for aligning ws
+  return L;
+}
+
+inline char *align_ptr(void *p) {
+  return (char *)(((uintptr_t)p + kAlign - 1) & ~(uintptr_t)(kAlign - 1));
+}
+
+gr::SelectOut make_out(float *score, int32_t *token, int32_t *parent, void *part, int R, int n_in, int vocab,
+                       int k) {
+  const SelGeo g = sel_geo(R, n_in, vocab, k);
+  gr::SelectOut o;
+  o.score = score;
+  o.token = token;
+  o.parent = parent;
+  o.partial = (uint64_t *)part;
+  o.n_groups = g.n_groups;
+  o.kk = g.kk;
+  return o;
+}
+
+gr_status attn_common(const gr_shape *shape, const void *prompt_k, const void *prompt_v, const void *q,
+                      int32_t n_beams, const gr_trie *trie, const int32_t *beam_node, int32_t *dev_err) {
+  gr_status st = check_shape(shape);
+  if (st) return st;
+  if (!prompt_k || !prompt_v || !q || !dev_err) return GR_ERR_NULL;
+  if (n_beams <= 0) return GR_ERR_SHAPE;
+  if ((long long)shape->R * n_beams * shape->H > (1ll << 30)) return GR_ERR_SHAPE;
+  if (!aligned16(prompt_k) || !aligned16(prompt_v) || !aligned16(q)) return GR_ERR_UNSUPPORTED;
+  return check_trie(shape, trie, beam_node != nullptr);
+}
+
+gr::AttnArgs attn_args(const gr_shape *shape, const void *prompt_k, const void *prompt_v, const void *q,
+                       int32_t n_beams, const gr_trie *trie, const int32_t *beam_node, int32_t *dev_err) {
+  gr::AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.dtype = shape->dtype;
+  a.pk = prompt_k;
+  a.pv = prompt_v;
+  a.q = q;
+  if (beam_node) {
+    a.ak = trie->k;
+    a.av = trie->v;
+    a.parent = trie->parent;
+    a.cap = trie->capacity;
+    a.max_depth = trie->max_depth;
+  }
+  a.beam_node = beam_node;
+  a.dev_err = dev_err;
+  a.R = shape->R;
+  a.H = shape->H;
+  a.hd = shape->head_dim;
+  a.Lp = shape->prompt_len;
+  a.Lw = prompt_window(shape);
+  a.nb = n_beams;
+  a.scale = eff_scale(shape);
+  return a;
+}
+
+inline gr_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return GR_OK;
+  fprintf(stderr, "gr_beam: HIP launch failed: %s (%s)\n", hipGetErrorName(e), hipGetErrorString(e));
+  return GR_ERR_HIP;
+}
+
+// hipGetLastError is sticky per thread: drop an error some earlier, unrelated
+// runtime call left behind so that a launch is judged on its own status.
+inline void clear_stale_error() { (void)hipGetLastError(); }
+
+}  // namespace
+
+extern "C" {
+
+const char *gr_status_string(gr_status s) {
+  switch (s) {
+    case GR_OK: return "ok";
+    case GR_ERR_NULL: return "a required pointer is NULL";
+    case GR_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case GR_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, vocab, flags, alignment or limit";
+    case GR_ERR_CAPACITY: return "append past the arena capacity";
+    case GR_ERR_K_TOO_LARGE: return "k exceeds the candidate count or GR_MAX_K";
+    case GR_ERR_WORKSPACE: return "workspace too small";
+    case GR_ERR_HIP: return "a HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t gr_attn_workspace_size(const gr_shape *shape, int32_t n_beams) {
+  (void)shape;
+  (void)n_beams;
+  return 0;
+}
+
+size_t gr_topk_workspace_size(int32_t R, int32_t n_in, int32_t vocab, int32_t k) {
+  if (R <= 0 || n_in <= 0 || k <= 0 || (vocab != 1 && vocab != 256)) return 0;
+  const SelGeo g = sel_geo(R, n_in, vocab, k);
+  return g.bytes ? g.bytes + kAlign : 0;
+}
+
+size_t gr_decode_workspace_size(const gr_shape *shape, int32_t n_beams, int32_t vocab, int32_t k) {
+  if (check_shape(shape) || n_beams <= 0 || k <= 0 || (vocab != 1 && vocab != 256)) return 0;
+  return decode_layout(shape, n_beams, vocab, k).total;
+}
+
+gr_status gr_trie_append(const gr_shape *shape, const gr_trie *trie, int32_t base, int32_t n_new,
+                         const void *k_new, const void *v_new, const int32_t *parent_beam,
+                         const int32_t *prev_nodes, int32_t n_prev, int32_t *node_out, int32_t *dev_err,
+                         hipStream_t stream) {
+  gr_status st = check_shape(shape);
+  if (st) return st;
+  if (!trie || !k_new || !v_new || !dev_err) return GR_ERR_NULL;
+  if (!trie->k || !trie->v || !trie->parent) return GR_ERR_NULL;
+  if (n_new <= 0 || base < 0 || trie->capacity <= 0) return GR_ERR_SHAPE;
+  if ((parent_beam == nullptr) != (prev_nodes == nullptr)) return GR_ERR_NULL;
+  if (prev_nodes && n_prev <= 0) return GR_ERR_SHAPE;
+  if ((long long)base + n_new > trie->capacity) return GR_ERR_CAPACITY;
+  if (!aligned16(trie->k) || !aligned16(trie->v) || !aligned16(k_new) || !aligned16(v_new))
+    return GR_ERR_UNSUPPORTED;
+  if ((long long)shape->R * trie->capacity * shape->H * shape->head_dim > (1ll << 40)) return GR_ERR_SHAPE;
+  gr::AppendArgs a;
+  a.elem_bytes = elem_bytes(shape->dtype);
+  a.ak = trie->k;
+  a.av = trie->v;
+  a.parent = trie->parent;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.parent_beam = parent_beam;
+  a.prev_nodes = prev_nodes;
+  a.node_out = node_out;
+  a.dev_err = dev_err;
+  a.R = shape->R;
+  a.H = shape->H;
+  a.hd = shape->head_dim;
+  a.cap = trie->capacity;
+  a.base = base;
+  a.n_new = n_new;
+  a.n_prev = prev_nodes ? n_prev : 0;
+  clear_stale_error();
+  return hip_status(gr::launch_trie_append(a, stream));
+}
+
+gr_status gr_prefix_attn(const gr_shape *shape, const void *prompt_k, const void *prompt_v, const void *q,
+                         int32_t n_beams, const gr_trie *trie, const int32_t *beam_node, float *out, void *ws,
+                         size_t ws_bytes, int32_t *dev_err, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  gr_status st = attn_common(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, dev_err);
+  if (st) return st;
+  if (!out) return GR_ERR_NULL;
+  if (!aligned16(out)) return GR_ERR_UNSUPPORTED;
+  gr::AttnArgs a = attn_args(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, dev_err);
+  a.out_f32 = out;
+  clear_stale_error();
+  return hip_status(gr::launch_attn(a, stream));
+}
+
+gr_status gr_beam_topk(int32_t R, int32_t n_in, int32_t vocab, int32_t k, int32_t flags, const float *logits,
+                       const float *prior, float *out_score, int32_t *out_token, int32_t *out_parent,
+                       float *cand_out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  gr_status st = check_select(R, n_in, vocab, k, flags);
+  if (st) return st;
+  if (!logits || !out_score || !out_token || !out_parent) return GR_ERR_NULL;
+  if (!aligned16(logits) || (cand_out && !aligned16(cand_out))) return GR_ERR_UNSUPPORTED;
+  const size_t need = gr_topk_workspace_size(R, n_in, vocab, k);
+  if (need && (!ws || ws_bytes < need)) return GR_ERR_WORKSPACE;
+  gr::ScoreSelectArgs a;
+  a.logits = logits;
+  a.prior = prior;
+  a.cand_out = cand_out;
+  a.R = R;
+  a.n_in = n_in;
+  a.vocab = vocab;
+  a.k = k;
+  a.log_softmax = (flags & GR_TOPK_LOG_SOFTMAX) ? 1 : 0;
+  const gr::SelectOut o = make_out(out_score, out_token, out_parent, need ? align_ptr(ws) : nullptr, R, n_in,
+                                   vocab, k);
+  clear_stale_error();
+  return hip_status(gr::launch_score_select(a, o, stream));
+}
+
+gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void *prompt_v, const void *q,
+                         int32_t n_beams, const gr_trie *trie, const int32_t *beam_node, const void *W,
+                         int32_t vocab, const float *prior, int32_t beam_width, int32_t flags, float *out_score,
+                         int32_t *out_token, int32_t *out_parent, float *attn_out, float *cand_out, void *ws,
+                         size_t ws_bytes, int32_t *dev_err, hipStream_t stream) {
+  gr_status st = attn_common(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, dev_err);
+  if (st) return st;
+  st = check_select(shape->R, n_beams, vocab, beam_width, flags);
+  if (st) return st;
+  if (!W || !out_score || !out_token || !out_parent) return GR_ERR_NULL;
+  if (!aligned16(W) || (attn_out && !aligned16(attn_out)) || (cand_out && !aligned16(cand_out)))
+    return GR_ERR_UNSUPPORTED;
+  const DecodeLayout L = decode_layout(shape, n_beams, vocab, beam_width);
+  if (!ws || ws_bytes < L.total) return GR_ERR_WORKSPACE;
+  char *base = align_ptr(ws);
+  void *o_buf = base + L.o_off;
+  float *z_buf = (float *)(base + L.z_off);
+  void *part = L.part_bytes ? base + L.part_off : nullptr;
+  const int R = shape->R;
+  const int D = shape->H * shape->head_dim;
+  const int lsm = (flags & GR_TOPK_LOG_SOFTMAX) ? 1 : 0;
+  const gr::SelectOut so = make_out(out_score, out_token, out_parent, part, R, n_beams, vocab, beam_width);
+
+  gr::AttnArgs a = attn_args(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, dev_err);
+  const bool mfma_logits = shape->dtype == GR_BF16 && vocab == 256;
+  const float *o_f32 = nullptr;
+  if (mfma_logits) {
+    a.out_lowp = o_buf;
+    a.out_f32 = attn_out;
+  } else {
+    a.out_f32 = attn_out ? attn_out : (float *)o_buf;
+    o_f32 = a.out_f32;
+  }
+  clear_stale_error();
+  hipError_t e = gr::launch_attn(a, stream);
+  if (e != hipSuccess) return hip_status(e);
+
+  if (mfma_logits) {
+    gr::LogitsArgs l;
+    l.o = (const uint16_t *)o_buf;
+    l.W = (const uint16_t *)W;
+    l.prior = prior;
+    l.cand_out = cand_out;
+    l.R = R;
+    l.n_in = n_beams;
+    l.D = D;
+    l.k = beam_width;
+    l.log_softmax = lsm;
+    return hip_status(gr::launch_logits_select_bf16(l, so, stream));
+  }
+  gr::ProjArgs pj;
+  pj.dtype = shape->dtype;
+  pj.o = o_f32;
+  pj.W = W;
+  pj.prior = prior;
+  pj.z = z_buf;
+  pj.R = R;
+  pj.n = n_beams;
+  pj.D = D;
+  pj.vocab = vocab;
+  pj.add_prior = vocab == 1 ? 1 : 0;
+  e = gr::launch_project(pj, stream);
+  if (e != hipSuccess) return hip_status(e);
+  gr::ScoreSelectArgs sa;
+  sa.logits = z_buf;
+  sa.prior = vocab == 1 ? nullptr : prior;   // the scalar path added it already
+  sa.cand_out = cand_out;
+  sa.R = R;
+  sa.n_in = n_beams;
+  sa.vocab = vocab;
+  sa.k = beam_width;
+  sa.log_softmax = lsm;
+  return hip_status(gr::launch_score_select(sa, so, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Device-side helpers shared by the gfx950 kernels of the decode step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gr_beam.h"
+
+namespace gr {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Dot product of 8 bf16 pairs held as two uint4 (fp32 accumulate).
+__device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b) {
+  float s = bf16_lo(a.x) * bf16_lo(b.x);
+  s = fmaf(bf16_hi(a.x), bf16_hi(b.x), s);
+  s = fmaf(bf16_lo(a.y), bf16_lo(b.y), s);
+  s = fmaf(bf16_hi(a.y), bf16_hi(b.y), s);
+  s = fmaf(bf16_lo(a.z), bf16_lo(b.z), s);
+  s = fmaf(bf16_hi(a.z), bf16_hi(b.z), s);
+  s = fmaf(bf16_lo(a.w), bf16_lo(b.w), s);
+  s = fmaf(bf16_hi(a.w), bf16_hi(b.w), s);
+  return s;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Ordering key of a score: a smaller key means a larger score.  -0 is folded
+// into +0 and NaN ranks like -inf, so the order is total on real scores.
+__device__ __forceinline__ uint32_t rank_key(float s) {
+  if (s != s) s = -__builtin_inff();
+  s = s + 0.0f;
+  const uint32_t u = __float_as_uint(s);
+  const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ~asc;
+}
+__device__ __forceinline__ float key_score(uint32_t rk) {
+  const uint32_t asc = ~rk;
+  const uint32_t u = (asc & 0x80000000u) ? (asc & 0x7FFFFFFFu) : ~asc;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+}  // namespace gr

@@ -1,0 +1,86 @@
+// Host-side launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gr {
+
+// Attention of every beam over the shared prompt window plus its own chain.
+struct AttnArgs {
+  int dtype;                       // GR_BF16 or GR_F32
+  const void *pk, *pv, *q;         // [R][Lp][H][hd], [R][Lp][H][hd], [R][nb][H][hd]
+  const void *ak, *av;             // arena [R][cap][H][hd] (may be null if no chains)
+  const int32_t *parent;           // [R][cap]
+  const int32_t *beam_node;        // [R][nb] or null (prompt only)
+  float *out_f32;                  // optional [R][nb][H*hd]
+  void *out_lowp;                  // optional [R][nb][H*hd] in dtype (bf16 feed of the logits)
+  int32_t *dev_err;
+  int R, H, hd, Lp, Lw, nb, cap, max_depth;
+  float scale;
+};
+hipError_t launch_attn(const AttnArgs &a, hipStream_t s);
+
+struct AppendArgs {
+  int elem_bytes;
+  void *ak, *av;
+  int32_t *parent;
+  const void *k_new, *v_new;
+  const int32_t *parent_beam, *prev_nodes;
+  int32_t *node_out, *dev_err;
+  int R, H, hd, cap, base, n_new, n_prev;
+};
+hipError_t launch_trie_append(const AppendArgs &a, hipStream_t s);
+
+// Selection outputs / partial lists shared by the scoring kernels.
+struct SelectOut {
+  float *score;
+  int32_t *token, *parent;
+  uint64_t *partial;               // [R][n_groups][kk] when n_groups > 1
+  int n_groups, kk;
+};
+
+// Codebook projection on MFMA (bf16 o, bf16 W [256][D]), log-softmax, prior,
+// selection of each group of <= 128 beams.
+struct LogitsArgs {
+  const uint16_t *o;               // [R][n_in][D] bf16
+  const uint16_t *W;               // [256][D] bf16
+  const float *prior;              // [R][n_in] or null
+  float *cand_out;                 // optional [R][n_in][256]
+  int R, n_in, D, k, log_softmax;
+};
+hipError_t launch_logits_select_bf16(const LogitsArgs &a, const SelectOut &o, hipStream_t s);
+
+// Scores from fp32 logits in global memory ([R][n_in][vocab]), then selection.
+struct ScoreSelectArgs {
+  const float *logits;
+  const float *prior;              // [R][n_in] or null
+  float *cand_out;                 // optional
+  int R, n_in, vocab, k, log_softmax;
+};
+hipError_t launch_score_select(const ScoreSelectArgs &a, const SelectOut &o, hipStream_t s);
+
+// Final merge of per-group partial lists.
+hipError_t launch_select_merge(const SelectOut &o, int R, int k, int vocab, hipStream_t s);
+
+// fp32 projections: z = o . W^T ([R][n][vocab]); scalar path uses vocab = 1.
+struct ProjArgs {
+  int dtype;                       // dtype of o and W
+  const void *o, *W;               // o [R][n][D], W [vocab][D]
+  const float *prior;              // added when add_prior (scalar path)
+  float *z;                        // [R][n][vocab]
+  int R, n, D, vocab, add_prior;
+};
+hipError_t launch_project(const ProjArgs &a, hipStream_t s);
+
+// Group geometry shared by host sizing and the kernels.
+constexpr int kGroupBeams = 128;          // beams per selection group at vocab 256
+constexpr int kGroupPositions = 32768;    // candidates per selection group
+constexpr int kMergeCapacity = 16384;     // partial entries the final merge holds
+inline int select_groups(int n_in, int vocab) {
+  const long long n = (long long)n_in * vocab;
+  return (int)((n + kGroupPositions - 1) / kGroupPositions);
+}
+
+}  // namespace gr

@@ -1,0 +1,74 @@
+// Append-only record arena (the beam trie).
+//
+// OneLA, Abstract: each beam is the shared prompt plus compact append-only
+// records of its own transitions, located through a light ancestry index;
+// beams advance without moving or copying records already stored.
+// Engineering Exploration of Generative Recall, 4.4: a shared prefix is
+// stored once.  One new record per new beam lands at node base + j and its
+// parent id is the node of the beam it extends; nothing else is written.
+//
+// One thread per 16-byte chunk of a (k, v) record pair; the first chunk's
+// thread also resolves and validates the parent id.
+
+#include "gr_device.h"
+#include "gr_launch.h"
+
+namespace gr {
+namespace {
+
+struct AP {
+  uint4 *ak, *av;
+  int32_t *parent;
+  const uint4 *k_new, *v_new;
+  const int32_t *parent_beam, *prev_nodes;
+  int32_t *node_out, *dev_err;
+  long long total;     // R * n_new * cpr
+  int cpr;             // 16-byte chunks per record
+  int cap, base, n_new, n_prev;
+};
+
+__global__ __launch_bounds__(256) void trie_append_kernel(AP p) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= p.total) return;
+  const long long rowi = idx / p.cpr;            // r * n_new + j
+  const int ch = (int)(idx % p.cpr);
+  const int r = (int)(rowi / p.n_new), j = (int)(rowi % p.n_new);
+  const long long dst = ((long long)r * p.cap + p.base + j) * p.cpr + ch;
+  p.ak[dst] = p.k_new[idx];
+  p.av[dst] = p.v_new[idx];
+  if (ch != 0) return;
+  const int n = p.base + j;
+  int par = -1, err = 0;
+  if (p.parent_beam != nullptr) {
+    const int pb = p.parent_beam[rowi];
+    if (pb < 0 || pb >= p.n_prev) {
+      err = GR_DEVERR_BEAM_RANGE;
+    } else {
+      const int q = p.prev_nodes[(long long)r * p.n_prev + pb];
+      if (q < -1 || q >= p.cap) err = GR_DEVERR_PARENT_RANGE;
+      else if (q >= n) err = GR_DEVERR_PARENT_ORDER;
+      else par = q;
+    }
+  }
+  p.parent[(long long)r * p.cap + n] = par;
+  if (p.node_out) p.node_out[rowi] = n;
+  if (err) atomicOr(p.dev_err, err);
+}
+
+}  // namespace
+
+hipError_t launch_trie_append(const AppendArgs &a, hipStream_t s) {
+  AP p;
+  p.ak = (uint4 *)a.ak; p.av = (uint4 *)a.av; p.parent = a.parent;
+  p.k_new = (const uint4 *)a.k_new; p.v_new = (const uint4 *)a.v_new;
+  p.parent_beam = a.parent_beam; p.prev_nodes = a.prev_nodes;
+  p.node_out = a.node_out; p.dev_err = a.dev_err;
+  p.cpr = a.H * a.hd * a.elem_bytes / 16;
+  p.total = (long long)a.R * a.n_new * p.cpr;
+  p.cap = a.cap; p.base = a.base; p.n_new = a.n_new; p.n_prev = a.n_prev;
+  const long long blocks = (p.total + 255) / 256;
+  hipLaunchKernelGGL(trie_append_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace gr

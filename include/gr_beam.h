@@ -1,0 +1,203 @@
+/*
+ * gr_beam.h -- C ABI of the shared-prefix large-beam decode step (gfx950).
+ *
+ * One decode step of semantic-ID generative recall in which every beam of a
+ * request shares one prompt:
+ *   1. each beam's query attends once to the shared prompt K/V (stored a
+ *      single time) plus its own short chain of ancestor records;
+ *   2. the attention output is projected onto the 256 codes of the current
+ *      semantic-ID level;
+ *   3. log-softmax over those 256 codes;
+ *   4. the running beam score is added;
+ *   5. the best B of the B_in x 256 candidates are selected.
+ *
+ * Sources (page title, section):
+ *   - Engineering Exploration of Generative Recall (ASGR), 4.1 Superman
+ *     Optimizer (attention as QK^T, scale, mask, softmax, weighted sum),
+ *     4.2 Custom Beam Search (only the 256 codes of the current position are
+ *     scored and ranked), 4.4 Tree-Based Attention (beams in a trie, shared
+ *     prefixes stored once, a token sees only ancestors on its own branch),
+ *     4.5 Sliding-Window Attention (window over the most recent prompt
+ *     tokens).
+ *   - TransRetrieval, Hardware-aware inference optimization (one user KV
+ *     cache broadcast to all candidates without copies; packed single-query
+ *     candidates isolated by masking) and Model-based Retrieval / GPU
+ *     retrieval (scalar candidate scores, candidate selection on the GPU).
+ *   - OneLA, Abstract (one shared prompt-derived state, compact append-only
+ *     records of each beam's divergent transitions, a light ancestry index,
+ *     beams advance without moving or copying records).
+ *
+ * Conventions for every entry point:
+ *   - All tensor arguments are DEVICE pointers, row-major, owned by the
+ *     caller.  The library never allocates, frees or synchronises; it keeps no
+ *     global state and is re-entrant across streams.  Work is enqueued on
+ *     `stream` and the call returns at once.
+ *   - The return value reports host-checkable errors only.  When it is not
+ *     GR_OK nothing was enqueued and no output was touched.
+ *   - Data-dependent errors are found on the device and OR-ed into *dev_err
+ *     (a device int32 the caller zeroes before the call and reads after
+ *     synchronising).  Outputs are undefined when it is nonzero.
+ *   - Element type `dtype`: GR_BF16 (bfloat16 storage, fp32 accumulation) or
+ *     GR_F32 (fp32 storage and arithmetic).  Attention outputs and scores are
+ *     always fp32.
+ *   - head_dim must be 32 or 64; vocab must be 256 (codebook step) or 1
+ *     (scalar scoring).
+ */
+#ifndef GR_BEAM_H
+#define GR_BEAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t gr_status;
+enum {
+  GR_OK = 0,
+  GR_ERR_NULL = 1,         /* a required pointer is NULL */
+  GR_ERR_SHAPE = 2,        /* a size is <= 0 or inconsistent */
+  GR_ERR_UNSUPPORTED = 3,  /* dtype, head_dim, vocab, flags or depth limit */
+  GR_ERR_CAPACITY = 4,     /* base + n_new > capacity */
+  GR_ERR_K_TOO_LARGE = 5,  /* k > n_in * vocab, or k above GR_MAX_K */
+  GR_ERR_WORKSPACE = 6,    /* ws too small (see the *_workspace_size calls) */
+  GR_ERR_HIP = 7           /* a HIP launch failed */
+};
+enum { GR_F32 = 0, GR_BF16 = 1 };
+
+/* Bits OR-ed into *dev_err by the device. */
+enum {
+  GR_DEVERR_PARENT_RANGE = 1, /* a node or parent id outside [-1, capacity) */
+  GR_DEVERR_PARENT_ORDER = 2, /* a parent id not older than its child */
+  GR_DEVERR_DEPTH = 4,        /* a chain longer than max_depth */
+  GR_DEVERR_BEAM_RANGE = 8    /* parent_beam outside [0, n_prev) */
+};
+
+/* gr_beam_topk / gr_decode_step flags */
+enum { GR_TOPK_LOG_SOFTMAX = 1 };
+
+#define GR_MAX_DEPTH 8    /* longest ancestor chain a beam may have */
+#define GR_MAX_K 2048     /* largest k (beam width / selected count) */
+
+/* Shape of one batched step.  R requests, each with prompt_len prompt rows of
+ * H heads x head_dim.  window = number of most recent prompt rows attended
+ * (0 = all; values >= prompt_len mean all).  scale = score scale (0 means
+ * 1/sqrt(head_dim)). */
+typedef struct {
+  int32_t R, H, head_dim, prompt_len, window, dtype;
+  float scale;
+} gr_shape;
+
+/* The append-only record arena (the trie).  For request r and node n:
+ *   k[r][n][H][head_dim], v[r][n][H][head_dim]  (dtype)
+ *   parent[r][n] in [-1, n)  (-1 = child of the prompt)
+ * capacity = nodes per request; max_depth <= GR_MAX_DEPTH bounds the chain
+ * length a step walks (a longer chain sets GR_DEVERR_DEPTH). */
+typedef struct {
+  void *k, *v;
+  int32_t *parent;
+  int32_t capacity, max_depth;
+} gr_trie;
+
+/* gr_trie_append -- append one record per new beam (OneLA, Abstract:
+ * append-only records; existing records are neither moved nor copied).
+ *   For every request r and j < n_new, node n = base + j receives
+ *     trie.k[r][n] = k_new[r][j],  trie.v[r][n] = v_new[r][j]
+ *     trie.parent[r][n] = prev_nodes[r][parent_beam[r][j]]   (or -1 when
+ *                         parent_beam and prev_nodes are both NULL: a first
+ *                         level hanging off the prompt)
+ *     node_out[r][j] = n   (optional, may be NULL)
+ *   k_new, v_new: [R][n_new][H][head_dim] dtype.  parent_beam: [R][n_new]
+ *   int32 index of the previous beam each new beam extends.  prev_nodes:
+ *   [R][n_prev] int32 arena node of each previous beam.
+ *   Host errors: NULL pointers (shape, trie, k_new, v_new, dev_err, trie
+ *   arrays), n_new <= 0, base < 0, base + n_new > capacity (CAPACITY),
+ *   exactly one of parent_beam / prev_nodes NULL, n_prev <= 0 with
+ *   prev_nodes.  Device errors: parent_beam outside [0, n_prev)
+ *   (BEAM_RANGE), a previous node outside [-1, n) (PARENT_ORDER or
+ *   PARENT_RANGE); the offending parent is stored as -1. */
+gr_status gr_trie_append(const gr_shape *shape, const gr_trie *trie,
+                         int32_t base, int32_t n_new, const void *k_new,
+                         const void *v_new, const int32_t *parent_beam,
+                         const int32_t *prev_nodes, int32_t n_prev,
+                         int32_t *node_out, int32_t *dev_err,
+                         hipStream_t stream);
+
+/* gr_prefix_attn -- attention of every beam over the shared prompt plus its
+ * own ancestor chain (ASGR 4.1, 4.4, 4.5; TransRetrieval, Hardware-aware
+ * inference optimization; OneLA, Abstract).
+ *   keys(r,b) = prompt rows [prompt_len - Lw, prompt_len) then the chain of
+ *               beam_node[r][b] from its root-most record down to itself;
+ *   s_j = scale * q[r][b][h] . k_j[h];  p = softmax(s) over keys(r,b);
+ *   out[r][b][h*head_dim + i] = sum_j p_j v_j[h][i].
+ *   prompt_k, prompt_v: [R][prompt_len][H][head_dim] dtype (read once per
+ *   request and head, never copied per beam).  q: [R][n_beams][H][head_dim].
+ *   beam_node: [R][n_beams] int32 arena node of each beam, or NULL for
+ *   prompt-only beams (trie may then be NULL).  out: [R][n_beams][H*head_dim]
+ *   fp32.  ws / ws_bytes: scratch, gr_attn_workspace_size() bytes (currently
+ *   0; NULL is accepted then).
+ *   Host errors: NULL pointers, sizes <= 0, unsupported dtype/head_dim,
+ *   max_depth outside [1, GR_MAX_DEPTH].  Device errors: PARENT_RANGE,
+ *   PARENT_ORDER, DEPTH while walking a chain. */
+gr_status gr_prefix_attn(const gr_shape *shape, const void *prompt_k,
+                         const void *prompt_v, const void *q, int32_t n_beams,
+                         const gr_trie *trie, const int32_t *beam_node,
+                         float *out, void *ws, size_t ws_bytes,
+                         int32_t *dev_err, hipStream_t stream);
+
+/* gr_beam_topk -- candidate scores and exact top-k (ASGR 4.2).
+ *   c[r][b][t] = prior[r][b] + (flags & GR_TOPK_LOG_SOFTMAX
+ *                               ? logits[r][b][t] - logsumexp_t logits[r][b]
+ *                               : logits[r][b][t])
+ *   Per request, the k candidates with the largest c, ordered by c
+ *   descending and then by the flat index f = b*vocab + t ascending:
+ *     out_score[r][j] = c,  out_token[r][j] = f mod vocab,
+ *     out_parent[r][j] = f div vocab (index into the input beams).
+ *   logits: [R][n_in][vocab] fp32.  prior: [R][n_in] fp32 or NULL (= 0).
+ *   cand_out: optional [R][n_in][vocab] fp32 copy of c.  ws: at least
+ *   gr_topk_workspace_size(R, n_in, vocab, k) bytes.
+ *   Host errors: NULL pointers, sizes <= 0, vocab not 1 or 256, unknown
+ *   flags, k > n_in*vocab or k > GR_MAX_K, workspace too small. */
+gr_status gr_beam_topk(int32_t R, int32_t n_in, int32_t vocab, int32_t k,
+                       int32_t flags, const float *logits, const float *prior,
+                       float *out_score, int32_t *out_token,
+                       int32_t *out_parent, float *cand_out, void *ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* gr_decode_step -- the whole step: gr_prefix_attn, then the codebook
+ * projection of the current level z[r][b][t] = sum_i o[r][b][i] W[t][i]
+ * (only the vocab = 256 valid codes, ASGR 4.2), then gr_beam_topk's scoring
+ * and selection with k = beam_width.
+ *   W: [vocab][H*head_dim] dtype (row t = code t's projection vector).
+ *   vocab = 1 is scalar scoring (TransRetrieval): score = o . W[0] (+ prior),
+ *   flags must be 0.
+ *   attn_out: optional [R][n_beams][H*head_dim] fp32 copy of the attention
+ *   output; cand_out: optional [R][n_beams][vocab] fp32 copy of c.
+ *   ws: at least gr_decode_workspace_size(shape, n_beams, vocab, beam_width)
+ *   bytes.  Errors: those of gr_prefix_attn and gr_beam_topk. */
+gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k,
+                         const void *prompt_v, const void *q, int32_t n_beams,
+                         const gr_trie *trie, const int32_t *beam_node,
+                         const void *W, int32_t vocab, const float *prior,
+                         int32_t beam_width, int32_t flags, float *out_score,
+                         int32_t *out_token, int32_t *out_parent,
+                         float *attn_out, float *cand_out, void *ws,
+                         size_t ws_bytes, int32_t *dev_err,
+                         hipStream_t stream);
+
+/* Scratch sizes in bytes (0 when none is needed; sizes <= 0 give 0). */
+size_t gr_attn_workspace_size(const gr_shape *shape, int32_t n_beams);
+size_t gr_topk_workspace_size(int32_t R, int32_t n_in, int32_t vocab,
+                              int32_t k);
+size_t gr_decode_workspace_size(const gr_shape *shape, int32_t n_beams,
+                                int32_t vocab, int32_t k);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *gr_status_string(gr_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GR_BEAM_H */

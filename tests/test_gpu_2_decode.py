@@ -1,0 +1,176 @@
+"""GPU parity of gr_decode_step (the whole hot path) against the oracle.
+
+* Reduced versions of every workload family (beam 50/100/512 with windows,
+  scalar scoring), compared in full: attention outputs, all candidate scores,
+  the selected scores (max|err|/RMS bar), the index rule and exact
+  self-consistency of the selection with the GPU's own candidate scores.
+* The tiny fp32 workload run end to end for three chained steps, the trie grown
+  by the decode itself through gr_trie_append (teacher forcing only if a
+  near-tie < 1e-3 swaps a pick).
+* Every full-size workload in the launch configuration the benchmark times
+  (no debug outputs), checked on sampled requests that the oracle computes in
+  full, plus a second call with debug outputs for attention and candidates.
+* Determinism: two calls give bit-identical outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from generative_recommendation_beam_amd import _lib as L
+from generative_recommendation_beam_amd import harness as HN
+from parity import (announce, assert_close, check_index_rule, check_self_consistent)
+
+pytestmark = pytest.mark.gpu
+
+CF = W.CONFIGS
+SMALL = {
+    "beam50_small": W.reduced(CF["beam50_p600"], R=5, Lp=131, n_in=50, level_sizes=(41, 50)),
+    "beam100_small": W.reduced(CF["beam100_p600"], R=4, Lp=200, n_in=100,
+                               level_sizes=(100, 100, 100)),
+    "beam100_flat_prior": W.reduced(CF["beam100_p600"], R=3, Lp=77, n_in=100,
+                                    level_sizes=(90, 100, 100), prior="flat"),
+    "beam512_window_small": W.reduced(CF["beam512_p2048_w512"], R=2, Lp=300, window=130, H=4,
+                                      level_sizes=(256, 512, 512, 512)),
+    "beam130_two_groups": W.reduced(CF["beam100_p600"], R=2, Lp=90, n_in=130, k=130,
+                                    level_sizes=(100, 130, 130), H=4),
+    "scalar_small": W.reduced(CF["broadcast40k_u256"], n_in=3000, k=333, level_sizes=(3000,)),
+    "f32_beam16": W.reduced(CF["beam100_p600"], R=2, Lp=40, H=4, d=32, n_in=16, k=16,
+                            level_sizes=(9, 16, 16), dtype="f32"),
+}
+
+
+def oracle_step(x, rsel=None):
+    """Oracle decode of the requests in rsel (all when None)."""
+    cfg = x.cfg
+    rs = list(range(cfg.R)) if rsel is None else list(rsel)
+    sl = lambda a: None if a is None else a[rs]
+    levels = [(sl(pb), k[rs], v[rs]) for (pb, k, v) in x.levels]
+    cap = max(sum(k.shape[1] for (_, k, _) in levels), 1)
+    ak, av, par = oracle.new_arena(len(rs), cap, cfg.H, cfg.d)
+    prev, base = None, 0
+    for (pb, k, v) in levels:
+        ak, av, par, prev = oracle.trie_append(ak, av, par, base, k, v, pb, prev)
+        base += k.shape[1]
+    return oracle.decode_step(x.prompt_k[rs], x.prompt_v[rs], x.q[rs], par, ak, av,
+                              sl(x.beam_node), x.W, sl(x.prior), cfg.k,
+                              use_log_softmax=cfg.vocab > 1, window=cfg.window)
+
+
+def compare(cfg, got, ref, rs, name, debug=True):
+    tol = cfg.dtype
+    if debug:
+        assert_close(got["attn"][rs], ref["attn"], tol, f"{name} attention")
+        assert_close(got["cand"][rs], ref["cand"], tol, f"{name} candidates")
+        check_self_consistent(got["cand"], got["token"], got["parent"])
+    assert_close(got["score"][rs], ref["score"], tol, f"{name} selected scores")
+    band = 0
+    for i, r in enumerate(rs):
+        band += check_index_rule(ref["cand"][i], got["token"][r], got["parent"][r])
+    return band
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_decode_small_parity(name):
+    cfg = SMALL[name]
+    announce(f"gr_decode_step {name}")
+    x = W.make_step_inputs(cfg)
+    ds = HN.upload_step(x)
+    buf = HN.decode_buffers(ds, debug_outputs=True)
+    HN.decode_step(ds, buf)
+    torch.cuda.synchronize()
+    assert int(ds.dev_err.item()) == 0
+    got = HN.results_to_host(buf)
+    ref = oracle_step(x)
+    band = compare(cfg, got, ref, list(range(cfg.R)), name)
+    print(f"{name}: picks in the near-tie band: {band}")
+
+
+def test_chained_fp32_three_steps():
+    cfg = CF["tiny_f32_3step"]
+    announce("gr_decode_step tiny_f32_3step chained")
+    ci = W.make_chained_inputs(cfg)
+    R, H, d, k = cfg.R, cfg.H, cfg.d, cfg.k
+    shape = HN.make_shape(R, H, d, cfg.Lp, 0, L.GR_F32)
+    pk, pv = HN.to_dev(ci.prompt_k, L.GR_F32), HN.to_dev(ci.prompt_v, L.GR_F32)
+    cap = k * (cfg.steps - 1)
+    ak_d, av_d, par_d, trie = HN.new_arena(shape, cap)
+    ak, av, par = oracle.new_arena(R, cap, H, d)
+    dev_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    node_d, node = None, None
+    prior_d, prior = torch.zeros((R, 1), device="cuda"), ci.prior0
+    base, forced = 0, 0
+    for s in range(cfg.steps):
+        q = ci.q[s]
+        n_in = q.shape[1]
+        ds = HN.DeviceStep(shape, pk, pv, HN.to_dev(q, L.GR_F32), HN.to_dev(ci.W[s], L.GR_F32), prior_d,
+                           ak_d, av_d, par_d, trie if node_d is not None else None, node_d, n_in, k, 256,
+                           L.GR_TOPK_LOG_SOFTMAX, dev_err)
+        buf = HN.decode_buffers(ds, debug_outputs=True)
+        HN.decode_step(ds, buf)
+        torch.cuda.synchronize()
+        assert int(dev_err.item()) == 0
+        got = HN.results_to_host(buf)
+        ref = oracle.decode_step(ci.prompt_k, ci.prompt_v, q, par, ak, av, node, ci.W[s], prior, k)
+        compare(cfg, got, ref, list(range(R)), f"step {s}")
+        same = (np.array_equal(got["token"], ref["token"]) and np.array_equal(got["parent"], ref["parent"]))
+        if not same:
+            forced += 1            # continue both sides from the oracle's picks
+        tok, parent = ref["token"], ref["parent"]
+        score_g = got["score"] if same else ref["score"]
+        if s + 1 < cfg.steps:
+            kn, vn = ci.rec[s]
+            pb = parent if node is not None else None
+            node_d = HN.append_level(shape, trie, base, kn, vn, pb, node_d, dev_err)
+            ak, av, par, node = oracle.trie_append(ak, av, par, base, kn, vn, pb, node)
+            base += k
+            prior_d = torch.from_numpy(np.ascontiguousarray(score_g)).cuda()
+            prior = ref["score"]
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(node_d.cpu().numpy(), node)
+    np.testing.assert_array_equal(par_d.cpu().numpy(), par)
+    print(f"teacher-forced steps: {forced}")
+
+
+FULL = [("beam50_p600", None), ("beam100_p600", [0, 97, 255]),
+        ("broadcast40k_u256", None), ("beam512_p2048_w512", [17])]
+
+
+@pytest.mark.parametrize("name,rsel", FULL, ids=[n for n, _ in FULL])
+def test_decode_full_size_sampled(name, rsel):
+    cfg = CF[name]
+    announce(f"gr_decode_step {name} full size")
+    x = W.make_step_inputs(cfg)
+    ds = HN.upload_step(x)
+    buf = HN.decode_buffers(ds, debug_outputs=False)       # as timed by the benchmark
+    HN.decode_step(ds, buf)
+    torch.cuda.synchronize()
+    assert int(ds.dev_err.item()) == 0
+    got = HN.results_to_host(buf)
+    rs = list(range(cfg.R)) if rsel is None else rsel
+    ref = oracle_step(x, rs)
+    compare(cfg, got, ref, rs, name, debug=False)
+    # same call with the debug outputs: attention and every candidate score
+    buf2 = HN.decode_buffers(ds, debug_outputs=True)
+    HN.decode_step(ds, buf2)
+    torch.cuda.synchronize()
+    got2 = HN.results_to_host(buf2)
+    for key in ("score", "token", "parent"):
+        np.testing.assert_array_equal(got2[key], got[key])
+    compare(cfg, got2, ref, rs, name, debug=True)
+
+
+def test_determinism():
+    cfg = SMALL["beam100_small"]
+    announce("gr_decode_step determinism")
+    x = W.make_step_inputs(cfg)
+    ds = HN.upload_step(x)
+    outs = []
+    for _ in range(2):
+        buf = HN.decode_buffers(ds, debug_outputs=True)
+        HN.decode_step(ds, buf)
+        torch.cuda.synchronize()
+        outs.append(HN.results_to_host(buf))
+    for key in outs[0]:
+        np.testing.assert_array_equal(outs[0][key], outs[1][key], err_msg=key)

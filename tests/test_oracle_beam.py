@@ -316,3 +316,8 @@ def test_workload_generators_are_seeded_and_shaped():
     np.testing.assert_array_equal(a.beam_node[0], np.arange(10, 16))
     x = np.array([1.0, 1.00390625, 1.005859375, -3.1415927, 65504.0], np.float32)
     np.testing.assert_array_equal(W.bf16_round(x), [1.0, 1.0, 1.0078125, -3.140625, 65536.0])
+    # bit-level definition of round-to-nearest-even on the upper 16 bits
+    y = np.random.default_rng(1).standard_normal(100000).astype(np.float32) * 10
+    u = y.view(np.uint32).astype(np.uint64)
+    ref = ((u + ((u >> 16) & 1) + 0x7FFF) & 0xFFFF0000).astype(np.uint32).view(np.float32)
+    np.testing.assert_array_equal(W.bf16_round(y), ref)

@@ -110,18 +110,22 @@ def reduced(cfg: Config, **changes) -> Config:
     return dataclasses.replace(cfg, **changes)
 
 
-def bf16_round(x: np.ndarray) -> np.ndarray:
+def bf16_round(x: np.ndarray, inplace: bool = False) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even) and return
-    them as float32 (every result is exactly representable in bf16)."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    bias = ((u >> np.uint64(16)) & np.uint64(1)) + np.uint64(0x7FFF)
-    r = ((u + bias) & np.uint64(0xFFFF0000)).astype(np.uint32)
-    return r.view(np.float32).reshape(x.shape)
+    them as float32 (every result is exactly representable in bf16).  Uses
+    torch's float32 -> bfloat16 conversion (round to nearest even) for speed;
+    the tests pin it against the bit-level definition."""
+    import torch
+    if inplace and isinstance(x, np.ndarray) and x.dtype == np.float32 and x.flags.c_contiguous:
+        t = torch.from_numpy(x)
+        t.copy_(t.to(torch.bfloat16))
+        return x
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
 
 
 def _maybe_round(x: np.ndarray, dtype: str) -> np.ndarray:
-    return bf16_round(x) if dtype == "bf16" else np.ascontiguousarray(x, np.float32)
+    return bf16_round(x, inplace=True) if dtype == "bf16" else np.ascontiguousarray(x, np.float32)
 
 
 def _normal(rng, shape, std=1.0) -> np.ndarray:

@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Throughput of the shared-prefix beam-decode step on one MI355X.
+
+A step is one gr_decode_step over the whole batch of the headline workload
+(256 requests, 600-token prompts, 8 heads x 64, beam 100, chains of 3 records,
+256 codes per level, bf16): attention of every beam over its request's shared
+prompt plus its own ancestor chain, codebook projection, log-softmax, prior
+add and top-100 of 100 x 256 per request.  Inputs are seeded synthetic data
+(workloads module), uploaded once and resident in HBM; two independent copies
+alternate between steps so that each step reads cold data (the working set of
+one copy exceeds the 256 MB last-level cache).
+
+Printed: one JSON line with steps/s (value), beam-steps/s, algorithmic HBM
+GB/s of the step, the attention kernel's roofline (algorithmic bytes per
+launch / its event-timed average duration, against 8 TB/s), and the oracle
+timed on a bounded sample of the same workload on the host CPU.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0    # dense bf16 MFMA, published peak
+COUNTERS = os.path.join(ROOT, "profiles", "attn_bf16_beam100_p600_counters.json")
+ATTN_SOURCE = os.path.join(ROOT, "generative_recommendation_beam_amd", "csrc", "attn.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="beam100_p600")
+    ap.add_argument("--sets", type=int, default=2, help="independent input copies rotated between steps")
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 512 MiB device copy (counter calibration, copy bandwidth)")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------- accounting
+def chain_nodes(x):
+    """Distinct arena nodes on the live beams' chains, per request (from the
+    seeded parent draws: level l node j extends level l-1 node parent_beam)."""
+    cfg = x.cfg
+    if not x.levels:
+        return [0] * cfg.R
+    import numpy as np
+    counts = np.zeros(cfg.R, np.int64)
+    live = np.tile(np.arange(cfg.n_in), (cfg.R, 1))          # deepest-level indices
+    for li in range(len(x.levels) - 1, -1, -1):
+        for r in range(cfg.R):
+            counts[r] += len(np.unique(live[r]))
+        pb = x.levels[li][0]
+        if pb is None:
+            break
+        live = np.take_along_axis(pb, live, axis=1)
+    return counts.tolist()
+
+
+def algorithmic(x):
+    """Bytes the step must move and flops it must do (no re-reads, no padding,
+    no debug outputs): the prompt window once per request, the queries, every
+    distinct chain record once (k and v) with its parent id, the beam nodes, the
+    codebook slice once, the prior, and the selected score/token/parent."""
+    cfg = x.cfg
+    es = 2 if cfg.dtype == "bf16" else 4
+    D, R, B, Lw = cfg.D, cfg.R, cfg.n_in, cfg.Lw
+    n_chain = sum(chain_nodes(x))
+    prompt = R * Lw * D * 2 * es
+    q = R * B * D * es
+    records = n_chain * (D * 2 * es + 4) + (R * B * 4 if x.levels else 0)
+    attn_out = R * B * D * es                     # attention output handed to the scoring stage
+    W = cfg.vocab * D * es
+    prior = 0 if x.prior is None else R * B * 4
+    outs = R * cfg.k * 12
+    delta = cfg.depth
+    flops = R * (4 * B * Lw * D + 4 * B * delta * D + 2 * B * D * cfg.vocab)
+    return dict(step_bytes=prompt + q + records + W + prior + outs,
+                attn_kernel_bytes=prompt + q + records + attn_out,
+                prompt=prompt, q=q, records=records, n_chain_records=n_chain, flops=flops)
+
+
+# ------------------------------------------------------------------ devices
+def clone_step(ds):
+    """An independent device copy of one uploaded step (same values)."""
+    import dataclasses
+    from generative_recommendation_beam_amd import _lib as L
+    c = lambda t: None if t is None else t.clone()
+    ak, av, par = c(ds.arena_k), c(ds.arena_v), c(ds.parent)
+    trie = None
+    if ds.trie is not None:
+        trie = L.Trie(k=ak.data_ptr(), v=av.data_ptr(), parent=par.data_ptr(),
+                      capacity=ds.trie.capacity, max_depth=ds.trie.max_depth)
+        trie._tensors = (ak, av, par)
+    return dataclasses.replace(ds, prompt_k=c(ds.prompt_k), prompt_v=c(ds.prompt_v), q=c(ds.q), W=c(ds.W),
+                               prior=c(ds.prior), arena_k=ak, arena_v=av, parent=par, trie=trie,
+                               beam_node=c(ds.beam_node))
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_counters(attn_bytes_alg):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, or None when absent or taken on another version of the kernel."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha") != source_sha(ATTN_SOURCE):
+        return None
+    return int((c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024)
+
+
+def cpu_baseline(x, seconds):
+    """The oracle (plain NumPy, one BLAS thread) on the first requests of the
+    same workload until `seconds` of work have accumulated."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:            # pragma: no cover
+        threadpool_limits = None
+    cfg = x.cfg
+    done, spent, beams = 0, 0.0, 0
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        while done < cfg.R and (spent < seconds or done < 2):
+            r = [done]
+            sl = lambda a: None if a is None else a[r]
+            ak, av, par = oracle.new_arena(1, max(cfg.capacity, 1), cfg.H, cfg.d)
+            prev, base = None, 0
+            for (pb, k, v) in x.levels:
+                ak, av, par, prev = oracle.trie_append(ak, av, par, base, k[r], v[r], sl(pb), prev)
+                base += k.shape[1]
+            t0 = time.perf_counter()
+            oracle.decode_step(x.prompt_k[r], x.prompt_v[r], x.q[r], par, ak, av, sl(x.beam_node), x.W,
+                               sl(x.prior), cfg.k, use_log_softmax=cfg.vocab > 1, window=cfg.window)
+            spent += time.perf_counter() - t0
+            done += 1
+            beams += cfg.n_in
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    steps_per_s = (done / cfg.R) / spent
+    return {"value": steps_per_s, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {cfg.R} requests ({done * cfg.n_in} beams), "
+                      f"{spent:.1f} s of oracle time, scaled to whole steps",
+            "beam_steps_per_s": beams / spent}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(requests are independent: see the sharding notes in the design document)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import workloads as W
+    from generative_recommendation_beam_amd import _lib as L
+    from generative_recommendation_beam_amd import harness as HN
+
+    cfg = W.CONFIGS[args.workload]
+    assert cfg.steps == 1, "the benchmark times single-step workloads"
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    x = W.make_step_inputs(cfg)
+    print(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    acc = algorithmic(x)
+    sets = [HN.upload_step(x)]
+    for _ in range(args.sets - 1):
+        sets.append(clone_step(sets[0]))
+    bufs = [HN.decode_buffers(ds) for ds in sets]
+    torch.cuda.synchronize()
+    print(f"[bench] {len(sets)} input set(s) resident on the GPU", file=sys.stderr, flush=True)
+
+    def step(i, flags_extra=0):
+        ds, buf = sets[i % len(sets)], bufs[i % len(bufs)]
+        L.gr_decode_step(ds.shape, ds.prompt_k, ds.prompt_v, ds.q, ds.n_beams, ds.trie, ds.beam_node, ds.W,
+                         ds.vocab, ds.prior, ds.k, ds.flags | flags_extra, buf.score, buf.token, buf.parent,
+                         None, None, buf.ws, buf.ws_bytes, ds.dev_err)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region 1: K whole steps, one call each
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+
+    # timed region 2: the same K steps with events between the attention
+    # stage and the scoring/selection stage (same kernels, same arguments)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        evs[i][0].record()
+        step(i, L.GR_STEP_ATTENTION)
+        evs[i][1].record()
+        step(i, L.GR_STEP_SELECTION)
+        evs[i][2].record()
+    torch.cuda.synchronize()
+    attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    sel_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    errs = [int(ds.dev_err.item()) for ds in sets]
+    assert not any(errs), f"device error bits set: {errs}"
+
+    copy_gbps = None
+    if args.calibrate_copy:
+        n = 512 * 1024 * 1024 // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(10):
+            torch.mul(a, 1.0, out=b)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_gbps = 2 * n * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+
+    steps_per_s = 1e3 / ms_step
+    attn_avg_ms = float(np.mean(attn_ms))
+    achieved = acc["attn_kernel_bytes"] / (attn_avg_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_from_counters(acc["attn_kernel_bytes"]),
+                "kernel": "attn_bf16_kernel", "avg_launch_ms": round(attn_avg_ms, 5),
+                "algorithmic_bytes_per_launch": acc["attn_kernel_bytes"]}
+    step_gbps = acc["step_bytes"] / (ms_step * 1e-3) / 1e9
+    out = {
+        "metric": "beam decode steps/s & achieved HBM GB/s, beam=100, prompt=600 tok (1 GPU)",
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) K/V/Q, N(0,0.02) codebook, cumsum(-x^2) priors)",
+        "config": {"workload": cfg.name, "requests": cfg.R, "prompt_len": cfg.Lp, "window": cfg.Lw,
+                   "heads": cfg.H, "head_dim": cfg.d, "beams": cfg.n_in, "beam_width": cfg.k,
+                   "chain_records": cfg.depth, "codes_per_level": cfg.vocab, "input_sets": len(sets)},
+        "beam_steps_per_s": round(steps_per_s * cfg.R * cfg.n_in, 0),
+        "achieved_GBps": round(step_gbps, 1),
+        "hbm_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": acc["step_bytes"],
+        "flops_per_step": acc["flops"],
+        "achieved_TFLOPs": round(acc["flops"] / (ms_step * 1e-3) / 1e12, 2),
+        "stage_ms": {"attention": round(attn_avg_ms, 5), "scoring_selection": round(float(np.mean(sel_ms)), 5)},
+        "roofline": roofline,
+    }
+    if copy_gbps is not None:
+        out["copy_GBps"] = round(copy_gbps, 1)
+    if not args.skip_cpu_baseline:
+        print("[bench] timing the oracle on a sample of the same workload", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

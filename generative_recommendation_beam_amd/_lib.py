@@ -26,6 +26,7 @@ GR_F32, GR_BF16 = 0, 1
 GR_DEVERR_PARENT_RANGE, GR_DEVERR_PARENT_ORDER = 1, 2
 GR_DEVERR_DEPTH, GR_DEVERR_BEAM_RANGE = 4, 8
 GR_TOPK_LOG_SOFTMAX = 1
+GR_STEP_ATTENTION, GR_STEP_SELECTION = 2, 4
 GR_MAX_DEPTH, GR_MAX_K = 8, 2048
 
 EXPORTED = ["gr_trie_append", "gr_prefix_attn", "gr_beam_topk", "gr_decode_step",

@@ -279,6 +279,10 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void
                          size_t ws_bytes, int32_t *dev_err, hipStream_t stream) {
   gr_status st = attn_common(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, dev_err);
   if (st) return st;
+  const int32_t stage = flags & (GR_STEP_ATTENTION | GR_STEP_SELECTION);
+  const bool run_attn = stage != GR_STEP_SELECTION;
+  const bool run_select = stage != GR_STEP_ATTENTION;
+  flags &= ~(GR_STEP_ATTENTION | GR_STEP_SELECTION);
   st = check_select(shape->R, n_beams, vocab, beam_width, flags);
   if (st) return st;
   if (!W || !out_score || !out_token || !out_parent) return GR_ERR_NULL;
@@ -306,8 +310,12 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void
     o_f32 = a.out_f32;
   }
   clear_stale_error();
-  hipError_t e = gr::launch_attn(a, stream);
-  if (e != hipSuccess) return hip_status(e);
+  hipError_t e = hipSuccess;
+  if (run_attn) {
+    e = gr::launch_attn(a, stream);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (!run_select) return GR_OK;
 
   if (mfma_logits) {
     gr::LogitsArgs l;

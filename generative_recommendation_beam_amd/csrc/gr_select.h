@@ -1,55 +1,52 @@
-// Block-wide exact top-k selection over candidates held in LDS.
+// Block-wide exact top-k selection over candidates held in registers.
 //
 // Candidate selection on the GPU (TransRetrieval, GPU retrieval) for the
 // 256-way beam search (Engineering Exploration of Generative Recall, 4.2).
 // Every candidate has a unique 64-bit composite key
 //     comp = rank_key(score) << 32 | flat index,
 // so "best k by score, ties by lower index" is "k smallest composites".
-// The k-th smallest is found by MSB-first radix select (8-bit digits,
-// starting at the highest bit where the composites differ), with per-wave
-// histograms in LDS.  As soon as the bucket holding the k-th candidate has at
-// most kBinCap members the loop stops; everything below that bucket is taken,
-// the bucket is sorted (bitonic) and its first `need` members complete the
-// set, which is then sorted (bitonic) into the output order.  Integer counts
-// only, so the result is deterministic.
+//
+// Each thread holds J candidates in registers (rank key + a way to name its
+// index).  The k-th smallest composite is located by MSB-first radix passes
+// of 11-bit digits that start at the highest bit where the keys differ; each
+// pass histograms the candidates still in play with non-returning LDS atomics
+// and one block scan picks the bucket holding the k-th.  As soon as that
+// bucket has at most kBucketCap members, every candidate at or below the
+// bucket is copied to an LDS list (two ballot sweeps, one atomic per wave),
+// and one bitonic sort orders the list; its first k entries are the answer.
+// Integer counts only, so the result is deterministic.
 #pragma once
 
 #include "gr_device.h"
 
 namespace gr {
 
-constexpr int kBinCap = 512;      // bucket size that is sorted directly
-constexpr int kMaxK = GR_MAX_K;   // 2048
+constexpr uint32_t kInvalidKey = 0xFFFFFFFFu;   // empty register slot (never a real key)
+constexpr int kHistBits = 11;
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kBucketCap = 512;
+constexpr int kListCap = 4096;                  // >= GR_MAX_K + kBucketCap, power of two
+constexpr int kMaxK = GR_MAX_K;
 
-// LDS scratch of the selection (one union: histograms during the radix
-// passes, bucket + output lists afterwards).
 template <int NT>
 struct SelectSmem {
   static constexpr int NW = NT / 64;
   union {
-    uint32_t hist[NW][256];
-    struct {
-      uint64_t bin[kBinCap];
-      uint64_t out[kMaxK];
-    } l;
+    uint32_t hist[kHistBins];
+    uint64_t list[kListCap];
   } u;
-  uint32_t wave_tot[NW];
-  uint64_t cmin, cmax, prefix;
-  int fixed_lo, need, bin_cnt, n_out, n_bin;
-  uint64_t red[NW];
-  uint64_t red2[NW];
+  uint32_t wmin[NW], wmax[NW], wtot[NW];
+  uint64_t prefix;
+  int fixed_lo, need, bucket_cnt, n_list;
 };
 
-__device__ __forceinline__ uint64_t comp_of(const uint32_t *rk, const uint32_t *ix, uint32_t base, int i) {
-  return ((uint64_t)rk[i] << 32) | (uint64_t)(ix ? ix[i] : (base + (uint32_t)i));
+__device__ __forceinline__ int pow2_ceil(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Ascending bitonic sort of arr[0..P) (P a power of two, padded with ~0).
+// Ascending bitonic sort of arr[0..P) (P a power of two).
 template <int NT>
 __device__ void bitonic_sort_u64(uint64_t *arr, int P) {
   for (int size = 2; size <= P; size <<= 1) {
@@ -66,152 +63,140 @@ __device__ void bitonic_sort_u64(uint64_t *arr, int P) {
   }
 }
 
-__device__ __forceinline__ int pow2_ceil(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
 }
 
-// Selects the k smallest composites among n candidates (rk[i], ix[i] or
-// base + i) and leaves them sorted ascending in sm.u.l.out[0..k).  Requires
-// 1 <= k <= min(n, kMaxK).  All threads of the block must call it.
-template <int NT>
-__device__ void block_select(const uint32_t *rk, const uint32_t *ix, uint32_t base, int n, int k,
-                             SelectSmem<NT> &sm) {
+// Selects the k smallest composites among the valid register candidates of
+// the block (key[j] != kInvalidKey; the index of slot j is idx_of(j)).  n_valid
+// is their number, 1 <= k <= min(n_valid, kMaxK).  On return the first k
+// entries of sm.u.list hold them in ascending order.  All threads call it.
+template <int NT, int J, typename IdxFn>
+__device__ void select_regs(const uint32_t (&key)[J], IdxFn idx_of, int n_valid, int k, SelectSmem<NT> &sm) {
+  static_assert(NT % 64 == 0 && kHistBins % NT == 0, "block size");
   constexpr int NW = NT / 64;
+  constexpr int BPT = kHistBins / NT;   // histogram bins scanned per thread
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
-  // min / max composite
-  uint64_t mn = ~0ull, mx = 0ull;
-  for (int i = tid; i < n; i += NT) {
-    const uint64_t x = comp_of(rk, ix, base, i);
-    mn = x < mn ? x : mn;
-    mx = x > mx ? x : mx;
-  }
+  // ---- range of the keys: the bits above their highest difference are common
+  uint32_t kmin = kInvalidKey, kmax = 0u;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t a = shfl_xor_u64(mn, o), b = shfl_xor_u64(mx, o);
-    mn = a < mn ? a : mn;
-    mx = b > mx ? b : mx;
+  for (int j = 0; j < J; ++j) {
+    if (key[j] != kInvalidKey) {
+      kmin = min(kmin, key[j]);
+      kmax = max(kmax, key[j]);
+    }
   }
-  if (lane == 0) { sm.red[wave] = mn; sm.red2[wave] = mx; }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) { sm.wmin[wave] = kmin; sm.wmax[wave] = kmax; }
   __syncthreads();
   if (tid == 0) {
-    uint64_t a = sm.red[0], b = sm.red2[0];
-    for (int w = 1; w < NW; ++w) {
-      a = sm.red[w] < a ? sm.red[w] : a;
-      b = sm.red2[w] > b ? sm.red2[w] : b;
-    }
-    const uint64_t diff = a ^ b;
-    const int lo = diff ? 64 - __builtin_clzll(diff) : 0;
-    sm.cmin = a;
-    sm.cmax = b;
+    uint32_t a = sm.wmin[0], b = sm.wmax[0];
+    for (int w = 1; w < NW; ++w) { a = min(a, sm.wmin[w]); b = max(b, sm.wmax[w]); }
+    const uint32_t diff = a ^ b;
+    const int lo = diff ? 64 - __builtin_clz(diff) : 32;   // key bits differ, or only the index does
     sm.fixed_lo = lo;
-    sm.prefix = lo >= 64 ? 0ull : (a & ~((1ull << lo) - 1ull));
+    sm.prefix = lo >= 64 ? 0ull : (((uint64_t)a << 32) & ~((1ull << lo) - 1ull));
     sm.need = k;
-    sm.bin_cnt = n;
+    sm.bucket_cnt = n_valid;
+    sm.n_list = 0;
   }
   __syncthreads();
 
-  // radix passes until the bucket of the k-th candidate is small
-  static_assert(NT >= 256 && NT % 64 == 0, "the bin scan needs >= 256 threads");
-  // each pass fixes up to 8 more bits of a 64-bit key: at most 8 passes
-  for (int pass = 0; pass < 8 && sm.fixed_lo > 0 && sm.bin_cnt > kBinCap && k < n; ++pass) {
+  // ---- radix passes over the bucket of the k-th candidate
+  for (int pass = 0; pass < 8; ++pass) {
     const int fixed_lo = sm.fixed_lo;
     const uint32_t need = (uint32_t)sm.need;
-    const int shift = fixed_lo > 8 ? fixed_lo - 8 : 0;
-    const int nbins = 1 << (fixed_lo - shift);
+    if (fixed_lo == 0 || sm.bucket_cnt <= kBucketCap) break;
+    const int shift = fixed_lo > kHistBits ? fixed_lo - kHistBits : 0;
+    const uint32_t mask = (1u << (fixed_lo - shift)) - 1u;
     const uint64_t pre = fixed_lo >= 64 ? 0ull : (sm.prefix >> fixed_lo);
-    for (int i = tid; i < NW * 256; i += NT) (&sm.u.hist[0][0])[i] = 0;
+    for (int i = tid; i < kHistBins; i += NT) sm.u.hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += NT) {
-      const uint64_t x = comp_of(rk, ix, base, i);
-      const uint64_t hi = fixed_lo >= 64 ? 0ull : (x >> fixed_lo);
-      if (hi == pre) atomicAdd(&sm.u.hist[wave][(int)((x >> shift) & (uint64_t)(nbins - 1))], 1u);
-    }
-    __syncthreads();
-    // bins 0..255: total over waves, inclusive scan across the block
-    uint32_t cnt = 0;
-    if (tid < 256) {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) cnt += sm.u.hist[w][tid];
+    for (int j = 0; j < J; ++j) {
+      if (key[j] != kInvalidKey) {
+        const uint64_t x = ((uint64_t)key[j] << 32) | idx_of(j);
+        const uint64_t hi = fixed_lo >= 64 ? 0ull : (x >> fixed_lo);
+        if (hi == pre) atomicAdd(&sm.u.hist[(uint32_t)(x >> shift) & mask], 1u);
+      }
     }
-    uint32_t inc = cnt;
+    __syncthreads();
+    uint32_t c[BPT], s = 0;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) { c[q] = sm.u.hist[tid * BPT + q]; s += c[q]; }
+    uint32_t inc = s;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t v = __shfl_up(inc, o);
+      const uint32_t v = (uint32_t)__shfl_up((int)inc, o);
       if (lane >= o) inc += v;
     }
-    if (lane == 63 && wave < 4) sm.wave_tot[wave] = inc;
+    if (lane == 63) sm.wtot[wave] = inc;
     __syncthreads();
-    if (tid < 256) {
-      uint32_t before_wave = 0;
-      for (int w = 0; w < wave; ++w) before_wave += sm.wave_tot[w];
-      inc += before_wave;
-      const uint32_t excl = inc - cnt;
-      if (cnt > 0 && excl < need && need <= inc) {
-        sm.need = (int)(need - excl);
-        sm.prefix |= ((uint64_t)tid) << shift;
-        sm.fixed_lo = shift;
-        sm.bin_cnt = (int)cnt;
+    uint32_t excl = inc - s;
+    for (int w = 0; w < wave; ++w) excl += sm.wtot[w];
+    if (excl < need && need <= excl + s) {
+#pragma unroll
+      for (int q = 0; q < BPT; ++q) {
+        if (c[q] > 0 && excl < need && need <= excl + c[q]) {
+          sm.need = (int)(need - excl);
+          sm.prefix |= ((uint64_t)(tid * BPT + q)) << shift;
+          sm.fixed_lo = shift;
+          sm.bucket_cnt = (int)c[q];
+        }
+        excl += c[q];
       }
     }
     __syncthreads();
   }
 
-  // compaction: everything below the bucket is taken, the bucket is sorted
+  // ---- everything at or below the bucket goes to the list
   const int fixed_lo = sm.fixed_lo;
-  const uint64_t lo_bound = sm.prefix;
-  const uint64_t hi_bound = fixed_lo >= 64 ? ~0ull : lo_bound + ((1ull << fixed_lo) - 1ull);
-  const bool take_all = k >= n;
-  if (tid == 0) { sm.n_out = 0; sm.n_bin = 0; }
-  __syncthreads();
-  for (int i0 = 0; i0 < n; i0 += NT) {
-    const int i = i0 + tid;
-    const uint64_t x = i < n ? comp_of(rk, ix, base, i) : ~0ull;
-    const bool to_out = i < n && (take_all || x < lo_bound);
-    const bool to_bin = i < n && !to_out && x <= hi_bound;
-    const uint64_t below = __lanemask_lt();
-    const uint64_t mo = __ballot(to_out), mb = __ballot(to_bin);
-    int bo = 0, bb = 0;
-    if (lane == 0) {
-      if (mo) bo = atomicAdd(&sm.n_out, (int)__popcll(mo));
-      if (mb) bb = atomicAdd(&sm.n_bin, (int)__popcll(mb));
-    }
-    bo = __shfl(bo, 0);
-    bb = __shfl(bb, 0);
-    const int so = bo + (int)__popcll(mo & below), sb = bb + (int)__popcll(mb & below);
-    if (to_out && so < kMaxK) sm.u.l.out[so] = x;
-    if (to_bin && sb < kBinCap) sm.u.l.bin[sb] = x;
+  const uint64_t hi_bound = fixed_lo >= 64 ? ~0ull : (sm.prefix | ((1ull << fixed_lo) - 1ull));
+  const uint64_t below = __lanemask_lt();
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const bool sel = key[j] != kInvalidKey && ((((uint64_t)key[j] << 32) | idx_of(j)) <= hi_bound);
+    cnt += (int)__popcll(__ballot(sel));
+  }
+  int base = 0;
+  if (lane == 0 && cnt) base = atomicAdd(&sm.n_list, cnt);
+  base = __shfl(base, 0);
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint64_t x = ((uint64_t)key[j] << 32) | idx_of(j);
+    const bool sel = key[j] != kInvalidKey && x <= hi_bound;
+    const uint64_t m = __ballot(sel);
+    const int at = base + (int)__popcll(m & below);
+    if (sel && at < kListCap) sm.u.list[at] = x;
+    base += (int)__popcll(m);
   }
   __syncthreads();
-  if (!take_all) {
-    const int nb = min(sm.n_bin, kBinCap);
-    const int P = pow2_ceil(nb);
-    for (int i = nb + tid; i < P; i += NT) sm.u.l.bin[i] = ~0ull;
-    __syncthreads();
-    bitonic_sort_u64<NT>(sm.u.l.bin, P);
-    const int off = sm.n_out;
-    const int need = sm.need;
-    for (int i = tid; i < need && i < nb && off + i < kMaxK; i += NT) sm.u.l.out[off + i] = sm.u.l.bin[i];
-    __syncthreads();
-  }
-  const int P = pow2_ceil(k);
-  for (int i = k + tid; i < P; i += NT) sm.u.l.out[i] = ~0ull;
+  const int L = min(sm.n_list, kListCap);
+  const int P = pow2_ceil(max(L, k));
+  for (int i = L + tid; i < P; i += NT) sm.u.list[i] = ~0ull;
   __syncthreads();
-  bitonic_sort_u64<NT>(sm.u.l.out, P);
+  bitonic_sort_u64<NT>(sm.u.list, P);
 }
 
 // Writes the sorted selection of k_sel candidates: the final outputs (one
 // group per request) or this group's partial list of kk entries (entries past
 // k_sel are ~0, which sorts after every real candidate).
 template <int NT>
-__device__ void emit_selection(const SelectSmem<NT> &sm, int k_sel, int r, int grp, int vocab,
-                               float *score, int32_t *token, int32_t *parent, uint64_t *partial,
-                               int n_groups, int kk) {
+__device__ void emit_selection(const SelectSmem<NT> &sm, int k_sel, int r, int grp, int vocab, float *score,
+                               int32_t *token, int32_t *parent, uint64_t *partial, int n_groups, int kk) {
   if (n_groups == 1) {
     for (int j = threadIdx.x; j < k_sel; j += NT) {
-      const uint64_t x = sm.u.l.out[j];
+      const uint64_t x = sm.u.list[j];
       const uint32_t f = (uint32_t)x;
       score[(size_t)r * k_sel + j] = key_score((uint32_t)(x >> 32));
       token[(size_t)r * k_sel + j] = (int32_t)(f % (uint32_t)vocab);
@@ -219,7 +204,7 @@ __device__ void emit_selection(const SelectSmem<NT> &sm, int k_sel, int r, int g
     }
   } else {
     for (int j = threadIdx.x; j < kk; j += NT)
-      partial[((size_t)r * n_groups + grp) * kk + j] = j < k_sel ? sm.u.l.out[j] : ~0ull;
+      partial[((size_t)r * n_groups + grp) * kk + j] = j < k_sel ? sm.u.list[j] : ~0ull;
   }
 }
 

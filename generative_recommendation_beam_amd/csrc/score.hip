@@ -7,13 +7,16 @@
 // candidate selection runs on the device, next to scoring.
 //
 // logits_select_bf16: one workgroup (8 waves) per (request, group of <= 128
-// beams).  z^T = W o^T on v_mfma_f32_32x32x16_bf16 (codes x beams; wave w
-// owns beams 32*(w/2).. and codes 128*(w%2)..), so each lane holds one beam's
-// codes and the log-softmax is in-lane plus one lane^32 swap and one LDS
-// exchange between the two code halves.  The scores never leave the chip:
-// they become ordering keys in LDS and are selected there (gr_select.h).
+// beams).  z^T = W o^T on v_mfma_f32_32x32x16_bf16 (codes x beams; wave w owns
+// beams 32*(w/2).. and codes 128*(w%2)..).  W streams through LDS in chunks of
+// 64 columns (cooperative, double-buffered loads, read once per workgroup);
+// o fragments come straight from global memory one chunk ahead.  Each lane
+// then holds 64 codes of one beam in registers: the log-softmax is in-lane
+// plus one lane^32 swap and one LDS exchange between the two code halves, and
+// the selection (gr_select.h) runs on those registers; scores never leave the
+// chip unless the caller asks for them.
 //
-// score_select: same scoring and selection starting from fp32 logits in
+// score_select: the same scoring and selection starting from fp32 logits in
 // global memory (the standalone top-k entry point, the fp32 path and scalar
 // scoring).  select_merge: final selection over per-group partial lists.
 // project: VALU projection z = o . W^T for the fp32 path and the scalar
@@ -27,10 +30,16 @@ namespace gr {
 namespace {
 
 constexpr int kNT = 512;
+constexpr int kChunk = 64;                 // W columns per LDS chunk
+constexpr int kWS = kChunk + 8;            // LDS row stride (bf16), 144 B
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 struct LogitsSmem {
-  uint32_t keys[kGroupPositions];
-  SelectSmem<kNT> sel;
+  union {
+    uint16_t w[2][256 * kWS];              // W chunks during the projection
+    SelectSmem<kNT> sel;                   // selection afterwards
+  } u;
   float red_max[4][2][32];
   float red_sum[4][2][32];
 };
@@ -56,28 +65,70 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
   const int bl = bb * 32 + c;
   const bool valid = bl < nbg;
   const int beam = b_begin + bl;
+  const int n_chunks = (p.D + kChunk - 1) / kChunk;
+
+  // cooperative W chunk loads: 256 rows x 8 pieces of 16 B = 2048 pieces
+  uint4 wreg[4];
+  auto load_w = [&](int chunk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int piece = tid + i * kNT;
+      const int row = piece >> 3, col = chunk * kChunk + (piece & 7) * 8;
+      wreg[i] = col < p.D ? *(const uint4 *)(p.W + (size_t)row * p.D + col) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_w = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int piece = tid + i * kNT;
+      *(uint4 *)&sm.u.w[buf][(piece >> 3) * kWS + (piece & 7) * 8] = wreg[i];
+    }
+  };
+  // B fragments (o) of one chunk: 4 k-steps of 16 columns
+  const uint16_t *orow = p.o + ((size_t)r * p.n_in + (valid ? beam : 0)) * p.D + 8 * g;
+  uint4 ocur[4], onext[4];
+  auto load_o = [&](int chunk, uint4 (&dst)[4]) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int col = chunk * kChunk + 16 * kk;
+      dst[kk] = (valid && col < p.D) ? *(const uint4 *)(orow + col) : make_uint4(0, 0, 0, 0);
+    }
+  };
 
   f32x16 acc[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
-  if (bb * 32 < nbg) {
-    const uint16_t *orow = p.o + ((size_t)r * p.n_in + (valid ? beam : 0)) * p.D + 8 * g;
-    const uint16_t *wrow = p.W + (size_t)(ch * 128 + c) * p.D + 8 * g;
-    const size_t wstep = (size_t)32 * p.D;
-#pragma unroll 2
-    for (int kk = 0; kk < p.D; kk += 16) {
-      const uint4 braw = valid ? *(const uint4 *)(orow + kk) : make_uint4(0, 0, 0, 0);
-      const bf16x8 b = __builtin_bit_cast(bf16x8, braw);
+
+  load_w(0);
+  load_o(0, ocur);
+  store_w(0);
+  __syncthreads();
+  for (int chunk = 0; chunk < n_chunks; ++chunk) {
+    const int buf = chunk & 1;
+    if (chunk + 1 < n_chunks) {
+      load_w(chunk + 1);
+      load_o(chunk + 1, onext);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 b = __builtin_bit_cast(bf16x8, ocur[kk]);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const bf16x8 a = *(const bf16x8 *)(wrow + m * wstep + kk);
+        const bf16x8 a = *(const bf16x8 *)&sm.u.w[buf][(ch * 128 + 32 * m + c) * kWS + 16 * kk + 8 * g];
         acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[m], 0, 0, 0);
       }
     }
+    if (chunk + 1 < n_chunks) {
+      store_w(buf ^ 1);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) ocur[kk] = onext[kk];
+    }
+    __syncthreads();
   }
 
+  // log-softmax over the 256 codes of each beam (two waves hold its halves)
   float lse = 0.f;
   if (p.lsm) {
     float mx = acc[0][0];
@@ -89,37 +140,42 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
     if (lane < 32) sm.red_max[bb][ch][c] = mx;
     __syncthreads();
     const float M = fmaxf(sm.red_max[bb][0][c], sm.red_max[bb][1][c]);
+    const float Ml = M * kLog2e;
     float se = 0.f;
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) se += expf(acc[m][i] - M);
+      for (int i = 0; i < 16; ++i) se += fast_exp2(fmaf(acc[m][i], kLog2e, -Ml));
     se += __shfl_xor(se, 32);
     if (lane < 32) sm.red_sum[bb][ch][c] = se;
     __syncthreads();
-    lse = M + logf(sm.red_sum[bb][0][c] + sm.red_sum[bb][1][c]);
+    lse = M + __builtin_amdgcn_logf(sm.red_sum[bb][0][c] + sm.red_sum[bb][1][c]) * kLn2;
   }
-  if (valid) {
-    const float pr = p.prior ? p.prior[(size_t)r * p.n_in + beam] : 0.f;
-    float *crow = p.cand ? p.cand + ((size_t)r * p.n_in + beam) * 256 : nullptr;
+
+  // candidate scores -> ordering keys in registers
+  uint32_t key[64];
+  const float pr = (valid && p.prior) ? p.prior[(size_t)r * p.n_in + beam] : 0.f;
+  float *crow = (valid && p.cand) ? p.cand + ((size_t)r * p.n_in + beam) * 256 : nullptr;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int code = ch * 128 + 32 * m + 8 * q4 + 4 * g;
-        float v[4];
+    for (int q4 = 0; q4 < 4; ++q4) {
+      float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = (acc[m][4 * q4 + e] - lse) + pr;
-          sm.keys[bl * 256 + code + e] = rank_key(v[e]);
-        }
-        if (crow) *(float4 *)(crow + code) = make_float4(v[0], v[1], v[2], v[3]);
+      for (int e = 0; e < 4; ++e) {
+        v[e] = (acc[m][4 * q4 + e] - lse) + pr;
+        key[16 * m + 4 * q4 + e] = valid ? rank_key(v[e]) : kInvalidKey;
       }
-  }
-  __syncthreads();
+      if (crow) *(float4 *)(crow + ch * 128 + 32 * m + 8 * q4 + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  const uint32_t row_base = (uint32_t)beam * 256u + ch * 128 + 4 * g;
+  auto idx_of = [&](int j) -> uint32_t {
+    return row_base + 32u * (uint32_t)(j >> 4) + 8u * (uint32_t)((j >> 2) & 3) + (uint32_t)(j & 3);
+  };
   const int n = nbg * 256;
-  block_select<kNT>(sm.keys, nullptr, (uint32_t)b_begin * 256u, n, min(p.k, n), sm.sel);
-  emit_selection<kNT>(sm.sel, min(p.k, n), r, grp, 256, p.score, p.token, p.parent, p.partial, p.n_groups, p.kk);
+  const int k_sel = min(p.k, n);
+  select_regs<kNT, 64>(key, idx_of, n, k_sel, sm.u.sel);
+  emit_selection<kNT>(sm.u.sel, k_sel, r, grp, 256, p.score, p.token, p.parent, p.partial, p.n_groups, p.kk);
 }
 
 struct SP {
@@ -132,75 +188,79 @@ struct SP {
 };
 
 struct ScoreSmem {
-  uint32_t keys[kGroupPositions];
   SelectSmem<kNT> sel;
+  float lse[kGroupBeams];
 };
 
 __global__ __launch_bounds__(kNT) void score_select_kernel(SP p) {
   __shared__ ScoreSmem sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = blockIdx.x / p.n_groups, grp = blockIdx.x % p.n_groups;
-  int n;
-  uint32_t base;
-  if (p.vocab == 256) {
-    const int b_begin = grp * kGroupBeams;
-    const int nbg = min(kGroupBeams, p.n_in - b_begin);
-    for (int row = wave; row < nbg; row += kNT / 64) {
-      const int beam = b_begin + row;
-      const size_t off = ((size_t)r * p.n_in + beam) * 256 + lane * 4;
-      const float4 z = *(const float4 *)(p.z + off);
-      float lse = 0.f;
-      if (p.lsm) {
-        const float mx = wave_max(fmaxf(fmaxf(z.x, z.y), fmaxf(z.z, z.w)));
-        const float se = wave_sum(expf(z.x - mx) + expf(z.y - mx) + expf(z.z - mx) + expf(z.w - mx));
-        lse = mx + logf(se);
-      }
-      const float pr = p.prior ? p.prior[(size_t)r * p.n_in + beam] : 0.f;
-      const float v0 = (z.x - lse) + pr, v1 = (z.y - lse) + pr;
-      const float v2 = (z.z - lse) + pr, v3 = (z.w - lse) + pr;
-      uint32_t *kr = sm.keys + row * 256 + lane * 4;
-      kr[0] = rank_key(v0); kr[1] = rank_key(v1); kr[2] = rank_key(v2); kr[3] = rank_key(v3);
-      if (p.cand) *(float4 *)(p.cand + off) = make_float4(v0, v1, v2, v3);
+  const int p0 = grp * kGroupPositions;                   // first position of the group
+  const long long total = (long long)p.n_in * p.vocab;
+  const int n = (int)min((long long)kGroupPositions, total - p0);
+  const float *zr = p.z + (size_t)r * total;
+  if (p.vocab == 256 && p.lsm) {
+    const int nrows = n / 256;
+    for (int row = wave; row < nrows; row += kNT / 64) {
+      const float4 z = *(const float4 *)(zr + (size_t)p0 + row * 256 + lane * 4);
+      const float mx = wave_max(fmaxf(fmaxf(z.x, z.y), fmaxf(z.z, z.w)));
+      const float ml = mx * kLog2e;
+      const float se = wave_sum(fast_exp2(fmaf(z.x, kLog2e, -ml)) + fast_exp2(fmaf(z.y, kLog2e, -ml)) +
+                                fast_exp2(fmaf(z.z, kLog2e, -ml)) + fast_exp2(fmaf(z.w, kLog2e, -ml)));
+      if (lane == 0) sm.lse[row] = mx + __builtin_amdgcn_logf(se) * kLn2;
     }
-    n = nbg * 256;
-    base = (uint32_t)b_begin * 256u;
-  } else {
-    const int p0 = grp * kGroupPositions;
-    n = min(kGroupPositions, p.n_in - p0);
-    for (int i = tid; i < n; i += kNT) {
-      const size_t off = (size_t)r * p.n_in + p0 + i;
-      const float v = p.z[off] + (p.prior ? p.prior[off] : 0.f);
-      sm.keys[i] = rank_key(v);
-      if (p.cand) p.cand[off] = v;
-    }
-    base = (uint32_t)p0;
+    __syncthreads();
   }
-  __syncthreads();
-  block_select<kNT>(sm.keys, nullptr, base, n, min(p.k, n), sm.sel);
-  emit_selection<kNT>(sm.sel, min(p.k, n), r, grp, p.vocab, p.score, p.token, p.parent, p.partial, p.n_groups, p.kk);
+  uint32_t key[kGroupPositions / kNT];
+#pragma unroll
+  for (int j = 0; j < kGroupPositions / kNT; ++j) {
+    const int i = j * kNT + tid;
+    key[j] = kInvalidKey;
+    if (i < n) {
+      const int pos = p0 + i;
+      const int row = pos / p.vocab;
+      float v = zr[pos];
+      if (p.vocab == 256 && p.lsm) v -= sm.lse[i >> 8];
+      if (p.prior) v += p.prior[(size_t)r * p.n_in + row];
+      key[j] = rank_key(v);
+      if (p.cand) p.cand[(size_t)r * total + pos] = v;
+    }
+  }
+  auto idx_of = [&](int j) -> uint32_t { return (uint32_t)(p0 + j * kNT + tid); };
+  const int k_sel = min(p.k, n);
+  select_regs<kNT, kGroupPositions / kNT>(key, idx_of, n, k_sel, sm.sel);
+  emit_selection<kNT>(sm.sel, k_sel, r, grp, p.vocab, p.score, p.token, p.parent, p.partial, p.n_groups, p.kk);
 }
-
-struct MergeSmem {
-  uint32_t rk[kMergeCapacity];
-  uint32_t ix[kMergeCapacity];
-  SelectSmem<kNT> sel;
-};
 
 __global__ __launch_bounds__(kNT) void select_merge_kernel(const uint64_t *partial, int n_groups, int kk, int k,
                                                            int vocab, float *score, int32_t *token,
                                                            int32_t *parent) {
-  __shared__ MergeSmem sm;
-  const int r = blockIdx.x;
+  __shared__ SelectSmem<kNT> sm;
+  constexpr int J = kMergeCapacity / kNT;
+  const int r = blockIdx.x, tid = threadIdx.x;
   const int n = n_groups * kk;
   const uint64_t *src = partial + (size_t)r * n;
-  for (int i = threadIdx.x; i < n; i += kNT) {
-    const uint64_t x = src[i];
-    sm.rk[i] = (uint32_t)(x >> 32);
-    sm.ix[i] = (uint32_t)x;
+  uint32_t key[J], ix[J];
+  uint32_t n_valid = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = j * kNT + tid;
+    const uint64_t x = i < n ? src[i] : ~0ull;
+    key[j] = (uint32_t)(x >> 32);          // group padding (~0) reads as kInvalidKey
+    ix[j] = (uint32_t)x;
+    n_valid += key[j] != kInvalidKey ? 1u : 0u;
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) n_valid += (uint32_t)__shfl_xor((int)n_valid, o);
+  if ((tid & 63) == 0) sm.wtot[tid >> 6] = n_valid;
   __syncthreads();
-  block_select<kNT>(sm.rk, sm.ix, 0u, n, k, sm.sel);
-  emit_selection<kNT>(sm.sel, k, r, 0, vocab, score, token, parent, nullptr, 1, k);
+  int tot = 0;
+  for (int w = 0; w < kNT / 64; ++w) tot += (int)sm.wtot[w];
+  __syncthreads();
+  auto idx_of = [&](int j) -> uint32_t { return ix[j]; };
+  select_regs<kNT, J>(key, idx_of, tot, k, sm);
+  emit_selection<kNT>(sm, k, r, 0, vocab, score, token, parent, nullptr, 1, k);
 }
 
 // z[row][t] = sum_i o[row][i] W[t][i] (+ prior[row] for the scalar path).

@@ -76,7 +76,18 @@ enum {
 };
 
 /* gr_beam_topk / gr_decode_step flags */
-enum { GR_TOPK_LOG_SOFTMAX = 1 };
+enum {
+  GR_TOPK_LOG_SOFTMAX = 1,
+  /* gr_decode_step only: enqueue just one stage of the step.  With neither
+   * bit (or both) the whole step runs.  ATTENTION writes the attention output
+   * into the workspace; SELECTION reads it from there, so a SELECTION call
+   * must follow an ATTENTION call with the same arguments and workspace on the
+   * same stream.  Splitting lets a caller place other work or timing events
+   * between the stages; the kernels and their arguments are the same as in
+   * the single call. */
+  GR_STEP_ATTENTION = 2,
+  GR_STEP_SELECTION = 4
+};
 
 #define GR_MAX_DEPTH 8    /* longest ancestor chain a beam may have */
 #define GR_MAX_K 2048     /* largest k (beam width / selected count) */
@@ -169,7 +180,8 @@ gr_status gr_beam_topk(int32_t R, int32_t n_in, int32_t vocab, int32_t k,
 /* gr_decode_step -- the whole step: gr_prefix_attn, then the codebook
  * projection of the current level z[r][b][t] = sum_i o[r][b][i] W[t][i]
  * (only the vocab = 256 valid codes, ASGR 4.2), then gr_beam_topk's scoring
- * and selection with k = beam_width.
+ * and selection with k = beam_width.  flags: GR_TOPK_LOG_SOFTMAX, plus the
+ * optional stage bits GR_STEP_ATTENTION / GR_STEP_SELECTION.
  *   W: [vocab][H*head_dim] dtype (row t = code t's projection vector).
  *   vocab = 1 is scalar scoring (TransRetrieval): score = o . W[0] (+ prior),
  *   flags must be 0.

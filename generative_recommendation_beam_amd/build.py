@@ -33,6 +33,7 @@ def hipcc() -> str:
 def common_flags():
     return ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wno-unused-command-line-argument",
             f"-I{INCLUDE}", f"-I{CSRC}"]
 

@@ -29,6 +29,8 @@ gr_status check_shape(const gr_shape *s) {
   // every tensor index must fit comfortably in 63 bits and grids in 31 bits
   const long long D = (long long)s->H * s->head_dim;
   if (D > 4096 || (long long)s->R * s->prompt_len * D > (1ll << 40)) return GR_ERR_SHAPE;
+  // one request's prompt is addressed with 32-bit element offsets
+  if ((long long)s->prompt_len * D >= (1ll << 31)) return GR_ERR_SHAPE;
   return GR_OK;
 }
 

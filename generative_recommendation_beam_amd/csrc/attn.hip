@@ -8,17 +8,20 @@
 //   o[b][h*hd+i] = sum_j softmax_j(scale * q.k_j) v_j[i].
 //
 // bf16 path (gfx950 MFMA).  One workgroup per (request, head, group of NW x 32
-// beams).  The prompt window of (r, h) streams through LDS in tiles of 64
-// keys; every wave of the workgroup reuses each tile for its own 32 beams, so
-// the prompt is read from HBM once per (request, head) and never copied per
-// beam.  Scores are formed transposed, S^T = K Q^T (keys x beams), with
-// v_mfma_f32_32x32x16_bf16: the accumulator then holds one beam per lane
-// column, so the softmax row reductions are in-lane plus one lane^32 swap, and
-// the probabilities are already in the B-operand layout of O^T += V^T P^T.
-// V is written to LDS transposed (d-major) with a key permutation that matches
-// the S^T accumulator order.  The chain records are walked per lane through the
-// parent array (pointer chasing, no mask tensor) and folded into the same
-// online-softmax state before the prompt tiles.
+// beams).  The prompt window of (r, h) streams from HBM straight into an
+// NS-stage LDS ring (global_load_lds_dwordx4, no register staging) in tiles
+// of 64 keys, NS-1 tiles in flight; every wave reuses each tile for its own
+// 32 beams, so the prompt is read from HBM once per (request, head) and never
+// copied per beam.  Scores are formed transposed, S^T = K Q^T (keys x beams),
+// with v_mfma_f32_32x32x16_bf16: the accumulator holds one beam per lane
+// column, so the softmax reductions are in-lane plus one lane^32 swap, and the
+// probabilities are already the B operand of O^T += V^T P^T.  The V^T operand
+// comes from the row-major V tile through ds_read_b64_tr_b16 (each 16-lane
+// group reads a 4 key x 16 dim block transposed).  Each lane fetches its 16
+// bytes from an XOR-permuted source address, so the dense LDS rows come out
+// bank-swizzled for both the K reads and the transposed V reads.  The chain
+// records are walked per lane through the parent array (pointer chasing, no
+// mask tensor) and folded into the same online-softmax state.
 //
 // fp32 path: plain VALU kernel, one thread per beam, same semantics.
 
@@ -30,6 +33,18 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+
+template <int I>
+struct Stage {
+  static constexpr int value = I;
+};
+#define GR_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+#define GR_LDS4(p) ((__attribute__((address_space(3))) i16x4 *)(p))
+
+// s_waitcnt with only the vector-memory counter constrained to <= n.
+#define GR_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
 struct AttnP {
   const uint16_t *pk, *pv, *q, *ak, *av;
   const int32_t *parent, *beam_node;
@@ -40,34 +55,59 @@ struct AttnP {
   float sl2;  // scale * log2(e)
 };
 
-// Position of tile key kk in the transposed V tile: inside each group of 16
-// keys the order is (lane group, half, 4 keys) so that a lane's 8 B-operand
-// elements of one MFMA k-step are 8 contiguous bf16.
-__device__ __forceinline__ int vt_pos(int kk) {
-  const int t = kk >> 4, w = kk & 15;
-  return (t << 4) + (((w >> 2) & 1) << 3) + ((w >> 3) << 2) + (w & 3);
-}
-
-template <int HD, int NW>
+template <int HD, int NW, int NS>
 struct Geo {
   static constexpr int KT = 64;                 // keys per tile
-  static constexpr int NT = NW * 64;            // threads
-  static constexpr int KS = HD + 8;             // K tile row stride (bf16), 16 B pad
-  static constexpr int VS = KT + 8;             // V^T tile row stride (bf16), 144 B
-  static constexpr int CPR = HD / 8;            // 16-byte chunks per row
-  static constexpr int NCH = KT * CPR;          // chunks per tile (K or V)
-  static constexpr int CPT = (NCH + NT - 1) / NT;
+  static constexpr int RB = HD * 2;             // bytes per tile row
+  static constexpr int CPR = RB / 16;           // 16-byte chunks per row
+  static constexpr int RPW = 128 / RB;          // rows per 128-byte bank window
+  static constexpr int TB = KT * RB;            // bytes per tile (K or V)
+  static constexpr int NBLK = TB / 1024;        // 1 KB DMA blocks per tile
+  static constexpr int IPW = (NBLK + NW - 1) / NW;  // DMA blocks per wave (K or V)
   static constexpr int KSTEP = HD / 16;         // MFMA k-steps over the head dim
   static constexpr int DT = HD / 32;            // 32-row d tiles of O^T
 };
 
-template <int HD, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
-  using G = Geo<HD, NW>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][G::KT * G::KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][HD * G::VS];
+// Bank swizzles (physical chunk = logical chunk ^ swizzle(row)).  K: the 8
+// lanes of one b128 read cycle read 8 consecutive rows at one logical chunk.
+// V: a 16-lane transposed read touches 4 consecutive rows (from a multiple of
+// 4) x 2 adjacent chunks.
+template <int HD>
+__device__ __forceinline__ int swz_k(int row) {
+  return HD == 64 ? (row & 7) : ((row >> 1) & 3);
+}
+template <int HD>
+__device__ __forceinline__ int swz_v(int row) {
+  return HD == 64 ? 2 * (row & 3) : 2 * ((row >> 1) & 1);
+}
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+template <int HD, int NW, int NS>
+__global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
+  using G = Geo<HD, NW, NS>;
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  // One LDS object per ring stage: the compiler then sees that a DMA into one
+  // stage does not touch the stage being read, and adds no waits for it.
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[G::TB / 2], K1[G::TB / 2], K2[NS > 2 ? G::TB / 2 : 8],
+      K3[NS > 3 ? G::TB / 2 : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[G::TB / 2], V1[G::TB / 2], V2[NS > 2 ? G::TB / 2 : 8],
+      V3[NS > 3 ? G::TB / 2 : 8];
+  auto kst = [&](auto S) -> uint16_t * {
+    constexpr int st = decltype(S)::value;
+    if constexpr (st == 0) return K0;
+    else if constexpr (st == 1) return K1;
+    else if constexpr (st == 2) return K2;
+    else return K3;
+  };
+  auto vst = [&](auto S) -> uint16_t * {
+    constexpr int st = decltype(S)::value;
+    if constexpr (st == 0) return V0;
+    else if constexpr (st == 1) return V1;
+    else if constexpr (st == 2) return V2;
+    else return V3;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, c = lane & 31;
   int bid = blockIdx.x;
   const int grp = bid % p.n_grp;
@@ -81,57 +121,59 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
   const int k_begin = p.Lp - p.Lw;
   const int n_tiles = (p.Lw + G::KT - 1) / G::KT;
 
-  uint4 kreg[G::CPT], vreg[G::CPT];
-  auto load_tile = [&](int tile) {
+  // DMA of one tile into ring stage `st`: wave w moves 1 KB blocks w*IPW..;
+  // lane l lands at byte 16*l of its block; it fetches the logical chunk that
+  // the swizzle assigns to that physical position.  Rows past the prompt end
+  // read the last prompt row (their scores are masked to -inf).
+  // per-lane tile row and (swizzled) element offsets of its DMA pieces
+  int dma_row[G::IPW];
+  uint32_t dma_k[G::IPW], dma_v[G::IPW];
 #pragma unroll
-    for (int i = 0; i < G::CPT; ++i) {
-      const int ch = tid + i * G::NT;
-      if (G::NCH % G::NT == 0 || ch < G::NCH) {
-        const int kk = ch / G::CPR, dc = ch % G::CPR;
-        const int key = k_begin + tile * G::KT + kk;
-        if (key < p.Lp) {
-          kreg[i] = *(const uint4 *)(pk + (size_t)key * row + dc * 8);
-          vreg[i] = *(const uint4 *)(pv + (size_t)key * row + dc * 8);
-        } else {
-          kreg[i] = make_uint4(0, 0, 0, 0);
-          vreg[i] = make_uint4(0, 0, 0, 0);
-        }
+  for (int i = 0; i < G::IPW; ++i) {
+    const int byte = (wave * G::IPW + i) * 1024 + 16 * lane;
+    const int tr = byte / G::RB, pch = (byte % G::RB) / 16;
+    dma_row[i] = tr;
+    dma_k[i] = (uint32_t)((pch ^ swz_k<HD>(tr)) * 8);
+    dma_v[i] = (uint32_t)((pch ^ swz_v<HD>(tr)) * 8);
+  }
+  const uint32_t row32 = (uint32_t)row;
+  auto issue = [&](int tile, auto S) {
+    const int key0 = k_begin + tile * G::KT;
+#pragma unroll
+    for (int i = 0; i < G::IPW; ++i) {
+      const int blk = wave * G::IPW + i;
+      if (blk < G::NBLK) {
+        const uint32_t src = (uint32_t)min(key0 + dma_row[i], p.Lp - 1) * row32;
+        __builtin_amdgcn_global_load_lds((const void *)(pk + (src + dma_k[i])), GR_LDS(kst(S) + blk * 512), 16, 0,
+                                         0);
+        __builtin_amdgcn_global_load_lds((const void *)(pv + (src + dma_v[i])), GR_LDS(vst(S) + blk * 512), 16, 0,
+                                         0);
       }
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < G::CPT; ++i) {
-      const int ch = tid + i * G::NT;
-      if (G::NCH % G::NT == 0 || ch < G::NCH) {
-        const int kk = ch / G::CPR, dc = ch % G::CPR;
-        *(uint4 *)&Ks[buf][kk * G::KS + dc * 8] = kreg[i];
-        const int pos = vt_pos(kk);
-        // 16-byte chunk index of this key inside a V^T row, XOR-swizzled by
-        // the row's d/8 so that rows 8 apart land in different banks.
-        const int phys = (((pos >> 3) ^ (dc & 7)) << 3) + (pos & 7);
-        const uint32_t w[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint16_t val = (e & 1) ? (uint16_t)(w[e >> 1] >> 16) : (uint16_t)(w[e >> 1] & 0xFFFFu);
-          Vt[buf][(dc * 8 + e) * G::VS + phys] = val;
-        }
-      }
-    }
+  // wait until this wave's DMAs of all but the `ahead` most recent tiles landed
+  auto wait_tiles = [&](int ahead) {
+    constexpr int per = 2 * G::IPW;
+    if (ahead >= 3) GR_WAIT_VMCNT(3 * per);
+    else if (ahead == 2) GR_WAIT_VMCNT(2 * per);
+    else if (ahead == 1) GR_WAIT_VMCNT(per);
+    else GR_WAIT_VMCNT(0);
   };
-
-  load_tile(0);
 
   // Query fragments (B operand of S^T): lane (g, c) holds beam c, head dims
   // (HD/2)*g + 8j .. +8 for k-step j.
   bf16x8 qf[G::KSTEP];
-  uint4 qraw[G::KSTEP];
   const uint16_t *qp = p.q + ((size_t)r * p.nb + (valid ? beam : 0)) * row + (size_t)h * HD + (HD / 2) * g;
 #pragma unroll
   for (int j = 0; j < G::KSTEP; ++j) {
-    qraw[j] = valid ? *(const uint4 *)(qp + 8 * j) : make_uint4(0, 0, 0, 0);
-    qf[j] = __builtin_bit_cast(bf16x8, qraw[j]);
+    const uint4 raw = valid ? *(const uint4 *)(qp + 8 * j) : make_uint4(0, 0, 0, 0);
+    qf[j] = __builtin_bit_cast(bf16x8, raw);
   }
+
+  // prologue: tiles 0 .. NS-2 in flight while the chains are walked
+  issue(0, Stage<0>{});
+  if (NS > 2 && n_tiles > 1) issue(1, Stage<1>{});
+  if (NS > 3 && n_tiles > 2) issue(2, Stage<2>{});
 
   float m_run = -__builtin_inff(), l_run = 0.f;
   f32x16 O[G::DT];
@@ -153,7 +195,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
       const uint16_t *kn = p.ak + rec + (HD / 2) * g;
       float s = 0.f;
 #pragma unroll
-      for (int j = 0; j < G::KSTEP; ++j) s += dot8_bf16(qraw[j], *(const uint4 *)(kn + 8 * j));
+      for (int j = 0; j < G::KSTEP; ++j)
+        s += dot8_bf16(__builtin_bit_cast(uint4, qf[j]), *(const uint4 *)(kn + 8 * j));
       s += __shfl_xor(s, 32);
       const float t = s * p.sl2;
       const float m_new = fmaxf(m_run, t);
@@ -179,70 +222,108 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
     if (err) atomicOr(p.dev_err, err);
   }
 
-  // ---- shared prompt window, tile by tile.
-  store_tile(0);
-  __syncthreads();
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
-    if (tile + 1 < n_tiles) load_tile(tile + 1);
-
-    f32x16 S0, S1;
+  // per-lane LDS byte offsets of the operand reads (stage base added later)
+  int koff[2][G::KSTEP];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { S0[i] = 0.f; S1[i] = 0.f; }
+  for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
     for (int j = 0; j < G::KSTEP; ++j) {
-      const bf16x8 a0 = *(const bf16x8 *)&Ks[buf][c * G::KS + (HD / 2) * g + 8 * j];
-      const bf16x8 a1 = *(const bf16x8 *)&Ks[buf][(32 + c) * G::KS + (HD / 2) * g + 8 * j];
-      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[j], S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[j], S1, 0, 0, 0);
+      const int tr = 32 * sub + c;
+      koff[sub][j] = tr * G::RB + ((((HD / 16) * g + j) ^ swz_k<HD>(tr)) << 4);
     }
-    const int key0 = k_begin + tile * G::KT;
-    if (key0 + G::KT > p.Lp) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kk = 8 * (i >> 2) + 4 * g + (i & 3);
-        if (key0 + kk >= p.Lp) S0[i] = -__builtin_inff();
-        if (key0 + 32 + kk >= p.Lp) S1[i] = -__builtin_inff();
-      }
-    }
-    float mx = fmaxf(S0[0], S1[0]);
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(S0[i], S1[i]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * p.sl2);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    float ls = 0.f;
-    uint32_t pw[16];
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const float e0 = fast_exp2(fmaf(S0[i], p.sl2, -m_new));
-      const float e1 = fast_exp2(fmaf(S0[i + 1], p.sl2, -m_new));
-      const float f0 = fast_exp2(fmaf(S1[i], p.sl2, -m_new));
-      const float f1 = fast_exp2(fmaf(S1[i + 1], p.sl2, -m_new));
-      ls += (e0 + e1) + (f0 + f1);
-      pw[i >> 1] = pack_bf16x2(e0, e1);
-      pw[8 + (i >> 1)] = pack_bf16x2(f0, f1);
-    }
-    l_run = l_run * alpha + ls;
+  int voff[G::DT][4][2];
+  {
+    const int q16 = lane >> 4, j16 = lane & 15;
 #pragma unroll
     for (int dt = 0; dt < G::DT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) O[dt][i] *= alpha;
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint4 pk4 = make_uint4(pw[4 * t], pw[4 * t + 1], pw[4 * t + 2], pw[4 * t + 3]);
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pk4);
+        for (int hh = 0; hh < 2; ++hh) {
+          const int tr = 16 * t + 8 * hh + 4 * g + (j16 >> 2);
+          const int d = 32 * dt + 16 * (q16 & 1) + 4 * (j16 & 3);
+          voff[dt][t][hh] = tr * G::RB + (((d >> 3) ^ swz_v<HD>(tr)) << 4) + ((d & 7) << 1);
+        }
+  }
+
+  // ---- shared prompt window through the LDS ring
+  auto step = [&](int t0, auto S) {
+    constexpr int st = decltype(S)::value;
+    const int tile = t0 + st;
+    if (tile < n_tiles) {
+        wait_tiles(min(NS - 2, n_tiles - 1 - tile));
+        __builtin_amdgcn_s_barrier();
+        // every wave is past tile-1: its stage can be refilled
+        if (tile + NS - 1 < n_tiles) issue(tile + NS - 1, Stage<(st + NS - 1) % NS>{});
+        const char *kb = (const char *)kst(S);
+        const char *vb = (const char *)vst(S);
+
+        f32x16 S0, S1;
 #pragma unroll
-      for (int dt = 0; dt < G::DT; ++dt) {
-        const int d = 32 * dt + c;
-        const int phys = ((2 * t + g) ^ ((d >> 3) & 7)) << 3;
-        const bf16x8 a = *(const bf16x8 *)&Vt[buf][d * G::VS + phys];
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, O[dt], 0, 0, 0);
-      }
+        for (int i = 0; i < 16; ++i) { S0[i] = 0.f; S1[i] = 0.f; }
+#pragma unroll
+        for (int j = 0; j < G::KSTEP; ++j) {
+          const bf16x8 a0 = *(const bf16x8 *)(kb + koff[0][j]);
+          const bf16x8 a1 = *(const bf16x8 *)(kb + koff[1][j]);
+          S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[j], S0, 0, 0, 0);
+          S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[j], S1, 0, 0, 0);
+        }
+        const int key0 = k_begin + tile * G::KT;
+        if (key0 + G::KT > p.Lp) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kk = 8 * (i >> 2) + 4 * g + (i & 3);
+            if (key0 + kk >= p.Lp) S0[i] = -__builtin_inff();
+            if (key0 + 32 + kk >= p.Lp) S1[i] = -__builtin_inff();
+          }
+        }
+        float mx = fmaxf(S0[0], S1[0]);
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(S0[i], S1[i]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.sl2;
+        // Exact running max: the key that sets it gets weight exactly 1, which
+        // bf16 holds exactly (it dominates a peaked softmax).  The rescale is
+        // skipped only when no lane's max grew (then alpha would be 1).
+        if (__ballot(mx > m_run)) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = fast_exp2(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) O[dt][i] *= alpha;
+        }
+        uint32_t pw[16];
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          pw[i >> 1] = pack_bf16x2(fast_exp2(fmaf(S0[i], p.sl2, -m_run)), fast_exp2(fmaf(S0[i + 1], p.sl2, -m_run)));
+          pw[8 + (i >> 1)] =
+              pack_bf16x2(fast_exp2(fmaf(S1[i], p.sl2, -m_run)), fast_exp2(fmaf(S1[i + 1], p.sl2, -m_run)));
+        }
+        // row sums of the rounded weights the PV product uses
+#pragma unroll
+        for (int i = 0; i < 16; ++i) l_run = add_bf16x2(pw[i], l_run);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint4 pk4 = make_uint4(pw[4 * t], pw[4 * t + 1], pw[4 * t + 2], pw[4 * t + 3]);
+          const bf16x8 pf = __builtin_bit_cast(bf16x8, pk4);
+#pragma unroll
+          for (int dt = 0; dt < G::DT; ++dt) {
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GR_LDS4(vb + voff[dt][t][0]));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GR_LDS4(vb + voff[dt][t][1]));
+            const i16x4 a8[2] = {lo, hi};
+            const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
+            O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, O[dt], 0, 0, 0);
+          }
+        }
     }
-    if (tile + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
+  };
+  for (int t0 = 0; t0 < n_tiles; t0 += NS) {
+    step(t0, Stage<0>{});
+    step(t0, Stage<1>{});
+    if constexpr (NS > 2) step(t0, Stage<2>{});
+    if constexpr (NS > 3) step(t0, Stage<3>{});
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -357,7 +438,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnPF p) {
   for (int i = 0; i < HD; ++i) op[i] = o[i] * inv;
 }
 
-template <int HD, int NW>
+template <int HD, int NW, int NS>
 hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
   AttnP p;
   p.pk = (const uint16_t *)a.pk; p.pv = (const uint16_t *)a.pv; p.q = (const uint16_t *)a.q;
@@ -370,16 +451,17 @@ hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
   p.n_grp = (nblk + NW - 1) / NW;
   p.sl2 = a.scale * kLog2e;
   const long long grid = (long long)a.R * a.H * p.n_grp;
-  hipLaunchKernelGGL((attn_bf16_kernel<HD, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p);
+  hipLaunchKernelGGL((attn_bf16_kernel<HD, NW, NS>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 
 template <int HD>
 hipError_t launch_bf16_nw(const AttnArgs &a, hipStream_t s) {
   const int nblk = (a.nb + 31) / 32;
-  if (nblk <= 1) return launch_bf16<HD, 1>(a, s);
-  if (nblk == 2) return launch_bf16<HD, 2>(a, s);
-  return launch_bf16<HD, 4>(a, s);
+  constexpr int NS = 4;
+  if (nblk <= 1) return launch_bf16<HD, 1, NS>(a, s);
+  if (nblk == 2) return launch_bf16<HD, 2, NS>(a, s);
+  return launch_bf16<HD, 4, NS>(a, s);
 }
 
 template <int HD>

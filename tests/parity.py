@@ -33,6 +33,7 @@ def rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
 
 def assert_close(gpu, ref, dtype: str, what: str) -> float:
     e = rel_err(gpu, ref)
+    print(f"[err] {what}: max|err|/RMS = {e:.3e} (bar {TOL[dtype]:.0e})", file=sys.stderr, flush=True)
     assert e <= TOL[dtype], f"{what}: max|err|/RMS = {e:.3e} > {TOL[dtype]:.0e}"
     return e
 

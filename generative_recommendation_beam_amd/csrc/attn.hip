@@ -85,6 +85,7 @@ template <int HD, int NW, int NS>
 __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
   using G = Geo<HD, NW, NS>;
   static_assert(NS >= 2 && NS <= 4, "ring depth");
+  static_assert(G::NBLK % NW == 0, "every wave moves the same number of 1 KB blocks");
   // One LDS object per ring stage: the compiler then sees that a DMA into one
   // stage does not touch the stage being read, and adds no waits for it.
   __shared__ __attribute__((aligned(1024))) uint16_t K0[G::TB / 2], K1[G::TB / 2], K2[NS > 2 ? G::TB / 2 : 8],
@@ -142,13 +143,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
 #pragma unroll
     for (int i = 0; i < G::IPW; ++i) {
       const int blk = wave * G::IPW + i;
-      if (blk < G::NBLK) {
-        const uint32_t src = (uint32_t)min(key0 + dma_row[i], p.Lp - 1) * row32;
-        __builtin_amdgcn_global_load_lds((const void *)(pk + (src + dma_k[i])), GR_LDS(kst(S) + blk * 512), 16, 0,
-                                         0);
-        __builtin_amdgcn_global_load_lds((const void *)(pv + (src + dma_v[i])), GR_LDS(vst(S) + blk * 512), 16, 0,
-                                         0);
-      }
+      const uint32_t src = (uint32_t)min(key0 + dma_row[i], p.Lp - 1) * row32;
+      __builtin_amdgcn_global_load_lds((const void *)(pk + (src + dma_k[i])), GR_LDS(kst(S) + blk * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(pv + (src + dma_v[i])), GR_LDS(vst(S) + blk * 512), 16, 0, 0);
     }
   };
   // wait until this wave's DMAs of all but the `ahead` most recent tiles landed
@@ -170,11 +167,6 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
     qf[j] = __builtin_bit_cast(bf16x8, raw);
   }
 
-  // prologue: tiles 0 .. NS-2 in flight while the chains are walked
-  issue(0, Stage<0>{});
-  if (NS > 2 && n_tiles > 1) issue(1, Stage<1>{});
-  if (NS > 3 && n_tiles > 2) issue(2, Stage<2>{});
-
   float m_run = -__builtin_inff(), l_run = 0.f;
   f32x16 O[G::DT];
 #pragma unroll
@@ -182,44 +174,96 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) O[t][i] = 0.f;
 
-  // ---- ancestor chain: walk parent ids from the beam's own record upward.
+  // ---- ancestor chain ids.  The parent links are chased before any prompt
+  // DMA is issued: vector loads complete in issue order, so a link fetched
+  // behind the prompt tiles would wait for all of them.
+  int ids[GR_MAX_DEPTH];
+  int cnt = 0;
+#pragma unroll
+  for (int d = 0; d < GR_MAX_DEPTH; ++d) ids[d] = -1;
   if (p.beam_node != nullptr) {
     int n = valid ? p.beam_node[(size_t)r * p.nb + beam] : -1;
     int err = 0;
     const int32_t *par = p.parent + (size_t)r * p.cap;
-    for (int depth = 0; n != -1; ++depth) {
-      if (n < 0 || n >= p.cap) { err |= GR_DEVERR_PARENT_RANGE; break; }
-      if (depth >= p.max_depth) { err |= GR_DEVERR_DEPTH; break; }
-      const int pn = par[n];
-      const size_t rec = ((size_t)r * p.cap + n) * row + (size_t)h * HD;
-      const uint16_t *kn = p.ak + rec + (HD / 2) * g;
-      float s = 0.f;
 #pragma unroll
-      for (int j = 0; j < G::KSTEP; ++j)
-        s += dot8_bf16(__builtin_bit_cast(uint4, qf[j]), *(const uint4 *)(kn + 8 * j));
-      s += __shfl_xor(s, 32);
-      const float t = s * p.sl2;
-      const float m_new = fmaxf(m_run, t);
-      const float alpha = fast_exp2(m_run - m_new);
-      const float pr = fast_exp2(t - m_new);
-      l_run = l_run * alpha + (g == 0 ? pr : 0.f);
-      const uint16_t *vn = p.av + rec;
-#pragma unroll
-      for (int dt = 0; dt < G::DT; ++dt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const uint2 vv = *(const uint2 *)(vn + 32 * dt + 8 * q4 + 4 * g);
-          O[dt][4 * q4 + 0] = fmaf(pr, bf16_lo(vv.x), O[dt][4 * q4 + 0] * alpha);
-          O[dt][4 * q4 + 1] = fmaf(pr, bf16_hi(vv.x), O[dt][4 * q4 + 1] * alpha);
-          O[dt][4 * q4 + 2] = fmaf(pr, bf16_lo(vv.y), O[dt][4 * q4 + 2] * alpha);
-          O[dt][4 * q4 + 3] = fmaf(pr, bf16_hi(vv.y), O[dt][4 * q4 + 3] * alpha);
+    for (int d = 0; d < GR_MAX_DEPTH; ++d) {
+      if (n != -1) {
+        if (n < 0 || n >= p.cap) {
+          err |= GR_DEVERR_PARENT_RANGE; n = -1;
+        } else if (d >= p.max_depth) {
+          err |= GR_DEVERR_DEPTH; n = -1;
+        } else {
+          const int pn = par[n];
+          ids[d] = n;
+          cnt = d + 1;
+          if (pn < -1 || pn >= p.cap) { err |= GR_DEVERR_PARENT_RANGE; n = -1; }
+          else if (pn >= n) { err |= GR_DEVERR_PARENT_ORDER; n = -1; }
+          else n = pn;
         }
-      m_run = m_new;
-      if (pn < -1 || pn >= p.cap) { err |= GR_DEVERR_PARENT_RANGE; break; }
-      if (pn >= n) { err |= GR_DEVERR_PARENT_ORDER; break; }
-      n = pn;
+      }
     }
+    if (n != -1) err |= GR_DEVERR_DEPTH;
     if (err) atomicOr(p.dev_err, err);
+  }
+
+  // ---- chain records, CH at a time.  The first batch is requested together
+  // with the prompt prologue.  Lanes past their chain read their own query
+  // row instead (a cache hit, no extra HBM traffic).
+  constexpr int CH = 4;
+  const size_t qrow = ((size_t)r * p.nb + (valid ? beam : 0)) * row + (size_t)h * HD;
+#pragma unroll
+  for (int d0 = 0; d0 < GR_MAX_DEPTH; d0 += CH) {
+    if (d0 == 0 || __ballot(cnt > d0)) {
+      uint4 kr[CH][G::KSTEP];
+      uint2 vr[CH][G::DT][4];
+#pragma unroll
+      for (int c4 = 0; c4 < CH; ++c4) {
+        const int n = ids[d0 + c4];
+        const uint16_t *kb = n >= 0 ? p.ak + ((size_t)r * p.cap + n) * row + (size_t)h * HD : p.q + qrow;
+        const uint16_t *vb = n >= 0 ? p.av + ((size_t)r * p.cap + n) * row + (size_t)h * HD : p.q + qrow;
+#pragma unroll
+        for (int j = 0; j < G::KSTEP; ++j) kr[c4][j] = *(const uint4 *)(kb + (HD / 2) * g + 8 * j);
+#pragma unroll
+        for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) vr[c4][dt][q4] = *(const uint2 *)(vb + 32 * dt + 8 * q4 + 4 * g);
+      }
+      if (d0 == 0) {
+        // prologue: tiles 0 .. NS-2 in flight, issued without a branch (a
+        // tile past the window reads the last prompt row and is never used;
+        // the first tile's wait covers it).
+        issue(0, Stage<0>{});
+        if constexpr (NS > 2) issue(1, Stage<1>{});
+        if constexpr (NS > 3) issue(2, Stage<2>{});
+        // keep the whole prologue ahead of the first wait for the records
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int c4 = 0; c4 < CH; ++c4) {
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < G::KSTEP; ++j) s += dot8_bf16(__builtin_bit_cast(uint4, qf[j]), kr[c4][j]);
+        s = xor32_sum(s);
+        if (d0 + c4 < cnt) {
+          const float t = s * p.sl2;
+          const float m_new = fmaxf(m_run, t);
+          const float alpha = fast_exp2(m_run - m_new);
+          const float pr = fast_exp2(t - m_new);
+          l_run = l_run * alpha + (g == 0 ? pr : 0.f);
+#pragma unroll
+          for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const uint2 vv = vr[c4][dt][q4];
+              O[dt][4 * q4 + 0] = fmaf(pr, bf16_lo(vv.x), O[dt][4 * q4 + 0] * alpha);
+              O[dt][4 * q4 + 1] = fmaf(pr, bf16_hi(vv.x), O[dt][4 * q4 + 1] * alpha);
+              O[dt][4 * q4 + 2] = fmaf(pr, bf16_lo(vv.y), O[dt][4 * q4 + 2] * alpha);
+              O[dt][4 * q4 + 3] = fmaf(pr, bf16_hi(vv.y), O[dt][4 * q4 + 3] * alpha);
+            }
+          m_run = m_new;
+        }
+      }
+    }
   }
 
   // per-lane LDS byte offsets of the operand reads (stage base added later)
@@ -277,10 +321,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
             if (key0 + 32 + kk >= p.Lp) S1[i] = -__builtin_inff();
           }
         }
-        float mx = fmaxf(S0[0], S1[0]);
+        // IEEE maximum (v_maximum3_f32): no operand canonicalisation needed
+        float mx = __builtin_elementwise_maximum(S0[0], S1[0]);
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(S0[i], S1[i]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.sl2;
+        for (int i = 1; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(S0[i], S1[i]));
+        mx = xor32_max(mx) * p.sl2;
         // Exact running max: the key that sets it gets weight exactly 1, which
         // bf16 holds exactly (it dominates a peaked softmax).  The rescale is
         // skipped only when no lane's max grew (then alpha would be 1).
@@ -326,7 +371,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
     if constexpr (NS > 3) step(t0, Stage<3>{});
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = xor32_sum(l_run);
   if (!valid) return;
   const float inv = 1.f / l_tot;
   const size_t obase = ((size_t)r * p.nb + beam) * row + (size_t)h * HD;

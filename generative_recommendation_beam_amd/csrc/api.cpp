@@ -77,8 +77,14 @@ gr_status check_select(int R, int n_in, int vocab, int k, int flags) {
   return GR_OK;
 }
 
+// bf16 attention: resolved chain ids ([R][GR_MAX_DEPTH][beams padded to whole
+// workgroups] int32), written by the chain-resolve kernel each call
+size_t attn_ids_bytes(const gr_shape *s, int n_beams) {
+  return s->dtype == GR_BF16 ? align_up(gr::attn_ids_bytes(s->R, n_beams)) : 0;
+}
+
 struct DecodeLayout {
-  size_t o_off, o_bytes, z_off, z_bytes, part_off, part_bytes, total;
+  size_t o_off, o_bytes, z_off, z_bytes, part_off, part_bytes, ids_off, ids_bytes, total;
 };
 DecodeLayout decode_layout(const gr_shape *s, int n_beams, int vocab, int k) {
   DecodeLayout L;
@@ -94,7 +100,9 @@ DecodeLayout decode_layout(const gr_shape *s, int n_beams, int vocab, int k) {
   L.o_off = 0;
   L.z_off = L.o_off + L.o_bytes;
   L.part_off = L.z_off + L.z_bytes;
-  L.total = L.part_off + L.part_bytes + kAlign;  // slack for aligning ws
+  L.ids_bytes = attn_ids_bytes(s, n_beams);
+  L.ids_off = L.part_off + L.part_bytes;
+  L.total = L.ids_off + L.ids_bytes + kAlign;  // slack for aligning ws
   return L;
 }
 
@@ -182,9 +190,9 @@ const char *gr_status_string(gr_status s) {
 }
 
 size_t gr_attn_workspace_size(const gr_shape *shape, int32_t n_beams) {
-  (void)shape;
-  (void)n_beams;
-  return 0;
+  if (check_shape(shape) || n_beams <= 0) return 0;
+  const size_t b = attn_ids_bytes(shape, n_beams);
+  return b ? b + kAlign : 0;
 }
 
 size_t gr_topk_workspace_size(int32_t R, int32_t n_in, int32_t vocab, int32_t k) {
@@ -238,14 +246,16 @@ gr_status gr_trie_append(const gr_shape *shape, const gr_trie *trie, int32_t bas
 gr_status gr_prefix_attn(const gr_shape *shape, const void *prompt_k, const void *prompt_v, const void *q,
                          int32_t n_beams, const gr_trie *trie, const int32_t *beam_node, float *out, void *ws,
                          size_t ws_bytes, int32_t *dev_err, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   gr_status st = attn_common(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, dev_err);
   if (st) return st;
   if (!out) return GR_ERR_NULL;
   if (!aligned16(out)) return GR_ERR_UNSUPPORTED;
   gr::AttnArgs a = attn_args(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, dev_err);
   a.out_f32 = out;
+  if (beam_node && attn_ids_bytes(shape, n_beams)) {
+    if (!ws || ws_bytes < gr_attn_workspace_size(shape, n_beams)) return GR_ERR_WORKSPACE;
+    a.chain_ids = (int32_t *)align_ptr(ws);
+  }
   clear_stale_error();
   return hip_status(gr::launch_attn(a, stream));
 }
@@ -302,6 +312,7 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void
   const gr::SelectOut so = make_out(out_score, out_token, out_parent, part, R, n_beams, vocab, beam_width);
 
   gr::AttnArgs a = attn_args(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, dev_err);
+  a.chain_ids = L.ids_bytes ? (int32_t *)(base + L.ids_off) : nullptr;
   const bool mfma_logits = shape->dtype == GR_BF16 && vocab == 256;
   const float *o_f32 = nullptr;
   if (mfma_logits) {

@@ -1,27 +1,39 @@
 // Attention of every beam over the shared prompt plus its own ancestor chain.
 //
 // Per request r, beam b, head h (Engineering Exploration of Generative Recall,
-// 4.1 attention steps, 4.4 tree-aware mask, 4.5 window; TransRetrieval,
-// Hardware-aware inference optimization: one user cache for all candidates;
-// OneLA, Abstract: shared prompt + append-only records + ancestry index):
+// 4.1 Superman Optimizer: QK^T, scale, softmax, weighted sum; 4.4 Tree-Based
+// Attention: a beam sees only its own branch; 4.5 Sliding-Window Attention;
+// TransRetrieval, Hardware-aware inference optimization: one user cache for
+// all candidates; OneLA, Abstract: shared prompt + append-only records + an
+// ancestry index):
 //   keys = prompt rows [Lp-Lw, Lp) then the records on chain(beam_node[b]),
 //   o[b][h*hd+i] = sum_j softmax_j(scale * q.k_j) v_j[i].
 //
-// bf16 path (gfx950 MFMA).  One workgroup per (request, head, group of NW x 32
-// beams).  The prompt window of (r, h) streams from HBM straight into an
-// NS-stage LDS ring (global_load_lds_dwordx4, no register staging) in tiles
-// of 64 keys, NS-1 tiles in flight; every wave reuses each tile for its own
-// 32 beams, so the prompt is read from HBM once per (request, head) and never
-// copied per beam.  Scores are formed transposed, S^T = K Q^T (keys x beams),
-// with v_mfma_f32_32x32x16_bf16: the accumulator holds one beam per lane
-// column, so the softmax reductions are in-lane plus one lane^32 swap, and the
+// bf16 path (gfx950 MFMA), two kernels.
+//
+// chain_resolve: one thread per beam follows the parent links from the beam's
+// own record to the root (checking range, order and depth) and stores the
+// node ids level-major, [r][level][beam].  This is the ancestry index of the
+// step: the attention kernel never chases a pointer.
+//
+// attn_bf16: one workgroup per (request, head, group of NW x 32 beams).
+// Everything the workgroup reads goes HBM -> LDS with global_load_lds_dwordx4
+// through one NS-stage ring of 64-row tiles, NS-1 tiles in flight: first the
+// chain ids and the queries, then the prompt window (read from HBM once per
+// (request, head), never copied per beam), then the chain records gathered
+// row by row (one tile per chain level and 64 beams).  Vector loads complete
+// in issue order, so keeping every load on this one in-order stream makes each
+// wait exact and keeps the ring full while the chain is processed.
+//
+// Scores are formed transposed, S^T = K Q^T (keys x beams), with
+// v_mfma_f32_32x32x16_bf16: the accumulator holds one beam per lane column,
+// so the softmax reductions are in-lane plus one lane^32 swap, and the
 // probabilities are already the B operand of O^T += V^T P^T.  The V^T operand
-// comes from the row-major V tile through ds_read_b64_tr_b16 (each 16-lane
-// group reads a 4 key x 16 dim block transposed).  Each lane fetches its 16
-// bytes from an XOR-permuted source address, so the dense LDS rows come out
-// bank-swizzled for both the K reads and the transposed V reads.  The chain
-// records are walked per lane through the parent array (pointer chasing, no
-// mask tensor) and folded into the same online-softmax state.
+// comes from the row-major V tile through ds_read_b64_tr_b16.  Each lane
+// fetches its 16 bytes from an XOR-permuted source address, so LDS rows come
+// out bank-swizzled for both the K reads and the transposed V reads.  Chain
+// records (one distinct key per beam) are folded into the same online-softmax
+// state on the VALU.
 //
 // fp32 path: plain VALU kernel, one thread per beam, same semantics.
 
@@ -45,27 +57,92 @@ struct Stage {
 // s_waitcnt with only the vector-memory counter constrained to <= n.
 #define GR_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
+// One global_load_lds_dwordx4: lane l's 16 bytes at src land at LDS byte
+// lds + 16*l (lds wave-uniform).  Written as inline asm so that the compiler
+// does not track these LDS writes: its own wait insertion would otherwise
+// turn into vmcnt(0) before every LDS read once several ring stages have DMAs
+// in flight.  Every read of DMA'd data is instead preceded by an explicit
+// vmcnt wait and a barrier (ring_barrier below).  No VGPR is written, so
+// nothing is left for the compiler to misjudge.  M0 (reserved by the
+// compiler) is saved and restored around the load, and needs one wait state
+// before the load reads it.
+__device__ __forceinline__ void dma16(const void *src, const void *lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)GR_LDS(lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(src)
+      : "memory");
+}
+// Workgroup barrier that also keeps the compiler from moving LDS reads above
+// it (DMA'd data is only valid past the wait + barrier).
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ------------------------------------------------------------ chain resolve
+struct ChainP {
+  const int32_t *parent, *beam_node;
+  int32_t *ids;        // [R][D][nb_pad]
+  int32_t *dev_err;
+  int R, nb, nb_pad, cap, D;
+};
+
+__global__ __launch_bounds__(256) void chain_resolve_kernel(ChainP p) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)p.R * p.nb_pad) return;
+  const int r = (int)(i / p.nb_pad), b = (int)(i % p.nb_pad);
+  const int32_t *par = p.parent + (size_t)r * p.cap;
+  int32_t *out = p.ids + (size_t)r * p.D * p.nb_pad + b;
+  int n = b < p.nb ? p.beam_node[(size_t)r * p.nb + b] : -1;
+  int err = 0;
+  for (int d = 0; d < p.D; ++d) {
+    int id = -1;
+    if (n != -1) {
+      if (n < 0 || n >= p.cap) {
+        err |= GR_DEVERR_PARENT_RANGE;
+        n = -1;
+      } else {
+        id = n;
+        const int pn = par[n];
+        if (pn < -1 || pn >= p.cap) { err |= GR_DEVERR_PARENT_RANGE; n = -1; }
+        else if (pn >= n) { err |= GR_DEVERR_PARENT_ORDER; n = -1; }
+        else n = pn;
+      }
+    }
+    out[(size_t)d * p.nb_pad] = id;
+  }
+  if (n != -1) err |= GR_DEVERR_DEPTH;   // longer than max_depth
+  if (err) atomicOr(p.dev_err, err);
+}
+
+// ------------------------------------------------------------ bf16 attention
 struct AttnP {
   const uint16_t *pk, *pv, *q, *ak, *av;
-  const int32_t *parent, *beam_node;
+  const int32_t *ids;  // [R][D][nb_pad] from chain_resolve, or null (prompt only)
   float *out_f32;
   uint16_t *out_bf16;
-  int32_t *dev_err;
-  int R, H, Lp, Lw, nb, cap, max_depth, n_grp;
+  int R, H, Lp, Lw, nb, cap, D, nb_pad, n_grp;
   float sl2;  // scale * log2(e)
 };
 
 template <int HD, int NW, int NS>
 struct Geo {
-  static constexpr int KT = 64;                 // keys per tile
+  static constexpr int KT = 64;                 // rows per tile
   static constexpr int RB = HD * 2;             // bytes per tile row
-  static constexpr int CPR = RB / 16;           // 16-byte chunks per row
-  static constexpr int RPW = 128 / RB;          // rows per 128-byte bank window
   static constexpr int TB = KT * RB;            // bytes per tile (K or V)
   static constexpr int NBLK = TB / 1024;        // 1 KB DMA blocks per tile
-  static constexpr int IPW = (NBLK + NW - 1) / NW;  // DMA blocks per wave (K or V)
+  static constexpr int IPW = NBLK / NW;         // DMA blocks per wave (K or V)
   static constexpr int KSTEP = HD / 16;         // MFMA k-steps over the head dim
   static constexpr int DT = HD / 32;            // 32-row d tiles of O^T
+  static constexpr int NB = NW * 32;            // beams per workgroup
+  static constexpr int NRB = (NB + KT - 1) / KT;  // record tiles per chain level
 };
 
 // Bank swizzles (physical chunk = logical chunk ^ swizzle(row)).  K: the 8
@@ -84,49 +161,52 @@ __device__ __forceinline__ int swz_v(int row) {
 template <int HD, int NW, int NS>
 __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
   using G = Geo<HD, NW, NS>;
-  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  static_assert(NS == 4, "ring depth: stage 3 carries the queries until tile 3 is requested");
   static_assert(G::NBLK % NW == 0, "every wave moves the same number of 1 KB blocks");
-  // One LDS object per ring stage: the compiler then sees that a DMA into one
-  // stage does not touch the stage being read, and adds no waits for it.
-  __shared__ __attribute__((aligned(1024))) uint16_t K0[G::TB / 2], K1[G::TB / 2], K2[NS > 2 ? G::TB / 2 : 8],
-      K3[NS > 3 ? G::TB / 2 : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t V0[G::TB / 2], V1[G::TB / 2], V2[NS > 2 ? G::TB / 2 : 8],
-      V3[NS > 3 ? G::TB / 2 : 8];
+  static_assert(G::NB <= 2 * G::KT, "queries of a workgroup fit the two buffers of one stage");
+  // One LDS object per ring stage (its K half, then its V half): the
+  // compiler then sees that a DMA into one stage does not touch the stage
+  // being read, and adds no waits for it.  (It tells apart only a few LDS
+  // DMA targets, so there are just five: four stages and the chain ids.)
+  __shared__ __attribute__((aligned(1024))) uint16_t KV0[G::TB], KV1[G::TB], KV2[G::TB], KV3[G::TB];
+  __shared__ __attribute__((aligned(1024))) int32_t ids_s[GR_MAX_DEPTH * G::NB];
   auto kst = [&](auto S) -> uint16_t * {
     constexpr int st = decltype(S)::value;
-    if constexpr (st == 0) return K0;
-    else if constexpr (st == 1) return K1;
-    else if constexpr (st == 2) return K2;
-    else return K3;
+    if constexpr (st == 0) return KV0;
+    else if constexpr (st == 1) return KV1;
+    else if constexpr (st == 2) return KV2;
+    else return KV3;
   };
-  auto vst = [&](auto S) -> uint16_t * {
-    constexpr int st = decltype(S)::value;
-    if constexpr (st == 0) return V0;
-    else if constexpr (st == 1) return V1;
-    else if constexpr (st == 2) return V2;
-    else return V3;
-  };
+  auto vst = [&](auto S) -> uint16_t * { return kst(S) + G::TB / 2; };
+  uint16_t *const K3 = KV3, *const V3 = KV3 + G::TB / 2;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, c = lane & 31;
+  // Consecutive workgroup ids go to the 8 XCDs in turn; give each XCD a
+  // contiguous range of (request, head) units so that the heads of one
+  // request stream their interleaved prompt rows from one L2 at about the
+  // same time.
   int bid = blockIdx.x;
+  if ((gridDim.x & 7) == 0) bid = (bid & 7) * (int)(gridDim.x >> 3) + (bid >> 3);
   const int grp = bid % p.n_grp;
   bid /= p.n_grp;
   const int h = bid % p.H, r = bid / p.H;
-  const int beam = (grp * NW + wave) * 32 + c;
+  const int wb = wave * 32 + c;                 // workgroup-local beam of this lane
+  const int beam = grp * G::NB + wb;
   const bool valid = beam < p.nb;
   const size_t row = (size_t)p.H * HD;          // elements between tokens
+  const uint32_t row32 = (uint32_t)row;
   const uint16_t *pk = p.pk + (size_t)r * p.Lp * row + (size_t)h * HD;
   const uint16_t *pv = p.pv + (size_t)r * p.Lp * row + (size_t)h * HD;
   const int k_begin = p.Lp - p.Lw;
   const int n_tiles = (p.Lw + G::KT - 1) / G::KT;
+  const int n_pre = max(n_tiles, NS - 1);       // prompt tiles, padded to fill the prologue
+  int n_total = n_pre;                          // + chain-record tiles, known after tile 0
 
-  // DMA of one tile into ring stage `st`: wave w moves 1 KB blocks w*IPW..;
-  // lane l lands at byte 16*l of its block; it fetches the logical chunk that
-  // the swizzle assigns to that physical position.  Rows past the prompt end
-  // read the last prompt row (their scores are masked to -inf).
-  // per-lane tile row and (swizzled) element offsets of its DMA pieces
+  // Per-lane tile row and (swizzled) element offsets of this lane's DMA
+  // pieces: wave w moves 1 KB blocks w*IPW..; lane l lands at byte 16*l of its
+  // block and fetches the logical chunk the swizzle assigns to that position.
   int dma_row[G::IPW];
   uint32_t dma_k[G::IPW], dma_v[G::IPW];
 #pragma unroll
@@ -137,134 +217,73 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
     dma_k[i] = (uint32_t)((pch ^ swz_k<HD>(tr)) * 8);
     dma_v[i] = (uint32_t)((pch ^ swz_v<HD>(tr)) * 8);
   }
-  const uint32_t row32 = (uint32_t)row;
-  auto issue = [&](int tile, auto S) {
+  // prompt tile: rows past the window end read the last prompt row (masked
+  // or never used)
+  auto issue_prompt = [&](int tile, auto S) {
     const int key0 = k_begin + tile * G::KT;
 #pragma unroll
     for (int i = 0; i < G::IPW; ++i) {
       const int blk = wave * G::IPW + i;
       const uint32_t src = (uint32_t)min(key0 + dma_row[i], p.Lp - 1) * row32;
-      __builtin_amdgcn_global_load_lds((const void *)(pk + (src + dma_k[i])), GR_LDS(kst(S) + blk * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(pv + (src + dma_v[i])), GR_LDS(vst(S) + blk * 512), 16, 0, 0);
+      dma16(pk + (src + dma_k[i]), kst(S) + blk * 512);
+      dma16(pv + (src + dma_v[i]), vst(S) + blk * 512);
+    }
+  };
+  // chain-record tile: row t holds the level-d record of workgroup beam
+  // 64*bb + t (a beam without one reads record 0 of the request, unused)
+  auto issue_records = [&](int d, int bb, auto S) {
+#pragma unroll
+    for (int i = 0; i < G::IPW; ++i) {
+      const int blk = wave * G::IPW + i;
+      const int b = bb * G::KT + dma_row[i];
+      const int id = b < G::NB ? ids_s[d * G::NB + b] : -1;
+      const size_t src = ((size_t)r * p.cap + (id >= 0 ? id : 0)) * row + (size_t)h * HD;
+      dma16(p.ak + src + dma_k[i], kst(S) + blk * 512);
+      dma16(p.av + src + dma_v[i], vst(S) + blk * 512);
+    }
+  };
+  auto issue = [&](int tile, auto S) {
+    if (tile < n_pre) {
+      issue_prompt(tile, S);
+    } else {
+      const int k = tile - n_pre;
+      issue_records(k / G::NRB, k % G::NRB, S);
     }
   };
   // wait until this wave's DMAs of all but the `ahead` most recent tiles landed
   auto wait_tiles = [&](int ahead) {
     constexpr int per = 2 * G::IPW;
-    if (ahead >= 3) GR_WAIT_VMCNT(3 * per);
-    else if (ahead == 2) GR_WAIT_VMCNT(2 * per);
+    if (ahead >= 2) GR_WAIT_VMCNT(2 * per);
     else if (ahead == 1) GR_WAIT_VMCNT(per);
     else GR_WAIT_VMCNT(0);
   };
 
-  // Query fragments (B operand of S^T): lane (g, c) holds beam c, head dims
-  // (HD/2)*g + 8j .. +8 for k-step j.
-  bf16x8 qf[G::KSTEP];
-  const uint16_t *qp = p.q + ((size_t)r * p.nb + (valid ? beam : 0)) * row + (size_t)h * HD + (HD / 2) * g;
-#pragma unroll
-  for (int j = 0; j < G::KSTEP; ++j) {
-    const uint4 raw = valid ? *(const uint4 *)(qp + 8 * j) : make_uint4(0, 0, 0, 0);
-    qf[j] = __builtin_bit_cast(bf16x8, raw);
-  }
-
-  float m_run = -__builtin_inff(), l_run = 0.f;
-  f32x16 O[G::DT];
-#pragma unroll
-  for (int t = 0; t < G::DT; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) O[t][i] = 0.f;
-
-  // ---- ancestor chain ids.  The parent links are chased before any prompt
-  // DMA is issued: vector loads complete in issue order, so a link fetched
-  // behind the prompt tiles would wait for all of them.
-  int ids[GR_MAX_DEPTH];
-  int cnt = 0;
-#pragma unroll
-  for (int d = 0; d < GR_MAX_DEPTH; ++d) ids[d] = -1;
-  if (p.beam_node != nullptr) {
-    int n = valid ? p.beam_node[(size_t)r * p.nb + beam] : -1;
-    int err = 0;
-    const int32_t *par = p.parent + (size_t)r * p.cap;
-#pragma unroll
-    for (int d = 0; d < GR_MAX_DEPTH; ++d) {
-      if (n != -1) {
-        if (n < 0 || n >= p.cap) {
-          err |= GR_DEVERR_PARENT_RANGE; n = -1;
-        } else if (d >= p.max_depth) {
-          err |= GR_DEVERR_DEPTH; n = -1;
-        } else {
-          const int pn = par[n];
-          ids[d] = n;
-          cnt = d + 1;
-          if (pn < -1 || pn >= p.cap) { err |= GR_DEVERR_PARENT_RANGE; n = -1; }
-          else if (pn >= n) { err |= GR_DEVERR_PARENT_ORDER; n = -1; }
-          else n = pn;
-        }
-      }
-    }
-    if (n != -1) err |= GR_DEVERR_DEPTH;
-    if (err) atomicOr(p.dev_err, err);
-  }
-
-  // ---- chain records, CH at a time.  The first batch is requested together
-  // with the prompt prologue.  Lanes past their chain read their own query
-  // row instead (a cache hit, no extra HBM traffic).
-  constexpr int CH = 4;
-  const size_t qrow = ((size_t)r * p.nb + (valid ? beam : 0)) * row + (size_t)h * HD;
-#pragma unroll
-  for (int d0 = 0; d0 < GR_MAX_DEPTH; d0 += CH) {
-    if (d0 == 0 || __ballot(cnt > d0)) {
-      uint4 kr[CH][G::KSTEP];
-      uint2 vr[CH][G::DT][4];
-#pragma unroll
-      for (int c4 = 0; c4 < CH; ++c4) {
-        const int n = ids[d0 + c4];
-        const uint16_t *kb = n >= 0 ? p.ak + ((size_t)r * p.cap + n) * row + (size_t)h * HD : p.q + qrow;
-        const uint16_t *vb = n >= 0 ? p.av + ((size_t)r * p.cap + n) * row + (size_t)h * HD : p.q + qrow;
-#pragma unroll
-        for (int j = 0; j < G::KSTEP; ++j) kr[c4][j] = *(const uint4 *)(kb + (HD / 2) * g + 8 * j);
-#pragma unroll
-        for (int dt = 0; dt < G::DT; ++dt)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) vr[c4][dt][q4] = *(const uint2 *)(vb + 32 * dt + 8 * q4 + 4 * g);
-      }
-      if (d0 == 0) {
-        // prologue: tiles 0 .. NS-2 in flight, issued without a branch (a
-        // tile past the window reads the last prompt row and is never used;
-        // the first tile's wait covers it).
-        issue(0, Stage<0>{});
-        if constexpr (NS > 2) issue(1, Stage<1>{});
-        if constexpr (NS > 3) issue(2, Stage<2>{});
-        // keep the whole prologue ahead of the first wait for the records
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int c4 = 0; c4 < CH; ++c4) {
-        float s = 0.f;
-#pragma unroll
-        for (int j = 0; j < G::KSTEP; ++j) s += dot8_bf16(__builtin_bit_cast(uint4, qf[j]), kr[c4][j]);
-        s = xor32_sum(s);
-        if (d0 + c4 < cnt) {
-          const float t = s * p.sl2;
-          const float m_new = fmaxf(m_run, t);
-          const float alpha = fast_exp2(m_run - m_new);
-          const float pr = fast_exp2(t - m_new);
-          l_run = l_run * alpha + (g == 0 ? pr : 0.f);
-#pragma unroll
-          for (int dt = 0; dt < G::DT; ++dt)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              const uint2 vv = vr[c4][dt][q4];
-              O[dt][4 * q4 + 0] = fmaf(pr, bf16_lo(vv.x), O[dt][4 * q4 + 0] * alpha);
-              O[dt][4 * q4 + 1] = fmaf(pr, bf16_hi(vv.x), O[dt][4 * q4 + 1] * alpha);
-              O[dt][4 * q4 + 2] = fmaf(pr, bf16_lo(vv.y), O[dt][4 * q4 + 2] * alpha);
-              O[dt][4 * q4 + 3] = fmaf(pr, bf16_hi(vv.y), O[dt][4 * q4 + 3] * alpha);
-            }
-          m_run = m_new;
-        }
-      }
+  // ---- prologue, in stream order: chain ids (wave 0), the queries of the
+  // workgroup into stage 3 (K3: beams 0..63, V3: beams 64..127, K-swizzled
+  // rows), then prompt tiles 0..2.
+  if (p.ids != nullptr && wave == 0) {
+    const int words = p.D * G::NB;
+    const int32_t *src0 = p.ids + (size_t)r * p.D * p.nb_pad + (size_t)grp * G::NB;
+    for (int i = 0; i * 256 < words; ++i) {
+      const int e = min(i * 256 + 4 * lane, words - 4);   // 4 ids per lane
+      const int d = e / G::NB, b = e % G::NB;
+      dma16(src0 + (size_t)d * p.nb_pad + b, ids_s + i * 256);
     }
   }
+#pragma unroll
+  for (int i = 0; i < G::IPW; ++i) {
+    const int blk = wave * G::IPW + i;
+    const int b0 = grp * G::NB + dma_row[i];
+    const size_t s0 = ((size_t)r * p.nb + min(b0, p.nb - 1)) * row + (size_t)h * HD;
+    dma16(p.q + s0 + dma_k[i], K3 + blk * 512);
+    if constexpr (G::NB > G::KT) {
+      const size_t s1 = ((size_t)r * p.nb + min(b0 + G::KT, p.nb - 1)) * row + (size_t)h * HD;
+      dma16(p.q + s1 + dma_k[i], V3 + blk * 512);
+    }
+  }
+  issue_prompt(0, Stage<0>{});
+  issue_prompt(1, Stage<1>{});
+  issue_prompt(2, Stage<2>{});
 
   // per-lane LDS byte offsets of the operand reads (stage base added later)
   int koff[2][G::KSTEP];
@@ -289,19 +308,67 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
           voff[dt][t][hh] = tr * G::RB + (((d >> 3) ^ swz_v<HD>(tr)) << 4) + ((d & 7) << 1);
         }
   }
+  // this lane's row in a query / chain-record tile: row wb % 64 of tile wb / 64
+  const int my_bb = (wave * 32) / G::KT;        // wave-uniform
+  const int rrow = wb % G::KT;
+  int roff_k[G::KSTEP], roff_v[G::DT][4];
+#pragma unroll
+  for (int j = 0; j < G::KSTEP; ++j) roff_k[j] = rrow * G::RB + ((((HD / 16) * g + j) ^ swz_k<HD>(rrow)) << 4);
+#pragma unroll
+  for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      roff_v[dt][q4] = rrow * G::RB + (((4 * dt + q4) ^ swz_v<HD>(rrow)) << 4) + 8 * g;
 
-  // ---- shared prompt window through the LDS ring
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  f32x16 O[G::DT];
+#pragma unroll
+  for (int t = 0; t < G::DT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[t][i] = 0.f;
+  bf16x8 qf[G::KSTEP];  // B operand of S^T: lane (g, c) holds head dims (HD/2)*g + 8j .. +8 of its beam
+  int cnt = 0;          // chain records of this lane's beam
+
   auto step = [&](int t0, auto S) {
     constexpr int st = decltype(S)::value;
     const int tile = t0 + st;
-    if (tile < n_tiles) {
-        wait_tiles(min(NS - 2, n_tiles - 1 - tile));
-        __builtin_amdgcn_s_barrier();
-        // every wave is past tile-1: its stage can be refilled
-        if (tile + NS - 1 < n_tiles) issue(tile + NS - 1, Stage<(st + NS - 1) % NS>{});
-        const char *kb = (const char *)kst(S);
-        const char *vb = (const char *)vst(S);
+    if (tile < n_total) {
+      // at tile 0 the prologue has put exactly NS-2 tiles behind it
+      wait_tiles(tile == 0 ? NS - 2 : min(NS - 2, n_total - 1 - tile));
+      ring_barrier();
+      if constexpr (st == 0) {
+        if (tile == 0) {
+          // queries and chain ids have landed (they precede tile 0)
+          if (wave * 32 < G::KT) {
+#pragma unroll
+            for (int j = 0; j < G::KSTEP; ++j) qf[j] = *(const bf16x8 *)((const char *)K3 + roff_k[j]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < G::KSTEP; ++j) qf[j] = *(const bf16x8 *)((const char *)V3 + roff_k[j]);
+          }
+          if (p.ids != nullptr) {
+            int depth = 0;
+            for (int d = 0; d < p.D; ++d) {
+              const int own = ids_s[d * G::NB + wb];
+              cnt += own >= 0 ? 1 : 0;
+              bool any = lane < G::NB && ids_s[d * G::NB + lane] >= 0;
+              if constexpr (G::NB > 64) any = any || ids_s[d * G::NB + 64 + lane] >= 0;
+              if (__ballot(any)) depth = d + 1;
+            }
+            n_total = n_pre + depth * G::NRB;
+          }
+          // every wave holds its queries before stage 3 is refilled
+          __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+          ring_barrier();
+        }
+      }
+      // every wave is past tile-1: its stage can be refilled
+      if (tile + NS - 1 < n_total) issue(tile + NS - 1, Stage<(st + NS - 1) % NS>{});
+      const char *kb = (const char *)kst(S);
+      const char *vb = (const char *)vst(S);
 
+      if (tile < n_tiles) {
+        // ---- shared prompt window
         f32x16 S0, S1;
 #pragma unroll
         for (int i = 0; i < 16; ++i) { S0[i] = 0.f; S1[i] = 0.f; }
@@ -362,13 +429,43 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
             O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, O[dt], 0, 0, 0);
           }
         }
+      } else if (tile >= n_pre) {
+        // ---- one chain level of the beams of record tile bb
+        const int k = tile - n_pre;
+        const int d = k / G::NRB, bb = k % G::NRB;
+        if (bb == my_bb) {
+          float s = 0.f;
+#pragma unroll
+          for (int j = 0; j < G::KSTEP; ++j)
+            s += dot8_bf16(__builtin_bit_cast(uint4, qf[j]), *(const uint4 *)(kb + roff_k[j]));
+          s = xor32_sum(s);
+          if (d < cnt) {
+            const float t = s * p.sl2;
+            const float m_new = fmaxf(m_run, t);
+            const float alpha = fast_exp2(m_run - m_new);
+            const float pr = fast_exp2(t - m_new);
+            l_run = l_run * alpha + (g == 0 ? pr : 0.f);
+#pragma unroll
+            for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4) {
+                const uint2 vv = *(const uint2 *)(vb + roff_v[dt][q4]);
+                O[dt][4 * q4 + 0] = fmaf(pr, bf16_lo(vv.x), O[dt][4 * q4 + 0] * alpha);
+                O[dt][4 * q4 + 1] = fmaf(pr, bf16_hi(vv.x), O[dt][4 * q4 + 1] * alpha);
+                O[dt][4 * q4 + 2] = fmaf(pr, bf16_lo(vv.y), O[dt][4 * q4 + 2] * alpha);
+                O[dt][4 * q4 + 3] = fmaf(pr, bf16_hi(vv.y), O[dt][4 * q4 + 3] * alpha);
+              }
+            m_run = m_new;
+          }
+        }
+      }
     }
   };
-  for (int t0 = 0; t0 < n_tiles; t0 += NS) {
+  for (int t0 = 0; t0 < n_total; t0 += NS) {
     step(t0, Stage<0>{});
     step(t0, Stage<1>{});
-    if constexpr (NS > 2) step(t0, Stage<2>{});
-    if constexpr (NS > 3) step(t0, Stage<3>{});
+    step(t0, Stage<2>{});
+    step(t0, Stage<3>{});
   }
 
   const float l_tot = xor32_sum(l_run);
@@ -483,18 +580,29 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnPF p) {
   for (int i = 0; i < HD; ++i) op[i] = o[i] * inv;
 }
 
-template <int HD, int NW, int NS>
+template <int HD, int NW>
 hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
+  constexpr int NS = 4;
   AttnP p;
   p.pk = (const uint16_t *)a.pk; p.pv = (const uint16_t *)a.pv; p.q = (const uint16_t *)a.q;
   p.ak = (const uint16_t *)a.ak; p.av = (const uint16_t *)a.av;
-  p.parent = a.parent; p.beam_node = a.beam_node;
-  p.out_f32 = a.out_f32; p.out_bf16 = (uint16_t *)a.out_lowp; p.dev_err = a.dev_err;
+  p.ids = nullptr;
+  p.out_f32 = a.out_f32; p.out_bf16 = (uint16_t *)a.out_lowp;
   p.R = a.R; p.H = a.H; p.Lp = a.Lp; p.Lw = a.Lw; p.nb = a.nb; p.cap = a.cap;
-  p.max_depth = a.max_depth;
-  const int nblk = (a.nb + 31) / 32;
-  p.n_grp = (nblk + NW - 1) / NW;
+  p.D = a.max_depth;
+  p.nb_pad = attn_beam_pad(a.nb);
+  p.n_grp = p.nb_pad / (NW * 32);
   p.sl2 = a.scale * kLog2e;
+  if (a.beam_node != nullptr) {
+    ChainP c;
+    c.parent = a.parent; c.beam_node = a.beam_node; c.ids = a.chain_ids; c.dev_err = a.dev_err;
+    c.R = a.R; c.nb = a.nb; c.nb_pad = p.nb_pad; c.cap = a.cap; c.D = a.max_depth;
+    const long long n = (long long)a.R * p.nb_pad;
+    hipLaunchKernelGGL(chain_resolve_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, c);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    p.ids = a.chain_ids;
+  }
   const long long grid = (long long)a.R * a.H * p.n_grp;
   hipLaunchKernelGGL((attn_bf16_kernel<HD, NW, NS>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
@@ -502,11 +610,11 @@ hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
 
 template <int HD>
 hipError_t launch_bf16_nw(const AttnArgs &a, hipStream_t s) {
-  const int nblk = (a.nb + 31) / 32;
-  constexpr int NS = 4;
-  if (nblk <= 1) return launch_bf16<HD, 1, NS>(a, s);
-  if (nblk == 2) return launch_bf16<HD, 2, NS>(a, s);
-  return launch_bf16<HD, 4, NS>(a, s);
+  switch (attn_waves(a.nb)) {
+    case 1: return launch_bf16<HD, 1>(a, s);
+    case 2: return launch_bf16<HD, 2>(a, s);
+    default: return launch_bf16<HD, 4>(a, s);
+  }
 }
 
 template <int HD>

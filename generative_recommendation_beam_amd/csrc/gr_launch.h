@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "gr_beam.h"
+
 namespace gr {
 
 // Attention of every beam over the shared prompt window plus its own chain.
@@ -14,6 +16,7 @@ struct AttnArgs {
   const void *ak, *av;             // arena [R][cap][H][hd] (may be null if no chains)
   const int32_t *parent;           // [R][cap]
   const int32_t *beam_node;        // [R][nb] or null (prompt only)
+  int32_t *chain_ids;              // bf16 path: workspace for the resolved chains, attn_ids_bytes(R, nb)
   float *out_f32;                  // optional [R][nb][H*hd]
   void *out_lowp;                  // optional [R][nb][H*hd] in dtype (bf16 feed of the logits)
   int32_t *dev_err;
@@ -21,6 +24,21 @@ struct AttnArgs {
   float scale;
 };
 hipError_t launch_attn(const AttnArgs &a, hipStream_t s);
+
+// bf16 attention geometry: a workgroup holds NW waves of 32 beams; the chain
+// ids of a request are stored level-major, [max_depth][beams padded to whole
+// workgroups].
+inline int attn_waves(int nb) {
+  const int nblk = (nb + 31) / 32;
+  return nblk <= 1 ? 1 : (nblk == 2 ? 2 : 4);
+}
+inline int attn_beam_pad(int nb) {
+  const int per = attn_waves(nb) * 32;
+  return (nb + per - 1) / per * per;
+}
+inline size_t attn_ids_bytes(int R, int nb) {
+  return (size_t)R * GR_MAX_DEPTH * attn_beam_pad(nb) * sizeof(int32_t);
+}
 
 struct AppendArgs {
   int elem_bytes;

@@ -121,8 +121,10 @@ def upload_step(x, window=None, device="cuda", max_depth: int = L.GR_MAX_DEPTH, 
 
 def prefix_attn(ds: DeviceStep, stream=None) -> torch.Tensor:
     out = torch.empty((ds.R, ds.n_beams, ds.D), dtype=torch.float32, device=ds.q.device)
+    nbytes = L.gr_attn_workspace_size(ds.shape, ds.n_beams)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=ds.q.device)
     L.gr_prefix_attn(ds.shape, ds.prompt_k, ds.prompt_v, ds.q, ds.n_beams, ds.trie, ds.beam_node, out,
-                     None, 0, ds.dev_err, stream)
+                     ws, nbytes, ds.dev_err, stream)
     return out
 
 

@@ -72,6 +72,16 @@ def test_prefix_attn_host_errors(case, expect):
     assert attn(**case) == expect
 
 
+def test_prefix_attn_workspace():
+    """bf16 chains need the chain-id workspace; nothing is launched without it."""
+    sh, tr = shape(), trie()
+    need = L.gr_attn_workspace_size(sh, 100)
+    call = lambda ws, nbytes: L._lib.gr_prefix_attn(ctypes.byref(sh), FAKE, FAKE, FAKE, 100, ctypes.byref(tr),
+                                                    FAKE, FAKE, ws, nbytes, FAKE, None)
+    assert call(None, 0) == L.GR_ERR_WORKSPACE
+    assert call(FAKE, need - 1) == L.GR_ERR_WORKSPACE
+
+
 def topk(R=2, n_in=100, vocab=256, k=100, flags=1, logits=FAKE, out=FAKE, ws=None, ws_bytes=0):
     return L._lib.gr_beam_topk(R, n_in, vocab, k, flags, logits, None, out, FAKE, FAKE, None, ws,
                                ws_bytes, None)
@@ -129,15 +139,19 @@ def test_decode_step_host_errors():
 
 def test_workspace_sizes():
     sh = shape(R=256)
-    # bf16 codebook path: bf16 copy of o, one selection group per request
-    assert L.gr_decode_workspace_size(sh, 100, 256, 100) >= 256 * 100 * 512 * 2
-    assert L.gr_decode_workspace_size(sh, 100, 256, 100) < 256 * 100 * 512 * 2 + 4096
+    # bf16 codebook path: bf16 copy of o and the chain ids, one selection
+    # group per request
+    ids = 256 * 8 * 128 * 4
+    assert L.gr_decode_workspace_size(sh, 100, 256, 100) >= 256 * 100 * 512 * 2 + ids
+    assert L.gr_decode_workspace_size(sh, 100, 256, 100) < 256 * 100 * 512 * 2 + ids + 4096
     # scalar path: fp32 o + one score per candidate + partial lists of 2 groups
     s4 = shape(R=1, H=4, head_dim=32, prompt_len=256)
     n4 = L.gr_decode_workspace_size(s4, 40000, 1, 2000)
     assert n4 >= 40000 * 128 * 4 + 40000 * 4 + 2 * 2000 * 8
     assert L.gr_topk_workspace_size(2, 100, 256, 100) == 0
     assert L.gr_topk_workspace_size(2, 300, 256, 100) >= 2 * 3 * 100 * 8
-    assert L.gr_attn_workspace_size(sh, 100) == 0
+    # bf16 attention: resolved chain ids, [R][8 levels][100 beams padded to 128]
+    assert L.gr_attn_workspace_size(sh, 100) == 256 * 8 * 128 * 4 + 256
+    assert L.gr_attn_workspace_size(shape(R=2, dtype=L.GR_F32), 100) == 0
     assert L.gr_decode_workspace_size(shape(head_dim=16), 100, 256, 100) == 0
     assert L.status_string(L.GR_ERR_CAPACITY).startswith("append")

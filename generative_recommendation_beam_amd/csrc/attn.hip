@@ -44,6 +44,10 @@ namespace gr {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Ring depth of the bf16 kernel: 3 stages of 64 keys (2 tiles in flight)
+// keep a 4-wave workgroup at 52 KB of LDS and <= 168 VGPRs, so three
+// workgroups share a CU.
+constexpr int kAttnStages = 3;
 
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 
@@ -158,17 +162,17 @@ __device__ __forceinline__ int swz_v(int row) {
   return HD == 64 ? 2 * (row & 3) : 2 * ((row >> 1) & 1);
 }
 
-template <int HD, int NW, int NS>
-__global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
+template <int HD, int NW, int NS, int OCC>
+__global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   using G = Geo<HD, NW, NS>;
-  static_assert(NS == 4, "ring depth: stage 3 carries the queries until tile 3 is requested");
+  static_assert(NS == 3 || NS == 4, "ring depth: the last stage carries the queries until it is first refilled");
   static_assert(G::NBLK % NW == 0, "every wave moves the same number of 1 KB blocks");
   static_assert(G::NB <= 2 * G::KT, "queries of a workgroup fit the two buffers of one stage");
   // One LDS object per ring stage (its K half, then its V half): the
   // compiler then sees that a DMA into one stage does not touch the stage
   // being read, and adds no waits for it.  (It tells apart only a few LDS
   // DMA targets, so there are just five: four stages and the chain ids.)
-  __shared__ __attribute__((aligned(1024))) uint16_t KV0[G::TB], KV1[G::TB], KV2[G::TB], KV3[G::TB];
+  __shared__ __attribute__((aligned(1024))) uint16_t KV0[G::TB], KV1[G::TB], KV2[G::TB], KV3[NS > 3 ? G::TB : 8];
   __shared__ __attribute__((aligned(1024))) int32_t ids_s[GR_MAX_DEPTH * G::NB];
   auto kst = [&](auto S) -> uint16_t * {
     constexpr int st = decltype(S)::value;
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
     else return KV3;
   };
   auto vst = [&](auto S) -> uint16_t * { return kst(S) + G::TB / 2; };
-  uint16_t *const K3 = KV3, *const V3 = KV3 + G::TB / 2;
+  uint16_t *const K3 = kst(Stage<NS - 1>{}), *const V3 = vst(Stage<NS - 1>{});
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -259,8 +263,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
   };
 
   // ---- prologue, in stream order: chain ids (wave 0), the queries of the
-  // workgroup into stage 3 (K3: beams 0..63, V3: beams 64..127, K-swizzled
-  // rows), then prompt tiles 0..2.
+  // workgroup into the last stage (its K half: beams 0..63, V half: beams
+  // 64..127, K-swizzled rows), then prompt tiles 0..NS-2.
   if (p.ids != nullptr && wave == 0) {
     const int words = p.D * G::NB;
     const int32_t *src0 = p.ids + (size_t)r * p.D * p.nb_pad + (size_t)grp * G::NB;
@@ -283,7 +287,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
   }
   issue_prompt(0, Stage<0>{});
   issue_prompt(1, Stage<1>{});
-  issue_prompt(2, Stage<2>{});
+  if constexpr (NS > 3) issue_prompt(2, Stage<2>{});
 
   // per-lane LDS byte offsets of the operand reads (stage base added later)
   int koff[2][G::KSTEP];
@@ -357,7 +361,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
             }
             n_total = n_pre + depth * G::NRB;
           }
-          // every wave holds its queries before stage 3 is refilled
+          // every wave holds its queries before the last stage is refilled
           __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
           ring_barrier();
         }
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
     step(t0, Stage<0>{});
     step(t0, Stage<1>{});
     step(t0, Stage<2>{});
-    step(t0, Stage<3>{});
+    if constexpr (NS > 3) step(t0, Stage<3>{});
   }
 
   const float l_tot = xor32_sum(l_run);
@@ -582,7 +586,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnPF p) {
 
 template <int HD, int NW>
 hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
-  constexpr int NS = 4;
+  constexpr int NS = kAttnStages, OCC = NW == 4 ? 3 : (NW == 2 ? 2 : 1);
   AttnP p;
   p.pk = (const uint16_t *)a.pk; p.pv = (const uint16_t *)a.pv; p.q = (const uint16_t *)a.q;
   p.ak = (const uint16_t *)a.ak; p.av = (const uint16_t *)a.av;
@@ -604,7 +608,7 @@ hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
     p.ids = a.chain_ids;
   }
   const long long grid = (long long)a.R * a.H * p.n_grp;
-  hipLaunchKernelGGL((attn_bf16_kernel<HD, NW, NS>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p);
+  hipLaunchKernelGGL((attn_bf16_kernel<HD, NW, NS, OCC>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 

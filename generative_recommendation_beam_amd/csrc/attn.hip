@@ -55,40 +55,7 @@ template <int I>
 struct Stage {
   static constexpr int value = I;
 };
-#define GR_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 #define GR_LDS4(p) ((__attribute__((address_space(3))) i16x4 *)(p))
-
-// s_waitcnt with only the vector-memory counter constrained to <= n.
-#define GR_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
-
-// One global_load_lds_dwordx4: lane l's 16 bytes at src land at LDS byte
-// lds + 16*l (lds wave-uniform).  Written as inline asm so that the compiler
-// does not track these LDS writes: its own wait insertion would otherwise
-// turn into vmcnt(0) before every LDS read once several ring stages have DMAs
-// in flight.  Every read of DMA'd data is instead preceded by an explicit
-// vmcnt wait and a barrier (ring_barrier below).  No VGPR is written, so
-// nothing is left for the compiler to misjudge.  M0 (reserved by the
-// compiler) is saved and restored around the load, and needs one wait state
-// before the load reads it.
-__device__ __forceinline__ void dma16(const void *src, const void *lds) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)GR_LDS(lds);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(m0), "v"(src)
-      : "memory");
-}
-// Workgroup barrier that also keeps the compiler from moving LDS reads above
-// it (DMA'd data is only valid past the wait + barrier).
-__device__ __forceinline__ void ring_barrier() {
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // ------------------------------------------------------------ chain resolve
 struct ChainP {
@@ -149,13 +116,14 @@ struct Geo {
   static constexpr int NRB = (NB + KT - 1) / KT;  // record tiles per chain level
 };
 
-// Bank swizzles (physical chunk = logical chunk ^ swizzle(row)).  K: the 8
-// lanes of one b128 read cycle read 8 consecutive rows at one logical chunk.
-// V: a 16-lane transposed read touches 4 consecutive rows (from a multiple of
-// 4) x 2 adjacent chunks.
+// Bank swizzles (physical chunk = logical chunk ^ swizzle(row)).  K: 16
+// consecutive lanes read 16 consecutive rows at one logical chunk; the
+// swizzle spreads them over distinct 16-byte slots of a 256-byte bank row
+// (and any 8 of them over a 128-byte one).  V: a 16-lane transposed read
+// touches 4 consecutive rows (from a multiple of 4) x 2 adjacent chunks.
 template <int HD>
 __device__ __forceinline__ int swz_k(int row) {
-  return HD == 64 ? (row & 7) : ((row >> 1) & 3);
+  return HD == 64 ? ((row & 7) ^ ((row >> 3) & 1)) : (((row >> 1) & 3) ^ ((row >> 3) & 1));
 }
 template <int HD>
 __device__ __forceinline__ int swz_v(int row) {

@@ -49,6 +49,42 @@ __device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- HBM -> LDS streaming (global_load_lds)
+#define GR_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+// s_waitcnt with only the vector-memory counter constrained to <= n.
+#define GR_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+// One global_load_lds_dwordx4: lane l's 16 bytes at src land at LDS byte
+// lds + 16*l (lds wave-uniform).  Written as inline asm so that the compiler
+// does not track these LDS writes: its own wait insertion would otherwise
+// turn into vmcnt(0) before every LDS read once several ring stages have DMAs
+// in flight.  Every read of DMA'd data is instead preceded by an explicit
+// vmcnt wait and a barrier (ring_barrier below).  No VGPR is written, so
+// nothing is left for the compiler to misjudge.  M0 (reserved by the
+// compiler) is saved and restored around the load, and needs one wait state
+// before the load reads it.
+__device__ __forceinline__ void dma16(const void *src, const void *lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)GR_LDS(lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(src)
+      : "memory");
+}
+// Workgroup barrier that also keeps the compiler from moving LDS reads above
+// it (DMA'd data is only valid past the wait + barrier).
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+
 // Ordering key of a score: a smaller key means a larger score.  -0 is folded
 // into +0 and NaN ranks like -inf, so the order is total on real scores.
 __device__ __forceinline__ uint32_t rank_key(float s) {

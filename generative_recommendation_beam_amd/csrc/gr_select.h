@@ -48,7 +48,7 @@ __device__ __forceinline__ int pow2_ceil(int x) {
 
 // Ascending bitonic sort of arr[0..P) (P a power of two).
 template <int NT>
-__device__ void bitonic_sort_u64(uint64_t *arr, int P) {
+__device__ __forceinline__ void bitonic_sort_u64(uint64_t *arr, int P) {
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int i = threadIdx.x; i < (P >> 1); i += NT) {
@@ -61,6 +61,35 @@ __device__ void bitonic_sort_u64(uint64_t *arr, int P) {
       __syncthreads();
     }
   }
+}
+
+// The same sort for P <= NT entries, one per thread, in registers: strides
+// below 64 exchange through lane shuffles, larger ones through LDS.  Entries
+// L..P-1 are padding (~0).  The sorted list is written back to arr[0..P).
+template <int NT>
+__device__ __forceinline__ void bitonic_sort_u64_reg(uint64_t *arr, int L, int P) {
+  const int tid = threadIdx.x;
+  uint64_t x = tid < L ? arr[tid] : ~0ull;
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      uint64_t y;
+      if (stride >= 64) {
+        __syncthreads();
+        if (tid < P) arr[tid] = x;
+        __syncthreads();
+        y = tid < P ? arr[tid ^ stride] : ~0ull;
+      } else {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, stride);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), stride);
+        y = ((uint64_t)hi << 32) | lo;
+      }
+      const bool up = (tid & size) == 0, lower = (tid & stride) == 0;
+      x = (lower == up) ? (x < y ? x : y) : (x < y ? y : x);
+    }
+  }
+  __syncthreads();
+  if (tid < P) arr[tid] = x;
+  __syncthreads();
 }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
@@ -78,8 +107,10 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // the block (key[j] != kInvalidKey; the index of slot j is idx_of(j)).  n_valid
 // is their number, 1 <= k <= min(n_valid, kMaxK).  On return the first k
 // entries of sm.u.list hold them in ascending order.  All threads call it.
+// Always inlined: the candidates must stay in registers (a call would pass
+// them through scratch memory).
 template <int NT, int J, typename IdxFn>
-__device__ void select_regs(const uint32_t (&key)[J], IdxFn idx_of, int n_valid, int k, SelectSmem<NT> &sm) {
+__device__ __forceinline__ void select_regs(const uint32_t (&key)[J], IdxFn idx_of, int n_valid, int k, SelectSmem<NT> &sm) {
   static_assert(NT % 64 == 0 && kHistBins % NT == 0, "block size");
   constexpr int NW = NT / 64;
   constexpr int BPT = kHistBins / NT;   // histogram bins scanned per thread
@@ -121,12 +152,24 @@ __device__ void select_regs(const uint32_t (&key)[J], IdxFn idx_of, int n_valid,
     const uint64_t pre = fixed_lo >= 64 ? 0ull : (sm.prefix >> fixed_lo);
     for (int i = tid; i < kHistBins; i += NT) sm.u.hist[i] = 0;
     __syncthreads();
+    if (shift >= 32) {
+      // digit and prefix lie in the score key: 32-bit arithmetic only
+      const int fl = fixed_lo - 32, sh = shift - 32;
+      const uint32_t pre32 = (uint32_t)pre;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      if (key[j] != kInvalidKey) {
-        const uint64_t x = ((uint64_t)key[j] << 32) | idx_of(j);
-        const uint64_t hi = fixed_lo >= 64 ? 0ull : (x >> fixed_lo);
-        if (hi == pre) atomicAdd(&sm.u.hist[(uint32_t)(x >> shift) & mask], 1u);
+      for (int j = 0; j < J; ++j) {
+        const uint32_t kj = key[j];
+        const bool in = kj != kInvalidKey && (fl >= 32 || (kj >> fl) == pre32);
+        if (in) atomicAdd(&sm.u.hist[(kj >> sh) & mask], 1u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        if (key[j] != kInvalidKey) {
+          const uint64_t x = ((uint64_t)key[j] << 32) | idx_of(j);
+          const uint64_t hi = fixed_lo >= 64 ? 0ull : (x >> fixed_lo);
+          if (hi == pre) atomicAdd(&sm.u.hist[(uint32_t)(x >> shift) & mask], 1u);
+        }
       }
     }
     __syncthreads();
@@ -161,38 +204,62 @@ __device__ void select_regs(const uint32_t (&key)[J], IdxFn idx_of, int n_valid,
   // ---- everything at or below the bucket goes to the list
   const int fixed_lo = sm.fixed_lo;
   const uint64_t hi_bound = fixed_lo >= 64 ? ~0ull : (sm.prefix | ((1ull << fixed_lo) - 1ull));
+  // With the bucket boundary inside the score key, the index half of
+  // hi_bound is all ones and one 32-bit compare decides.
   const uint64_t below = __lanemask_lt();
-  int cnt = 0;
+  if (fixed_lo >= 32) {
+    const uint32_t hi32 = (uint32_t)(hi_bound >> 32);
+    int cnt = 0;
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const bool sel = key[j] != kInvalidKey && ((((uint64_t)key[j] << 32) | idx_of(j)) <= hi_bound);
-    cnt += (int)__popcll(__ballot(sel));
-  }
-  int base = 0;
-  if (lane == 0 && cnt) base = atomicAdd(&sm.n_list, cnt);
-  base = __shfl(base, 0);
+    for (int j = 0; j < J; ++j) cnt += (int)__popcll(__ballot(key[j] <= hi32 && key[j] != kInvalidKey));
+    int base = 0;
+    if (lane == 0 && cnt) base = atomicAdd(&sm.n_list, cnt);
+    base = __shfl(base, 0);
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const uint64_t x = ((uint64_t)key[j] << 32) | idx_of(j);
-    const bool sel = key[j] != kInvalidKey && x <= hi_bound;
-    const uint64_t m = __ballot(sel);
-    const int at = base + (int)__popcll(m & below);
-    if (sel && at < kListCap) sm.u.list[at] = x;
-    base += (int)__popcll(m);
+    for (int j = 0; j < J; ++j) {
+      const bool sel = key[j] <= hi32 && key[j] != kInvalidKey;
+      const uint64_t m = __ballot(sel);
+      const int at = base + (int)__popcll(m & below);
+      if (sel && at < kListCap) sm.u.list[at] = ((uint64_t)key[j] << 32) | idx_of(j);
+      base += (int)__popcll(m);
+    }
+  } else {
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const bool sel = key[j] != kInvalidKey && ((((uint64_t)key[j] << 32) | idx_of(j)) <= hi_bound);
+      cnt += (int)__popcll(__ballot(sel));
+    }
+    int base = 0;
+    if (lane == 0 && cnt) base = atomicAdd(&sm.n_list, cnt);
+    base = __shfl(base, 0);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const uint64_t x = ((uint64_t)key[j] << 32) | idx_of(j);
+      const bool sel = key[j] != kInvalidKey && x <= hi_bound;
+      const uint64_t m = __ballot(sel);
+      const int at = base + (int)__popcll(m & below);
+      if (sel && at < kListCap) sm.u.list[at] = x;
+      base += (int)__popcll(m);
+    }
   }
   __syncthreads();
   const int L = min(sm.n_list, kListCap);
   const int P = pow2_ceil(max(L, k));
-  for (int i = L + tid; i < P; i += NT) sm.u.list[i] = ~0ull;
-  __syncthreads();
-  bitonic_sort_u64<NT>(sm.u.list, P);
+  if (P <= NT) {
+    bitonic_sort_u64_reg<NT>(sm.u.list, L, P);
+  } else {
+    for (int i = L + tid; i < P; i += NT) sm.u.list[i] = ~0ull;
+    __syncthreads();
+    bitonic_sort_u64<NT>(sm.u.list, P);
+  }
 }
 
 // Writes the sorted selection of k_sel candidates: the final outputs (one
 // group per request) or this group's partial list of kk entries (entries past
 // k_sel are ~0, which sorts after every real candidate).
 template <int NT>
-__device__ void emit_selection(const SelectSmem<NT> &sm, int k_sel, int r, int grp, int vocab, float *score,
+__device__ __forceinline__ void emit_selection(const SelectSmem<NT> &sm, int k_sel, int r, int grp, int vocab, float *score,
                                int32_t *token, int32_t *parent, uint64_t *partial, int n_groups, int kk) {
   if (n_groups == 1) {
     for (int j = threadIdx.x; j < k_sel; j += NT) {

@@ -30,14 +30,22 @@ namespace gr {
 namespace {
 
 constexpr int kNT = 512;
-constexpr int kChunk = 64;                 // W columns per LDS chunk
-constexpr int kWS = kChunk + 8;            // LDS row stride (bf16), 144 B
+constexpr int kOC = 32;                    // D columns per ring chunk (two MFMA k-steps)
+constexpr int kRS = 6;                     // ring stages (5 chunks in flight)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// One ring stage: a 32-column chunk of W (256 code rows) and of o (128 beam
+// rows), 64-byte rows whose 16-byte chunks are XOR-swizzled so that 16
+// consecutive rows read at one logical chunk hit 16 distinct 16-byte slots of
+// a 256-byte bank row (and any 8 of them distinct slots of a 128-byte one).
+struct LogitsStage {
+  uint16_t w[256 * kOC];                   // 16 KB
+  uint16_t o[kGroupBeams * kOC];           // 8 KB
+};
 struct LogitsSmem {
   union {
-    uint16_t w[2][256 * kWS];              // W chunks during the projection
+    LogitsStage ring[kRS];                 // projection
     SelectSmem<kNT> sel;                   // selection afterwards
   } u;
   float red_max[4][2][32];
@@ -54,9 +62,12 @@ struct LP {
   int R, n_in, D, k, lsm, n_groups, kk;
 };
 
+__device__ __forceinline__ int swz64(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+
 __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
   __shared__ LogitsSmem sm;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, c = lane & 31;
   const int r = blockIdx.x / p.n_groups, grp = blockIdx.x % p.n_groups;
   const int b_begin = grp * kGroupBeams;
@@ -65,35 +76,39 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
   const int bl = bb * 32 + c;
   const bool valid = bl < nbg;
   const int beam = b_begin + bl;
-  const int n_chunks = (p.D + kChunk - 1) / kChunk;
+  const int n_chunks = p.D / kOC;
 
-  // cooperative W chunk loads: 256 rows x 8 pieces of 16 B = 2048 pieces
-  uint4 wreg[4];
-  auto load_w = [&](int chunk) {
+  // ---- z^T = W o^T, W and o streamed HBM/L2 -> LDS through the ring.  A
+  // 1 KB DMA block is 16 rows x 64 B; lane l fetches row l/4 of its block at
+  // the logical chunk that the swizzle puts at physical chunk l%4.  Wave w
+  // moves W blocks 2w, 2w+1 and o block w of every chunk (3 DMAs per chunk).
+  // Chunks past the end re-read the last one (never used), so every step
+  // has exactly kRS-2 chunks in flight behind the one it consumes.
+  const int drow = lane >> 2, dpc = lane & 3;
+  const uint16_t *orow_base = p.o + (size_t)r * p.n_in * p.D;
+  auto issue = [&](int chunk, int st) {
+    const int col0 = min(chunk, n_chunks - 1) * kOC;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int piece = tid + i * kNT;
-      const int row = piece >> 3, col = chunk * kChunk + (piece & 7) * 8;
-      wreg[i] = col < p.D ? *(const uint4 *)(p.W + (size_t)row * p.D + col) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+      const int blk = wave * 2 + i, row = blk * 16 + drow;
+      const int lc = dpc ^ swz64(row);
+      dma16(p.W + (size_t)row * p.D + col0 + lc * 8, &sm.u.ring[st].w[blk * 512]);
+    }
+    {
+      const int row = wave * 16 + drow, lc = dpc ^ swz64(row);
+      const int b = min(b_begin + row, p.n_in - 1);
+      dma16(orow_base + (size_t)b * p.D + col0 + lc * 8, &sm.u.ring[st].o[wave * 512]);
     }
   };
-  auto store_w = [&](int buf) {
+  // per-lane LDS element offsets of the operand reads (logical chunk 2kk+g)
+  const int sw = swz64(c);                  // rows bl and ch*128+32m+c share bits 1..3 with c
+  int aoff[4][2], boff[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int piece = tid + i * kNT;
-      *(uint4 *)&sm.u.w[buf][(piece >> 3) * kWS + (piece & 7) * 8] = wreg[i];
-    }
-  };
-  // B fragments (o) of one chunk: 4 k-steps of 16 columns
-  const uint16_t *orow = p.o + ((size_t)r * p.n_in + (valid ? beam : 0)) * p.D + 8 * g;
-  uint4 ocur[4], onext[4];
-  auto load_o = [&](int chunk, uint4 (&dst)[4]) {
+  for (int kk = 0; kk < 2; ++kk) {
+    boff[kk] = bl * kOC + (((2 * kk + g) ^ sw) << 3);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int col = chunk * kChunk + 16 * kk;
-      dst[kk] = (valid && col < p.D) ? *(const uint4 *)(orow + col) : make_uint4(0, 0, 0, 0);
-    }
-  };
+    for (int m = 0; m < 4; ++m) aoff[m][kk] = (ch * 128 + 32 * m + c) * kOC + (((2 * kk + g) ^ sw) << 3);
+  }
 
   f32x16 acc[4];
 #pragma unroll
@@ -101,32 +116,25 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
 
-  load_w(0);
-  load_o(0, ocur);
-  store_w(0);
-  __syncthreads();
-  for (int chunk = 0; chunk < n_chunks; ++chunk) {
-    const int buf = chunk & 1;
-    if (chunk + 1 < n_chunks) {
-      load_w(chunk + 1);
-      load_o(chunk + 1, onext);
-    }
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 b = __builtin_bit_cast(bf16x8, ocur[kk]);
+  for (int c0 = 0; c0 < kRS - 1; ++c0) issue(c0, c0);
+  for (int chunk = 0; chunk < n_chunks; ++chunk) {
+    GR_WAIT_VMCNT(3 * (kRS - 2));           // this wave's pieces of `chunk` landed
+    ring_barrier();                         // everyone's, and stage chunk-1 is free
+    issue(chunk + kRS - 1, (chunk + kRS - 1) % kRS);
+    const LogitsStage &S = sm.u.ring[chunk % kRS];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 b = *(const bf16x8 *)&S.o[boff[kk]];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const bf16x8 a = *(const bf16x8 *)&sm.u.w[buf][(ch * 128 + 32 * m + c) * kWS + 16 * kk + 8 * g];
+        const bf16x8 a = *(const bf16x8 *)&S.w[aoff[m][kk]];
         acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[m], 0, 0, 0);
       }
     }
-    if (chunk + 1 < n_chunks) {
-      store_w(buf ^ 1);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) ocur[kk] = onext[kk];
-    }
-    __syncthreads();
   }
+  GR_WAIT_VMCNT(0);                         // the trailing re-reads landed
+  ring_barrier();                           // before the LDS is reused
 
   // log-softmax over the 256 codes of each beam (two waves hold its halves)
   float lse = 0.f;

@@ -12,8 +12,9 @@
 // pass histograms the candidates still in play with non-returning LDS atomics
 // and one block scan picks the bucket holding the k-th.  As soon as that
 // bucket has at most kBucketCap members, every candidate at or below the
-// bucket is copied to an LDS list (two ballot sweeps, one atomic per wave),
-// and one bitonic sort orders the list; its first k entries are the answer.
+// bucket is copied to an LDS list (per-lane counts, one prefix sum and one
+// atomic per wave), and one bitonic sort orders the list; its first k entries
+// are the answer.
 // Integer counts only, so the result is deterministic.
 #pragma once
 
@@ -103,6 +104,35 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// Appends every register candidate j with sel(j) to list (composites, in no
+// particular order): per-lane counts, one wave prefix sum and one LDS atomic
+// per wave reserve the slots, so the per-candidate work is VALU only.
+template <int J, typename IdxFn, typename Sel>
+__device__ __forceinline__ void append_selected(const uint32_t (&key)[J], IdxFn idx_of, Sel sel, int &n_list,
+                                                uint64_t *list) {
+  const int lane = threadIdx.x & 63;
+  int mine = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) mine += sel(j) ? 1 : 0;
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  const int wave_tot = __shfl(incl, 63);
+  int base = 0;
+  if (lane == 63 && wave_tot) base = atomicAdd(&n_list, wave_tot);
+  int at = __shfl(base, 63) + incl - mine;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (sel(j)) {
+      if (at < kListCap) list[at] = ((uint64_t)key[j] << 32) | idx_of(j);
+      ++at;
+    }
+  }
+}
+
 // Selects the k smallest composites among the valid register candidates of
 // the block (key[j] != kInvalidKey; the index of slot j is idx_of(j)).  n_valid
 // is their number, 1 <= k <= min(n_valid, kMaxK).  On return the first k
@@ -128,28 +158,24 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[J], IdxFn idx_
   kmin = wave_min_u32(kmin);
   kmax = wave_max_u32(kmax);
   if (lane == 0) { sm.wmin[wave] = kmin; sm.wmax[wave] = kmax; }
+  if (tid == 0) sm.n_list = 0;
   __syncthreads();
-  if (tid == 0) {
-    uint32_t a = sm.wmin[0], b = sm.wmax[0];
-    for (int w = 1; w < NW; ++w) { a = min(a, sm.wmin[w]); b = max(b, sm.wmax[w]); }
-    const uint32_t diff = a ^ b;
-    const int lo = diff ? 64 - __builtin_clz(diff) : 32;   // key bits differ, or only the index does
-    sm.fixed_lo = lo;
-    sm.prefix = lo >= 64 ? 0ull : (((uint64_t)a << 32) & ~((1ull << lo) - 1ull));
-    sm.need = k;
-    sm.bucket_cnt = n_valid;
-    sm.n_list = 0;
-  }
-  __syncthreads();
+  // every thread derives the same starting state from the wave extremes
+  uint32_t a = sm.wmin[0], b = sm.wmax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) { a = min(a, sm.wmin[w]); b = max(b, sm.wmax[w]); }
+  const uint32_t diff = a ^ b;
+  int fixed_lo = diff ? 64 - __builtin_clz(diff) : 32;   // key bits differ, or only the index does
+  uint64_t prefix = fixed_lo >= 64 ? 0ull : (((uint64_t)a << 32) & ~((1ull << fixed_lo) - 1ull));
+  uint32_t need = (uint32_t)k;
+  int bucket_cnt = n_valid;
 
   // ---- radix passes over the bucket of the k-th candidate
   for (int pass = 0; pass < 8; ++pass) {
-    const int fixed_lo = sm.fixed_lo;
-    const uint32_t need = (uint32_t)sm.need;
-    if (fixed_lo == 0 || sm.bucket_cnt <= kBucketCap) break;
+    if (fixed_lo == 0 || bucket_cnt <= kBucketCap) break;
     const int shift = fixed_lo > kHistBits ? fixed_lo - kHistBits : 0;
     const uint32_t mask = (1u << (fixed_lo - shift)) - 1u;
-    const uint64_t pre = fixed_lo >= 64 ? 0ull : (sm.prefix >> fixed_lo);
+    const uint64_t pre = fixed_lo >= 64 ? 0ull : (prefix >> fixed_lo);
     for (int i = tid; i < kHistBins; i += NT) sm.u.hist[i] = 0;
     __syncthreads();
     if (shift >= 32) {
@@ -191,7 +217,7 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[J], IdxFn idx_
       for (int q = 0; q < BPT; ++q) {
         if (c[q] > 0 && excl < need && need <= excl + c[q]) {
           sm.need = (int)(need - excl);
-          sm.prefix |= ((uint64_t)(tid * BPT + q)) << shift;
+          sm.prefix = prefix | (((uint64_t)(tid * BPT + q)) << shift);
           sm.fixed_lo = shift;
           sm.bucket_cnt = (int)c[q];
         }
@@ -199,49 +225,24 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[J], IdxFn idx_
       }
     }
     __syncthreads();
+    need = (uint32_t)sm.need;
+    prefix = sm.prefix;
+    fixed_lo = sm.fixed_lo;
+    bucket_cnt = sm.bucket_cnt;
   }
 
   // ---- everything at or below the bucket goes to the list
-  const int fixed_lo = sm.fixed_lo;
-  const uint64_t hi_bound = fixed_lo >= 64 ? ~0ull : (sm.prefix | ((1ull << fixed_lo) - 1ull));
+  const uint64_t hi_bound = fixed_lo >= 64 ? ~0ull : (prefix | ((1ull << fixed_lo) - 1ull));
   // With the bucket boundary inside the score key, the index half of
   // hi_bound is all ones and one 32-bit compare decides.
-  const uint64_t below = __lanemask_lt();
   if (fixed_lo >= 32) {
     const uint32_t hi32 = (uint32_t)(hi_bound >> 32);
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < J; ++j) cnt += (int)__popcll(__ballot(key[j] <= hi32 && key[j] != kInvalidKey));
-    int base = 0;
-    if (lane == 0 && cnt) base = atomicAdd(&sm.n_list, cnt);
-    base = __shfl(base, 0);
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const bool sel = key[j] <= hi32 && key[j] != kInvalidKey;
-      const uint64_t m = __ballot(sel);
-      const int at = base + (int)__popcll(m & below);
-      if (sel && at < kListCap) sm.u.list[at] = ((uint64_t)key[j] << 32) | idx_of(j);
-      base += (int)__popcll(m);
-    }
+    append_selected<J>(key, idx_of, [&](int j) { return key[j] <= hi32 && key[j] != kInvalidKey; }, sm.n_list,
+                       sm.u.list);
   } else {
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const bool sel = key[j] != kInvalidKey && ((((uint64_t)key[j] << 32) | idx_of(j)) <= hi_bound);
-      cnt += (int)__popcll(__ballot(sel));
-    }
-    int base = 0;
-    if (lane == 0 && cnt) base = atomicAdd(&sm.n_list, cnt);
-    base = __shfl(base, 0);
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const uint64_t x = ((uint64_t)key[j] << 32) | idx_of(j);
-      const bool sel = key[j] != kInvalidKey && x <= hi_bound;
-      const uint64_t m = __ballot(sel);
-      const int at = base + (int)__popcll(m & below);
-      if (sel && at < kListCap) sm.u.list[at] = x;
-      base += (int)__popcll(m);
-    }
+    append_selected<J>(key, idx_of, [&](int j) {
+      return key[j] != kInvalidKey && ((((uint64_t)key[j] << 32) | idx_of(j)) <= hi_bound);
+    }, sm.n_list, sm.u.list);
   }
   __syncthreads();
   const int L = min(sm.n_list, kListCap);

@@ -111,6 +111,69 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ---- VALU-only cross-lane exchanges (DPP and permlane swaps; no LDS pipe)
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+// value held by lane l ^ S, S in {1, 2, 4, 8}: quad permutes and row mirrors
+// (xor 4 = half-mirror then quad reverse, xor 8 = mirror then half-mirror)
+template <int S>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  static_assert(S == 1 || S == 2 || S == 4 || S == 8, "DPP xor distance");
+  if constexpr (S == 1) return dpp_u32<0xB1>(v);                     // quad_perm [1,0,3,2]
+  else if constexpr (S == 2) return dpp_u32<0x4E>(v);                // quad_perm [2,3,0,1]
+  else if constexpr (S == 4) return dpp_u32<0x1B>(dpp_u32<0x141>(v));  // row_half_mirror, quad_perm [3,2,1,0]
+  else return dpp_u32<0x141>(dpp_u32<0x140>(v));                     // row_mirror, row_half_mirror
+}
+// {value of lane l, value of lane l ^ S} for S in {16, 32}, in a lane-
+// dependent order (one v_permlane16_swap / v_permlane32_swap): enough for
+// min, max and sums, which do not care which is which.
+template <int S>
+__device__ __forceinline__ void xor_pair(uint32_t v, uint32_t &a, uint32_t &b) {
+  static_assert(S == 16 || S == 32, "permlane swap distance");
+  if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    a = r[0]; b = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    a = r[0]; b = r[1];
+  }
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, xor_lane<1>(v));
+  v = min(v, xor_lane<2>(v));
+  v = min(v, xor_lane<4>(v));
+  v = min(v, xor_lane<8>(v));
+  uint32_t a, b;
+  xor_pair<16>(v, a, b);
+  v = min(a, b);
+  xor_pair<32>(v, a, b);
+  return min(a, b);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, xor_lane<1>(v));
+  v = max(v, xor_lane<2>(v));
+  v = max(v, xor_lane<4>(v));
+  v = max(v, xor_lane<8>(v));
+  uint32_t a, b;
+  xor_pair<16>(v, a, b);
+  v = max(a, b);
+  xor_pair<32>(v, a, b);
+  return max(a, b);
+}
+// Inclusive prefix sum over the wave (row shifts within 16-lane rows, then
+// the row totals broadcast into the rows above).
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += dpp_u32<0x111>(v);          // row_shr:1
+  v += dpp_u32<0x112>(v);          // row_shr:2
+  v += dpp_u32<0x114>(v);          // row_shr:4
+  v += dpp_u32<0x118>(v);          // row_shr:8
+  v += dpp_u32<0x142, 0xA>(v);     // row_bcast:15 into rows 1 and 3
+  v += dpp_u32<0x143, 0xC>(v);     // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -93,17 +93,6 @@ __device__ __forceinline__ void bitonic_sort_u64_reg(uint64_t *arr, int L, int P
   __syncthreads();
 }
 
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
-}
-
 // Appends every register candidate j with sel(j) to list (composites, in no
 // particular order): per-lane counts, one wave prefix sum and one LDS atomic
 // per wave reserve the slots, so the per-candidate work is VALU only.
@@ -114,16 +103,11 @@ __device__ __forceinline__ void append_selected(const uint32_t (&key)[J], IdxFn 
   int mine = 0;
 #pragma unroll
   for (int j = 0; j < J; ++j) mine += sel(j) ? 1 : 0;
-  int incl = mine;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o);
-    if (lane >= o) incl += v;
-  }
-  const int wave_tot = __shfl(incl, 63);
+  const int incl = (int)wave_incl_scan_u32((uint32_t)mine);
+  const int wave_tot = __builtin_amdgcn_readlane(incl, 63);
   int base = 0;
   if (lane == 63 && wave_tot) base = atomicAdd(&n_list, wave_tot);
-  int at = __shfl(base, 63) + incl - mine;
+  int at = __builtin_amdgcn_readlane(base, 63) + incl - mine;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     if (sel(j)) {
@@ -202,12 +186,7 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[J], IdxFn idx_
     uint32_t c[BPT], s = 0;
 #pragma unroll
     for (int q = 0; q < BPT; ++q) { c[q] = sm.u.hist[tid * BPT + q]; s += c[q]; }
-    uint32_t inc = s;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t v = (uint32_t)__shfl_up((int)inc, o);
-      if (lane >= o) inc += v;
-    }
+    const uint32_t inc = wave_incl_scan_u32(s);
     if (lane == 63) sm.wtot[wave] = inc;
     __syncthreads();
     uint32_t excl = inc - s;

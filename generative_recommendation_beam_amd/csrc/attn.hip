@@ -96,11 +96,14 @@ __global__ __launch_bounds__(256) void chain_resolve_kernel(ChainP p) {
 // ------------------------------------------------------------ bf16 attention
 struct AttnP {
   const uint16_t *pk, *pv, *q, *ak, *av;
-  const int32_t *ids;  // [R][D][nb_pad] from chain_resolve, or null (prompt only)
+  const int32_t *ids;                  // chains resolved by chain_resolve ([R][D][nb_pad]), or null
+  const int32_t *parent, *beam_node;   // chains resolved in the kernel (small arenas), or null
+  int32_t *dev_err;
   float *out_f32;
   uint16_t *out_bf16;
   int R, H, Lp, Lw, nb, cap, D, nb_pad, n_grp;
-  float sl2;  // scale * log2(e)
+  int ids_words, par_words;  // dynamic LDS: ids [ids_words], parents [par_words], beam nodes
+  float sl2;                 // scale * log2(e)
 };
 
 template <int HD, int NW, int NS>
@@ -141,7 +144,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   // being read, and adds no waits for it.  (It tells apart only a few LDS
   // DMA targets, so there are just five: four stages and the chain ids.)
   __shared__ __attribute__((aligned(1024))) uint16_t KV0[G::TB], KV1[G::TB], KV2[G::TB], KV3[NS > 3 ? G::TB : 8];
-  __shared__ __attribute__((aligned(1024))) int32_t ids_s[GR_MAX_DEPTH * G::NB];
+  // dynamic LDS: chain ids [D][NB] (level-major), then, when the chains are
+  // resolved here, the request's parent array and the workgroup's beam nodes
+  extern __shared__ __attribute__((aligned(1024))) int32_t dyn_s[];
+  int32_t *const ids_s = dyn_s;
+  int32_t *const par_s = dyn_s + p.ids_words;
+  int32_t *const bn_s = par_s + p.par_words;
+  const bool chains = p.ids != nullptr || p.parent != nullptr;
   auto kst = [&](auto S) -> uint16_t * {
     constexpr int st = decltype(S)::value;
     if constexpr (st == 0) return KV0;
@@ -230,9 +239,16 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
     else GR_WAIT_VMCNT(0);
   };
 
-  // ---- prologue, in stream order: chain ids (wave 0), the queries of the
-  // workgroup into the last stage (its K half: beams 0..63, V half: beams
-  // 64..127, K-swizzled rows), then prompt tiles 0..NS-2.
+  // ---- prologue, in stream order: chain ids or the parent array and beam
+  // nodes (wave 0), the queries of the workgroup into the last stage (its K
+  // half: beams 0..63, V half: beams 64..127, K-swizzled rows), then prompt
+  // tiles 0..NS-2.
+  if (p.parent != nullptr && wave == 0) {
+    const int32_t *par = p.parent + (size_t)r * p.cap;
+    for (int i = 0; i * 64 < p.cap; ++i) dma4(par + min(i * 64 + lane, p.cap - 1), par_s + i * 64);
+    const int32_t *bnp = p.beam_node + (size_t)r * p.nb;
+    for (int i = 0; i * 64 < G::NB; ++i) dma4(bnp + min(grp * G::NB + i * 64 + lane, p.nb - 1), bn_s + i * 64);
+  }
   if (p.ids != nullptr && wave == 0) {
     const int words = p.D * G::NB;
     const int32_t *src0 = p.ids + (size_t)r * p.D * p.nb_pad + (size_t)grp * G::NB;
@@ -310,7 +326,32 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
       ring_barrier();
       if constexpr (st == 0) {
         if (tile == 0) {
-          // queries and chain ids have landed (they precede tile 0)
+          // queries and chain ids / parents have landed (they precede tile 0)
+          if (p.parent != nullptr && tid < G::NB) {
+            // resolve the chain of workgroup beam tid in LDS, checking range,
+            // order and depth (heads of one request see the same chains; the
+            // head-0 workgroup reports)
+            int n = grp * G::NB + tid < p.nb ? bn_s[tid] : -1;
+            int err = 0;
+            for (int d = 0; d < p.D; ++d) {
+              int id = -1;
+              if (n != -1) {
+                if (n < 0 || n >= p.cap) {
+                  err |= GR_DEVERR_PARENT_RANGE;
+                  n = -1;
+                } else {
+                  id = n;
+                  const int pn = par_s[n];
+                  if (pn < -1 || pn >= p.cap) { err |= GR_DEVERR_PARENT_RANGE; n = -1; }
+                  else if (pn >= n) { err |= GR_DEVERR_PARENT_ORDER; n = -1; }
+                  else n = pn;
+                }
+              }
+              ids_s[d * G::NB + tid] = id;
+            }
+            if (n != -1) err |= GR_DEVERR_DEPTH;
+            if (err && h == 0) atomicOr(p.dev_err, err);
+          }
           if (wave * 32 < G::KT) {
 #pragma unroll
             for (int j = 0; j < G::KSTEP; ++j) qf[j] = *(const bf16x8 *)((const char *)K3 + roff_k[j]);
@@ -318,7 +359,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
 #pragma unroll
             for (int j = 0; j < G::KSTEP; ++j) qf[j] = *(const bf16x8 *)((const char *)V3 + roff_k[j]);
           }
-          if (p.ids != nullptr) {
+          // every wave holds its queries before the last stage is refilled,
+          // and the chain ids are visible to all
+          __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+          ring_barrier();
+          if (chains) {
             int depth = 0;
             for (int d = 0; d < p.D; ++d) {
               const int own = ids_s[d * G::NB + wb];
@@ -329,9 +374,6 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
             }
             n_total = n_pre + depth * G::NRB;
           }
-          // every wave holds its queries before the last stage is refilled
-          __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-          ring_barrier();
         }
       }
       // every wave is past tile-1: its stage can be refilled
@@ -552,31 +594,48 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnPF p) {
   for (int i = 0; i < HD; ++i) op[i] = o[i] * inv;
 }
 
+// Arenas up to this many nodes per request have their parent array staged in
+// LDS and the chains resolved inside the attention kernel; larger ones go
+// through the chain_resolve pre-pass.
+constexpr int kLdsChainNodes = 4096;
+
 template <int HD, int NW>
 hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
   constexpr int NS = kAttnStages, OCC = NW == 4 ? 3 : (NW == 2 ? 2 : 1);
+  constexpr int NB = NW * 32;
   AttnP p;
   p.pk = (const uint16_t *)a.pk; p.pv = (const uint16_t *)a.pv; p.q = (const uint16_t *)a.q;
   p.ak = (const uint16_t *)a.ak; p.av = (const uint16_t *)a.av;
-  p.ids = nullptr;
+  p.ids = nullptr; p.parent = nullptr; p.beam_node = nullptr; p.dev_err = a.dev_err;
   p.out_f32 = a.out_f32; p.out_bf16 = (uint16_t *)a.out_lowp;
   p.R = a.R; p.H = a.H; p.Lp = a.Lp; p.Lw = a.Lw; p.nb = a.nb; p.cap = a.cap;
   p.D = a.max_depth;
   p.nb_pad = attn_beam_pad(a.nb);
-  p.n_grp = p.nb_pad / (NW * 32);
+  p.n_grp = p.nb_pad / NB;
   p.sl2 = a.scale * kLog2e;
+  p.ids_words = 0;
+  p.par_words = 0;
   if (a.beam_node != nullptr) {
-    ChainP c;
-    c.parent = a.parent; c.beam_node = a.beam_node; c.ids = a.chain_ids; c.dev_err = a.dev_err;
-    c.R = a.R; c.nb = a.nb; c.nb_pad = p.nb_pad; c.cap = a.cap; c.D = a.max_depth;
-    const long long n = (long long)a.R * p.nb_pad;
-    hipLaunchKernelGGL(chain_resolve_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, c);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    p.ids = a.chain_ids;
+    if (a.cap <= kLdsChainNodes) {
+      p.parent = a.parent;
+      p.beam_node = a.beam_node;
+      p.ids_words = a.max_depth * NB;
+      p.par_words = (a.cap + 63) / 64 * 64;
+    } else {
+      ChainP c;
+      c.parent = a.parent; c.beam_node = a.beam_node; c.ids = a.chain_ids; c.dev_err = a.dev_err;
+      c.R = a.R; c.nb = a.nb; c.nb_pad = p.nb_pad; c.cap = a.cap; c.D = a.max_depth;
+      const long long n = (long long)a.R * p.nb_pad;
+      hipLaunchKernelGGL(chain_resolve_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, c);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      p.ids = a.chain_ids;
+      p.ids_words = (a.max_depth * NB + 255) / 256 * 256;   // the ids arrive in 1 KB DMA blocks
+    }
   }
+  const size_t dyn = (size_t)(p.ids_words + p.par_words + (p.parent ? (NB + 63) / 64 * 64 : 0)) * sizeof(int32_t);
   const long long grid = (long long)a.R * a.H * p.n_grp;
-  hipLaunchKernelGGL((attn_bf16_kernel<HD, NW, NS, OCC>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p);
+  hipLaunchKernelGGL((attn_bf16_kernel<HD, NW, NS, OCC>), dim3((unsigned)grid), dim3(NW * 64), dyn, s, p);
   return hipGetLastError();
 }
 

@@ -77,6 +77,21 @@ __device__ __forceinline__ void dma16(const void *src, const void *lds) {
       : "s"(m0), "v"(src)
       : "memory");
 }
+// The same for one dword per lane (global_load_lds_dword): lane l's 4 bytes
+// land at LDS byte lds + 4*l.
+__device__ __forceinline__ void dma4(const void *src, const void *lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)GR_LDS(lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(src)
+      : "memory");
+}
 // Workgroup barrier that also keeps the compiler from moving LDS reads above
 // it (DMA'd data is only valid past the wait + barrier).
 __device__ __forceinline__ void ring_barrier() {

@@ -89,10 +89,12 @@ def append_level(shape, trie, base, k_new, v_new, parent_beam, prev_nodes, dev_e
     return nodes
 
 
-def upload_step(x, window=None, device="cuda", max_depth: int = L.GR_MAX_DEPTH, flags=None) -> DeviceStep:
+def upload_step(x, window=None, device="cuda", max_depth: int = L.GR_MAX_DEPTH, flags=None,
+                capacity: Optional[int] = None) -> DeviceStep:
     """Upload one single-step workload (an object with the fields of
     workloads.StepInputs) and build its arena level by level through
-    gr_trie_append."""
+    gr_trie_append.  `capacity` (default: exactly the appended records)
+    sizes the arena; extra slots stay unused."""
     cfg = x.cfg
     dt = dtype_code(cfg.dtype)
     R, Lp, H, hd = x.prompt_k.shape
@@ -106,7 +108,7 @@ def upload_step(x, window=None, device="cuda", max_depth: int = L.GR_MAX_DEPTH, 
     beam_node = None
     if x.levels:
         cap = sum(k.shape[1] for (_, k, _) in x.levels)
-        ak, av, par, trie = new_arena(shape, cap, max_depth, device)
+        ak, av, par, trie = new_arena(shape, max(cap, capacity or 0), max_depth, device)
         prev, base = None, 0
         for (pb, kk, vv) in x.levels:
             prev = append_level(shape, trie, base, kk, vv, pb, prev, dev_err, device)

@@ -107,22 +107,42 @@ def test_prefix_attn_parity(name):
     print(f"{name}: max|err|/RMS = {e:.3e}")
 
 
-def test_prefix_attn_device_errors():
-    announce("gr_prefix_attn device errors")
+# Arenas of up to 4096 nodes per request have their chains resolved inside
+# the attention kernel (parents staged in LDS); larger ones through the
+# chain-resolve pre-pass.  Both paths are exercised.
+LARGE_ARENA = 5000
+
+
+def test_prefix_attn_parity_large_arena():
+    announce("gr_prefix_attn bf16 chains in a 5000-node arena")
+    cfg = ATTN_CASES["bf16_d64_ragged_nw2"]
+    x = W.make_step_inputs(cfg)
+    ds = HN.upload_step(x, capacity=LARGE_ARENA)
+    out = HN.prefix_attn(ds)
+    torch.cuda.synchronize()
+    assert int(ds.dev_err.item()) == 0
+    ak, av, par = oracle_arena(x)
+    ref = oracle.prefix_attn(x.prompt_k, x.prompt_v, x.q, par, ak, av, x.beam_node, window=cfg.window)
+    assert_close(out.cpu().numpy(), ref, cfg.dtype, "bf16_large_arena")
+
+
+@pytest.mark.parametrize("capacity", [None, LARGE_ARENA])
+def test_prefix_attn_device_errors(capacity):
+    announce(f"gr_prefix_attn device errors, capacity {capacity}")
     cfg = W.reduced(C3, R=2, Lp=40, H=2, n_in=6, level_sizes=(3, 6, 6))
     x = W.make_step_inputs(cfg)
-    ds = HN.upload_step(x, max_depth=2)          # chains have 3 records
+    ds = HN.upload_step(x, max_depth=2, capacity=capacity)   # chains have 3 records
     HN.prefix_attn(ds)
     torch.cuda.synchronize()
     assert int(ds.dev_err.item()) == L.GR_DEVERR_DEPTH
-    ds = HN.upload_step(x)
+    ds = HN.upload_step(x, capacity=capacity)
     ds.parent[1, 9] = 12                         # beam 0's record gets a newer parent
     ds.dev_err.zero_()
     HN.prefix_attn(ds)
     torch.cuda.synchronize()
     assert int(ds.dev_err.item()) & L.GR_DEVERR_PARENT_ORDER
-    ds = HN.upload_step(x)
-    ds.beam_node[0, 2] = 1000                    # outside the arena
+    ds = HN.upload_step(x, capacity=capacity)
+    ds.beam_node[0, 2] = 100000                  # outside the arena
     ds.dev_err.zero_()
     HN.prefix_attn(ds)
     torch.cuda.synchronize()

@@ -81,7 +81,9 @@ def algorithmic(x):
     prompt = R * Lw * D * 2 * es
     q = R * B * D * es
     records = n_chain * (D * 2 * es + 4) + (R * B * 4 if x.levels else 0)
-    attn_out = R * B * D * es                     # attention output handed to the scoring stage
+    # attention output handed to the scoring stage: bf16 for the bf16
+    # codebook path (it feeds the MFMA projection), fp32 otherwise
+    attn_out = R * B * D * (2 if (cfg.dtype == "bf16" and cfg.vocab == 256) else 4)
     W = cfg.vocab * D * es
     prior = 0 if x.prior is None else R * B * 4
     outs = R * cfg.k * 12

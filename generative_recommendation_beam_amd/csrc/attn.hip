@@ -482,20 +482,63 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
     if constexpr (NS > 3) step(t0, Stage<3>{});
   }
 
+  // ---- epilogue.  o leaves through LDS: each lane holds 4-element pieces of
+  // one beam's row, and storing them directly would write 16 bytes into each
+  // of 32 rows per instruction (partial lines, several times their bytes in
+  // HBM time).  The rows are staged in the (now free) first ring stage with
+  // XOR-swizzled 16-byte chunks, then written with consecutive lanes covering
+  // whole rows.
   const float l_tot = xor32_sum(l_run);
-  if (!valid) return;
-  const float inv = 1.f / l_tot;
-  const size_t obase = ((size_t)r * p.nb + beam) * row + (size_t)h * HD;
+  const float inv = valid ? 1.f / l_tot : 0.f;
+  const size_t out_row0 = ((size_t)r * p.nb + (size_t)grp * G::NB) * row + (size_t)h * HD;
+  const int n_rows = min(G::NB, p.nb - grp * G::NB);   // rows of this workgroup that exist
+  __syncthreads();                                      // every wave is past its last tile
+  if (p.out_bf16 != nullptr) {
+    constexpr int CPR = HD / 8;                         // 16-byte chunks per bf16 row
+    uint16_t *st = KV0;                                 // NB rows x HD bf16 (<= 16 KB)
 #pragma unroll
-  for (int dt = 0; dt < G::DT; ++dt)
+    for (int dt = 0; dt < G::DT; ++dt)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d0 = 32 * dt + 8 * q4 + 4 * g;
-      const float o0 = O[dt][4 * q4] * inv, o1 = O[dt][4 * q4 + 1] * inv;
-      const float o2 = O[dt][4 * q4 + 2] * inv, o3 = O[dt][4 * q4 + 3] * inv;
-      if (p.out_f32) *(float4 *)(p.out_f32 + obase + d0) = make_float4(o0, o1, o2, o3);
-      if (p.out_bf16) *(uint2 *)(p.out_bf16 + obase + d0) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int pch = (4 * dt + q4) ^ (wb & (CPR - 1));
+        *(uint2 *)(st + wb * HD + pch * 8 + 4 * g) =
+            make_uint2(pack_bf16x2(O[dt][4 * q4] * inv, O[dt][4 * q4 + 1] * inv),
+                       pack_bf16x2(O[dt][4 * q4 + 2] * inv, O[dt][4 * q4 + 3] * inv));
+      }
+    __syncthreads();
+    for (int id = tid; id < n_rows * CPR; id += NW * 64) {
+      const int rr = id / CPR, ch = id % CPR;
+      const uint4 v = *(const uint4 *)(st + rr * HD + ((ch ^ (rr & (CPR - 1))) << 3));
+      *(uint4 *)(p.out_bf16 + out_row0 + (size_t)rr * row + ch * 8) = v;
     }
+    __syncthreads();
+  }
+  if (p.out_f32 != nullptr) {
+    constexpr int CPR = HD / 4;                         // 16-byte chunks per fp32 row
+    float *st = (float *)KV0;                           // 64 rows x HD fp32 (<= 16 KB)
+#pragma unroll
+    for (int half = 0; half < (G::NB + 63) / 64; ++half) {
+      if ((wb >> 6) == half) {                          // wave-uniform
+        const int lr = wb & 63;
+#pragma unroll
+        for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int pch = (8 * dt + 2 * q4 + g) ^ (lr & (CPR - 1));
+            *(float4 *)(st + lr * HD + pch * 4) = make_float4(O[dt][4 * q4] * inv, O[dt][4 * q4 + 1] * inv,
+                                                              O[dt][4 * q4 + 2] * inv, O[dt][4 * q4 + 3] * inv);
+          }
+      }
+      __syncthreads();
+      const int rows_h = min(64, n_rows - 64 * half);
+      for (int id = tid; id < rows_h * CPR; id += NW * 64) {
+        const int lr = id / CPR, ch = id % CPR;
+        const float4 v = *(const float4 *)(st + lr * HD + ((ch ^ (lr & (CPR - 1))) << 2));
+        *(float4 *)(p.out_f32 + out_row0 + (size_t)(64 * half + lr) * row + ch * 4) = v;
+      }
+      __syncthreads();
+    }
+  }
 }
 
 // ------------------------------------------------------------------ fp32

@@ -206,8 +206,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
     for (int i = 0; i < G::IPW; ++i) {
       const int blk = wave * G::IPW + i;
       const uint32_t src = (uint32_t)min(key0 + dma_row[i], p.Lp - 1) * row32;
-      dma16(pk + (src + dma_k[i]), kst(S) + blk * 512);
-      dma16(pv + (src + dma_v[i]), vst(S) + blk * 512);
+      dma16_stream(pk + (src + dma_k[i]), kst(S) + blk * 512);
+      dma16_stream(pv + (src + dma_v[i]), vst(S) + blk * 512);
     }
   };
   // chain-record tile: row t holds the level-d record of workgroup beam

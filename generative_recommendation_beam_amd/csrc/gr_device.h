@@ -51,6 +51,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // ---- HBM -> LDS streaming (global_load_lds)
 #define GR_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+#ifndef GR_STREAM_POLICY
+#define GR_STREAM_POLICY "nt"
+#endif
 
 // s_waitcnt with only the vector-memory counter constrained to <= n.
 #define GR_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
@@ -72,6 +75,20 @@ __device__ __forceinline__ void dma16(const void *src, const void *lds) {
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(src)
+      : "memory");
+}
+// Streaming variant (read once): non-temporal cache policy.
+__device__ __forceinline__ void dma16_stream(const void *src, const void *lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)GR_LDS(lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off " GR_STREAM_POLICY "\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(m0), "v"(src)

@@ -13,8 +13,9 @@
 // and one block scan picks the bucket holding the k-th.  As soon as that
 // bucket has at most kBucketCap members, every candidate at or below the
 // bucket is copied to an LDS list (per-lane counts, one prefix sum and one
-// atomic per wave), and one bitonic sort orders the list; its first k entries
-// are the answer.
+// atomic per wave), and the list is sorted (bitonic in registers up to one
+// entry per thread, block merge sort above); its first k entries are the
+// answer.
 // Integer counts only, so the result is deterministic.
 #pragma once
 
@@ -36,6 +37,7 @@ struct SelectSmem {
     uint32_t hist[kHistBins];
     uint64_t list[kListCap];
   } u;
+  uint64_t tmp[kListCap];                       // merge-sort ping-pong buffer
   uint32_t wmin[NW], wmax[NW], wtot[NW];
   uint64_t prefix;
   int fixed_lo, need, bucket_cnt, n_list;
@@ -91,6 +93,64 @@ __device__ __forceinline__ void bitonic_sort_u64_reg(uint64_t *arr, int L, int P
   __syncthreads();
   if (tid < P) arr[tid] = x;
   __syncthreads();
+}
+
+// Ascending sort of arr[0..P) for NT < P <= 8 NT (P a power of two): each
+// thread sorts E = P/NT consecutive entries in registers (a bitonic network
+// over 8 slots, padding sorting last), then log2(NT) merge-path rounds double
+// the sorted runs, ping-ponging between arr and tmp with one barrier each.
+// Keys are unique, so every split is unambiguous.
+template <int NT>
+__device__ __forceinline__ void merge_sort_u64(uint64_t *arr, uint64_t *tmp, int P) {
+  const int tid = threadIdx.x;
+  const int E = P / NT;
+  uint64_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = e < E ? arr[tid * E + e] : ~0ull;
+#pragma unroll
+  for (int size = 2; size <= 8; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int f = e ^ stride;
+        if (f > e) {
+          const bool up = (e & size) == 0;
+          const uint64_t a = v[e], b = v[f];
+          if ((a > b) == up) { v[e] = b; v[f] = a; }
+        }
+      }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (e < E) arr[tid * E + e] = v[e];
+  __syncthreads();
+  uint64_t *src = arr, *dst = tmp;
+  for (int run = E; run < P; run <<= 1) {
+    const int o0 = tid * E;
+    const int base = o0 & ~(2 * run - 1), pos = o0 - base;
+    const uint64_t *A = src + base, *B = A + run;
+    int lo = max(0, pos - run), hi = min(pos, run);
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (A[mid] < B[pos - 1 - mid]) lo = mid + 1;
+      else hi = mid;
+    }
+    int i = lo, j = pos - lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (e < E) {
+        const bool take_a = j >= run || (i < run && A[i] < B[j]);
+        dst[o0 + e] = take_a ? A[i++] : B[j++];
+      }
+    }
+    __syncthreads();
+    uint64_t *t = src; src = dst; dst = t;
+  }
+  if (src != arr) {
+    for (int t = tid; t < P; t += NT) arr[t] = src[t];
+    __syncthreads();
+  }
 }
 
 // Appends every register candidate j with sel(j) to list (composites, in no
@@ -231,7 +291,8 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[J], IdxFn idx_
   } else {
     for (int i = L + tid; i < P; i += NT) sm.u.list[i] = ~0ull;
     __syncthreads();
-    bitonic_sort_u64<NT>(sm.u.list, P);
+    if (P <= 8 * NT) merge_sort_u64<NT>(sm.u.list, sm.tmp, P);
+    else bitonic_sort_u64<NT>(sm.u.list, P);
   }
 }
 

@@ -83,6 +83,17 @@ size_t attn_ids_bytes(const gr_shape *s, int n_beams) {
   return s->dtype == GR_BF16 ? align_up(gr::attn_ids_bytes(s->R, n_beams)) : 0;
 }
 
+// The bf16 codebook step feeds the attention output to the projection MFMA
+// in bf16.  Its rounding perturbs a logit by about 2^-9 |o| |W|; over a long
+// window o is an average of many values and the perturbation stays far below
+// the near-tie scale of the selection, but with a handful of keys |o| can be
+// as large as one value row.  Windows shorter than this take the fp32 path
+// (fp32 o, fp32 projection, scoring from fp32 logits).
+constexpr int kMfmaLogitsMinWindow = 64;
+bool use_mfma_logits(const gr_shape *s, int vocab) {
+  return s->dtype == GR_BF16 && vocab == 256 && prompt_window(s) >= kMfmaLogitsMinWindow;
+}
+
 struct DecodeLayout {
   size_t o_off, o_bytes, z_off, z_bytes, part_off, part_bytes, ids_off, ids_bytes, total;
 };
@@ -90,7 +101,7 @@ DecodeLayout decode_layout(const gr_shape *s, int n_beams, int vocab, int k) {
   DecodeLayout L;
   const size_t rows = (size_t)s->R * n_beams;
   const size_t D = (size_t)s->H * s->head_dim;
-  const bool mfma_logits = s->dtype == GR_BF16 && vocab == 256;
+  const bool mfma_logits = use_mfma_logits(s, vocab);
   // bf16 codebook path feeds the MFMA projection with a bf16 copy of o; the
   // other paths keep o in fp32 and write logits / scalar scores to z.
   L.o_bytes = align_up(rows * D * (mfma_logits ? 2 : 4));
@@ -313,7 +324,7 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void
 
   gr::AttnArgs a = attn_args(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, dev_err);
   a.chain_ids = L.ids_bytes ? (int32_t *)(base + L.ids_off) : nullptr;
-  const bool mfma_logits = shape->dtype == GR_BF16 && vocab == 256;
+  const bool mfma_logits = use_mfma_logits(shape, vocab);
   const float *o_f32 = nullptr;
   if (mfma_logits) {
     a.out_lowp = o_buf;

@@ -158,6 +158,7 @@ TOPK_CASES = {
     "single_root": dict(R=4, n_in=1, vocab=256, k=8, lsm=True, prior="zero"),
     "scalar_2000_of_40000": dict(R=1, n_in=40000, vocab=1, k=2000, lsm=False, prior="none"),
     "scalar_ties": dict(R=2, n_in=5000, vocab=1, k=700, lsm=False, prior="none", quant=True),
+    "max_k": dict(R=2, n_in=20, vocab=256, k=2048, lsm=True, prior="cumsum"),   # k = GR_MAX_K
 }
 
 

@@ -38,6 +38,13 @@ SMALL = {
     "scalar_small": W.reduced(CF["broadcast40k_u256"], n_in=3000, k=333, level_sizes=(3000,)),
     "f32_beam16": W.reduced(CF["beam100_p600"], R=2, Lp=40, H=4, d=32, n_in=16, k=16,
                             level_sizes=(9, 16, 16), dtype="f32"),
+    # edge cases: chains of the maximum depth (8 records), a one-token prompt,
+    # a one-token window, a single live beam
+    "depth8_chains": W.reduced(CF["beam100_p600"], R=2, Lp=70, H=2, n_in=40, k=40, depth=8,
+                               level_sizes=(24, 40, 40, 40, 40, 40, 40, 40)),
+    "one_token_prompt": W.reduced(CF["beam50_p600"], R=2, Lp=1, level_sizes=(30, 50)),
+    "one_token_window": W.reduced(CF["beam50_p600"], R=2, Lp=100, window=1, level_sizes=(30, 50)),
+    "single_beam": W.reduced(CF["beam50_p600"], R=3, Lp=64, n_in=1, k=1, level_sizes=(1, 1)),
 }
 
 

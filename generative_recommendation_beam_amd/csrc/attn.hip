@@ -47,7 +47,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Ring depth of the bf16 kernel: 3 stages of 64 keys (2 tiles in flight)
 // keep a 4-wave workgroup at 52 KB of LDS and <= 168 VGPRs, so three
 // workgroups share a CU.
-constexpr int kAttnStages = 3;
+#ifndef GR_ATTN_STAGES
+#define GR_ATTN_STAGES 3
+#endif
+constexpr int kAttnStages = GR_ATTN_STAGES;
 
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 
@@ -136,14 +139,15 @@ __device__ __forceinline__ int swz_v(int row) {
 template <int HD, int NW, int NS, int OCC>
 __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   using G = Geo<HD, NW, NS>;
-  static_assert(NS == 3 || NS == 4, "ring depth: the last stage carries the queries until it is first refilled");
+  static_assert(NS >= 2 && NS <= 4, "ring depth: the last stage carries the queries until it is first refilled");
   static_assert(G::NBLK % NW == 0, "every wave moves the same number of 1 KB blocks");
   static_assert(G::NB <= 2 * G::KT, "queries of a workgroup fit the two buffers of one stage");
   // One LDS object per ring stage (its K half, then its V half): the
   // compiler then sees that a DMA into one stage does not touch the stage
   // being read, and adds no waits for it.  (It tells apart only a few LDS
   // DMA targets, so there are just five: four stages and the chain ids.)
-  __shared__ __attribute__((aligned(1024))) uint16_t KV0[G::TB], KV1[G::TB], KV2[G::TB], KV3[NS > 3 ? G::TB : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t KV0[G::TB], KV1[G::TB], KV2[NS > 2 ? G::TB : 8],
+      KV3[NS > 3 ? G::TB : 8];
   // dynamic LDS: chain ids [D][NB] (level-major), then, when the chains are
   // resolved here, the request's parent array and the workgroup's beam nodes
   extern __shared__ __attribute__((aligned(1024))) int32_t dyn_s[];
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
     }
   }
   issue_prompt(0, Stage<0>{});
-  issue_prompt(1, Stage<1>{});
+  if constexpr (NS > 2) issue_prompt(1, Stage<1>{});
   if constexpr (NS > 3) issue_prompt(2, Stage<2>{});
 
   // per-lane LDS byte offsets of the operand reads (stage base added later)
@@ -478,7 +482,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   for (int t0 = 0; t0 < n_total; t0 += NS) {
     step(t0, Stage<0>{});
     step(t0, Stage<1>{});
-    step(t0, Stage<2>{});
+    if constexpr (NS > 2) step(t0, Stage<2>{});
     if constexpr (NS > 3) step(t0, Stage<3>{});
   }
 
@@ -644,7 +648,7 @@ constexpr int kLdsChainNodes = 4096;
 
 template <int HD, int NW>
 hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
-  constexpr int NS = kAttnStages, OCC = NW == 4 ? 3 : (NW == 2 ? 2 : 1);
+  constexpr int NS = kAttnStages, OCC = NW == 4 ? 6 - NS : (NW == 2 ? 2 : 1);
   constexpr int NB = NW * 32;
   AttnP p;
   p.pk = (const uint16_t *)a.pk; p.pv = (const uint16_t *)a.pv; p.q = (const uint16_t *)a.q;

@@ -9,21 +9,24 @@
 //   keys = prompt rows [Lp-Lw, Lp) then the records on chain(beam_node[b]),
 //   o[b][h*hd+i] = sum_j softmax_j(scale * q.k_j) v_j[i].
 //
-// bf16 path (gfx950 MFMA), two kernels.
-//
-// chain_resolve: one thread per beam follows the parent links from the beam's
-// own record to the root (checking range, order and depth) and stores the
-// node ids level-major, [r][level][beam].  This is the ancestry index of the
-// step: the attention kernel never chases a pointer.
+// bf16 path (gfx950 MFMA).
 //
 // attn_bf16: one workgroup per (request, head, group of NW x 32 beams).
-// Everything the workgroup reads goes HBM -> LDS with global_load_lds_dwordx4
-// through one NS-stage ring of 64-row tiles, NS-1 tiles in flight: first the
-// chain ids and the queries, then the prompt window (read from HBM once per
-// (request, head), never copied per beam), then the chain records gathered
-// row by row (one tile per chain level and 64 beams).  Vector loads complete
-// in issue order, so keeping every load on this one in-order stream makes each
-// wait exact and keeps the ring full while the chain is processed.
+// Everything the workgroup reads goes HBM -> LDS with global_load_lds through
+// one NS-stage ring of 64-row tiles, NS-1 tiles in flight, in this order: the
+// request's parent ids and the workgroup's beam nodes, the queries, the prompt
+// window (read from HBM once per (request, head), never copied per beam), then
+// the chain records gathered row by row (one tile per chain level and 64
+// beams).  Vector loads complete in issue order, so keeping every load on this
+// one in-order stream makes each wait exact and keeps the ring full while the
+// chains are processed.  At the first tile each beam's chain is resolved in
+// LDS (parent links from the beam's own record to the root, with range, order
+// and depth checks) into level-major node ids: the ancestry index of the step.
+// The attention output leaves through LDS so that stores write whole lines.
+//
+// chain_resolve: the same chain walk, one thread per beam in global memory,
+// for arenas too large to stage in LDS; its ids reach the attention kernel
+// through the workspace.
 //
 // Scores are formed transposed, S^T = K Q^T (keys x beams), with
 // v_mfma_f32_32x32x16_bf16: the accumulator holds one beam per lane column,

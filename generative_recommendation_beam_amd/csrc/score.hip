@@ -8,13 +8,13 @@
 //
 // logits_select_bf16: one workgroup (8 waves) per (request, group of <= 128
 // beams).  z^T = W o^T on v_mfma_f32_32x32x16_bf16 (codes x beams; wave w owns
-// beams 32*(w/2).. and codes 128*(w%2)..).  W streams through LDS in chunks of
-// 64 columns (cooperative, double-buffered loads, read once per workgroup);
-// o fragments come straight from global memory one chunk ahead.  Each lane
-// then holds 64 codes of one beam in registers: the log-softmax is in-lane
-// plus one lane^32 swap and one LDS exchange between the two code halves, and
-// the selection (gr_select.h) runs on those registers; scores never leave the
-// chip unless the caller asks for them.
+// beams 32*(w/2).. and codes 128*(w%2)..).  W and o stream HBM/L2 -> LDS
+// through a ring of 32-column chunks (global_load_lds, several chunks in
+// flight, each read once per workgroup).  Each lane then holds 64 codes of one
+// beam in registers: the log-softmax is in-lane plus one lane^32 swap and one
+// LDS exchange between the two code halves, and the selection (gr_select.h)
+// runs on those registers; scores never leave the chip unless the caller asks
+// for them.
 //
 // score_select: the same scoring and selection starting from fp32 logits in
 // global memory (the standalone top-k entry point, the fp32 path and scalar

@@ -241,34 +241,47 @@ __global__ __launch_bounds__(kNT) void score_select_kernel(SP p) {
   emit_selection<kNT>(sm.sel, k_sel, r, grp, p.vocab, p.score, p.token, p.parent, p.partial, p.n_groups, p.kk);
 }
 
-__global__ __launch_bounds__(kNT) void select_merge_kernel(const uint64_t *partial, int n_groups, int kk, int k,
-                                                           int vocab, float *score, int32_t *token,
-                                                           int32_t *parent) {
-  __shared__ SelectSmem<kNT> sm;
-  constexpr int J = kMergeCapacity / kNT;
+// Final selection from n_groups sorted partial lists of kk composites each
+// (ascending, padded with ~0): the k smallest of their union.  Composites are
+// unique, so the output slot of an entry is its index in its own list plus,
+// for every other list, the number of entries below it (one binary search in
+// LDS each); entries whose slot falls below k are written directly.  Block
+// (r, y) stages all lists of request r and ranks entries y*kMergeNT onwards,
+// one per thread.
+constexpr int kMergeNT = 1024;
+
+__global__ __launch_bounds__(kMergeNT) void select_merge_kernel(const uint64_t *partial, int n_groups, int kk, int k,
+                                                                int vocab, float *score, int32_t *token,
+                                                                int32_t *parent) {
+  extern __shared__ uint64_t lists[];              // n_groups * kk entries
   const int r = blockIdx.x, tid = threadIdx.x;
   const int n = n_groups * kk;
   const uint64_t *src = partial + (size_t)r * n;
-  uint32_t key[J], ix[J];
-  uint32_t n_valid = 0;
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int i = j * kNT + tid;
-    const uint64_t x = i < n ? src[i] : ~0ull;
-    key[j] = (uint32_t)(x >> 32);          // group padding (~0) reads as kInvalidKey
-    ix[j] = (uint32_t)x;
-    n_valid += key[j] != kInvalidKey ? 1u : 0u;
+  for (int i = tid; i < n; i += kMergeNT) lists[i] = src[i];
+  __syncthreads();
+  const int e = blockIdx.y * kMergeNT + tid;
+  if (e >= n) return;
+  const uint64_t x = lists[e];
+  if (x == ~0ull) return;                          // group padding
+  const int g = e / kk;
+  int slot = e - g * kk;
+  for (int g2 = 0; g2 < n_groups && slot < k; ++g2) {
+    if (g2 == g) continue;
+    const uint64_t *Lg = lists + g2 * kk;
+    int lo = 0, hi = kk;                           // entries of list g2 below x
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (Lg[mid] < x) lo = mid + 1;
+      else hi = mid;
+    }
+    slot += lo;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) n_valid += (uint32_t)__shfl_xor((int)n_valid, o);
-  if ((tid & 63) == 0) sm.wtot[tid >> 6] = n_valid;
-  __syncthreads();
-  int tot = 0;
-  for (int w = 0; w < kNT / 64; ++w) tot += (int)sm.wtot[w];
-  __syncthreads();
-  auto idx_of = [&](int j) -> uint32_t { return ix[j]; };
-  select_regs<kNT, J>(key, idx_of, tot, k, sm);
-  emit_selection<kNT>(sm, k, r, 0, vocab, score, token, parent, nullptr, 1, k);
+  if (slot < k) {
+    const uint32_t f = (uint32_t)x;
+    score[(size_t)r * k + slot] = key_score((uint32_t)(x >> 32));
+    token[(size_t)r * k + slot] = (int32_t)(f % (uint32_t)vocab);
+    parent[(size_t)r * k + slot] = (int32_t)(f / (uint32_t)vocab);
+  }
 }
 
 // z[row][t] = sum_i o[row][i] W[t][i] (+ prior[row] for the scalar path).
@@ -325,8 +338,10 @@ hipError_t launch_score_select(const ScoreSelectArgs &a, const SelectOut &o, hip
 }
 
 hipError_t launch_select_merge(const SelectOut &o, int R, int k, int vocab, hipStream_t s) {
-  hipLaunchKernelGGL(select_merge_kernel, dim3((unsigned)R), dim3(kNT), 0, s, o.partial, o.n_groups, o.kk, k, vocab,
-                     o.score, o.token, o.parent);
+  const int n = o.n_groups * o.kk;                 // <= kMergeCapacity (checked by the caller)
+  const dim3 grid((unsigned)R, (unsigned)((n + kMergeNT - 1) / kMergeNT));
+  hipLaunchKernelGGL(select_merge_kernel, grid, dim3(kMergeNT), (size_t)n * sizeof(uint64_t), s, o.partial,
+                     o.n_groups, o.kk, k, vocab, o.score, o.token, o.parent);
   return hipGetLastError();
 }
 

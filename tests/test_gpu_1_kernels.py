@@ -159,6 +159,10 @@ TOPK_CASES = {
     "scalar_2000_of_40000": dict(R=1, n_in=40000, vocab=1, k=2000, lsm=False, prior="none"),
     "scalar_ties": dict(R=2, n_in=5000, vocab=1, k=700, lsm=False, prior="none", quant=True),
     "max_k": dict(R=2, n_in=20, vocab=256, k=2048, lsm=True, prior="cumsum"),   # k = GR_MAX_K
+    # final merge over several groups: exact ties across group boundaries, and
+    # 3 x 2048 partial entries ranked by several blocks per request
+    "merge_ties": dict(R=2, n_in=200, vocab=256, k=300, lsm=False, prior="int", quant=True),
+    "merge_max_k": dict(R=2, n_in=300, vocab=256, k=2048, lsm=True, prior="cumsum"),
 }
 
 

@@ -350,6 +350,7 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void
     l.R = R;
     l.n_in = n_beams;
     l.D = D;
+    l.hd = shape->head_dim;
     l.k = beam_width;
     l.log_softmax = lsm;
     return hip_status(gr::launch_logits_select_bf16(l, so, stream));

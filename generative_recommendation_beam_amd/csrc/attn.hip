@@ -499,6 +499,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   const float inv = valid ? 1.f / l_tot : 0.f;
   const size_t out_row0 = ((size_t)r * p.nb + (size_t)grp * G::NB) * row + (size_t)h * HD;
   const int n_rows = min(G::NB, p.nb - grp * G::NB);   // rows of this workgroup that exist
+  // bf16 feed of the projection: head-major [R][H][nb][HD], so that this
+  // workgroup's rows form one contiguous block
+  const size_t lowp_row0 = (((size_t)r * p.H + h) * p.nb + (size_t)grp * G::NB) * HD;
   __syncthreads();                                      // every wave is past its last tile
   if (p.out_bf16 != nullptr) {
     constexpr int CPR = HD / 8;                         // 16-byte chunks per bf16 row
@@ -516,7 +519,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
     for (int id = tid; id < n_rows * CPR; id += NW * 64) {
       const int rr = id / CPR, ch = id % CPR;
       const uint4 v = *(const uint4 *)(st + rr * HD + ((ch ^ (rr & (CPR - 1))) << 3));
-      *(uint4 *)(p.out_bf16 + out_row0 + (size_t)rr * row + ch * 8) = v;
+      *(uint4 *)(p.out_bf16 + lowp_row0 + (size_t)rr * HD + ch * 8) = v;
     }
     __syncthreads();
   }

@@ -18,7 +18,7 @@ struct AttnArgs {
   const int32_t *beam_node;        // [R][nb] or null (prompt only)
   int32_t *chain_ids;              // bf16 path: workspace for the resolved chains, attn_ids_bytes(R, nb)
   float *out_f32;                  // optional [R][nb][H*hd]
-  void *out_lowp;                  // optional [R][nb][H*hd] in dtype (bf16 feed of the logits)
+  void *out_lowp;                  // optional head-major [R][H][nb][hd] in dtype (bf16 feed of the logits)
   int32_t *dev_err;
   int R, H, hd, Lp, Lw, nb, cap, max_depth;
   float scale;
@@ -62,11 +62,11 @@ struct SelectOut {
 // Codebook projection on MFMA (bf16 o, bf16 W [256][D]), log-softmax, prior,
 // selection of each group of <= 128 beams.
 struct LogitsArgs {
-  const uint16_t *o;               // [R][n_in][D] bf16
+  const uint16_t *o;               // head-major [R][H][n_in][hd] bf16, D = H * hd
   const uint16_t *W;               // [256][D] bf16
   const float *prior;              // [R][n_in] or null
   float *cand_out;                 // optional [R][n_in][256]
-  int R, n_in, D, k, log_softmax;
+  int R, n_in, D, hd, k, log_softmax;
 };
 hipError_t launch_logits_select_bf16(const LogitsArgs &a, const SelectOut &o, hipStream_t s);
 

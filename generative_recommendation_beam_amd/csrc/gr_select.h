@@ -95,6 +95,83 @@ __device__ __forceinline__ void bitonic_sort_u64_reg(uint64_t *arr, int L, int P
   __syncthreads();
 }
 
+// Value of lane l ^ S (S < 64) of a 64-bit composite: DPP for S <= 8, one
+// permlane swap per half for 16 and 32 (the swap yields this lane's own half
+// and the partner's; where the two are equal either one is the partner's).
+template <int S>
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t x) {
+  const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+  if constexpr (S <= 8) {
+    return ((uint64_t)xor_lane<S>(hi) << 32) | xor_lane<S>(lo);
+  } else {
+    uint32_t a0, b0, a1, b1;
+    xor_pair<S>(lo, a0, b0);
+    xor_pair<S>(hi, a1, b1);
+    const uint32_t plo = a0 == lo ? b0 : a0, phi = a1 == hi ? b1 : a1;
+    return ((uint64_t)phi << 32) | plo;
+  }
+}
+
+// One compare-exchange step of the wave bitonic sort below (stride S < 64):
+// positions 64 e + l and 64 e + (l ^ S) keep min / max by direction.
+template <int E, int S>
+__device__ __forceinline__ void wave_bitonic_step(uint64_t (&v)[E], int size, int lane) {
+  const bool lower = (lane & S) == 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint64_t y = lane_xor_u64<S>(v[e]);
+    const bool up = ((64 * e + lane) & size) == 0;
+    const uint64_t mn = v[e] < y ? v[e] : y, mx = v[e] < y ? y : v[e];
+    v[e] = (lower == up) ? mn : mx;
+  }
+}
+
+// Ascending bitonic sort of 64 E composites held by one wave, E per lane
+// (v[e] of lane l is position 64 e + l).  Strides below 64 exchange across
+// lanes without LDS, larger ones between a lane's own registers; no barrier.
+template <int E>
+__device__ __forceinline__ void wave_bitonic_sort_u64(uint64_t (&v)[E]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 64 * E; size <<= 1) {
+#pragma unroll
+    for (int es = (size >> 7); es > 0; es >>= 1) {        // strides 64 es >= 64
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (e & es) continue;
+        const int f = e | es;
+        const bool up = ((64 * e) & size) == 0;
+        const uint64_t a = v[e], b = v[f];
+        const uint64_t mn = a < b ? a : b, mx = a < b ? b : a;
+        v[e] = up ? mn : mx;
+        v[f] = up ? mx : mn;
+      }
+    }
+    if (size >= 64) wave_bitonic_step<E, 32>(v, size, lane);
+    if (size >= 32) wave_bitonic_step<E, 16>(v, size, lane);
+    if (size >= 16) wave_bitonic_step<E, 8>(v, size, lane);
+    if (size >= 8) wave_bitonic_step<E, 4>(v, size, lane);
+    if (size >= 4) wave_bitonic_step<E, 2>(v, size, lane);
+    wave_bitonic_step<E, 1>(v, size, lane);
+  }
+}
+
+// Sorts arr[0..64 E) (entries L.. are padding) with wave 0 alone; the other
+// waves only take the trailing barrier.
+template <int E>
+__device__ __forceinline__ void wave_sort_list(uint64_t *arr, int L) {
+  if ((threadIdx.x >> 6) == 0) {
+    const int lane = threadIdx.x & 63;
+    uint64_t v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = 64 * e + lane < L ? arr[64 * e + lane] : ~0ull;
+    wave_bitonic_sort_u64<E>(v);
+#pragma unroll
+    for (int e = 0; e < E; ++e) arr[64 * e + lane] = v[e];
+  }
+  __syncthreads();
+}
+
 // Ascending sort of arr[0..P) for NT < P <= 8 NT (P a power of two): each
 // thread sorts E = P/NT consecutive entries in registers (a bitonic network
 // over 8 slots, padding sorting last), then log2(NT) merge-path rounds double
@@ -286,7 +363,13 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[J], IdxFn idx_
   __syncthreads();
   const int L = min(sm.n_list, kListCap);
   const int P = pow2_ceil(max(L, k));
-  if (P <= NT) {
+  if (P <= 64) {
+    wave_sort_list<1>(sm.u.list, L);
+  } else if (P <= 128) {
+    wave_sort_list<2>(sm.u.list, L);
+  } else if (P <= 256) {
+    wave_sort_list<4>(sm.u.list, L);
+  } else if (P <= NT) {
     bitonic_sort_u64_reg<NT>(sm.u.list, L, P);
   } else {
     for (int i = L + tid; i < P; i += NT) sm.u.list[i] = ~0ull;

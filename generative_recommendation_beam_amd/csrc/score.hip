@@ -59,7 +59,7 @@ struct LP {
   float *score;
   int32_t *token, *parent;
   uint64_t *partial;
-  int R, n_in, D, k, lsm, n_groups, kk;
+  int R, n_in, D, hd_log2, k, lsm, n_groups, kk;
 };
 
 __device__ __forceinline__ int swz64(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
@@ -83,11 +83,14 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
   // the logical chunk that the swizzle puts at physical chunk l%4.  Wave w
   // moves W blocks 2w, 2w+1 and o block w of every chunk (3 DMAs per chunk).
   // Chunks past the end re-read the last one (never used), so every step
-  // has exactly kRS-2 chunks in flight behind the one it consumes.
+  // has the same number of chunks in flight.
+  // o is head-major ([R][H][n_in][hd]); a 32-column chunk lies inside one head.
   const int drow = lane >> 2, dpc = lane & 3;
-  const uint16_t *orow_base = p.o + (size_t)r * p.n_in * p.D;
+  const int hd = 1 << p.hd_log2, H = p.D >> p.hd_log2;
+  const uint16_t *o_req = p.o + (size_t)r * H * p.n_in * hd;
   auto issue = [&](int chunk, int st) {
     const int col0 = min(chunk, n_chunks - 1) * kOC;
+    const int hc = col0 >> p.hd_log2, c_in = col0 & (hd - 1);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int blk = wave * 2 + i, row = blk * 16 + drow;
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
     {
       const int row = wave * 16 + drow, lc = dpc ^ swz64(row);
       const int b = min(b_begin + row, p.n_in - 1);
-      dma16(orow_base + (size_t)b * p.D + col0 + lc * 8, &sm.u.ring[st].o[wave * 512]);
+      dma16(o_req + ((size_t)hc * p.n_in + b) * hd + c_in + lc * 8, &sm.u.ring[st].o[wave * 512]);
     }
   };
   // per-lane LDS element offsets of the operand reads (logical chunk 2kk+g)
@@ -116,22 +119,46 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
 
-#pragma unroll
-  for (int c0 = 0; c0 < kRS - 1; ++c0) issue(c0, c0);
-  for (int chunk = 0; chunk < n_chunks; ++chunk) {
-    GR_WAIT_VMCNT(3 * (kRS - 2));           // this wave's pieces of `chunk` landed
-    ring_barrier();                         // everyone's, and stage chunk-1 is free
-    issue(chunk + kRS - 1, (chunk + kRS - 1) % kRS);
+  // Operands of chunk c+1 are read from LDS into registers while the MFMAs
+  // of chunk c run, so LDS reads, DMA fills and MFMAs overlap.
+  bf16x8 opa[2][2][4], opb[2][2];
+  auto read_ops = [&](int chunk, int buf) {
     const LogitsStage &S = sm.u.ring[chunk % kRS];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 b = *(const bf16x8 *)&S.o[boff[kk]];
+      opb[buf][kk] = *(const bf16x8 *)&S.o[boff[kk]];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const bf16x8 a = *(const bf16x8 *)&S.w[aoff[m][kk]];
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[m], 0, 0, 0);
-      }
+      for (int m = 0; m < 4; ++m) opa[buf][kk][m] = *(const bf16x8 *)&S.w[aoff[m][kk]];
     }
+  };
+  auto mfma_ops = [&](int buf) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[buf][kk][m], opb[buf][kk], acc[m], 0, 0, 0);
+  };
+#pragma unroll
+  for (int c0 = 0; c0 < kRS - 1; ++c0) issue(c0, c0);
+  GR_WAIT_VMCNT(3 * (kRS - 2));             // this wave's pieces of chunk 0 landed
+  ring_barrier();                           // everyone's
+  read_ops(0, 0);
+  // Iteration c: chunk c+1 must have landed (chunks c+2 .. c+kRS-2 may still
+  // be in flight); after the barrier every wave has consumed chunk c-1, whose
+  // stage receives chunk c+kRS-1.  The loop runs in pairs so that the two
+  // register buffers are fixed; an odd last chunk leaves after the first half.
+  for (int chunk = 0; chunk < n_chunks; chunk += 2) {
+    GR_WAIT_VMCNT(3 * (kRS - 3));
+    ring_barrier();
+    issue(chunk + kRS - 1, (chunk + kRS - 1) % kRS);
+    read_ops(chunk + 1, 1);                 // past the end: a landed re-read, unused
+    mfma_ops(0);
+    if (chunk + 1 == n_chunks) break;
+    GR_WAIT_VMCNT(3 * (kRS - 3));
+    ring_barrier();
+    issue(chunk + kRS, (chunk + kRS) % kRS);
+    read_ops(chunk + 2, 0);
+    mfma_ops(1);
   }
   GR_WAIT_VMCNT(0);                         // the trailing re-reads landed
   ring_barrier();                           // before the LDS is reused
@@ -317,8 +344,8 @@ hipError_t launch_logits_select_bf16(const LogitsArgs &a, const SelectOut &o, hi
   LP p;
   p.o = a.o; p.W = a.W; p.prior = a.prior; p.cand = a.cand_out;
   p.score = o.score; p.token = o.token; p.parent = o.parent; p.partial = o.partial;
-  p.R = a.R; p.n_in = a.n_in; p.D = a.D; p.k = a.k; p.lsm = a.log_softmax;
-  p.n_groups = o.n_groups; p.kk = o.kk;
+  p.R = a.R; p.n_in = a.n_in; p.D = a.D; p.hd_log2 = __builtin_ctz((unsigned)a.hd); p.k = a.k;
+  p.lsm = a.log_softmax; p.n_groups = o.n_groups; p.kk = o.kk;
   hipLaunchKernelGGL(logits_select_bf16_kernel, dim3((unsigned)(a.R * o.n_groups)), dim3(kNT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || o.n_groups == 1) return e;

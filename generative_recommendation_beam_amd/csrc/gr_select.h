@@ -66,35 +66,6 @@ __device__ __forceinline__ void bitonic_sort_u64(uint64_t *arr, int P) {
   }
 }
 
-// The same sort for P <= NT entries, one per thread, in registers: strides
-// below 64 exchange through lane shuffles, larger ones through LDS.  Entries
-// L..P-1 are padding (~0).  The sorted list is written back to arr[0..P).
-template <int NT>
-__device__ __forceinline__ void bitonic_sort_u64_reg(uint64_t *arr, int L, int P) {
-  const int tid = threadIdx.x;
-  uint64_t x = tid < L ? arr[tid] : ~0ull;
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      uint64_t y;
-      if (stride >= 64) {
-        __syncthreads();
-        if (tid < P) arr[tid] = x;
-        __syncthreads();
-        y = tid < P ? arr[tid ^ stride] : ~0ull;
-      } else {
-        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, stride);
-        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), stride);
-        y = ((uint64_t)hi << 32) | lo;
-      }
-      const bool up = (tid & size) == 0, lower = (tid & stride) == 0;
-      x = (lower == up) ? (x < y ? x : y) : (x < y ? y : x);
-    }
-  }
-  __syncthreads();
-  if (tid < P) arr[tid] = x;
-  __syncthreads();
-}
-
 // Value of lane l ^ S (S < 64) of a 64-bit composite: DPP for S <= 8, one
 // permlane swap per half for 16 and 32 (the swap yields this lane's own half
 // and the partner's; where the two are equal either one is the partner's).
@@ -115,12 +86,12 @@ __device__ __forceinline__ uint64_t lane_xor_u64(uint64_t x) {
 // One compare-exchange step of the wave bitonic sort below (stride S < 64):
 // positions 64 e + l and 64 e + (l ^ S) keep min / max by direction.
 template <int E, int S>
-__device__ __forceinline__ void wave_bitonic_step(uint64_t (&v)[E], int size, int lane) {
+__device__ __forceinline__ void wave_bitonic_step(uint64_t (&v)[E], int size, int lane, int base = 0) {
   const bool lower = (lane & S) == 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint64_t y = lane_xor_u64<S>(v[e]);
-    const bool up = ((64 * e + lane) & size) == 0;
+    const bool up = ((base + 64 * e + lane) & size) == 0;
     const uint64_t mn = v[e] < y ? v[e] : y, mx = v[e] < y ? y : v[e];
     v[e] = (lower == up) ? mn : mx;
   }
@@ -156,20 +127,62 @@ __device__ __forceinline__ void wave_bitonic_sort_u64(uint64_t (&v)[E]) {
   }
 }
 
-// Sorts arr[0..64 E) (entries L.. are padding) with wave 0 alone; the other
-// waves only take the trailing barrier.
-template <int E>
-__device__ __forceinline__ void wave_sort_list(uint64_t *arr, int L) {
-  if ((threadIdx.x >> 6) == 0) {
-    const int lane = threadIdx.x & 63;
-    uint64_t v[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) v[e] = 64 * e + lane < L ? arr[64 * e + lane] : ~0ull;
-    wave_bitonic_sort_u64<E>(v);
-#pragma unroll
-    for (int e = 0; e < E; ++e) arr[64 * e + lane] = v[e];
+// Ascending bitonic sort of arr[0..P) (P <= NT a power of two; entries L..
+// are padding), one entry per thread of the first ceil(P/64) waves: strides
+// below 64 exchange across lanes without LDS (DPP / permlane), strides of 64
+// and more through LDS with a barrier.  Every thread takes the barriers.
+template <int NT>
+__device__ __forceinline__ void block_bitonic_sort_u64(uint64_t *arr, int L, int P) {
+  const int tid = threadIdx.x, lane = tid & 63, base = tid & ~63;
+  const bool act = base < P;                             // whole waves
+  uint64_t v[1] = {act && tid < L ? arr[tid] : ~0ull};
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride >= 64; stride >>= 1) {
+      __syncthreads();
+      if (act) arr[tid] = v[0];
+      __syncthreads();
+      if (act) {
+        const uint64_t y = arr[tid ^ stride];
+        const bool up = (tid & size) == 0, lower = (tid & stride) == 0;
+        const uint64_t mn = v[0] < y ? v[0] : y, mx = v[0] < y ? y : v[0];
+        v[0] = (lower == up) ? mn : mx;
+      }
+    }
+    if (act) {
+      if (size >= 64) wave_bitonic_step<1, 32>(v, size, lane, base);
+      if (size >= 32) wave_bitonic_step<1, 16>(v, size, lane, base);
+      if (size >= 16) wave_bitonic_step<1, 8>(v, size, lane, base);
+      if (size >= 8) wave_bitonic_step<1, 4>(v, size, lane, base);
+      if (size >= 4) wave_bitonic_step<1, 2>(v, size, lane, base);
+      wave_bitonic_step<1, 1>(v, size, lane, base);
+    }
   }
   __syncthreads();
+  if (act) arr[tid] = v[0];
+  __syncthreads();
+}
+
+// The m-th smallest (m = 1 or 2, counting equal values) of one u32 per lane
+// across the wave: a butterfly that keeps each lane's two smallest.
+__device__ __forceinline__ uint32_t wave_small2_u32(uint32_t x, int m) {
+  uint32_t m1 = x, m2 = 0xFFFFFFFFu;
+  auto merge = [&](uint32_t p1, uint32_t p2) {
+    const uint32_t n2 = min(max(m1, p1), min(m2, p2));
+    m1 = min(m1, p1);
+    m2 = n2;
+  };
+  merge(xor_lane<1>(m1), xor_lane<1>(m2));
+  merge(xor_lane<2>(m1), xor_lane<2>(m2));
+  merge(xor_lane<4>(m1), xor_lane<4>(m2));
+  merge(xor_lane<8>(m1), xor_lane<8>(m2));
+  uint32_t a1, b1, a2, b2;
+  xor_pair<16>(m1, a1, b1);
+  xor_pair<16>(m2, a2, b2);
+  merge(a1 == m1 ? b1 : a1, a2 == m2 ? b2 : a2);
+  xor_pair<32>(m1, a1, b1);
+  xor_pair<32>(m2, a2, b2);
+  merge(a1 == m1 ? b1 : a1, a2 == m2 ? b2 : a2);
+  return m == 1 ? m1 : m2;
 }
 
 // Ascending sort of arr[0..P) for NT < P <= 8 NT (P a power of two): each
@@ -258,10 +271,13 @@ __device__ __forceinline__ void append_selected(const uint32_t (&key)[J], IdxFn 
 // the block (key[j] != kInvalidKey; the index of slot j is idx_of(j)).  n_valid
 // is their number, 1 <= k <= min(n_valid, kMaxK).  On return the first k
 // entries of sm.u.list hold them in ascending order.  All threads call it.
-// Always inlined: the candidates must stay in registers (a call would pass
-// them through scratch memory).
+// Radix passes continue while the bucket of the k-th candidate holds more
+// than bucket_cap (<= kBucketCap) members; a small cap trades passes for a
+// shorter list to sort.  Always inlined: the candidates must stay in
+// registers (a call would pass them through scratch memory).
 template <int NT, int J, typename IdxFn>
-__device__ __forceinline__ void select_regs(const uint32_t (&key)[J], IdxFn idx_of, int n_valid, int k, SelectSmem<NT> &sm) {
+__device__ __forceinline__ void select_regs(const uint32_t (&key)[J], IdxFn idx_of, int n_valid, int k, SelectSmem<NT> &sm,
+                                            int bucket_cap = kBucketCap) {
   static_assert(NT % 64 == 0 && kHistBins % NT == 0, "block size");
   constexpr int NW = NT / 64;
   constexpr int BPT = kHistBins / NT;   // histogram bins scanned per thread
@@ -293,7 +309,7 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[J], IdxFn idx_
 
   // ---- radix passes over the bucket of the k-th candidate
   for (int pass = 0; pass < 8; ++pass) {
-    if (fixed_lo == 0 || bucket_cnt <= kBucketCap) break;
+    if (fixed_lo == 0 || bucket_cnt <= bucket_cap) break;
     const int shift = fixed_lo > kHistBits ? fixed_lo - kHistBits : 0;
     const uint32_t mask = (1u << (fixed_lo - shift)) - 1u;
     const uint64_t pre = fixed_lo >= 64 ? 0ull : (prefix >> fixed_lo);
@@ -363,14 +379,8 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[J], IdxFn idx_
   __syncthreads();
   const int L = min(sm.n_list, kListCap);
   const int P = pow2_ceil(max(L, k));
-  if (P <= 64) {
-    wave_sort_list<1>(sm.u.list, L);
-  } else if (P <= 128) {
-    wave_sort_list<2>(sm.u.list, L);
-  } else if (P <= 256) {
-    wave_sort_list<4>(sm.u.list, L);
-  } else if (P <= NT) {
-    bitonic_sort_u64_reg<NT>(sm.u.list, L, P);
+  if (P <= NT) {
+    block_bitonic_sort_u64<NT>(sm.u.list, L, P);
   } else {
     for (int i = L + tid; i < P; i += NT) sm.u.list[i] = ~0ull;
     __syncthreads();

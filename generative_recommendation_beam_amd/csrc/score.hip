@@ -50,7 +50,14 @@ struct LogitsSmem {
   } u;
   float red_max[4][2][32];
   float red_sum[4][2][32];
+  uint32_t bound[kNT / 64];                // per-wave bound keys of the fast selection
+  uint32_t fast_cnt[kNT / 64];             // per-wave survivor counts
 };
+// Fast selection: per-wave survivor regions in the (then idle) ring, and at
+// most 8 survivors per thread for the exact selection.
+constexpr int kFastRegion = 2048;
+constexpr int kFastList = 8 * kNT;
+static_assert(sizeof(LogitsStage) * kRS >= sizeof(uint64_t) * (kFastRegion + 64) * (kNT / 64), "survivor regions");
 
 struct LP {
   const uint16_t *o, *W;
@@ -187,29 +194,134 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
     lse = M + __builtin_amdgcn_logf(sm.red_sum[bb][0][c] + sm.red_sum[bb][1][c]) * kLn2;
   }
 
-  // candidate scores -> ordering keys in registers
-  uint32_t key[64];
+  // ---- selection.  Candidate score of register slot j = 16 m + 4 q4 + e:
+  // (acc[m][4 q4 + e] - lse) + prior.  Each lane holds 64 candidates of one
+  // beam, or none.
   const float pr = (valid && p.prior) ? p.prior[(size_t)r * p.n_in + beam] : 0.f;
   float *crow = (valid && p.cand) ? p.cand + ((size_t)r * p.n_in + beam) * 256 : nullptr;
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      float v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = (acc[m][4 * q4 + e] - lse) + pr;
-        key[16 * m + 4 * q4 + e] = valid ? rank_key(v[e]) : kInvalidKey;
-      }
-      if (crow) *(float4 *)(crow + ch * 128 + 32 * m + 8 * q4 + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
-    }
   const uint32_t row_base = (uint32_t)beam * 256u + ch * 128 + 4 * g;
   auto idx_of = [&](int j) -> uint32_t {
     return row_base + 32u * (uint32_t)(j >> 4) + 8u * (uint32_t)((j >> 2) & 3) + (uint32_t)(j & 3);
   };
   const int n = nbg * 256;
   const int k_sel = min(p.k, n);
-  select_regs<kNT, 64>(key, idx_of, n, k_sel, sm.u.sel);
+
+  // Fast path.  If ml = ceil(k/64) lanes of one wave have no score below s,
+  // at least k candidates score >= s, so the k best all do.  s is the ml-th
+  // largest lane minimum of a wave (the largest such bound over the waves;
+  // the lane minimum comes from the minimum of acc, the score being monotonic
+  // in it).  One pass then computes the scores and compacts the candidates
+  // >= s into per-wave regions (a ballot per slot, skipped when empty); when
+  // they are few the exact selection runs on them alone, 8 per thread.
+  // Otherwise (too many survivors, or a degenerate bound) it runs on all 64
+  // register slots.  Every decision is block-uniform.
+  bool cand_done = false, fast = false;
+  {
+    float amin = acc[0][0];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amin = fminf(amin, acc[m][i]);
+    const float worst = (amin - lse) + pr;
+    const uint32_t wkey = valid ? rank_key(worst) : kInvalidKey;
+    const int ml = (k_sel + 63) >> 6;
+    uint32_t tw;                                        // ml-th smallest lane-minimum key of the wave
+    if (ml <= 2) {
+      tw = wave_small2_u32(wkey, ml);
+    } else {
+      uint64_t wv[1] = {((uint64_t)wkey << 32) | (uint32_t)lane};
+      wave_bitonic_sort_u64<1>(wv);                     // ascending keys: best lane minima first
+      tw = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(wv[0] >> 32), ml - 1);
+    }
+    if (lane == 0) sm.bound[wave] = tw;
+    __syncthreads();
+    uint32_t T = sm.bound[0];
+#pragma unroll
+    for (int w = 1; w < kNT / 64; ++w) T = min(T, sm.bound[w]);
+    const float Ts = key_score(T);
+    if (T != kInvalidKey && Ts > -__builtin_inff()) {
+      cand_done = true;
+      // Region of this wave: kFastRegion slots, then one dummy slot per lane
+      // that absorbs the stores of unselected lanes (no divergent branch).
+      uint64_t *region = reinterpret_cast<uint64_t *>(&sm.u.ring[0]) + wave * (kFastRegion + 64);
+      const float t_lane = valid ? Ts : __builtin_nanf("");   // nothing compares >= NaN
+      int cnt = 0;                                        // wave-uniform
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (acc[m][4 * q4 + e] - lse) + pr;
+          if (crow) *(float4 *)(crow + ch * 128 + 32 * m + 8 * q4 + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool sel = v[e] >= t_lane;
+            const uint64_t mask = __builtin_amdgcn_ballot_w64(sel);
+            if (mask) {
+              const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+              const int dst = (sel && pos < kFastRegion) ? pos : kFastRegion + lane;
+              // selected scores are >= Ts > -inf, so not NaN: the key is the
+              // order-preserving bit map of v + 0 (which folds -0 into +0)
+              const uint32_t u = __float_as_uint(v[e] + 0.0f);
+              const uint32_t kv = u ^ ((uint32_t)((int32_t)~u >> 31) & 0x7FFFFFFFu);
+              region[dst] = ((uint64_t)kv << 32) | idx_of(16 * m + 4 * q4 + e);
+              cnt += __builtin_popcountll(mask);
+            }
+          }
+        }
+      if (lane == 0) sm.fast_cnt[wave] = (uint32_t)cnt;
+      __syncthreads();
+      int total = 0;
+      bool over = false;
+#pragma unroll
+      for (int w = 0; w < kNT / 64; ++w) {
+        total += (int)sm.fast_cnt[w];
+        over = over || (int)sm.fast_cnt[w] > kFastRegion;
+      }
+      if (!over && total >= k_sel && total <= kFastList) {
+        fast = true;
+        uint32_t key8[8], idx8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          int pidx = j * kNT + tid, w = 0;                 // position in the concatenated regions
+#pragma unroll
+          for (int w2 = 0; w2 < kNT / 64 - 1; ++w2)
+            if (w == w2 && pidx >= (int)sm.fast_cnt[w2]) { pidx -= (int)sm.fast_cnt[w2]; w = w2 + 1; }
+          key8[j] = kInvalidKey;
+          idx8[j] = 0u;
+          if (j * kNT + tid < total) {
+            const uint64_t x = reinterpret_cast<const uint64_t *>(&sm.u.ring[0])[w * (kFastRegion + 64) + pidx];
+            key8[j] = (uint32_t)(x >> 32);
+            idx8[j] = (uint32_t)x;
+          }
+        }
+        __syncthreads();                                   // the regions overlap the selection state
+        // a bucket of at most pow2(k) + 1 - k members keeps the list within pow2(k)
+        const int cap = max(pow2_ceil(k_sel) + 1 - k_sel, 16);
+        select_regs<kNT, 8>(key8, [&](int j) -> uint32_t { return idx8[j]; }, total, k_sel, sm.u.sel, cap);
+      }
+    }
+  }
+  if (!fast) {
+    uint32_t key[64];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = (acc[m][4 * q4 + e] - lse) + pr;
+          key[16 * m + 4 * q4 + e] = valid ? rank_key(v[e]) : kInvalidKey;
+        }
+        if (crow && !cand_done)
+          *(float4 *)(crow + ch * 128 + 32 * m + 8 * q4 + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    __syncthreads();                                       // survivor regions may still be read
+    select_regs<kNT, 64>(key, idx_of, n, k_sel, sm.u.sel);
+  }
   emit_selection<kNT>(sm.u.sel, k_sel, r, grp, 256, p.score, p.token, p.parent, p.partial, p.n_groups, p.kk);
 }
 

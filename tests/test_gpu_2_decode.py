@@ -94,6 +94,33 @@ def test_decode_small_parity(name):
     print(f"{name}: picks in the near-tie band: {band}")
 
 
+@pytest.mark.parametrize("prior", ["cumsum", "flat"])
+def test_decode_zero_codebook_ties(prior):
+    """W = 0: every code of a beam has the same log-probability, so the
+    candidates tie within each beam (and across all beams with a flat prior).
+    The selection must follow the flat index among equal scores exactly."""
+    cfg = W.reduced(CF["beam100_p600"], R=3, Lp=50, H=2, n_in=100, level_sizes=(60, 100, 100),
+                    prior=prior)
+    announce(f"gr_decode_step zero codebook, {prior} prior")
+    x = W.make_step_inputs(cfg)
+    x.W = np.zeros_like(x.W)
+    ds = HN.upload_step(x)
+    buf = HN.decode_buffers(ds, debug_outputs=True)
+    HN.decode_step(ds, buf)
+    torch.cuda.synchronize()
+    assert int(ds.dev_err.item()) == 0
+    got = HN.results_to_host(buf)
+    check_self_consistent(got["cand"], got["token"], got["parent"])
+    ref = oracle_step(x)
+    compare(cfg, got, ref, list(range(cfg.R)), f"zero codebook {prior}")
+    if prior == "cumsum":
+        # the best beam's codes 0 .. k-1, in index order
+        best = np.argmax(x.prior, axis=1)
+        for r in range(cfg.R):
+            np.testing.assert_array_equal(got["parent"][r], np.full(cfg.k, best[r]))
+            np.testing.assert_array_equal(got["token"][r], np.arange(cfg.k))
+
+
 def test_chained_fp32_three_steps():
     cfg = CF["tiny_f32_3step"]
     announce("gr_decode_step tiny_f32_3step chained")

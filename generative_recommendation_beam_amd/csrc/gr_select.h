@@ -162,6 +162,31 @@ __device__ __forceinline__ void block_bitonic_sort_u64(uint64_t *arr, int L, int
   __syncthreads();
 }
 
+// Ascending order of the unique composites arr[0..L) (L <= NT) by ranking:
+// the thread holding entry x counts the entries below it (reading the list
+// two at a time, every lane the same address) and stores x at that rank.
+// Only the waves that hold entries count; every thread takes the barriers.
+template <int NT>
+__device__ __forceinline__ void rank_sort_u64(uint64_t *arr, int L) {
+  const int tid = threadIdx.x;
+  const uint64_t x = tid < L ? arr[tid] : ~0ull;
+  int rank = 0;
+  if ((tid & ~63) < L) {
+    // 16 entries per round, loads issued together (arr has room past L:
+    // L + 15 < kListCap; entries at or past L are not counted)
+    for (int i = 0; i < L; i += 16) {
+      uint64_t a[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) a[t] = arr[i + t];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) rank += (i + t < L && a[t] < x) ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  if (tid < L) arr[rank] = x;
+  __syncthreads();
+}
+
 // The m-th smallest (m = 1 or 2, counting equal values) of one u32 per lane
 // across the wave: a butterfly that keeps each lane's two smallest.
 __device__ __forceinline__ uint32_t wave_small2_u32(uint32_t x, int m) {
@@ -379,7 +404,9 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[J], IdxFn idx_
   __syncthreads();
   const int L = min(sm.n_list, kListCap);
   const int P = pow2_ceil(max(L, k));
-  if (P <= NT) {
+  if (L <= 256) {
+    rank_sort_u64<NT>(sm.u.list, L);
+  } else if (P <= NT) {
     block_bitonic_sort_u64<NT>(sm.u.list, L, P);
   } else {
     for (int i = L + tid; i < P; i += NT) sm.u.list[i] = ~0ull;

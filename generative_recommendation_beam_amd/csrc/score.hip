@@ -51,13 +51,12 @@ struct LogitsSmem {
   float red_max[4][2][32];
   float red_sum[4][2][32];
   uint32_t bound[kNT / 64];                // per-wave bound keys of the fast selection
-  uint32_t fast_cnt[kNT / 64];             // per-wave survivor counts
+  uint32_t fast_cnt[kNT / 64];             // per-wave counts of staged lanes
 };
-// Fast selection: per-wave survivor regions in the (then idle) ring, and at
-// most 8 survivors per thread for the exact selection.
-constexpr int kFastRegion = 2048;
+// Fast selection: at most 8 staged candidates per thread, staged (scores
+// and the row bases of their lanes) in the then idle ring.
 constexpr int kFastList = 8 * kNT;
-static_assert(sizeof(LogitsStage) * kRS >= sizeof(uint64_t) * (kFastRegion + 64) * (kNT / 64), "survivor regions");
+static_assert(sizeof(LogitsStage) * kRS >= (sizeof(float) + sizeof(uint32_t)) * kFastList, "staging area");
 
 struct LP {
   const uint16_t *o, *W;
@@ -172,13 +171,13 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
 
   // log-softmax over the 256 codes of each beam (two waves hold its halves)
   float lse = 0.f;
+  float amax = acc[0][0];                   // this lane's largest logit
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, acc[m][i]);
   if (p.lsm) {
-    float mx = acc[0][0];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[m][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mx = fmaxf(amax, __shfl_xor(amax, 32));
     if (lane < 32) sm.red_max[bb][ch][c] = mx;
     __syncthreads();
     const float M = fmaxf(sm.red_max[bb][0][c], sm.red_max[bb][1][c]);
@@ -209,21 +208,35 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
   // Fast path.  If ml = ceil(k/64) lanes of one wave have no score below s,
   // at least k candidates score >= s, so the k best all do.  s is the ml-th
   // largest lane minimum of a wave (the largest such bound over the waves;
-  // the lane minimum comes from the minimum of acc, the score being monotonic
-  // in it).  One pass then computes the scores and compacts the candidates
-  // >= s into per-wave regions (a ballot per slot, skipped when empty); when
-  // they are few the exact selection runs on them alone, 8 per thread.
-  // Otherwise (too many survivors, or a degenerate bound) it runs on all 64
-  // register slots.  Every decision is block-uniform.
+  // lane extremes come from those of acc, the score being monotonic in it).
+  // Only lanes whose maximum reaches s can hold a selected candidate: they
+  // stage their 64 scores in LDS, and the exact selection runs over the
+  // staged candidates, 8 per thread.  If too many lanes qualify, or the bound
+  // is degenerate, it runs over all 64 register slots.  Every decision is
+  // block-uniform.
   bool cand_done = false, fast = false;
   {
     float amin = acc[0][0];
+    bool nan_in = false;                                // fminf / fmaxf skip NaN
+    if (p.lsm) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) amin = fminf(amin, acc[m][i]);
-    const float worst = (amin - lse) + pr;
-    const uint32_t wkey = valid ? rank_key(worst) : kInvalidKey;
+        for (int i = 0; i < 16; ++i) amin = fminf(amin, acc[m][i]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          amin = fminf(amin, acc[m][i]);
+          nan_in = nan_in || acc[m][i] != acc[m][i];
+        }
+    }
+    // A lane with a NaN score (which ranks like -inf) bounds nothing.  With
+    // the log-softmax a NaN logit makes every score of its beam NaN, and so
+    // the lane minimum too.
+    const float lmin = nan_in ? -__builtin_inff() : (amin - lse) + pr, lmax = (amax - lse) + pr;
+    const uint32_t wkey = valid ? rank_key(lmin) : kInvalidKey;
     const int ml = (k_sel + 63) >> 6;
     uint32_t tw;                                        // ml-th smallest lane-minimum key of the wave
     if (ml <= 2) {
@@ -240,67 +253,54 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
     for (int w = 1; w < kNT / 64; ++w) T = min(T, sm.bound[w]);
     const float Ts = key_score(T);
     if (T != kInvalidKey && Ts > -__builtin_inff()) {
-      cand_done = true;
-      // Region of this wave: kFastRegion slots, then one dummy slot per lane
-      // that absorbs the stores of unselected lanes (no divergent branch).
-      uint64_t *region = reinterpret_cast<uint64_t *>(&sm.u.ring[0]) + wave * (kFastRegion + 64);
-      const float t_lane = valid ? Ts : __builtin_nanf("");   // nothing compares >= NaN
-      int cnt = 0;                                        // wave-uniform
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (acc[m][4 * q4 + e] - lse) + pr;
-          if (crow) *(float4 *)(crow + ch * 128 + 32 * m + 8 * q4 + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bool sel = v[e] >= t_lane;
-            const uint64_t mask = __builtin_amdgcn_ballot_w64(sel);
-            if (mask) {
-              const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-              const int dst = (sel && pos < kFastRegion) ? pos : kFastRegion + lane;
-              // selected scores are >= Ts > -inf, so not NaN: the key is the
-              // order-preserving bit map of v + 0 (which folds -0 into +0)
-              const uint32_t u = __float_as_uint(v[e] + 0.0f);
-              const uint32_t kv = u ^ ((uint32_t)((int32_t)~u >> 31) & 0x7FFFFFFFu);
-              region[dst] = ((uint64_t)kv << 32) | idx_of(16 * m + 4 * q4 + e);
-              cnt += __builtin_popcountll(mask);
-            }
-          }
-        }
-      if (lane == 0) sm.fast_cnt[wave] = (uint32_t)cnt;
+      const bool has = valid && lmax >= Ts;
+      const uint64_t hm = __builtin_amdgcn_ballot_w64(has);
+      if (lane == 0) sm.fast_cnt[wave] = (uint32_t)__builtin_popcountll(hm);
       __syncthreads();
-      int total = 0;
-      bool over = false;
+      int n_st = 0, base_w = 0;
 #pragma unroll
       for (int w = 0; w < kNT / 64; ++w) {
-        total += (int)sm.fast_cnt[w];
-        over = over || (int)sm.fast_cnt[w] > kFastRegion;
+        base_w += w < wave ? (int)sm.fast_cnt[w] : 0;
+        n_st += (int)sm.fast_cnt[w];
       }
-      if (!over && total >= k_sel && total <= kFastList) {
+      const int S = n_st * 64;                           // staged candidates
+      if (S <= kFastList) {
         fast = true;
+        cand_done = true;
+        float *st_v = reinterpret_cast<float *>(&sm.u.ring[0]);     // [n_st][64] scores
+        uint32_t *st_row = reinterpret_cast<uint32_t *>(st_v + kFastList);   // [n_st] row bases
+        const int s_idx = base_w + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(hm >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)hm, 0u));
+        if (has || crow) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              float v[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = (acc[m][4 * q4 + e] - lse) + pr;
+              const float4 v4 = make_float4(v[0], v[1], v[2], v[3]);
+              if (crow) *(float4 *)(crow + ch * 128 + 32 * m + 8 * q4 + 4 * g) = v4;
+              if (has) *(float4 *)(st_v + s_idx * 64 + 16 * m + 4 * q4) = v4;
+            }
+          if (has) st_row[s_idx] = row_base;
+        }
+        __syncthreads();
         uint32_t key8[8], idx8[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          int pidx = j * kNT + tid, w = 0;                 // position in the concatenated regions
-#pragma unroll
-          for (int w2 = 0; w2 < kNT / 64 - 1; ++w2)
-            if (w == w2 && pidx >= (int)sm.fast_cnt[w2]) { pidx -= (int)sm.fast_cnt[w2]; w = w2 + 1; }
-          key8[j] = kInvalidKey;
-          idx8[j] = 0u;
-          if (j * kNT + tid < total) {
-            const uint64_t x = reinterpret_cast<const uint64_t *>(&sm.u.ring[0])[w * (kFastRegion + 64) + pidx];
-            key8[j] = (uint32_t)(x >> 32);
-            idx8[j] = (uint32_t)x;
+        for (int i = 0; i < 8; ++i) {
+          const int t = i * kNT + tid, sl = t >> 6, j = t & 63;
+          key8[i] = kInvalidKey;
+          idx8[i] = 0u;
+          if (t < S) {
+            key8[i] = rank_key(st_v[t]);
+            idx8[i] = st_row[sl] + 32u * (uint32_t)(j >> 4) + 8u * (uint32_t)((j >> 2) & 3) + (uint32_t)(j & 3);
           }
         }
-        __syncthreads();                                   // the regions overlap the selection state
+        __syncthreads();                                   // the staging area overlaps the selection state
         // a bucket of at most pow2(k) + 1 - k members keeps the list within pow2(k)
         const int cap = max(pow2_ceil(k_sel) + 1 - k_sel, 16);
-        select_regs<kNT, 8>(key8, [&](int j) -> uint32_t { return idx8[j]; }, total, k_sel, sm.u.sel, cap);
+        select_regs<kNT, 8>(key8, [&](int i) -> uint32_t { return idx8[i]; }, S, k_sel, sm.u.sel, cap);
       }
     }
   }

@@ -151,13 +151,19 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   // DMA targets, so there are just five: four stages and the chain ids.)
   __shared__ __attribute__((aligned(1024))) uint16_t KV0[G::TB], KV1[G::TB], KV2[NS > 2 ? G::TB : 8],
       KV3[NS > 3 ? G::TB : 8];
-  // dynamic LDS: chain ids [D][NB] (level-major), then, when the chains are
-  // resolved here, the request's parent array and the workgroup's beam nodes
+  // dynamic LDS: chain ids [D][NB] (level-major; int32 as delivered by the
+  // pre-pass, or int16 when the chains are resolved here, the arena then
+  // holding at most kLdsChainNodes nodes), then in the second case the
+  // request's parent array and the workgroup's beam nodes
   extern __shared__ __attribute__((aligned(1024))) int32_t dyn_s[];
   int32_t *const ids_s = dyn_s;
+  int16_t *const ids16 = reinterpret_cast<int16_t *>(dyn_s);
   int32_t *const par_s = dyn_s + p.ids_words;
   int32_t *const bn_s = par_s + p.par_words;
   const bool chains = p.ids != nullptr || p.parent != nullptr;
+  auto chain_id = [&](int d, int b) -> int {
+    return p.parent != nullptr ? (int)ids16[d * G::NB + b] : ids_s[d * G::NB + b];
+  };
   auto kst = [&](auto S) -> uint16_t * {
     constexpr int st = decltype(S)::value;
     if constexpr (st == 0) return KV0;
@@ -224,7 +230,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
     for (int i = 0; i < G::IPW; ++i) {
       const int blk = wave * G::IPW + i;
       const int b = bb * G::KT + dma_row[i];
-      const int id = b < G::NB ? ids_s[d * G::NB + b] : -1;
+      const int id = b < G::NB ? chain_id(d, b) : -1;
       const size_t src = ((size_t)r * p.cap + (id >= 0 ? id : 0)) * row + (size_t)h * HD;
       dma16(p.ak + src + dma_k[i], kst(S) + blk * 512);
       dma16(p.av + src + dma_v[i], vst(S) + blk * 512);
@@ -354,7 +360,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
                   else n = pn;
                 }
               }
-              ids_s[d * G::NB + tid] = id;
+              ids16[d * G::NB + tid] = (int16_t)id;
             }
             if (n != -1) err |= GR_DEVERR_DEPTH;
             if (err && h == 0) atomicOr(p.dev_err, err);
@@ -373,10 +379,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
           if (chains) {
             int depth = 0;
             for (int d = 0; d < p.D; ++d) {
-              const int own = ids_s[d * G::NB + wb];
+              const int own = chain_id(d, wb);
               cnt += own >= 0 ? 1 : 0;
-              bool any = lane < G::NB && ids_s[d * G::NB + lane] >= 0;
-              if constexpr (G::NB > 64) any = any || ids_s[d * G::NB + 64 + lane] >= 0;
+              bool any = lane < G::NB && chain_id(d, lane) >= 0;
+              if constexpr (G::NB > 64) any = any || chain_id(d, 64 + lane) >= 0;
               if (__ballot(any)) depth = d + 1;
             }
             n_total = n_pre + depth * G::NRB;
@@ -668,11 +674,21 @@ hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
   p.sl2 = a.scale * kLog2e;
   p.ids_words = 0;
   p.par_words = 0;
+  // The in-kernel resolve stages the parent array; when that would cost a
+  // resident workgroup per CU (and the pre-pass ids would not), the chains
+  // go through the pre-pass instead.
+  using G = Geo<HD, NW, NS>;
+  const size_t static_lds = (size_t)(NS < 4 ? NS : 4) * G::TB * sizeof(uint16_t) + 1024;   // upper bound
+  const size_t lds_per_cu = 160 * 1024;
+  const size_t inkernel_dyn = ((size_t)(a.max_depth * NB + 1) / 2 + (a.cap + 63) / 64 * 64 + (NB + 63) / 64 * 64) * 4;
+  const size_t prepass_dyn = (size_t)(a.max_depth * NB + 255) / 256 * 256 * 4;
+  const bool inkernel_fits = (static_lds + inkernel_dyn) * OCC <= lds_per_cu;
+  const bool prepass_fits = (static_lds + prepass_dyn) * OCC <= lds_per_cu;
   if (a.beam_node != nullptr) {
-    if (a.cap <= kLdsChainNodes) {
+    if (a.cap <= kLdsChainNodes && (inkernel_fits || !prepass_fits || a.chain_ids == nullptr)) {
       p.parent = a.parent;
       p.beam_node = a.beam_node;
-      p.ids_words = a.max_depth * NB;
+      p.ids_words = (a.max_depth * NB + 1) / 2;           // int16 ids, two per word
       p.par_words = (a.cap + 63) / 64 * 64;
     } else {
       ChainP c;

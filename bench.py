@@ -214,22 +214,22 @@ def main():
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
 
-    # timed region 2: the two stages of the same K steps, each stage run K
-    # times back to back between two events on the launch stream (same
-    # kernels, same arguments; the input sets still alternate, so every
-    # attention launch streams a prompt set the previous one evicted)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    # timed region 2: the same K steps, each split into its two stages with
+    # an event before, between and after them on the launch stream (same
+    # kernels, same arguments, same order as in region 1; the input sets
+    # still alternate, so every attention launch streams a prompt set the
+    # previous one evicted).  Stage time = mean event-to-event interval.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
     torch.cuda.synchronize()
     ev[0].record()
     for i in range(args.steps):
         step(i, L.GR_STEP_ATTENTION)
-    ev[1].record()
-    for i in range(args.steps):
+        ev[2 * i + 1].record()
         step(i, L.GR_STEP_SELECTION)
-    ev[2].record()
+        ev[2 * i + 2].record()
     torch.cuda.synchronize()
-    attn_avg_ms = ev[0].elapsed_time(ev[1]) / args.steps
-    sel_avg_ms = ev[1].elapsed_time(ev[2]) / args.steps
+    attn_avg_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)) / args.steps
+    sel_avg_ms = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(args.steps)) / args.steps
     errs = [int(ds.dev_err.item()) for ds in sets]
     assert not any(errs), f"device error bits set: {errs}"
 

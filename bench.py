@@ -39,7 +39,8 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first (the GPU takes some tens of ms to reach steady clocks)")
     ap.add_argument("--workload", default="beam100_p600")
     ap.add_argument("--sets", type=int, default=2, help="independent input copies rotated between steps")
     ap.add_argument("--skip-cpu-baseline", action="store_true")

@@ -162,25 +162,29 @@ __device__ __forceinline__ void block_bitonic_sort_u64(uint64_t *arr, int L, int
   __syncthreads();
 }
 
-// Ascending order of the unique composites arr[0..L) (L <= NT) by ranking:
-// the thread holding entry x counts the entries below it (reading the list
-// two at a time, every lane the same address) and stores x at that rank.
+// Ascending order of the unique composites arr[0..L) (L <= NT, L + 16 <=
+// kListCap) by ranking: the thread holding entry x counts the entries below
+// it (every lane reading the same addresses, 16 loads in flight) and stores x
+// at that rank.  The list is padded with ~0 to a multiple of 16 first, so the
+// count needs no bound check; four partial counts keep the adds independent.
 // Only the waves that hold entries count; every thread takes the barriers.
 template <int NT>
 __device__ __forceinline__ void rank_sort_u64(uint64_t *arr, int L) {
   const int tid = threadIdx.x;
   const uint64_t x = tid < L ? arr[tid] : ~0ull;
+  if (tid >= L && tid < L + 16) arr[tid] = ~0ull;
+  __syncthreads();
   int rank = 0;
   if ((tid & ~63) < L) {
-    // 16 entries per round, loads issued together (arr has room past L:
-    // L + 15 < kListCap; entries at or past L are not counted)
+    int r4[4] = {0, 0, 0, 0};
     for (int i = 0; i < L; i += 16) {
       uint64_t a[16];
 #pragma unroll
       for (int t = 0; t < 16; ++t) a[t] = arr[i + t];
 #pragma unroll
-      for (int t = 0; t < 16; ++t) rank += (i + t < L && a[t] < x) ? 1 : 0;
+      for (int t = 0; t < 16; ++t) r4[t & 3] += a[t] < x ? 1 : 0;
     }
+    rank = (r4[0] + r4[1]) + (r4[2] + r4[3]);
   }
   __syncthreads();
   if (tid < L) arr[rank] = x;

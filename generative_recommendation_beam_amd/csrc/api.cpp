@@ -52,17 +52,29 @@ float eff_scale(const gr_shape *s) {
   return s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
 }
 
-// partial-list geometry of a selection over n_in x vocab candidates
+// Partial-list geometry of a selection over n_in x vocab candidates.  The
+// MFMA codebook path selects per group of 128 beams (32768 candidates).
+// score_select uses the same groups unless they leave most CUs idle (few
+// requests, many candidates each): then groups of 8192, as long as their
+// partial lists still fit the final merge.
 struct SelGeo {
-  int n_groups, kk;
+  int n_groups, kk, gpos;
   size_t bytes;  // partial lists (0 with a single group)
 };
-SelGeo sel_geo(int R, int n_in, int vocab, int k) {
+SelGeo make_geo(int R, int n_in, int vocab, int k, int gpos) {
   SelGeo g;
-  g.n_groups = gr::select_groups(n_in, vocab);
-  g.kk = k < gr::kGroupPositions ? k : gr::kGroupPositions;
+  g.gpos = gpos;
+  g.n_groups = gr::select_groups(n_in, vocab, gpos);
+  g.kk = k < gpos ? k : gpos;
   g.bytes = g.n_groups > 1 ? align_up((size_t)R * g.n_groups * g.kk * sizeof(uint64_t)) : 0;
   return g;
+}
+SelGeo sel_geo(int R, int n_in, int vocab, int k, bool mfma_logits = false) {
+  const SelGeo big = make_geo(R, n_in, vocab, k, gr::kGroupPositions);
+  if (mfma_logits || (long long)R * big.n_groups >= gr::kSelectCUs) return big;
+  const SelGeo small = make_geo(R, n_in, vocab, k, gr::kSmallGroupPositions);
+  if (small.n_groups > big.n_groups && (long long)small.n_groups * small.kk <= gr::kMergeCapacity) return small;
+  return big;
 }
 
 gr_status check_select(int R, int n_in, int vocab, int k, int flags) {
@@ -106,7 +118,7 @@ DecodeLayout decode_layout(const gr_shape *s, int n_beams, int vocab, int k) {
   // other paths keep o in fp32 and write logits / scalar scores to z.
   L.o_bytes = align_up(rows * D * (mfma_logits ? 2 : 4));
   L.z_bytes = mfma_logits ? 0 : align_up(rows * (size_t)vocab * sizeof(float));
-  const SelGeo g = sel_geo(s->R, n_beams, vocab, k);
+  const SelGeo g = sel_geo(s->R, n_beams, vocab, k, mfma_logits);
   L.part_bytes = g.bytes;
   L.o_off = 0;
   L.z_off = L.o_off + L.o_bytes;
@@ -122,8 +134,8 @@ inline char *align_ptr(void *p) {
 }
 
 gr::SelectOut make_out(float *score, int32_t *token, int32_t *parent, void *part, int R, int n_in, int vocab,
-                       int k) {
-  const SelGeo g = sel_geo(R, n_in, vocab, k);
+                       int k, bool mfma_logits = false) {
+  const SelGeo g = sel_geo(R, n_in, vocab, k, mfma_logits);
   gr::SelectOut o;
   o.score = score;
   o.token = token;
@@ -131,6 +143,7 @@ gr::SelectOut make_out(float *score, int32_t *token, int32_t *parent, void *part
   o.partial = (uint64_t *)part;
   o.n_groups = g.n_groups;
   o.kk = g.kk;
+  o.gpos = g.gpos;
   return o;
 }
 
@@ -320,7 +333,8 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void
   const int R = shape->R;
   const int D = shape->H * shape->head_dim;
   const int lsm = (flags & GR_TOPK_LOG_SOFTMAX) ? 1 : 0;
-  const gr::SelectOut so = make_out(out_score, out_token, out_parent, part, R, n_beams, vocab, beam_width);
+  const gr::SelectOut so = make_out(out_score, out_token, out_parent, part, R, n_beams, vocab, beam_width,
+                                    use_mfma_logits(shape, vocab));
 
   gr::AttnArgs a = attn_args(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, dev_err);
   a.chain_ids = L.ids_bytes ? (int32_t *)(base + L.ids_off) : nullptr;

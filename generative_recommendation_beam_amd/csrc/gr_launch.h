@@ -57,6 +57,7 @@ struct SelectOut {
   int32_t *token, *parent;
   uint64_t *partial;               // [R][n_groups][kk] when n_groups > 1
   int n_groups, kk;
+  int gpos;                        // candidates per group of score_select (kSmallGroupPositions or kGroupPositions)
 };
 
 // Codebook projection on MFMA (bf16 o, bf16 W [256][D]), log-softmax, prior,
@@ -95,10 +96,12 @@ hipError_t launch_project(const ProjArgs &a, hipStream_t s);
 // Group geometry shared by host sizing and the kernels.
 constexpr int kGroupBeams = 128;          // beams per selection group at vocab 256
 constexpr int kGroupPositions = 32768;    // candidates per selection group
+constexpr int kSmallGroupPositions = 8192;   // score_select groups when few requests leave CUs idle
+constexpr int kSelectCUs = 256;           // workgroups below which score_select splits finer
 constexpr int kMergeCapacity = 16384;     // partial entries the final merge holds
-inline int select_groups(int n_in, int vocab) {
+inline int select_groups(int n_in, int vocab, int gpos = kGroupPositions) {
   const long long n = (long long)n_in * vocab;
-  return (int)((n + kGroupPositions - 1) / kGroupPositions);
+  return (int)((n + gpos - 1) / gpos);
 }
 
 }  // namespace gr

@@ -339,13 +339,17 @@ struct ScoreSmem {
   float lse[kGroupBeams];
 };
 
+// J register slots per thread: groups of kNT * J candidates (32768 or 8192).
+template <int J>
 __global__ __launch_bounds__(kNT) void score_select_kernel(SP p) {
+  constexpr int GPOS = kNT * J;
+  static_assert(GPOS / 256 <= kGroupBeams, "log-softmax rows per group");
   __shared__ ScoreSmem sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = blockIdx.x / p.n_groups, grp = blockIdx.x % p.n_groups;
-  const int p0 = grp * kGroupPositions;                   // first position of the group
+  const int p0 = grp * GPOS;                              // first position of the group
   const long long total = (long long)p.n_in * p.vocab;
-  const int n = (int)min((long long)kGroupPositions, total - p0);
+  const int n = (int)min((long long)GPOS, total - p0);
   const float *zr = p.z + (size_t)r * total;
   if (p.vocab == 256 && p.lsm) {
     const int nrows = n / 256;
@@ -359,9 +363,9 @@ __global__ __launch_bounds__(kNT) void score_select_kernel(SP p) {
     }
     __syncthreads();
   }
-  uint32_t key[kGroupPositions / kNT];
+  uint32_t key[J];
 #pragma unroll
-  for (int j = 0; j < kGroupPositions / kNT; ++j) {
+  for (int j = 0; j < J; ++j) {
     const int i = j * kNT + tid;
     key[j] = kInvalidKey;
     if (i < n) {
@@ -376,7 +380,7 @@ __global__ __launch_bounds__(kNT) void score_select_kernel(SP p) {
   }
   auto idx_of = [&](int j) -> uint32_t { return (uint32_t)(p0 + j * kNT + tid); };
   const int k_sel = min(p.k, n);
-  select_regs<kNT, kGroupPositions / kNT>(key, idx_of, n, k_sel, sm.sel);
+  select_regs<kNT, J>(key, idx_of, n, k_sel, sm.sel);
   emit_selection<kNT>(sm.sel, k_sel, r, grp, p.vocab, p.score, p.token, p.parent, p.partial, p.n_groups, p.kk);
 }
 
@@ -470,7 +474,12 @@ hipError_t launch_score_select(const ScoreSelectArgs &a, const SelectOut &o, hip
   p.score = o.score; p.token = o.token; p.parent = o.parent; p.partial = o.partial;
   p.R = a.R; p.n_in = a.n_in; p.vocab = a.vocab; p.k = a.k; p.lsm = a.log_softmax;
   p.n_groups = o.n_groups; p.kk = o.kk;
-  hipLaunchKernelGGL(score_select_kernel, dim3((unsigned)(a.R * o.n_groups)), dim3(kNT), 0, s, p);
+  if (o.gpos == kSmallGroupPositions)
+    hipLaunchKernelGGL(score_select_kernel<kSmallGroupPositions / kNT>, dim3((unsigned)(a.R * o.n_groups)), dim3(kNT),
+                       0, s, p);
+  else
+    hipLaunchKernelGGL(score_select_kernel<kGroupPositions / kNT>, dim3((unsigned)(a.R * o.n_groups)), dim3(kNT), 0,
+                       s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || o.n_groups == 1) return e;
   return launch_select_merge(o, a.R, a.k, a.vocab, s);

@@ -144,12 +144,19 @@ def test_workspace_sizes():
     ids = 256 * 8 * 128 * 4
     assert L.gr_decode_workspace_size(sh, 100, 256, 100) >= 256 * 100 * 512 * 2 + ids
     assert L.gr_decode_workspace_size(sh, 100, 256, 100) < 256 * 100 * 512 * 2 + ids + 4096
-    # scalar path: fp32 o + one score per candidate + partial lists of 2 groups
+    # scalar path: fp32 o + one score per candidate + partial lists.  With a
+    # single request, 40 000 candidates split into groups of 8192 (5 lists of
+    # 2000) rather than 32768, as 5 x 2000 still fits the final merge.
     s4 = shape(R=1, H=4, head_dim=32, prompt_len=256)
     n4 = L.gr_decode_workspace_size(s4, 40000, 1, 2000)
-    assert n4 >= 40000 * 128 * 4 + 40000 * 4 + 2 * 2000 * 8
-    assert L.gr_topk_workspace_size(2, 100, 256, 100) == 0
-    assert L.gr_topk_workspace_size(2, 300, 256, 100) >= 2 * 3 * 100 * 8
+    assert n4 >= 40000 * 128 * 4 + 40000 * 4 + 5 * 2000 * 8
+    # top-k from logits: many requests keep one group of up to 32768 each;
+    # few requests split into groups of 8192 (4 groups for 100 x 256)
+    assert L.gr_topk_workspace_size(256, 100, 256, 100) == 0
+    assert L.gr_topk_workspace_size(2, 100, 256, 100) >= 2 * 4 * 100 * 8
+    assert L.gr_topk_workspace_size(2, 300, 256, 100) >= 2 * 10 * 100 * 8
+    # k = 2048 over 16 groups of 8192 would exceed the merge: 4 groups of 32768
+    assert L.gr_topk_workspace_size(1, 512, 256, 2048) == 4 * 2048 * 8 + 256
     # bf16 attention: resolved chain ids, [R][8 levels][100 beams padded to 128]
     assert L.gr_attn_workspace_size(sh, 100) == 256 * 8 * 128 * 4 + 256
     assert L.gr_attn_workspace_size(shape(R=2, dtype=L.GR_F32), 100) == 0

@@ -22,6 +22,8 @@
 // project: VALU projection z = o . W^T for the fp32 path and the scalar
 // score o . w.
 
+#include <type_traits>
+
 #include "gr_device.h"
 #include "gr_launch.h"
 #include "gr_select.h"
@@ -286,21 +288,27 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
           if (has) st_row[s_idx] = row_base;
         }
         __syncthreads();
-        uint32_t key8[8], idx8[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int t = i * kNT + tid, sl = t >> 6, j = t & 63;
-          key8[i] = kInvalidKey;
-          idx8[i] = 0u;
-          if (t < S) {
-            key8[i] = rank_key(st_v[t]);
-            idx8[i] = st_row[sl] + 32u * (uint32_t)(j >> 4) + 8u * (uint32_t)((j >> 2) & 3) + (uint32_t)(j & 3);
-          }
-        }
-        __syncthreads();                                   // the staging area overlaps the selection state
         // a bucket of at most pow2(k) + 1 - k members keeps the list within pow2(k)
         const int cap = max(pow2_ceil(k_sel) + 1 - k_sel, 16);
-        select_regs<kNT, 8>(key8, [&](int i) -> uint32_t { return idx8[i]; }, S, k_sel, sm.u.sel, cap);
+        // staged candidate t -> (key, flat index), NJ per thread (t = i kNT + tid)
+        auto select_staged = [&](auto nj) {
+          constexpr int NJ = decltype(nj)::value;
+          uint32_t keyj[NJ], idxj[NJ];
+#pragma unroll
+          for (int i = 0; i < NJ; ++i) {
+            const int t = i * kNT + tid, sl = t >> 6, j = t & 63;
+            keyj[i] = kInvalidKey;
+            idxj[i] = 0u;
+            if (t < S) {
+              keyj[i] = rank_key(st_v[t]);
+              idxj[i] = st_row[sl] + 32u * (uint32_t)(j >> 4) + 8u * (uint32_t)((j >> 2) & 3) + (uint32_t)(j & 3);
+            }
+          }
+          __syncthreads();                                 // the staging area overlaps the selection state
+          select_regs<kNT, NJ>(keyj, [&](int i) -> uint32_t { return idxj[i]; }, S, k_sel, sm.u.sel, cap);
+        };
+        if (S <= kNT) select_staged(std::integral_constant<int, 1>{});
+        else select_staged(std::integral_constant<int, kFastList / kNT>{});
       }
     }
   }

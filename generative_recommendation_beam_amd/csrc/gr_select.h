@@ -162,32 +162,42 @@ __device__ __forceinline__ void block_bitonic_sort_u64(uint64_t *arr, int L, int
   __syncthreads();
 }
 
-// Ascending order of the unique composites arr[0..L) (L <= NT, L + 16 <=
-// kListCap) by ranking: the thread holding entry x counts the entries below
-// it (every lane reading the same addresses, 16 loads in flight) and stores x
-// at that rank.  The list is padded with ~0 to a multiple of 16 first, so the
-// count needs no bound check; four partial counts keep the adds independent.
-// Only the waves that hold entries count; every thread takes the barriers.
+// Ascending order of the unique composites arr[0..L) (L <= 256 <= NT/2) by
+// ranking: the rank of x is the number of entries below it.  Entry e is
+// counted by NT / Lp threads (Lp = 64, 128 or 256 >= L), each over one slice
+// of the list (every lane of a wave reading the same addresses, 16 loads in
+// flight, four independent partial counts); the slices' counts meet in LDS
+// (arr[512..] as scratch) and x is stored at its rank.  The list is padded
+// with ~0 to a multiple of 16 first, so the count needs no bound check.
+// Every thread takes the barriers.
 template <int NT>
 __device__ __forceinline__ void rank_sort_u64(uint64_t *arr, int L) {
+  static_assert(NT >= 512, "two or more slices per entry");
   const int tid = threadIdx.x;
-  const uint64_t x = tid < L ? arr[tid] : ~0ull;
+  const int Lp = L <= 64 ? 64 : (L <= 128 ? 128 : 256);
+  const int parts = NT / Lp;
+  const int e = tid % Lp, part = tid / Lp;
+  uint32_t *rank_s = reinterpret_cast<uint32_t *>(arr + 512);
+  const uint64_t x = e < L ? arr[e] : ~0ull;
+  if (tid < Lp) rank_s[tid] = 0u;
   if (tid >= L && tid < L + 16) arr[tid] = ~0ull;
   __syncthreads();
-  int rank = 0;
-  if ((tid & ~63) < L) {
+  const int chunk = ((L + parts - 1) / parts + 15) & ~15;
+  const int i0 = part * chunk, i1 = min(L, i0 + chunk);
+  if (e < L && i0 < i1) {
     int r4[4] = {0, 0, 0, 0};
-    for (int i = 0; i < L; i += 16) {
+    for (int i = i0; i < i1; i += 16) {
       uint64_t a[16];
 #pragma unroll
       for (int t = 0; t < 16; ++t) a[t] = arr[i + t];
 #pragma unroll
       for (int t = 0; t < 16; ++t) r4[t & 3] += a[t] < x ? 1 : 0;
     }
-    rank = (r4[0] + r4[1]) + (r4[2] + r4[3]);
+    const int c = (r4[0] + r4[1]) + (r4[2] + r4[3]);
+    if (c) atomicAdd(&rank_s[e], (uint32_t)c);
   }
   __syncthreads();
-  if (tid < L) arr[rank] = x;
+  if (part == 0 && e < L) arr[rank_s[e]] = x;
   __syncthreads();
 }
 

@@ -345,6 +345,7 @@ struct SP {
 struct ScoreSmem {
   SelectSmem<kNT> sel;
   float lse[kGroupBeams];
+  float prior[kGroupBeams];                // vocab 256: the group's rows
 };
 
 // J register slots per thread: groups of kNT * J candidates (32768 or 8192).
@@ -371,19 +372,34 @@ __global__ __launch_bounds__(kNT) void score_select_kernel(SP p) {
     }
     __syncthreads();
   }
+  // All loads before any candidate store (the compiler cannot know that the
+  // output aliases no input): one memory latency for the J slots.  With 256
+  // codes the priors of the group's rows come from LDS.
+  if (p.vocab == 256 && p.prior) {
+    for (int row = tid; row < (n + 255) / 256; row += kNT) sm.prior[row] = p.prior[(size_t)r * p.n_in + p0 / 256 + row];
+    __syncthreads();
+  }
+  float zv[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = j * kNT + tid;
+    zv[j] = i < n ? zr[p0 + i] : 0.f;
+  }
   uint32_t key[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int i = j * kNT + tid;
     key[j] = kInvalidKey;
     if (i < n) {
-      const int pos = p0 + i;
-      const int row = pos / p.vocab;
-      float v = zr[pos];
-      if (p.vocab == 256 && p.lsm) v -= sm.lse[i >> 8];
-      if (p.prior) v += p.prior[(size_t)r * p.n_in + row];
+      float v = zv[j];
+      if (p.vocab == 256) {
+        if (p.lsm) v -= sm.lse[i >> 8];
+        if (p.prior) v += sm.prior[i >> 8];
+      } else if (p.prior) {
+        v += p.prior[(size_t)r * p.n_in + p0 + i];
+      }
       key[j] = rank_key(v);
-      if (p.cand) p.cand[(size_t)r * total + pos] = v;
+      if (p.cand) p.cand[(size_t)r * total + p0 + i] = v;
     }
   }
   auto idx_of = [&](int j) -> uint32_t { return (uint32_t)(p0 + j * kNT + tid); };
@@ -408,7 +424,20 @@ __global__ __launch_bounds__(kMergeNT) void select_merge_kernel(const uint64_t *
   const int r = blockIdx.x, tid = threadIdx.x;
   const int n = n_groups * kk;
   const uint64_t *src = partial + (size_t)r * n;
-  for (int i = tid; i < n; i += kMergeNT) lists[i] = src[i];
+  // all loads first (n <= kMergeCapacity = kMergeLoads * kMergeNT), then the
+  // LDS stores: one memory latency rather than one per pass
+  constexpr int kMergeLoads = kMergeCapacity / kMergeNT;
+  uint64_t ld[kMergeLoads];
+#pragma unroll
+  for (int j = 0; j < kMergeLoads; ++j) {
+    const int i = j * kMergeNT + tid;
+    ld[j] = i < n ? src[i] : 0ull;
+  }
+#pragma unroll
+  for (int j = 0; j < kMergeLoads; ++j) {
+    const int i = j * kMergeNT + tid;
+    if (i < n) lists[i] = ld[j];
+  }
   __syncthreads();
   const int e = blockIdx.y * kMergeNT + tid;
   if (e >= n) return;
@@ -416,16 +445,26 @@ __global__ __launch_bounds__(kMergeNT) void select_merge_kernel(const uint64_t *
   if (x == ~0ull) return;                          // group padding
   const int g = e / kk;
   int slot = e - g * kk;
-  for (int g2 = 0; g2 < n_groups && slot < k; ++g2) {
-    if (g2 == g) continue;
-    const uint64_t *Lg = lists + g2 * kk;
-    int lo = 0, hi = kk;                           // entries of list g2 below x
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (Lg[mid] < x) lo = mid + 1;
-      else hi = mid;
+  // entries of list g2 below x: a branch-free lower bound whose step count
+  // does not depend on the data, four lists at a time so that their LDS
+  // reads are in flight together (list g itself counts 0)
+  for (int g0 = 0; g0 < n_groups && slot < k; g0 += 4) {
+    int base[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) base[u] = 0;
+    for (int len = kk; len > 1; len -= len >> 1) {
+      const int half = len >> 1;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int g2 = min(g0 + u, n_groups - 1);
+        base[u] = lists[g2 * kk + base[u] + half] < x ? base[u] + half : base[u];
+      }
     }
-    slot += lo;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int g2 = g0 + u;
+      if (g2 < n_groups && g2 != g) slot += base[u] + (lists[g2 * kk + base[u]] < x ? 1 : 0);
+    }
   }
   if (slot < k) {
     const uint32_t f = (uint32_t)x;
@@ -443,12 +482,20 @@ template <typename TO, typename TW>
 __global__ __launch_bounds__(256) void project_kernel(const TO *o, const TW *W, const float *prior, float *z,
                                                       int rows, int D, int vocab, int add_prior) {
   if (vocab == 1) {
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-    if (row >= rows) return;
+    // 16 lanes per row (one DPP row), 4 consecutive elements per lane and
+    // step: a 16-lane group reads 256 contiguous bytes of fp32 o per step
+    const int row = blockIdx.x * 16 + (threadIdx.x >> 4), l16 = threadIdx.x & 15;
+    if (row >= rows) return;                      // whole 16-lane groups leave together
     float s = 0.f;
-    for (int i = lane; i < D; i += 64) s = fmaf(ldv(o, (size_t)row * D + i), ldv(W, (size_t)i), s);
-    s = wave_sum(s);
-    if (lane == 0) z[row] = s + (add_prior && prior ? prior[row] : 0.f);
+    for (int i = 4 * l16; i < D; i += 64) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = fmaf(ldv(o, (size_t)row * D + i + e), ldv(W, (size_t)(i + e)), s);
+    }
+    s += __uint_as_float(xor_lane<1>(__float_as_uint(s)));
+    s += __uint_as_float(xor_lane<2>(__float_as_uint(s)));
+    s += __uint_as_float(xor_lane<4>(__float_as_uint(s)));
+    s += __uint_as_float(xor_lane<8>(__float_as_uint(s)));
+    if (l16 == 0) z[row] = s + (add_prior && prior ? prior[row] : 0.f);
     return;
   }
   __shared__ float orow[4096];
@@ -503,7 +550,7 @@ hipError_t launch_select_merge(const SelectOut &o, int R, int k, int vocab, hipS
 
 hipError_t launch_project(const ProjArgs &a, hipStream_t s) {
   const int rows = a.R * a.n;
-  const dim3 grid(a.vocab == 1 ? (unsigned)((rows + 3) / 4) : (unsigned)rows);
+  const dim3 grid(a.vocab == 1 ? (unsigned)((rows + 15) / 16) : (unsigned)rows);
   if (a.dtype == GR_F32) {
     hipLaunchKernelGGL((project_kernel<float, float>), grid, dim3(256), 0, s, (const float *)a.o,
                        (const float *)a.W, a.prior, a.z, rows, a.D, a.vocab, a.add_prior);

@@ -404,7 +404,8 @@ __global__ __launch_bounds__(kNT) void score_select_kernel(SP p) {
   }
   auto idx_of = [&](int j) -> uint32_t { return (uint32_t)(p0 + j * kNT + tid); };
   const int k_sel = min(p.k, n);
-  select_regs<kNT, J>(key, idx_of, n, k_sel, sm.sel);
+  // a bucket of at most pow2(k) + 1 - k members keeps the list within pow2(k)
+  select_regs<kNT, J>(key, idx_of, n, k_sel, sm.sel, max(pow2_ceil(k_sel) + 1 - k_sel, 16));
   emit_selection<kNT>(sm.sel, k_sel, r, grp, p.vocab, p.score, p.token, p.parent, p.partial, p.n_groups, p.kk);
 }
 

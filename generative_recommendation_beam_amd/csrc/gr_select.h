@@ -37,10 +37,12 @@ struct SelectSmem {
     uint32_t hist[kHistBins];
     uint64_t list[kListCap];
   } u;
-  uint64_t tmp[kListCap];                       // merge-sort ping-pong buffer
+  uint64_t tmp[kListCap];                       // merge-sort ping-pong buffer, bucket-sort scatter target
+  uint32_t bstart[kHistBins + 1];               // bucket sort: bucket starts (exclusive scan)
+  uint32_t bfill[kHistBins];                    // bucket sort: counts, then fill cursors
   uint32_t wmin[NW], wmax[NW], wtot[NW];
   uint64_t prefix;
-  int fixed_lo, need, bucket_cnt, n_list;
+  int fixed_lo, need, bucket_cnt, n_list, crowded;
 };
 
 __device__ __forceinline__ int pow2_ceil(int x) {
@@ -224,35 +226,39 @@ __device__ __forceinline__ uint32_t wave_small2_u32(uint32_t x, int m) {
   return m == 1 ? m1 : m2;
 }
 
-// Ascending sort of arr[0..P) for NT < P <= 8 NT (P a power of two): each
-// thread sorts E = P/NT consecutive entries in registers (a bitonic network
-// over 8 slots, padding sorting last), then log2(NT) merge-path rounds double
-// the sorted runs, ping-ponging between arr and tmp with one barrier each.
-// Keys are unique, so every split is unambiguous.
-template <int NT>
-__device__ __forceinline__ void merge_sort_u64(uint64_t *arr, uint64_t *tmp, int P) {
+// Ascending sort of arr[0..NT E) (E = 2, 4 or 8; entries are unique): each
+// thread sorts E consecutive entries in registers (a bitonic network), then
+// log2(NT) merge-path rounds double the sorted runs, ping-ponging between arr
+// and tmp with one barrier each.  In a round a thread finds where its E
+// outputs start in the two runs (a binary search), loads the next E entries
+// of each run at once, and merges them in registers: A ascending followed by
+// B reversed is bitonic, its lower half-cleaner keeps the E smallest, and
+// log2(E) further half-cleaners order them.
+template <int NT, int E>
+__device__ __forceinline__ void merge_sort_u64(uint64_t *arr, uint64_t *tmp) {
+  constexpr int P = NT * E;
   const int tid = threadIdx.x;
-  const int E = P / NT;
-  uint64_t v[8];
+  uint64_t v[E];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = e < E ? arr[tid * E + e] : ~0ull;
+  for (int e = 0; e < E; ++e) v[e] = arr[tid * E + e];
 #pragma unroll
-  for (int size = 2; size <= 8; size <<= 1)
+  for (int size = 2; size <= E; size <<= 1)
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < E; ++e) {
         const int f = e ^ stride;
         if (f > e) {
           const bool up = (e & size) == 0;
-          const uint64_t a = v[e], b = v[f];
-          if ((a > b) == up) { v[e] = b; v[f] = a; }
+          const uint64_t x = v[e], y = v[f];
+          const uint64_t mn = x < y ? x : y, mx = x < y ? y : x;
+          v[e] = up ? mn : mx;
+          v[f] = up ? mx : mn;
         }
       }
   __syncthreads();
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (e < E) arr[tid * E + e] = v[e];
+  for (int e = 0; e < E; ++e) arr[tid * E + e] = v[e];
   __syncthreads();
   uint64_t *src = arr, *dst = tmp;
   for (int run = E; run < P; run <<= 1) {
@@ -265,14 +271,27 @@ __device__ __forceinline__ void merge_sort_u64(uint64_t *arr, uint64_t *tmp, int
       if (A[mid] < B[pos - 1 - mid]) lo = mid + 1;
       else hi = mid;
     }
-    int i = lo, j = pos - lo;
+    const int i = lo, j = pos - lo;
+    uint64_t c[E];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (e < E) {
-        const bool take_a = j >= run || (i < run && A[i] < B[j]);
-        dst[o0 + e] = take_a ? A[i++] : B[j++];
-      }
+    for (int e = 0; e < E; ++e) {
+      const uint64_t x = i + e < run ? A[i + e] : ~0ull;
+      const uint64_t y = j + E - 1 - e < run ? B[j + E - 1 - e] : ~0ull;
+      c[e] = x < y ? x : y;
     }
+#pragma unroll
+    for (int stride = E / 2; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int f = e ^ stride;
+        if (f > e) {
+          const uint64_t x = c[e], y = c[f];
+          c[e] = x < y ? x : y;
+          c[f] = x < y ? y : x;
+        }
+      }
+#pragma unroll
+    for (int e = 0; e < E; ++e) dst[o0 + e] = c[e];
     __syncthreads();
     uint64_t *t = src; src = dst; dst = t;
   }
@@ -280,6 +299,66 @@ __device__ __forceinline__ void merge_sort_u64(uint64_t *arr, uint64_t *tmp, int
     for (int t = tid; t < P; t += NT) arr[t] = src[t];
     __syncthreads();
   }
+}
+
+// Ascending order of the unique composites list[0..L) (L <= kListCap), all
+// in [lo, hi], by one bucket pass: the 11-bit digit (x - lo) >> shift (shift
+// chosen so that hi maps below 2048) is histogrammed, scanned into bucket
+// starts, entries are scattered to tmp through per-bucket cursors, and each
+// entry's final slot is its bucket start plus the number of smaller entries
+// in its bucket.  Returns false (list untouched) if some bucket holds more
+// than kMaxBucket entries; the caller then sorts otherwise.  Every thread
+// takes the barriers and gets the same result.
+constexpr int kMaxBucket = 48;
+template <int NT>
+__device__ __forceinline__ bool bucket_sort_u64(SelectSmem<NT> &sm, int L, uint64_t lo, uint64_t hi) {
+  constexpr int NW = NT / 64, BPT = kHistBins / NT;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint64_t span = hi - lo;
+  const int bits = span ? 64 - __builtin_clzll(span) : 0;
+  const int shift = bits > kHistBits ? bits - kHistBits : 0;
+  for (int i = tid; i < kHistBins; i += NT) sm.bfill[i] = 0u;
+  if (tid == 0) sm.crowded = 0;
+  __syncthreads();
+  for (int i = tid; i < L; i += NT) atomicAdd(&sm.bfill[(uint32_t)((sm.u.list[i] - lo) >> shift)], 1u);
+  __syncthreads();
+  uint32_t c[BPT], sum = 0, mx = 0;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    c[q] = sm.bfill[tid * BPT + q];
+    sum += c[q];
+    mx = max(mx, c[q]);
+  }
+  const uint32_t inc = wave_incl_scan_u32(sum);
+  if (lane == 63) sm.wtot[wave] = inc;
+  if (mx > (uint32_t)kMaxBucket) sm.crowded = 1;
+  __syncthreads();
+  if (sm.crowded) return false;
+  uint32_t excl = inc - sum;
+  for (int w = 0; w < wave; ++w) excl += sm.wtot[w];
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    sm.bstart[tid * BPT + q] = excl;
+    sm.bfill[tid * BPT + q] = excl;               // cursor
+    excl += c[q];
+  }
+  if (tid == NT - 1) sm.bstart[kHistBins] = excl;
+  __syncthreads();
+  for (int i = tid; i < L; i += NT) {
+    const uint64_t x = sm.u.list[i];
+    sm.tmp[atomicAdd(&sm.bfill[(uint32_t)((x - lo) >> shift)], 1u)] = x;
+  }
+  __syncthreads();
+  for (int i = tid; i < L; i += NT) {
+    const uint64_t x = sm.tmp[i];
+    const uint32_t d = (uint32_t)((x - lo) >> shift);
+    const int b0 = (int)sm.bstart[d], b1 = (int)sm.bstart[d + 1];
+    int rank = b0;
+    for (int q = b0; q < b1; ++q) rank += sm.tmp[q] < x ? 1 : 0;
+    sm.u.list[rank] = x;
+  }
+  __syncthreads();
+  return true;
 }
 
 // Appends every register candidate j with sel(j) to list (composites, in no
@@ -420,12 +499,15 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[J], IdxFn idx_
   const int P = pow2_ceil(max(L, k));
   if (L <= 256) {
     rank_sort_u64<NT>(sm.u.list, L);
+  } else if (bucket_sort_u64<NT>(sm, L, (uint64_t)a << 32, hi_bound)) {
   } else if (P <= NT) {
     block_bitonic_sort_u64<NT>(sm.u.list, L, P);
   } else {
     for (int i = L + tid; i < P; i += NT) sm.u.list[i] = ~0ull;
     __syncthreads();
-    if (P <= 8 * NT) merge_sort_u64<NT>(sm.u.list, sm.tmp, P);
+    if (P == 2 * NT) merge_sort_u64<NT, 2>(sm.u.list, sm.tmp);
+    else if (P == 4 * NT) merge_sort_u64<NT, 4>(sm.u.list, sm.tmp);
+    else if (P == 8 * NT) merge_sort_u64<NT, 8>(sm.u.list, sm.tmp);
     else bitonic_sort_u64<NT>(sm.u.list, P);
   }
 }

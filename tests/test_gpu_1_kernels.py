@@ -163,6 +163,11 @@ TOPK_CASES = {
     # 3 x 2048 partial entries ranked by several blocks per request
     "merge_ties": dict(R=2, n_in=200, vocab=256, k=300, lsm=False, prior="int", quant=True),
     "merge_max_k": dict(R=2, n_in=300, vocab=256, k=2048, lsm=True, prior="cumsum"),
+    # integer-valued scores with many exact ties: the selection lists (about
+    # 1000 and 1700 entries) crowd single buckets of the bucket sort, so they
+    # are ordered by the merge sort (runs of 2 and 4 entries per thread)
+    "ties_merge_sort_1k": dict(R=2, n_in=64, vocab=256, k=1000, lsm=False, prior="int", quant=True),
+    "ties_merge_sort_2k": dict(R=2, n_in=40, vocab=256, k=1500, lsm=False, prior="int", quant=True),
 }
 
 

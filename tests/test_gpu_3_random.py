@@ -1,0 +1,64 @@
+"""Seeded sweep of small random decode-step shapes against the oracle.
+
+Each case draws its shape from a fixed seed: requests, prompt length and
+window (sometimes below 64 keys, which takes the fp32 projection), heads and
+head dim (odd D / 32 included, so the scoring ring ends on an odd chunk),
+live beams (1..300, one or several beam groups), chain depth (0..5), beam
+width (up to the candidate count or GR_MAX_K), dtype and prior.  Every case
+is compared in full (attention outputs, all candidate scores, the selected
+scores, the index rule and the exact self-consistency of the selection).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from generative_recommendation_beam_amd import _lib as L
+from generative_recommendation_beam_amd import harness as HN
+from parity import announce
+from test_gpu_2_decode import compare, oracle_step
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 24
+
+
+def random_config(seed: int) -> W.Config:
+    rng = np.random.default_rng(5000 + seed)
+    dtype = "f32" if seed % 6 == 5 else "bf16"
+    H = int(rng.integers(1, 5))
+    d = int(rng.choice([32, 64]))
+    R = int(rng.integers(1, 4))
+    Lp = int(rng.choice([1, 7, 40, 65, 130, 257]))
+    window = int(rng.choice([0, 0, 1, 33, 64, 100])) if Lp > 1 else 0
+    n_in = int(rng.choice([1, 5, 31, 32, 33, 64, 100, 129, 200, 300]))
+    depth = int(rng.integers(0, 6))
+    if depth == 0 and n_in > 256:
+        n_in = 256                        # a prompt-only step has at most one level of beams
+    sizes = []
+    for li in range(depth):
+        sizes.append(n_in if li == depth - 1 else int(rng.integers(1, 2 * n_in + 1)))
+    sizes = tuple(sizes)
+    if sizes:
+        sizes = tuple(min(s, 256) if i == 0 and len(sizes) > 1 else s for i, s in enumerate(sizes))
+    cand = n_in * 256
+    k = int(min(cand, L.GR_MAX_K, rng.choice([1, 8, 50, 100, 257, 700])))
+    prior = str(rng.choice(["cumsum", "flat", "zero"]))
+    return W.reduced(W.CONFIGS["beam100_p600"], R=R, Lp=Lp, window=window, H=H, d=d, n_in=n_in, k=k,
+                     depth=depth, level_sizes=sizes, dtype=dtype, prior=prior)
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_decode_random_shapes(seed):
+    cfg = random_config(seed)
+    announce(f"gr_decode_step random case {seed}: R={cfg.R} Lp={cfg.Lp} window={cfg.window} H={cfg.H} "
+             f"d={cfg.d} n_in={cfg.n_in} k={cfg.k} levels={cfg.level_sizes} {cfg.dtype} prior={cfg.prior}")
+    x = W.make_step_inputs(cfg, seed=9000 + seed)
+    ds = HN.upload_step(x)
+    buf = HN.decode_buffers(ds, debug_outputs=True)
+    HN.decode_step(ds, buf)
+    torch.cuda.synchronize()
+    assert int(ds.dev_err.item()) == 0
+    got = HN.results_to_host(buf)
+    ref = oracle_step(x)
+    compare(cfg, got, ref, list(range(cfg.R)), f"random {seed}")

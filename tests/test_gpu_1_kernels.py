@@ -175,7 +175,14 @@ TOPK_CASES = {
 def test_beam_topk_parity(name):
     c = TOPK_CASES[name]
     announce(f"gr_beam_topk {name}")
-    rng = np.random.default_rng(len(name))
+    check_topk_case(name, c, np.random.default_rng(len(name)))
+
+
+def check_topk_case(name, c, rng):
+    """gr_beam_topk on seeded logits (N(0, 0.1) codes or N(0, 1) scalars,
+    optionally rounded to multiples of 1/40 for exact ties) against the
+    oracle: exact values and indices without the log-softmax, the index rule
+    with it, and exact self-consistency with the returned candidate scores."""
     R, n_in, V, k = c["R"], c["n_in"], c["vocab"], c["k"]
     z = rng.standard_normal((R, n_in, V)).astype(np.float32) * (0.1 if V == 256 else 1.0)
     if c.get("quant"):

@@ -1,4 +1,4 @@
-"""Seeded sweep of small random decode-step shapes against the oracle.
+"""Seeded sweeps of small random shapes against the oracle.
 
 Each case draws its shape from a fixed seed: requests, prompt length and
 window (sometimes below 64 keys, which takes the fp32 projection), heads and
@@ -7,6 +7,11 @@ live beams (1..300, one or several beam groups), chain depth (0..5), beam
 width (up to the candidate count or GR_MAX_K), dtype and prior.  Every case
 is compared in full (attention outputs, all candidate scores, the selected
 scores, the index rule and the exact self-consistency of the selection).
+
+The top-k sweep draws requests, candidate counts (up to 120 000, several
+selection groups and the final merge), k (1 .. GR_MAX_K), the 256-code or
+scalar mode, the log-softmax, priors and exact ties, covering the counting
+rank, bucket, bitonic and merge orderings of the selection list.
 """
 import numpy as np
 import pytest
@@ -16,6 +21,7 @@ import workloads as W
 from generative_recommendation_beam_amd import _lib as L
 from generative_recommendation_beam_amd import harness as HN
 from parity import announce
+from test_gpu_1_kernels import check_topk_case
 from test_gpu_2_decode import compare, oracle_step
 
 pytestmark = pytest.mark.gpu
@@ -62,3 +68,22 @@ def test_decode_random_shapes(seed):
     got = HN.results_to_host(buf)
     ref = oracle_step(x)
     compare(cfg, got, ref, list(range(cfg.R)), f"random {seed}")
+
+
+def random_topk_case(seed: int) -> dict:
+    rng = np.random.default_rng(7000 + seed)
+    vocab = int(rng.choice([1, 256, 256]))
+    R = int(rng.integers(1, 4))
+    n_in = int(rng.choice([1, 3, 40, 129, 300, 470])) if vocab == 256 else int(rng.choice([5, 700, 9000, 40000, 120000]))
+    k = int(min(n_in * vocab, L.GR_MAX_K, rng.choice([1, 7, 100, 256, 300, 1000, 2048])))
+    lsm = vocab == 256 and bool(rng.integers(0, 2))
+    quant = not lsm and bool(rng.integers(0, 2))
+    prior = str(rng.choice(["cumsum", "flat", "int", "none"]))
+    return dict(R=R, n_in=n_in, vocab=vocab, k=k, lsm=lsm, prior=prior, quant=quant)
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_topk_random_shapes(seed):
+    c = random_topk_case(seed)
+    announce(f"gr_beam_topk random case {seed}: {c}")
+    check_topk_case(f"random {seed}", c, np.random.default_rng(8000 + seed))

@@ -11,12 +11,12 @@
 // of 11-bit digits that start at the highest bit where the keys differ; each
 // pass histograms the candidates still in play with non-returning LDS atomics
 // and one block scan picks the bucket holding the k-th.  As soon as that
-// bucket has at most kBucketCap members, every candidate at or below the
-// bucket is copied to an LDS list (per-lane counts, one prefix sum and one
-// atomic per wave), and the list is sorted (bitonic in registers up to one
-// entry per thread, block merge sort above); its first k entries are the
-// answer.
-// Integer counts only, so the result is deterministic.
+// bucket is small enough, every candidate at or below the bucket is copied to
+// an LDS list (per-lane counts, one prefix sum and one atomic per wave), and
+// the list is ordered: by counting ranks up to 256 entries, by one bucket pass
+// above (a bitonic or merge sort when ties crowd a bucket).  Its first k
+// entries are the answer.
+// Integer counts and comparisons only, so the result is deterministic.
 #pragma once
 
 #include "gr_device.h"

@@ -12,9 +12,11 @@
 // through a ring of 32-column chunks (global_load_lds, several chunks in
 // flight, each read once per workgroup).  Each lane then holds 64 codes of one
 // beam in registers: the log-softmax is in-lane plus one lane^32 swap and one
-// LDS exchange between the two code halves, and the selection (gr_select.h)
-// runs on those registers; scores never leave the chip unless the caller asks
-// for them.
+// LDS exchange between the two code halves.  The selection first bounds the
+// k-th best score from lane minima and stages only the lanes that can reach
+// the bound, then runs the exact selection (gr_select.h) on the staged
+// candidates (on all registers when the bound prunes too little); scores never
+// leave the chip unless the caller asks for them.
 //
 // score_select: the same scoring and selection starting from fp32 logits in
 // global memory (the standalone top-k entry point, the fp32 path and scalar

@@ -19,6 +19,9 @@ Modules:
              split prefix/suffix with a log-sum-exp merge)
   beam       codebook logits, log-softmax, prior add, exact top-k, the whole
              decode step, chained decoding, scalar scoring
+  generate   whole-ID generation: the q/k/v table of each level's codes,
+             every level's step with the chosen codes' records appended in
+             between, and the final IDs traced back through the parents
 
 Pins: every function here is checked in tests/test_oracle_*.py against closed
 forms, library special cases, invariants and brute force (see the docstrings
@@ -31,10 +34,11 @@ from .attention import (attend_materialized, attend_masked, attend_split,
 from .beam import (codebook_logits, log_softmax, candidate_scores,
                    select_topk, decode_step, scalar_scores, beam_topk,
                    run_chained)
+from . import generate
 
 __all__ = [
     "trie_append", "chain", "TrieError", "new_arena", "attend_materialized",
     "attend_masked", "attend_split", "prefix_attn", "codebook_logits",
     "log_softmax", "candidate_scores", "select_topk", "decode_step",
-    "scalar_scores", "beam_topk", "run_chained",
+    "scalar_scores", "beam_topk", "run_chained", "generate",
 ]

@@ -39,6 +39,7 @@ import numpy as np
 __all__ = [
     "Config", "CONFIGS", "HEADLINE", "bf16_round", "make_step_inputs",
     "make_chained_inputs", "StepInputs", "ChainedInputs", "reduced",
+    "GEN_CONFIGS", "GenInputs", "make_generate_inputs",
 ]
 
 
@@ -236,3 +237,53 @@ def make_chained_inputs(cfg: Config, seed: Optional[int] = None) -> ChainedInput
         n = cfg.n_in if s == 0 else cfg.k
         q.append(_maybe_round(_normal(rng, (R, n, H, d)), cfg.dtype))
     return ChainedInputs(cfg, pk, pv, W, prior0, rec, q)
+
+
+# Whole-ID generation: `steps` levels, one root hypothesis per request, beam
+# width k; level_sizes are the records appended between the steps (the kept
+# beams of every step but the last).
+GEN_CONFIGS: Dict[str, Config] = {c.name: c for c in [
+    Config("gen_tiny_f32", 6, R=2, Lp=64, window=0, H=4, d=32, n_in=1, k=8,
+           depth=0, level_sizes=(8, 8, 8), dtype="f32", vocab=256,
+           prior="zero", steps=4),
+    # four-level IDs at the headline shape (beam 100, 600-token prompt)
+    Config("gen_beam100_p600", 7, R=256, Lp=600, window=0, H=8, d=64, n_in=1,
+           k=100, depth=0, level_sizes=(100, 100, 100), dtype="bf16",
+           vocab=256, prior="zero", steps=4),
+]}
+
+
+@dataclasses.dataclass
+class GenInputs:
+    """Inputs of a whole-ID generation.  q0 [R][1][H][d] is the root
+    hypothesis's query; W[l] [vocab][D] level l's codebook projection;
+    emb[l] [vocab][d_emb] the embeddings of the codes chosen at step l
+    (l < steps - 1); w_qkv [3D][d_emb] the query, key and value projections
+    stacked by rows."""
+    cfg: Config
+    d_emb: int
+    prompt_k: np.ndarray
+    prompt_v: np.ndarray
+    q0: np.ndarray
+    W: List[np.ndarray]
+    emb: List[np.ndarray]
+    w_qkv: np.ndarray
+
+
+def make_generate_inputs(cfg: Config, d_emb: Optional[int] = None,
+                         seed: Optional[int] = None, R: Optional[int] = None) -> GenInputs:
+    """Draw order: prompt K, prompt V, W per level, embeddings per level,
+    w_qkv, q0.  Embeddings ~ N(0, 1) and w_qkv ~ N(0, 1/d_emb) give q, k, v of
+    unit variance like the other queries and records.  R overrides the
+    request count (fewer requests of the same shape for parity runs)."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    R = cfg.R if R is None else R
+    d_emb = cfg.D if d_emb is None else d_emb
+    H, d, D = cfg.H, cfg.d, cfg.D
+    pk = _maybe_round(_normal(rng, (R, cfg.Lp, H, d)), cfg.dtype)
+    pv = _maybe_round(_normal(rng, (R, cfg.Lp, H, d)), cfg.dtype)
+    Wl = [_maybe_round(_normal(rng, (cfg.vocab, D), 0.02), cfg.dtype) for _ in range(cfg.steps)]
+    emb = [_maybe_round(_normal(rng, (cfg.vocab, d_emb)), cfg.dtype) for _ in range(cfg.steps - 1)]
+    w_qkv = _maybe_round(_normal(rng, (3 * D, d_emb), float(d_emb) ** -0.5), cfg.dtype)
+    q0 = _maybe_round(_normal(rng, (R, 1, H, d)), cfg.dtype)
+    return GenInputs(cfg, d_emb, pk, pv, q0, Wl, emb, w_qkv)

@@ -16,6 +16,12 @@ launch / its event-timed average duration, against 8 TB/s), and the oracle
 timed on a bounded sample of the same workload on the host CPU.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+With a whole-ID generation workload (--workload gen_beam100_p600) a step is
+one complete generation instead: the q/k/v tables of the chosen codes
+(gr_code_table per level) and gr_generate (four decode steps with the chosen
+codes' records appended in between, and the IDs traced back), captured once
+in a HIP graph and replayed.
 """
 from __future__ import annotations
 
@@ -167,6 +173,143 @@ def cpu_baseline(x, seconds):
             "beam_steps_per_s": beams / spent}
 
 
+def gen_accounting(g, steps):
+    """Algorithmic bytes of one generation: per step, the prompt window once
+    per request, the queries, every distinct record on a live chain once (k,
+    v, parent id), the level's codebook, priors and outputs; per append, the
+    written records, queries and node ids; the code tables (embeddings and
+    projections read, tables written).  Distinct chain records are counted
+    from the parents the run selected."""
+    import numpy as np
+    sh = g.shape
+    es = 2 if sh.dtype == 1 else 4
+    R, D, V = sh.R, sh.H * sh.head_dim, g.vocab
+    Lw = sh.prompt_len if sh.window <= 0 else min(sh.window, sh.prompt_len)
+    total, attn_prompt = 0, 0
+    for lv, (n, k) in enumerate(g.sizes):
+        total += R * Lw * D * 2 * es + R * n * D * es + V * D * es + R * k * 12 + (R * n * 4 if lv else 0)
+        attn_prompt += R * Lw * D * 2 * es
+        # records on the chains of step lv's n beams: levels lv, lv-1, .., 1
+        if lv:
+            live = np.tile(np.arange(n), (R, 1))
+            for up in range(lv - 1, -1, -1):
+                recs = sum(len(np.unique(live[r])) for r in range(R))
+                total += recs * (D * 2 * es + 4)
+                live = np.take_along_axis(steps[up]["parent"], live, axis=1)
+        if lv + 1 < len(g.sizes):
+            total += R * k * (3 * D * es + 4 + 8)
+    total += (g.levels - 1) * (V * g.d_emb * es + 3 * D * g.d_emb * es + V * 3 * D * es)
+    return total, attn_prompt
+
+
+def bench_generate(args, cfg):
+    import numpy as np
+    import torch
+    import workloads as W
+    from generative_recommendation_beam_amd import harness as HN
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    x = W.make_generate_inputs(cfg)
+    print(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    sets = [HN.upload_generate(x) for _ in range(args.sets)]
+    torch.cuda.synchronize()
+    print(f"[bench] {len(sets)} input set(s) resident on the GPU", file=sys.stderr, flush=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+
+    def one(g):
+        HN.code_tables(g, s)
+        HN.generate(g, s)
+
+    with torch.cuda.stream(s):
+        for g in sets:
+            one(g)
+    torch.cuda.synchronize()
+    graphs = []
+    for g in sets:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=s):
+            one(g)
+        graphs.append(gr)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        ev0.record(s)
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+        ev1.record(s)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    # the same generations launched eagerly (no graph), for the launch cost
+    with torch.cuda.stream(s):
+        ev0.record(s)
+        for i in range(args.steps):
+            one(sets[i % len(sets)])
+        ev1.record(s)
+    torch.cuda.synchronize()
+    ms_eager = ev0.elapsed_time(ev1) / args.steps
+    errs = [int(g.dev_err.item()) for g in sets]
+    assert not any(errs), f"device error bits set: {errs}"
+    host = HN.generate_to_host(sets[0])
+    nbytes, prompt_bytes = gen_accounting(sets[0], host["steps"])
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    gens = 1e3 / ms
+    out = {
+        "metric": "whole-ID generations/s, 4 levels, beam=100, prompt=600 tok (1 GPU)",
+        "value": round(gens, 2), "unit": "generations/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) K/V, q0 and code embeddings, N(0,1/De) q/k/v projections, "
+                "N(0,0.02) codebooks)",
+        "config": {"workload": cfg.name, "requests": cfg.R, "prompt_len": cfg.Lp, "heads": cfg.H,
+                   "head_dim": cfg.d, "beam_width": cfg.k, "levels": cfg.steps, "d_emb": x.d_emb,
+                   "codes_per_level": cfg.vocab, "input_sets": len(sets), "hip_graph": True},
+        "ids_per_s": round(gens * cfg.R * cfg.k, 0),
+        "ms_per_generation_eager": round(ms_eager, 5),
+        "algorithmic_bytes_per_generation": nbytes,
+        "achieved_GBps": round(gbps, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "whole generation (all launches of one graph replay)",
+                     "prompt_bytes_per_generation": prompt_bytes},
+    }
+    if not args.skip_cpu_baseline:
+        print("[bench] timing the oracle on a sample of the same workload", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_generate(x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_generate(x, seconds):
+    """The oracle's whole-ID generation (one BLAS thread) request by request
+    until `seconds` of work have accumulated, scaled to whole batches."""
+    from oracle import generate as OG
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:            # pragma: no cover
+        threadpool_limits = None
+    cfg = x.cfg
+    done, spent = 0, 0.0
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        tables = [OG.code_table(e, x.w_qkv, cfg.H, cfg.d, cfg.dtype) for e in x.emb]
+        while done < cfg.R and (spent < seconds or done < 2):
+            r = [done]
+            t0 = time.perf_counter()
+            OG.generate(x.prompt_k[r], x.prompt_v[r], x.q0[r], x.W, tables, cfg.k)
+            spent += time.perf_counter() - t0
+            done += 1
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    return {"value": (done / cfg.R) / spent, "unit": "generations/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {cfg.R} requests, {spent:.1f} s of oracle time (code tables "
+                      f"excluded), scaled to whole batches"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -180,6 +323,9 @@ def main():
     from generative_recommendation_beam_amd import _lib as L
     from generative_recommendation_beam_amd import harness as HN
 
+    if args.workload in W.GEN_CONFIGS:
+        bench_generate(args, W.GEN_CONFIGS[args.workload])
+        return
     cfg = W.CONFIGS[args.workload]
     assert cfg.steps == 1, "the benchmark times single-step workloads"
     torch.cuda.set_device(0)

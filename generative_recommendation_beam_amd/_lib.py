@@ -24,14 +24,15 @@ GR_OK, GR_ERR_NULL, GR_ERR_SHAPE, GR_ERR_UNSUPPORTED = 0, 1, 2, 3
 GR_ERR_CAPACITY, GR_ERR_K_TOO_LARGE, GR_ERR_WORKSPACE, GR_ERR_HIP = 4, 5, 6, 7
 GR_F32, GR_BF16 = 0, 1
 GR_DEVERR_PARENT_RANGE, GR_DEVERR_PARENT_ORDER = 1, 2
-GR_DEVERR_DEPTH, GR_DEVERR_BEAM_RANGE = 4, 8
+GR_DEVERR_DEPTH, GR_DEVERR_BEAM_RANGE, GR_DEVERR_TOKEN_RANGE = 4, 8, 16
 GR_TOPK_LOG_SOFTMAX = 1
 GR_STEP_ATTENTION, GR_STEP_SELECTION = 2, 4
 GR_MAX_DEPTH, GR_MAX_K = 8, 2048
 
 EXPORTED = ["gr_trie_append", "gr_prefix_attn", "gr_beam_topk", "gr_decode_step",
+            "gr_code_table", "gr_append_codes", "gr_generate",
             "gr_attn_workspace_size", "gr_topk_workspace_size",
-            "gr_decode_workspace_size", "gr_status_string"]
+            "gr_decode_workspace_size", "gr_generate_workspace_size", "gr_status_string"]
 
 
 class GrError(RuntimeError):
@@ -71,6 +72,12 @@ _sig = {
     "gr_beam_topk": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P],
     "gr_decode_step": [ctypes.POINTER(Shape), _P, _P, _P, _I, ctypes.POINTER(Trie), _P, _P, _I, _P, _I, _I,
                        _P, _P, _P, _P, _P, _P, _S, _P, _P],
+    "gr_code_table": [ctypes.POINTER(Shape), _I, _I, _P, _P, _P, _P],
+    "gr_append_codes": [ctypes.POINTER(Shape), ctypes.POINTER(Trie), _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P,
+                        _P],
+    "gr_generate": [ctypes.POINTER(Shape), _P, _P, _P, _I, _P, _P, _I, _I, ctypes.POINTER(Trie), _P, _P, _P, _P,
+                    _P, _S, _P, _P],
+    "gr_generate_workspace_size": [ctypes.POINTER(Shape), _I, _I, _I],
     "gr_attn_workspace_size": [ctypes.POINTER(Shape), _I],
     "gr_topk_workspace_size": [_I, _I, _I, _I],
     "gr_decode_workspace_size": [ctypes.POINTER(Shape), _I, _I, _I],
@@ -80,7 +87,8 @@ for _name, _args in _sig.items():
     _f = getattr(_lib, _name)
     _f.argtypes = _args
     _f.restype = ctypes.c_int32
-for _name in ("gr_attn_workspace_size", "gr_topk_workspace_size", "gr_decode_workspace_size"):
+for _name in ("gr_attn_workspace_size", "gr_topk_workspace_size", "gr_decode_workspace_size",
+              "gr_generate_workspace_size"):
     getattr(_lib, _name).restype = ctypes.c_size_t
 _lib.gr_status_string.restype = ctypes.c_char_p
 
@@ -146,6 +154,32 @@ def gr_decode_step(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, W, vo
                                int(vocab), _ptr(prior), int(beam_width), int(flags), _ptr(out_score),
                                _ptr(out_token), _ptr(out_parent), _ptr(attn_out), _ptr(cand_out), _ptr(ws),
                                int(ws_bytes), _ptr(dev_err), _stream(stream)), "gr_decode_step")
+
+
+def gr_code_table(shape, vocab, d_emb, emb, w_qkv, table, stream=None):
+    _check(_lib.gr_code_table(_shape_ref(shape), int(vocab), int(d_emb), _ptr(emb), _ptr(w_qkv), _ptr(table),
+                              _stream(stream)), "gr_code_table")
+
+
+def gr_append_codes(shape, trie, base, n_new, table, vocab, token, parent_beam, prev_nodes, n_prev, q_out,
+                    node_out, dev_err, stream=None):
+    _check(_lib.gr_append_codes(_shape_ref(shape), None if trie is None else ctypes.byref(trie), int(base),
+                                int(n_new), _ptr(table), int(vocab), _ptr(token), _ptr(parent_beam),
+                                _ptr(prev_nodes), int(n_prev), _ptr(q_out), _ptr(node_out), _ptr(dev_err),
+                                _stream(stream)), "gr_append_codes")
+
+
+def gr_generate(shape, prompt_k, prompt_v, q0, levels, W, tables, vocab, beam_width, trie, out_score,
+                out_token, out_parent, out_ids, ws, ws_bytes, dev_err, stream=None):
+    _check(_lib.gr_generate(_shape_ref(shape), _ptr(prompt_k), _ptr(prompt_v), _ptr(q0), int(levels), _ptr(W),
+                            _ptr(tables), int(vocab), int(beam_width),
+                            None if trie is None else ctypes.byref(trie), _ptr(out_score), _ptr(out_token),
+                            _ptr(out_parent), _ptr(out_ids), _ptr(ws), int(ws_bytes), _ptr(dev_err),
+                            _stream(stream)), "gr_generate")
+
+
+def gr_generate_workspace_size(shape, levels, vocab, beam_width) -> int:
+    return int(_lib.gr_generate_workspace_size(_shape_ref(shape), int(levels), int(vocab), int(beam_width)))
 
 
 def gr_attn_workspace_size(shape, n_beams) -> int:

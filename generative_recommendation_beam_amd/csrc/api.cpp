@@ -195,6 +195,52 @@ inline gr_status hip_status(hipError_t e) {
 // runtime call left behind so that a launch is judged on its own status.
 inline void clear_stale_error() { (void)hipGetLastError(); }
 
+// Beams in and out of every step of a generation: n_0 = 1,
+// k_l = min(beam_width, n_l * vocab), n_{l+1} = k_l.
+struct GenLevels {
+  int n[gr::kMaxLevels], k[gr::kMaxLevels];
+  long long records;  // k_0 + ... + k_{levels-2}
+  int k_max;
+};
+GenLevels gen_levels(int levels, int vocab, int beam_width) {
+  GenLevels g;
+  long long n = 1;
+  g.records = 0;
+  g.k_max = 0;
+  for (int l = 0; l < levels; ++l) {
+    const long long k = n * vocab < beam_width ? n * vocab : beam_width;
+    g.n[l] = (int)n;
+    g.k[l] = (int)k;
+    if (l + 1 < levels) g.records += k;
+    if (k > g.k_max) g.k_max = (int)k;
+    n = k;
+  }
+  return g;
+}
+
+// Workspace of a generation: the decode workspace (the largest step), the
+// queries of the next step [R][k_max][D], and two node-id buffers [R][k_max]
+// (the nodes of a step's input beams, and of its output beams once appended).
+struct GenLayout {
+  size_t dec_bytes, q_off, node_off[2], total;
+};
+GenLayout gen_layout(const gr_shape *s, int levels, int vocab, int beam_width) {
+  const GenLevels g = gen_levels(levels, vocab, beam_width);
+  GenLayout L;
+  L.dec_bytes = 0;
+  for (int l = 0; l < levels; ++l) {
+    const size_t b = decode_layout(s, g.n[l], vocab, g.k[l]).total;
+    if (b > L.dec_bytes) L.dec_bytes = b;
+  }
+  L.dec_bytes = align_up(L.dec_bytes);
+  const size_t rows = (size_t)s->R * g.k_max;
+  L.q_off = L.dec_bytes;
+  L.node_off[0] = L.q_off + align_up(rows * s->H * s->head_dim * elem_bytes(s->dtype));
+  L.node_off[1] = L.node_off[0] + align_up(rows * sizeof(int32_t));
+  L.total = L.node_off[1] + align_up(rows * sizeof(int32_t)) + kAlign;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -392,6 +438,147 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void
   sa.k = beam_width;
   sa.log_softmax = lsm;
   return hip_status(gr::launch_score_select(sa, so, stream));
+}
+
+gr_status gr_code_table(const gr_shape *shape, int32_t vocab, int32_t d_emb, const void *emb, const void *w_qkv,
+                        void *table, hipStream_t stream) {
+  gr_status st = check_shape(shape);
+  if (st) return st;
+  if (!emb || !w_qkv || !table) return GR_ERR_NULL;
+  if (vocab != 256) return GR_ERR_UNSUPPORTED;
+  if (d_emb <= 0 || d_emb % 16 != 0 || d_emb > 16384) return GR_ERR_UNSUPPORTED;
+  if (!aligned16(emb) || !aligned16(w_qkv) || !aligned16(table)) return GR_ERR_UNSUPPORTED;
+  gr::CodeTableArgs a;
+  a.dtype = shape->dtype;
+  a.emb = emb;
+  a.w_qkv = w_qkv;
+  a.table = table;
+  a.V = vocab;
+  a.D = shape->H * shape->head_dim;
+  a.De = d_emb;
+  clear_stale_error();
+  return hip_status(gr::launch_code_table(a, stream));
+}
+
+gr_status gr_append_codes(const gr_shape *shape, const gr_trie *trie, int32_t base, int32_t n_new,
+                          const void *table, int32_t vocab, const int32_t *token, const int32_t *parent_beam,
+                          const int32_t *prev_nodes, int32_t n_prev, void *q_out, int32_t *node_out,
+                          int32_t *dev_err, hipStream_t stream) {
+  gr_status st = check_shape(shape);
+  if (st) return st;
+  if (!trie || !table || !token || !dev_err) return GR_ERR_NULL;
+  if (!trie->k || !trie->v || !trie->parent) return GR_ERR_NULL;
+  if (vocab != 256) return GR_ERR_UNSUPPORTED;
+  if (n_new <= 0 || base < 0 || trie->capacity <= 0) return GR_ERR_SHAPE;
+  if ((parent_beam == nullptr) != (prev_nodes == nullptr)) return GR_ERR_NULL;
+  if (prev_nodes && n_prev <= 0) return GR_ERR_SHAPE;
+  if ((long long)base + n_new > trie->capacity) return GR_ERR_CAPACITY;
+  if (!aligned16(trie->k) || !aligned16(trie->v) || !aligned16(table) || (q_out && !aligned16(q_out)))
+    return GR_ERR_UNSUPPORTED;
+  if ((long long)shape->R * trie->capacity * shape->H * shape->head_dim > (1ll << 40)) return GR_ERR_SHAPE;
+  gr::AppendCodesArgs a;
+  a.elem_bytes = elem_bytes(shape->dtype);
+  a.ak = trie->k;
+  a.av = trie->v;
+  a.q_out = q_out;
+  a.parent = trie->parent;
+  a.table = table;
+  a.token = token;
+  a.parent_beam = parent_beam;
+  a.prev_nodes = prev_nodes;
+  a.node_out = node_out;
+  a.dev_err = dev_err;
+  a.R = shape->R;
+  a.H = shape->H;
+  a.hd = shape->head_dim;
+  a.cap = trie->capacity;
+  a.base = base;
+  a.n_new = n_new;
+  a.n_prev = prev_nodes ? n_prev : 0;
+  a.V = vocab;
+  clear_stale_error();
+  return hip_status(gr::launch_append_codes(a, stream));
+}
+
+size_t gr_generate_workspace_size(const gr_shape *shape, int32_t levels, int32_t vocab, int32_t beam_width) {
+  if (check_shape(shape) || levels < 1 || levels > gr::kMaxLevels || vocab != 256 || beam_width <= 0 ||
+      beam_width > GR_MAX_K)
+    return 0;
+  return gen_layout(shape, levels, vocab, beam_width).total;
+}
+
+gr_status gr_generate(const gr_shape *shape, const void *prompt_k, const void *prompt_v, const void *q0,
+                      int32_t levels, const void *W, const void *tables, int32_t vocab, int32_t beam_width,
+                      const gr_trie *trie, float *out_score, int32_t *out_token, int32_t *out_parent,
+                      int32_t *out_ids, void *ws, size_t ws_bytes, int32_t *dev_err, hipStream_t stream) {
+  gr_status st = check_shape(shape);
+  if (st) return st;
+  if (!prompt_k || !prompt_v || !q0 || !W || !out_score || !out_token || !out_parent || !out_ids || !dev_err)
+    return GR_ERR_NULL;
+  if (levels < 1 || levels > gr::kMaxLevels || vocab != 256) return GR_ERR_UNSUPPORTED;
+  if (beam_width <= 0) return GR_ERR_SHAPE;
+  if (beam_width > GR_MAX_K) return GR_ERR_K_TOO_LARGE;
+  if (!aligned16(W) || !aligned16(q0) || (tables && !aligned16(tables))) return GR_ERR_UNSUPPORTED;
+  const GenLevels g = gen_levels(levels, vocab, beam_width);
+  if (levels > 1) {
+    if (!tables || !trie) return GR_ERR_NULL;
+    st = check_trie(shape, trie, true);
+    if (st) return st;
+    if (g.records > trie->capacity) return GR_ERR_CAPACITY;
+    if (trie->max_depth < levels - 1) return GR_ERR_UNSUPPORTED;
+  }
+  // every step's own checks, before anything is enqueued
+  for (int l = 0; l < levels; ++l) {
+    st = attn_common(shape, prompt_k, prompt_v, q0, g.n[l], nullptr, nullptr, dev_err);
+    if (st) return st;
+    st = check_select(shape->R, g.n[l], vocab, g.k[l], GR_TOPK_LOG_SOFTMAX);
+    if (st) return st;
+  }
+  const GenLayout L = gen_layout(shape, levels, vocab, beam_width);
+  if (!ws || ws_bytes < L.total) return GR_ERR_WORKSPACE;
+  char *base = align_ptr(ws);
+  void *dec_ws = base;
+  void *qbuf = base + L.q_off;
+  int32_t *nodes[2] = {(int32_t *)(base + L.node_off[0]), (int32_t *)(base + L.node_off[1])};
+  const int R = shape->R;
+  const size_t D = (size_t)shape->H * shape->head_dim;
+  const size_t eb = elem_bytes(shape->dtype);
+  const size_t w_level = (size_t)vocab * D * eb;
+  const size_t t_level = (size_t)vocab * 3 * D * eb;
+
+  gr::TraceArgs tr;
+  tr.R = R;
+  tr.levels = levels;
+  long long off = 0, rec_base = 0;
+  for (int l = 0; l < levels; ++l) {
+    tr.off[l] = off;
+    tr.k[l] = g.k[l];
+    float *score = out_score + off;
+    int32_t *token = out_token + off;
+    int32_t *parent = out_parent + off;
+    const int32_t *beam_node = l > 0 ? nodes[(l - 1) & 1] : nullptr;
+    st = gr_decode_step(shape, prompt_k, prompt_v, l > 0 ? qbuf : q0, g.n[l], l > 0 ? trie : nullptr, beam_node,
+                        (const char *)W + l * w_level, vocab, l > 0 ? out_score + tr.off[l - 1] : nullptr,
+                        g.k[l], GR_TOPK_LOG_SOFTMAX, score, token, parent, nullptr, nullptr, dec_ws, L.dec_bytes,
+                        dev_err, stream);
+    if (st) return st;
+    if (l + 1 < levels) {
+      // the chosen codes become the next step's beams: records at nodes
+      // [rec_base, rec_base + k_l), their queries into qbuf
+      st = gr_append_codes(shape, trie, (int32_t)rec_base, g.k[l], (const char *)tables + l * t_level, vocab,
+                           token, l > 0 ? parent : nullptr, l > 0 ? beam_node : nullptr, g.n[l], qbuf,
+                           nodes[l & 1], dev_err, stream);
+      if (st) return st;
+      rec_base += g.k[l];
+    }
+    off += (long long)R * g.k[l];
+  }
+  tr.token = out_token;
+  tr.parent = out_parent;
+  tr.ids = out_ids;
+  tr.dev_err = dev_err;
+  clear_stale_error();
+  return hip_status(gr::launch_trace_ids(tr, stream));
 }
 
 }  // extern "C"

@@ -51,6 +51,37 @@ struct AppendArgs {
 };
 hipError_t launch_trie_append(const AppendArgs &a, hipStream_t s);
 
+// Whole-ID generation (generate.hip).  Levels of one generation call.
+constexpr int kMaxLevels = GR_MAX_DEPTH + 1;
+
+struct CodeTableArgs {
+  int dtype;
+  const void *emb, *w_qkv;     // [V][De], [3D][De]
+  void *table;                 // [V][3D]
+  int V, D, De;
+};
+hipError_t launch_code_table(const CodeTableArgs &a, hipStream_t s);
+
+struct AppendCodesArgs {
+  int elem_bytes;
+  void *ak, *av, *q_out;
+  int32_t *parent;
+  const void *table;
+  const int32_t *token, *parent_beam, *prev_nodes;
+  int32_t *node_out, *dev_err;
+  int R, H, hd, cap, base, n_new, n_prev, V;
+};
+hipError_t launch_append_codes(const AppendCodesArgs &a, hipStream_t s);
+
+struct TraceArgs {
+  const int32_t *token, *parent;   // per-level blocks [R][k[l]] at offset off[l]
+  int32_t *ids, *dev_err;          // ids [R][k[levels-1]][levels]
+  long long off[kMaxLevels];
+  int k[kMaxLevels];
+  int R, levels;
+};
+hipError_t launch_trace_ids(const TraceArgs &a, hipStream_t s);
+
 // Selection outputs / partial lists shared by the scoring kernels.
 struct SelectOut {
   float *score;

@@ -183,3 +183,95 @@ def results_to_host(buf: DecodeBuffers) -> dict:
     if buf.cand is not None:
         out["cand"] = buf.cand.cpu().numpy()
     return out
+
+
+# ------------------------------------------------------- whole-ID generation
+
+
+def level_sizes(levels: int, beam_width: int, vocab: int = 256):
+    """(n_l, k_l) of every step of a generation: beams in and kept."""
+    n, out = 1, []
+    for _ in range(levels):
+        k = min(beam_width, n * vocab)
+        out.append((n, k))
+        n = k
+    return out
+
+
+@dataclasses.dataclass
+class DeviceGen:
+    """A whole-ID generation on the device: inputs, the code tables, the
+    arena, outputs and workspace, ready for gr_generate."""
+    shape: L.Shape
+    levels: int
+    beam_width: int
+    vocab: int
+    d_emb: int
+    prompt_k: torch.Tensor
+    prompt_v: torch.Tensor
+    q0: torch.Tensor
+    W: torch.Tensor            # [levels][vocab][D]
+    emb: Optional[torch.Tensor]      # [levels-1][vocab][d_emb]
+    w_qkv: torch.Tensor        # [3D][d_emb]
+    tables: Optional[torch.Tensor]   # [levels-1][vocab][3][H][hd]
+    trie: Optional[L.Trie]
+    out_score: torch.Tensor
+    out_token: torch.Tensor
+    out_parent: torch.Tensor
+    out_ids: torch.Tensor
+    ws: torch.Tensor
+    dev_err: torch.Tensor
+    sizes: list
+
+    def level(self, name: str, lv: int) -> torch.Tensor:
+        """Step lv's block [R][k_l] of out_score / out_token / out_parent."""
+        R = self.shape.R
+        off = R * sum(k for _, k in self.sizes[:lv])
+        k = self.sizes[lv][1]
+        return getattr(self, name)[off:off + R * k].view(R, k)
+
+
+def upload_generate(x, device="cuda") -> DeviceGen:
+    """Upload a workloads.GenInputs and allocate everything gr_generate needs
+    (the code tables are left empty: code_tables() fills them)."""
+    cfg = x.cfg
+    dt = dtype_code(cfg.dtype)
+    R = x.prompt_k.shape[0]
+    shape = make_shape(R, cfg.H, cfg.d, cfg.Lp, cfg.window, dt)
+    levels, B, V = cfg.steps, cfg.k, cfg.vocab
+    sizes = level_sizes(levels, B, V)
+    total = R * sum(k for _, k in sizes)
+    trie, tables, emb = None, None, None
+    if levels > 1:
+        cap = sum(k for _, k in sizes[:-1])
+        trie = new_arena(shape, cap, max_depth=max(levels - 1, 1), device=device)[3]
+        emb = to_dev(np.stack(x.emb), dt, device)
+        tables = torch.empty((levels - 1, V, 3, cfg.H, cfg.d), dtype=_TORCH[dt], device=device)
+    ws_bytes = L.gr_generate_workspace_size(shape, levels, V, B)
+    return DeviceGen(shape, levels, B, V, x.d_emb, to_dev(x.prompt_k, dt, device), to_dev(x.prompt_v, dt, device),
+                     to_dev(x.q0, dt, device), to_dev(np.stack(x.W), dt, device), emb,
+                     to_dev(x.w_qkv, dt, device), tables, trie,
+                     torch.empty(total, dtype=torch.float32, device=device),
+                     torch.empty(total, dtype=torch.int32, device=device),
+                     torch.empty(total, dtype=torch.int32, device=device),
+                     torch.empty((R, sizes[-1][1], levels), dtype=torch.int32, device=device),
+                     torch.empty(ws_bytes, dtype=torch.uint8, device=device),
+                     torch.zeros(1, dtype=torch.int32, device=device), sizes)
+
+
+def code_tables(g: DeviceGen, stream=None) -> None:
+    """gr_code_table for every level whose chosen codes become records."""
+    for lv in range(g.levels - 1):
+        L.gr_code_table(g.shape, g.vocab, g.d_emb, g.emb[lv], g.w_qkv, g.tables[lv], stream)
+
+
+def generate(g: DeviceGen, stream=None) -> None:
+    L.gr_generate(g.shape, g.prompt_k, g.prompt_v, g.q0, g.levels, g.W, g.tables, g.vocab, g.beam_width, g.trie,
+                  g.out_score, g.out_token, g.out_parent, g.out_ids, g.ws, g.ws.numel(), g.dev_err, stream)
+
+
+def generate_to_host(g: DeviceGen) -> dict:
+    """Per-step results and the final IDs as numpy arrays."""
+    steps = [dict(score=g.level("out_score", lv).cpu().numpy(), token=g.level("out_token", lv).cpu().numpy(),
+                  parent=g.level("out_parent", lv).cpu().numpy()) for lv in range(g.levels)]
+    return dict(steps=steps, ids=g.out_ids.cpu().numpy())

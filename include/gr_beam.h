@@ -72,7 +72,9 @@ enum {
   GR_DEVERR_PARENT_RANGE = 1, /* a node or parent id outside [-1, capacity) */
   GR_DEVERR_PARENT_ORDER = 2, /* a parent id not older than its child */
   GR_DEVERR_DEPTH = 4,        /* a chain longer than max_depth */
-  GR_DEVERR_BEAM_RANGE = 8    /* parent_beam outside [0, n_prev) */
+  GR_DEVERR_BEAM_RANGE = 8,   /* parent_beam outside [0, n_prev) */
+  GR_DEVERR_TOKEN_RANGE = 16  /* a chosen code outside [0, vocab), or a traced
+                                 parent outside the previous step's beams */
 };
 
 /* gr_beam_topk / gr_decode_step flags */
@@ -204,12 +206,91 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k,
                          size_t ws_bytes, int32_t *dev_err,
                          hipStream_t stream);
 
+/* gr_code_table -- query, key and value of every code of one level
+ * (Engineering Exploration of Generative Recall, 4.1: attention starts from
+ * the per-token query, key and value; 4.2: each level has its own 256
+ * codes).  A code chosen at one step enters the next as a token whose
+ * embedding is projected by the model's query, key and value projections; as
+ * that depends only on the code, the level's vocab rows are projected once:
+ *   table[t][c] = sum_i emb[t][i] * w_qkv[c][i],  c < 3*D, D = H*head_dim,
+ * so that table[t] = [q | k | v] of code t, each [H][head_dim].
+ *   emb: [vocab][d_emb] dtype.  w_qkv: [3*D][d_emb] dtype (the D query
+ *   projection rows, then the key rows, then the value rows).  table:
+ *   [vocab][3][H][head_dim] dtype (fp32 accumulation, one rounding to the
+ *   storage dtype, round to nearest even for bf16).  Only shape->H, head_dim
+ *   and dtype are used.
+ *   Host errors: NULL pointers, vocab != 256, d_emb not a positive multiple
+ *   of 16 or above 16384, unsupported dtype/head_dim, unaligned pointers. */
+gr_status gr_code_table(const gr_shape *shape, int32_t vocab, int32_t d_emb,
+                        const void *emb, const void *w_qkv, void *table,
+                        hipStream_t stream);
+
+/* gr_append_codes -- gr_trie_append for beams that just chose a code (OneLA,
+ * Abstract: one append-only record per surviving beam).  For every request r
+ * and j < n_new, with t = token[r][j] and node n = base + j:
+ *     trie.k[r][n] = table[t][1],  trie.v[r][n] = table[t][2],
+ *     q_out[r][j] = table[t][0]    (q_out optional, may be NULL),
+ *     trie.parent[r][n], node_out[r][j]: as gr_trie_append.
+ *   table: [vocab][3][H][head_dim] dtype (gr_code_table).  token: [R][n_new]
+ *   int32 (a step's out_token).  parent_beam / prev_nodes / n_prev: as
+ *   gr_trie_append (a step's out_parent and the nodes of its input beams).
+ *   q_out: [R][n_new][H][head_dim] dtype, the next step's queries.
+ *   Host errors: those of gr_trie_append, plus NULL table/token and
+ *   vocab != 256.  Device errors: those of gr_trie_append, and TOKEN_RANGE for
+ *   a code outside [0, vocab) (code 0 is used in its place). */
+gr_status gr_append_codes(const gr_shape *shape, const gr_trie *trie,
+                          int32_t base, int32_t n_new, const void *table,
+                          int32_t vocab, const int32_t *token,
+                          const int32_t *parent_beam,
+                          const int32_t *prev_nodes, int32_t n_prev,
+                          void *q_out, int32_t *node_out, int32_t *dev_err,
+                          hipStream_t stream);
+
+/* gr_generate -- a whole semantic ID: `levels` decode steps, each followed
+ * (but the last) by gr_append_codes of its chosen codes, then the trace-back
+ * of the final beams' code sequences; all enqueued on `stream` with no host
+ * synchronisation, so the whole call can be captured in one HIP graph
+ * (TransRetrieval, GPU retrieval: the iterations of the search stay on the
+ * device; Engineering Exploration of Generative Recall, 4.2: level l is
+ * scored over its own 256 codes with W_l).
+ *   Step 0 has one root hypothesis per request (query q0, prior 0, no
+ *   records); step l keeps k_l = min(beam_width, n_l * vocab) beams, with
+ *   n_0 = 1 and n_{l+1} = k_l.  Step l+1's beams are step l's output slots:
+ *   their queries and records come from tables[l] at their chosen codes, and
+ *   their priors are step l's scores.
+ *   q0: [R][1][H][head_dim] dtype.  W: [levels][vocab][H*head_dim] dtype.
+ *   tables: [levels-1][vocab][3][H][head_dim] dtype (gr_code_table per
+ *   level; NULL when levels == 1).  trie: arena for the appended records,
+ *   capacity >= k_0 + ... + k_{levels-2} and max_depth >= levels - 1 (NULL
+ *   when levels == 1); nodes [0, k_0) hold level-1 records, the next k_1
+ *   level-2 records, and so on.
+ *   out_score / out_token / out_parent: per-step results packed step after
+ *   step; step l's block is [R][k_l] and starts at element
+ *   R * (k_0 + ... + k_{l-1}) (for beam_width <= 256 simply
+ *   [levels][R][beam_width]).  out_parent indexes the step's input beams.
+ *   out_ids: [R][k_{levels-1}][levels] int32, the code of every level of
+ *   each final beam.  ws: gr_generate_workspace_size() bytes.
+ *   Host errors: those of gr_decode_step and gr_append_codes, vocab != 256,
+ *   levels outside [1, GR_MAX_DEPTH + 1], capacity or max_depth too small
+ *   (CAPACITY / UNSUPPORTED).  Device errors: those of both, OR-ed into
+ *   *dev_err; the outputs are undefined when it is nonzero.  GR_ERR_HIP can
+ *   leave earlier levels enqueued. */
+gr_status gr_generate(const gr_shape *shape, const void *prompt_k,
+                      const void *prompt_v, const void *q0, int32_t levels,
+                      const void *W, const void *tables, int32_t vocab,
+                      int32_t beam_width, const gr_trie *trie,
+                      float *out_score, int32_t *out_token,
+                      int32_t *out_parent, int32_t *out_ids, void *ws,
+                      size_t ws_bytes, int32_t *dev_err, hipStream_t stream);
+
 /* Scratch sizes in bytes (0 when none is needed; sizes <= 0 give 0). */
 size_t gr_attn_workspace_size(const gr_shape *shape, int32_t n_beams);
 size_t gr_topk_workspace_size(int32_t R, int32_t n_in, int32_t vocab,
                               int32_t k);
 size_t gr_decode_workspace_size(const gr_shape *shape, int32_t n_beams,
                                 int32_t vocab, int32_t k);
+size_t gr_generate_workspace_size(const gr_shape *shape, int32_t levels,
+                                  int32_t vocab, int32_t beam_width);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *gr_status_string(gr_status status);

@@ -162,3 +162,74 @@ def test_workspace_sizes():
     assert L.gr_attn_workspace_size(shape(R=2, dtype=L.GR_F32), 100) == 0
     assert L.gr_decode_workspace_size(shape(head_dim=16), 100, 256, 100) == 0
     assert L.status_string(L.GR_ERR_CAPACITY).startswith("append")
+
+
+def test_code_table_host_errors():
+    sh = shape()
+    call = lambda **kw: L._lib.gr_code_table(
+        ctypes.byref(kw.get("sh", sh)), kw.get("vocab", 256), kw.get("d_emb", 512), kw.get("emb", FAKE), FAKE,
+        kw.get("table", FAKE), None)
+    assert call(emb=None) == L.GR_ERR_NULL
+    assert call(table=None) == L.GR_ERR_NULL
+    assert call(vocab=128) == L.GR_ERR_UNSUPPORTED
+    assert call(d_emb=24) == L.GR_ERR_UNSUPPORTED              # not a multiple of 16
+    assert call(d_emb=0) == L.GR_ERR_UNSUPPORTED
+    assert call(emb=FAKE + 8) == L.GR_ERR_UNSUPPORTED          # unaligned
+    assert call(sh=shape(head_dim=128)) == L.GR_ERR_UNSUPPORTED
+
+
+def test_append_codes_host_errors():
+    sh, tr = shape(), trie()
+    call = lambda **kw: L._lib.gr_append_codes(
+        ctypes.byref(kw.get("sh", sh)), ctypes.byref(kw.get("tr", tr)), kw.get("base", 0), kw.get("n_new", 100),
+        kw.get("table", FAKE), kw.get("vocab", 256), kw.get("token", FAKE), kw.get("pb", None),
+        kw.get("prev", None), kw.get("n_prev", 0), kw.get("q_out", None), None, kw.get("dev_err", FAKE), None)
+    assert call(table=None) == L.GR_ERR_NULL
+    assert call(token=None) == L.GR_ERR_NULL
+    assert call(vocab=1) == L.GR_ERR_UNSUPPORTED
+    assert call(base=250) == L.GR_ERR_CAPACITY
+    assert call(n_new=0) == L.GR_ERR_SHAPE
+    assert call(pb=FAKE) == L.GR_ERR_NULL                      # parent_beam without prev_nodes
+    assert call(pb=FAKE, prev=FAKE, n_prev=0) == L.GR_ERR_SHAPE
+    assert call(q_out=FAKE + 4) == L.GR_ERR_UNSUPPORTED
+    assert call(dev_err=None) == L.GR_ERR_NULL
+
+
+def test_generate_host_errors():
+    sh = shape()
+    need = L.gr_generate_workspace_size(sh, 4, 256, 100)
+    tr = trie(capacity=300, max_depth=3)
+
+    def call(**kw):
+        t = kw.get("tr", tr)
+        return L._lib.gr_generate(
+            ctypes.byref(kw.get("sh", sh)), FAKE, FAKE, FAKE, kw.get("levels", 4), FAKE, kw.get("tables", FAKE),
+            kw.get("vocab", 256), kw.get("B", 100), None if t is None else ctypes.byref(t), FAKE, FAKE, FAKE,
+            kw.get("ids", FAKE), kw.get("ws", FAKE), kw.get("ws_bytes", need), FAKE, None)
+    assert call(ids=None) == L.GR_ERR_NULL
+    assert call(tables=None) == L.GR_ERR_NULL
+    assert call(tr=None) == L.GR_ERR_NULL
+    assert call(vocab=1) == L.GR_ERR_UNSUPPORTED
+    assert call(levels=0) == L.GR_ERR_UNSUPPORTED
+    assert call(levels=L.GR_MAX_DEPTH + 2) == L.GR_ERR_UNSUPPORTED
+    assert call(B=0) == L.GR_ERR_SHAPE
+    assert call(B=L.GR_MAX_K + 1) == L.GR_ERR_K_TOO_LARGE
+    assert call(tr=trie(capacity=299, max_depth=3)) == L.GR_ERR_CAPACITY   # 3 levels of 100 records
+    assert call(tr=trie(capacity=300, max_depth=2)) == L.GR_ERR_UNSUPPORTED
+    assert call(ws_bytes=need - 1) == L.GR_ERR_WORKSPACE
+    assert call(ws=None) == L.GR_ERR_WORKSPACE
+    # one level needs neither tables nor a trie; it still needs its workspace
+    one = L.gr_generate_workspace_size(sh, 1, 256, 100)
+    assert call(levels=1, tables=None, tr=None, ws_bytes=one - 1) == L.GR_ERR_WORKSPACE
+
+
+def test_generate_workspace_size():
+    sh = shape(R=256)
+    n = L.gr_generate_workspace_size(sh, 4, 256, 100)
+    dec = L.gr_decode_workspace_size(sh, 100, 256, 100)
+    q = 256 * 100 * 512 * 2
+    nodes = 2 * 256 * 100 * 4
+    assert dec + q + nodes <= n <= dec + q + nodes + 4 * 256
+    assert L.gr_generate_workspace_size(sh, 0, 256, 100) == 0
+    assert L.gr_generate_workspace_size(sh, 4, 1, 100) == 0
+    assert L.gr_generate_workspace_size(sh, 4, 256, L.GR_MAX_K + 1) == 0

@@ -19,7 +19,7 @@ timed on a bounded sample of the same workload on the host CPU.
 
 With a whole-ID generation workload (--workload gen_beam100_p600) a step is
 one complete generation instead: the q/k/v tables of the chosen codes
-(gr_code_table per level) and gr_generate (four decode steps with the chosen
+(one gr_code_table over the levels) and gr_generate (four decode steps with the chosen
 codes' records appended in between, and the IDs traced back), captured once
 in a HIP graph and replayed.
 """

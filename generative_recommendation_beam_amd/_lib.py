@@ -72,7 +72,7 @@ _sig = {
     "gr_beam_topk": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P],
     "gr_decode_step": [ctypes.POINTER(Shape), _P, _P, _P, _I, ctypes.POINTER(Trie), _P, _P, _I, _P, _I, _I,
                        _P, _P, _P, _P, _P, _P, _S, _P, _P],
-    "gr_code_table": [ctypes.POINTER(Shape), _I, _I, _P, _P, _P, _P],
+    "gr_code_table": [ctypes.POINTER(Shape), _I, _I, _I, _P, _P, _P, _P],
     "gr_append_codes": [ctypes.POINTER(Shape), ctypes.POINTER(Trie), _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P,
                         _P],
     "gr_generate": [ctypes.POINTER(Shape), _P, _P, _P, _I, _P, _P, _I, _I, ctypes.POINTER(Trie), _P, _P, _P, _P,
@@ -156,9 +156,9 @@ def gr_decode_step(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, W, vo
                                int(ws_bytes), _ptr(dev_err), _stream(stream)), "gr_decode_step")
 
 
-def gr_code_table(shape, vocab, d_emb, emb, w_qkv, table, stream=None):
-    _check(_lib.gr_code_table(_shape_ref(shape), int(vocab), int(d_emb), _ptr(emb), _ptr(w_qkv), _ptr(table),
-                              _stream(stream)), "gr_code_table")
+def gr_code_table(shape, levels, vocab, d_emb, emb, w_qkv, table, stream=None):
+    _check(_lib.gr_code_table(_shape_ref(shape), int(levels), int(vocab), int(d_emb), _ptr(emb), _ptr(w_qkv),
+                              _ptr(table), _stream(stream)), "gr_code_table")
 
 
 def gr_append_codes(shape, trie, base, n_new, table, vocab, token, parent_beam, prev_nodes, n_prev, q_out,

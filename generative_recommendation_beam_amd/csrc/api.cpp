@@ -440,12 +440,13 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void
   return hip_status(gr::launch_score_select(sa, so, stream));
 }
 
-gr_status gr_code_table(const gr_shape *shape, int32_t vocab, int32_t d_emb, const void *emb, const void *w_qkv,
-                        void *table, hipStream_t stream) {
+gr_status gr_code_table(const gr_shape *shape, int32_t levels, int32_t vocab, int32_t d_emb, const void *emb,
+                        const void *w_qkv, void *table, hipStream_t stream) {
   gr_status st = check_shape(shape);
   if (st) return st;
   if (!emb || !w_qkv || !table) return GR_ERR_NULL;
-  if (vocab != 256) return GR_ERR_UNSUPPORTED;
+  if (levels <= 0) return GR_ERR_SHAPE;
+  if (levels > gr::kMaxLevels || vocab != 256) return GR_ERR_UNSUPPORTED;
   if (d_emb <= 0 || d_emb % 16 != 0 || d_emb > 16384) return GR_ERR_UNSUPPORTED;
   if (!aligned16(emb) || !aligned16(w_qkv) || !aligned16(table)) return GR_ERR_UNSUPPORTED;
   gr::CodeTableArgs a;
@@ -453,6 +454,7 @@ gr_status gr_code_table(const gr_shape *shape, int32_t vocab, int32_t d_emb, con
   a.emb = emb;
   a.w_qkv = w_qkv;
   a.table = table;
+  a.levels = levels;
   a.V = vocab;
   a.D = shape->H * shape->head_dim;
   a.De = d_emb;

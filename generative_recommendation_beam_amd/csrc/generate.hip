@@ -21,44 +21,67 @@
 namespace gr {
 namespace {
 
-// T[t][c] = sum_i E[t][i] Wq[c][i] in bf16 on v_mfma_f32_32x32x16_bf16: one
-// wave per 32 x 32 output tile (A: 32 embedding rows, B: 32 projection rows,
-// both contiguous along i), operands loaded straight from global memory (the
-// whole problem is a few hundred KB and stays in L2).  Output element (row
-// 8*(i/4) + 4*(lane/32) + i%4, column lane%32) sits in accumulator i.
+// T[t][c] = sum_i E[t][i] Wq[c][i] in bf16 on v_mfma_f32_32x32x16_bf16.  One
+// workgroup of 4 waves per 32 x 32 output tile of one level (A: 32 embedding
+// rows, B: 32 projection rows, both contiguous along i).  The 16-wide k-steps
+// are dealt round-robin to the 4 waves, each of which issues the loads of 8
+// steps before their MFMAs (operands straight from global memory: the problem
+// is a few hundred KB and stays in L2), and the partial tiles meet in LDS.
+// Output element (row 8*(i/4) + 4*(lane/32) + i%4, column lane%32) sits in
+// accumulator i.
 __global__ __launch_bounds__(256) void code_table_bf16_kernel(const uint16_t *E, const uint16_t *Wq,
                                                               uint16_t *T, int V, int N, int De) {
-  const int lane = threadIdx.x & 63;
-  const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int tm = V / 32;
-  if (tile >= tm * (N / 32)) return;
+  __shared__ float red[3][16][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tm = V / 32, tiles = tm * (N / 32);
+  const int lv = blockIdx.x / tiles, tile = blockIdx.x % tiles;
   const int t0 = (tile % tm) * 32, c0 = (tile / tm) * 32;
   const int g = lane >> 5, c = lane & 31;
-  const uint16_t *a = E + (size_t)(t0 + c) * De + 8 * g;
+  const uint16_t *a = E + ((size_t)lv * V + t0 + c) * De + 8 * g;
   const uint16_t *b = Wq + (size_t)(c0 + c) * De + 8 * g;
   f32x16 acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll 4
-  for (int k0 = 0; k0 < De; k0 += 16) {
-    const bf16x8 av = *(const bf16x8 *)(a + k0);
-    const bf16x8 bv = *(const bf16x8 *)(b + k0);
+  const int steps = De / 16;
+  int st = wave;
+  for (; st + 28 < steps; st += 32) {
+    bf16x8 av[8], bv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      av[u] = *(const bf16x8 *)(a + (st + 4 * u) * 16);
+      bv[u] = *(const bf16x8 *)(b + (st + 4 * u) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[u], bv[u], acc, 0, 0, 0);
+  }
+  for (; st < steps; st += 4) {
+    const bf16x8 av = *(const bf16x8 *)(a + st * 16);
+    const bf16x8 bv = *(const bf16x8 *)(b + st * 16);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
   }
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[wave - 1][i][lane] = acc[i];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  uint16_t *out = T + (size_t)lv * V * N;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
+    const float v = acc[i] + red[0][i][lane] + red[1][i][lane] + red[2][i][lane];
     const int t = t0 + 8 * (i >> 2) + 4 * g + (i & 3);
-    T[(size_t)t * N + c0 + c] = f32_to_bf16(acc[i]);
+    out[(size_t)t * N + c0 + c] = f32_to_bf16(v);
   }
 }
 
 // fp32 storage: one thread per table entry, an fp32 fma chain over i.
 __global__ __launch_bounds__(256) void code_table_f32_kernel(const float *E, const float *Wq, float *T,
-                                                             int V, int N, int De) {
+                                                             int V, int N, int De, long long n) {
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long long)V * N) return;
-  const int t = (int)(idx / N), c = (int)(idx % N);
-  const float *a = E + (size_t)t * De, *b = Wq + (size_t)c * De;
+  if (idx >= n) return;
+  const long long row = idx / N;                  // level * V + t
+  const int c = (int)(idx % N);
+  const float *a = E + (size_t)row * De, *b = Wq + (size_t)c * De;
   float s = 0.f;
   for (int i = 0; i < De; ++i) s = fmaf(a[i], b[i], s);
   T[idx] = s;
@@ -134,12 +157,12 @@ hipError_t launch_code_table(const CodeTableArgs &a, hipStream_t s) {
   const int N = 3 * a.D;
   if (a.dtype == GR_BF16) {
     const int tiles = (a.V / 32) * (N / 32);
-    hipLaunchKernelGGL(code_table_bf16_kernel, dim3((tiles + 3) / 4), dim3(256), 0, s,
+    hipLaunchKernelGGL(code_table_bf16_kernel, dim3(tiles * a.levels), dim3(256), 0, s,
                        (const uint16_t *)a.emb, (const uint16_t *)a.w_qkv, (uint16_t *)a.table, a.V, N, a.De);
   } else {
-    const long long n = (long long)a.V * N;
+    const long long n = (long long)a.levels * a.V * N;
     hipLaunchKernelGGL(code_table_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       (const float *)a.emb, (const float *)a.w_qkv, (float *)a.table, a.V, N, a.De);
+                       (const float *)a.emb, (const float *)a.w_qkv, (float *)a.table, a.V, N, a.De, n);
   }
   return hipGetLastError();
 }

@@ -56,9 +56,9 @@ constexpr int kMaxLevels = GR_MAX_DEPTH + 1;
 
 struct CodeTableArgs {
   int dtype;
-  const void *emb, *w_qkv;     // [V][De], [3D][De]
-  void *table;                 // [V][3D]
-  int V, D, De;
+  const void *emb, *w_qkv;     // [levels][V][De], [3D][De]
+  void *table;                 // [levels][V][3D]
+  int levels, V, D, De;
 };
 hipError_t launch_code_table(const CodeTableArgs &a, hipStream_t s);
 

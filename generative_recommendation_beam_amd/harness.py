@@ -260,9 +260,8 @@ def upload_generate(x, device="cuda") -> DeviceGen:
 
 
 def code_tables(g: DeviceGen, stream=None) -> None:
-    """gr_code_table for every level whose chosen codes become records."""
-    for lv in range(g.levels - 1):
-        L.gr_code_table(g.shape, g.vocab, g.d_emb, g.emb[lv], g.w_qkv, g.tables[lv], stream)
+    """gr_code_table over every level whose chosen codes become records."""
+    L.gr_code_table(g.shape, g.levels - 1, g.vocab, g.d_emb, g.emb, g.w_qkv, g.tables, stream)
 
 
 def generate(g: DeviceGen, stream=None) -> None:

@@ -206,24 +206,26 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k,
                          size_t ws_bytes, int32_t *dev_err,
                          hipStream_t stream);
 
-/* gr_code_table -- query, key and value of every code of one level
+/* gr_code_table -- query, key and value of every code of each level
  * (Engineering Exploration of Generative Recall, 4.1: attention starts from
  * the per-token query, key and value; 4.2: each level has its own 256
  * codes).  A code chosen at one step enters the next as a token whose
  * embedding is projected by the model's query, key and value projections; as
- * that depends only on the code, the level's vocab rows are projected once:
- *   table[t][c] = sum_i emb[t][i] * w_qkv[c][i],  c < 3*D, D = H*head_dim,
- * so that table[t] = [q | k | v] of code t, each [H][head_dim].
- *   emb: [vocab][d_emb] dtype.  w_qkv: [3*D][d_emb] dtype (the D query
- *   projection rows, then the key rows, then the value rows).  table:
- *   [vocab][3][H][head_dim] dtype (fp32 accumulation, one rounding to the
- *   storage dtype, round to nearest even for bf16).  Only shape->H, head_dim
- *   and dtype are used.
- *   Host errors: NULL pointers, vocab != 256, d_emb not a positive multiple
- *   of 16 or above 16384, unsupported dtype/head_dim, unaligned pointers. */
-gr_status gr_code_table(const gr_shape *shape, int32_t vocab, int32_t d_emb,
-                        const void *emb, const void *w_qkv, void *table,
-                        hipStream_t stream);
+ * that depends only on (level, code), the vocab rows of each level are
+ * projected once:
+ *   table[l][t][c] = sum_i emb[l][t][i] * w_qkv[c][i],  c < 3*D, D = H*head_dim,
+ * so that table[l][t] = [q | k | v] of code t of level l, each [H][head_dim].
+ *   emb: [levels][vocab][d_emb] dtype.  w_qkv: [3*D][d_emb] dtype (the D
+ *   query projection rows, then the key rows, then the value rows).  table:
+ *   [levels][vocab][3][H][head_dim] dtype (fp32 accumulation, one rounding to
+ *   the storage dtype, round to nearest even for bf16).  Only shape->H,
+ *   head_dim and dtype are used.
+ *   Host errors: NULL pointers, levels <= 0 (SHAPE) or above GR_MAX_DEPTH + 1,
+ *   vocab != 256, d_emb not a positive multiple of 16 or above 16384,
+ *   unsupported dtype/head_dim, unaligned pointers. */
+gr_status gr_code_table(const gr_shape *shape, int32_t levels, int32_t vocab,
+                        int32_t d_emb, const void *emb, const void *w_qkv,
+                        void *table, hipStream_t stream);
 
 /* gr_append_codes -- gr_trie_append for beams that just chose a code (OneLA,
  * Abstract: one append-only record per surviving beam).  For every request r

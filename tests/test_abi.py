@@ -167,11 +167,13 @@ def test_workspace_sizes():
 def test_code_table_host_errors():
     sh = shape()
     call = lambda **kw: L._lib.gr_code_table(
-        ctypes.byref(kw.get("sh", sh)), kw.get("vocab", 256), kw.get("d_emb", 512), kw.get("emb", FAKE), FAKE,
-        kw.get("table", FAKE), None)
+        ctypes.byref(kw.get("sh", sh)), kw.get("levels", 3), kw.get("vocab", 256), kw.get("d_emb", 512),
+        kw.get("emb", FAKE), FAKE, kw.get("table", FAKE), None)
     assert call(emb=None) == L.GR_ERR_NULL
     assert call(table=None) == L.GR_ERR_NULL
     assert call(vocab=128) == L.GR_ERR_UNSUPPORTED
+    assert call(levels=0) == L.GR_ERR_SHAPE
+    assert call(levels=L.GR_MAX_DEPTH + 2) == L.GR_ERR_UNSUPPORTED
     assert call(d_emb=24) == L.GR_ERR_UNSUPPORTED              # not a multiple of 16
     assert call(d_emb=0) == L.GR_ERR_UNSUPPORTED
     assert call(emb=FAKE + 8) == L.GR_ERR_UNSUPPORTED          # unaligned

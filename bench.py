@@ -6,9 +6,18 @@ A step is one gr_decode_step over the whole batch of the headline workload
 256 codes per level, bf16): attention of every beam over its request's shared
 prompt plus its own ancestor chain, codebook projection, log-softmax, prior
 add and top-100 of 100 x 256 per request.  Inputs are seeded synthetic data
-(workloads module), uploaded once and resident in HBM; two independent copies
-alternate between steps so that each step reads cold data (the working set of
+(workloads module), uploaded once and resident in HBM; independent copies
+rotate between steps so that each step reads cold data (the working set of
 one copy exceeds the 256 MB last-level cache).
+
+The timed steps are independent batches.  By default they are spread over two
+HIP streams (step i on stream i % 2, each stream with its own input copies,
+outputs and workspace), as a serving process keeps two batches in flight:
+one batch's scoring, a latency-bound pass with one workgroup per request,
+overlaps the other's HBM-bound attention.  `value` is K steps over the time
+of the whole timed region; the same K steps run back to back on one stream
+give `ms_per_step_one_stream`, and a third pass with an event between the two
+stages of every step gives the stage times and the attention roofline.
 
 Printed: one JSON line with steps/s (value), beam-steps/s, algorithmic HBM
 GB/s of the step, the attention kernel's roofline (algorithmic bytes per
@@ -48,7 +57,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed steps first (the GPU takes some tens of ms to reach steady clocks)")
     ap.add_argument("--workload", default="beam100_p600")
-    ap.add_argument("--sets", type=int, default=2, help="independent input copies rotated between steps")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="independent input copies rotated between steps (default: 2 per stream)")
+    ap.add_argument("--streams", type=int, default=2,
+                    help="HIP streams carrying independent batches concurrently (1 = one after another)")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -211,7 +223,7 @@ def bench_generate(args, cfg):
     t0 = time.perf_counter()
     x = W.make_generate_inputs(cfg)
     print(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
-    sets = [HN.upload_generate(x) for _ in range(args.sets)]
+    sets = [HN.upload_generate(x) for _ in range(args.sets if args.sets > 0 else 2)]
     torch.cuda.synchronize()
     print(f"[bench] {len(sets)} input set(s) resident on the GPU", file=sys.stderr, flush=True)
     s = torch.cuda.Stream()
@@ -333,21 +345,48 @@ def main():
     x = W.make_step_inputs(cfg)
     print(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
     acc = algorithmic(x)
+    n_streams = max(1, args.streams)
+    n_sets = args.sets if args.sets > 0 else 2 * n_streams
+    assert n_sets % n_streams == 0, "every stream needs its own input sets"
     sets = [HN.upload_step(x)]
-    for _ in range(args.sets - 1):
+    for _ in range(n_sets - 1):
         sets.append(clone_step(sets[0]))
     bufs = [HN.decode_buffers(ds) for ds in sets]
     torch.cuda.synchronize()
     print(f"[bench] {len(sets)} input set(s) resident on the GPU", file=sys.stderr, flush=True)
 
-    def step(i, flags_extra=0):
+    def step(i, flags_extra=0, stream=None):
         ds, buf = sets[i % len(sets)], bufs[i % len(bufs)]
         L.gr_decode_step(ds.shape, ds.prompt_k, ds.prompt_v, ds.q, ds.n_beams, ds.trie, ds.beam_node, ds.W,
                          ds.vocab, ds.prior, ds.k, ds.flags | flags_extra, buf.score, buf.token, buf.parent,
-                         None, None, buf.ws, buf.ws_bytes, ds.dev_err)
+                         None, None, buf.ws, buf.ws_bytes, ds.dev_err, stream)
+
+    # Independent batches on several streams (a serving process keeping
+    # several batches in flight, as concurrent workers sharing one GPU do):
+    # step i runs on stream i % S with input set i % n_sets, so a stream
+    # only ever touches its own sets, outputs and workspaces.  One batch's
+    # scoring, a latency-bound pass with one workgroup per request, then
+    # overlaps another batch's HBM-bound attention.
+    main_stream = torch.cuda.current_stream()
+    streams = [main_stream] + [torch.cuda.Stream() for _ in range(n_streams - 1)]
+
+    def run_streams(k):
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(main_stream)
+        for st in streams[1:]:
+            st.wait_event(start)
+        for i in range(k):
+            step(i, stream=streams[i % n_streams])
+        for st in streams[1:]:
+            e = torch.cuda.Event()
+            e.record(st)
+            main_stream.wait_event(e)
+        stop.record(main_stream)
+        return start, stop
 
     for i in range(args.warmup):
         step(i)
+    run_streams(args.warmup)
     torch.cuda.synchronize()
 
     # timed region 1: K whole steps, one call each
@@ -359,7 +398,15 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
+    ms_step_one_stream = ms_total / args.steps
+
+    # timed region 1b: the same K steps spread over the streams
+    ms_step = ms_step_one_stream
+    if n_streams > 1:
+        torch.cuda.synchronize()
+        e0, e1 = run_streams(args.steps)
+        torch.cuda.synchronize()
+        ms_step = e0.elapsed_time(e1) / args.steps
 
     # timed region 2: the same K steps, each split into its two stages with
     # an event before, between and after them on the launch stream (same
@@ -417,13 +464,16 @@ def main():
         "data": "synthetic (seeded N(0,1) K/V/Q, N(0,0.02) codebook, cumsum(-x^2) priors)",
         "config": {"workload": cfg.name, "requests": cfg.R, "prompt_len": cfg.Lp, "window": cfg.Lw,
                    "heads": cfg.H, "head_dim": cfg.d, "beams": cfg.n_in, "beam_width": cfg.k,
-                   "chain_records": cfg.depth, "codes_per_level": cfg.vocab, "input_sets": len(sets)},
+                   "chain_records": cfg.depth, "codes_per_level": cfg.vocab, "input_sets": len(sets),
+                   "concurrent_batches": n_streams},
         "beam_steps_per_s": round(steps_per_s * cfg.R * cfg.n_in, 0),
         "achieved_GBps": round(step_gbps, 1),
         "hbm_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": acc["step_bytes"],
         "flops_per_step": acc["flops"],
         "achieved_TFLOPs": round(acc["flops"] / (ms_step * 1e-3) / 1e12, 2),
+        "streams": n_streams,
+        "ms_per_step_one_stream": round(ms_step_one_stream, 5),
         "stage_ms": {"attention": round(attn_avg_ms, 5), "scoring_selection": round(sel_avg_ms, 5)},
         "roofline": roofline,
     }

@@ -19,6 +19,8 @@ Modules:
              split prefix/suffix with a log-sum-exp merge)
   beam       codebook logits, log-softmax, prior add, exact top-k, the whole
              decode step, chained decoding, scalar scoring
+  linear     linear attention (feature map elu + 1) over the shared prompt
+             state plus each beam's records, in three formulations
   generate   whole-ID generation: the q/k/v table of each level's codes,
              every level's step with the chosen codes' records appended in
              between, and the final IDs traced back through the parents
@@ -34,11 +36,11 @@ from .attention import (attend_materialized, attend_masked, attend_split,
 from .beam import (codebook_logits, log_softmax, candidate_scores,
                    select_topk, decode_step, scalar_scores, beam_topk,
                    run_chained)
-from . import generate
+from . import generate, linear
 
 __all__ = [
     "trie_append", "chain", "TrieError", "new_arena", "attend_materialized",
     "attend_masked", "attend_split", "prefix_attn", "codebook_logits",
     "log_softmax", "candidate_scores", "select_topk", "decode_step",
-    "scalar_scores", "beam_topk", "run_chained", "generate",
+    "scalar_scores", "beam_topk", "run_chained", "generate", "linear",
 ]

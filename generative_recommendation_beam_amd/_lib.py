@@ -30,6 +30,7 @@ GR_STEP_ATTENTION, GR_STEP_SELECTION = 2, 4
 GR_MAX_DEPTH, GR_MAX_K = 8, 2048
 
 EXPORTED = ["gr_trie_append", "gr_prefix_attn", "gr_beam_topk", "gr_decode_step",
+            "gr_linear_state", "gr_linear_attn", "gr_linear_decode_step",
             "gr_code_table", "gr_append_codes", "gr_generate",
             "gr_attn_workspace_size", "gr_topk_workspace_size",
             "gr_decode_workspace_size", "gr_generate_workspace_size", "gr_status_string"]
@@ -59,8 +60,8 @@ class Trie(ctypes.Structure):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m "
-        "generative_recommendation_beam_amd.build` (there is no fallback path)")
+        f"{LIB_PATH} is missing: build it with `python "
+        "generative_recommendation_beam_amd/build.py` (there is no fallback path)")
 _lib = ctypes.CDLL(LIB_PATH)
 
 _P = ctypes.c_void_p
@@ -72,6 +73,10 @@ _sig = {
     "gr_beam_topk": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P],
     "gr_decode_step": [ctypes.POINTER(Shape), _P, _P, _P, _I, ctypes.POINTER(Trie), _P, _P, _I, _P, _I, _I,
                        _P, _P, _P, _P, _P, _P, _S, _P, _P],
+    "gr_linear_state": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P],
+    "gr_linear_attn": [ctypes.POINTER(Shape), _P, _P, _P, _I, ctypes.POINTER(Trie), _P, _P, _P, _P],
+    "gr_linear_decode_step": [ctypes.POINTER(Shape), _P, _P, _P, _I, ctypes.POINTER(Trie), _P, _P, _I, _P, _I,
+                              _I, _P, _P, _P, _P, _P, _P, _S, _P, _P],
     "gr_code_table": [ctypes.POINTER(Shape), _I, _I, _I, _P, _P, _P, _P],
     "gr_append_codes": [ctypes.POINTER(Shape), ctypes.POINTER(Trie), _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P,
                         _P],
@@ -154,6 +159,28 @@ def gr_decode_step(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, W, vo
                                int(vocab), _ptr(prior), int(beam_width), int(flags), _ptr(out_score),
                                _ptr(out_token), _ptr(out_parent), _ptr(attn_out), _ptr(cand_out), _ptr(ws),
                                int(ws_bytes), _ptr(dev_err), _stream(stream)), "gr_decode_step")
+
+
+def gr_linear_state(shape, prompt_k, prompt_v, state, norm, stream=None):
+    _check(_lib.gr_linear_state(_shape_ref(shape), _ptr(prompt_k), _ptr(prompt_v), _ptr(state), _ptr(norm),
+                                _stream(stream)), "gr_linear_state")
+
+
+def gr_linear_attn(shape, state, norm, q, n_beams, trie, beam_node, out, dev_err, stream=None):
+    _check(_lib.gr_linear_attn(_shape_ref(shape), _ptr(state), _ptr(norm), _ptr(q), int(n_beams),
+                               None if trie is None else ctypes.byref(trie), _ptr(beam_node), _ptr(out),
+                               _ptr(dev_err), _stream(stream)), "gr_linear_attn")
+
+
+def gr_linear_decode_step(shape, state, norm, q, n_beams, trie, beam_node, W, vocab, prior, beam_width, flags,
+                          out_score, out_token, out_parent, attn_out, cand_out, ws, ws_bytes, dev_err,
+                          stream=None):
+    _check(_lib.gr_linear_decode_step(_shape_ref(shape), _ptr(state), _ptr(norm), _ptr(q), int(n_beams),
+                                      None if trie is None else ctypes.byref(trie), _ptr(beam_node), _ptr(W),
+                                      int(vocab), _ptr(prior), int(beam_width), int(flags), _ptr(out_score),
+                                      _ptr(out_token), _ptr(out_parent), _ptr(attn_out), _ptr(cand_out),
+                                      _ptr(ws), int(ws_bytes), _ptr(dev_err), _stream(stream)),
+           "gr_linear_decode_step")
 
 
 def gr_code_table(shape, levels, vocab, d_emb, emb, w_qkv, table, stream=None):

@@ -1,6 +1,8 @@
 """Build libgrbeam.so (gfx950) in-tree with hipcc.
 
-    python -m generative_recommendation_beam_amd.build
+    python generative_recommendation_beam_amd/build.py
+
+(run as a file: importing the package would load the library first)
 
 Every HIP source is compiled for gfx950 only; packed-fp32 instructions are
 disabled for device code.  Objects go to _build/ at the repo root, the shared
@@ -20,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgrbeam.so")
-SOURCES = ["api.cpp", "attn.hip", "score.hip", "trie.hip", "generate.hip"]
+SOURCES = ["api.cpp", "attn.hip", "score.hip", "trie.hip", "generate.hip", "linear.hip"]
 
 
 def hipcc() -> str:
@@ -50,7 +52,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs

@@ -195,6 +195,91 @@ inline gr_status hip_status(hipError_t e) {
 // runtime call left behind so that a launch is judged on its own status.
 inline void clear_stale_error() { (void)hipGetLastError(); }
 
+// The scoring half of a decode step (codebook logits of the current level,
+// log-softmax, prior add, exact top-k) on the attention output the attention
+// half left behind: bf16 head-major in the workspace for the MFMA codebook
+// path, else fp32 at o_f32 (logits then go through the workspace).
+gr_status enqueue_scoring(const gr_shape *shape, int n_beams, const void *W, int vocab, const float *prior,
+                          int beam_width, int lsm, float *cand_out, const gr::SelectOut &so,
+                          const DecodeLayout &L, char *base, const float *o_f32, hipStream_t stream) {
+  const int R = shape->R;
+  const int D = shape->H * shape->head_dim;
+  void *o_buf = base + L.o_off;
+  float *z_buf = (float *)(base + L.z_off);
+  if (use_mfma_logits(shape, vocab)) {
+    gr::LogitsArgs l;
+    l.o = (const uint16_t *)o_buf;
+    l.W = (const uint16_t *)W;
+    l.prior = prior;
+    l.cand_out = cand_out;
+    l.R = R;
+    l.n_in = n_beams;
+    l.D = D;
+    l.hd = shape->head_dim;
+    l.k = beam_width;
+    l.log_softmax = lsm;
+    return hip_status(gr::launch_logits_select_bf16(l, so, stream));
+  }
+  gr::ProjArgs pj;
+  pj.dtype = shape->dtype;
+  pj.o = o_f32;
+  pj.W = W;
+  pj.prior = prior;
+  pj.z = z_buf;
+  pj.R = R;
+  pj.n = n_beams;
+  pj.D = D;
+  pj.vocab = vocab;
+  pj.add_prior = vocab == 1 ? 1 : 0;
+  hipError_t e = gr::launch_project(pj, stream);
+  if (e != hipSuccess) return hip_status(e);
+  gr::ScoreSelectArgs sa;
+  sa.logits = z_buf;
+  sa.prior = vocab == 1 ? nullptr : prior;   // the scalar path added it already
+  sa.cand_out = cand_out;
+  sa.R = R;
+  sa.n_in = n_beams;
+  sa.vocab = vocab;
+  sa.k = beam_width;
+  sa.log_softmax = lsm;
+  return hip_status(gr::launch_score_select(sa, so, stream));
+}
+
+gr_status linear_common(const gr_shape *shape, const float *state, const float *norm, const void *q,
+                        int32_t n_beams, const gr_trie *trie, const int32_t *beam_node, int32_t *dev_err) {
+  gr_status st = check_shape(shape);
+  if (st) return st;
+  if (!state || !norm || !q || !dev_err) return GR_ERR_NULL;
+  if (n_beams <= 0) return GR_ERR_SHAPE;
+  if ((long long)shape->R * n_beams * shape->H > (1ll << 30)) return GR_ERR_SHAPE;
+  if (!aligned16(state) || !aligned16(q)) return GR_ERR_UNSUPPORTED;
+  return check_trie(shape, trie, beam_node != nullptr);
+}
+
+gr::LinearAttnArgs linear_args(const gr_shape *shape, const float *state, const float *norm, const void *q,
+                               int32_t n_beams, const gr_trie *trie, const int32_t *beam_node, int32_t *dev_err) {
+  gr::LinearAttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.dtype = shape->dtype;
+  a.S = state;
+  a.z = norm;
+  a.q = q;
+  if (beam_node) {
+    a.ak = trie->k;
+    a.av = trie->v;
+    a.parent = trie->parent;
+    a.cap = trie->capacity;
+    a.max_depth = trie->max_depth;
+  }
+  a.beam_node = beam_node;
+  a.dev_err = dev_err;
+  a.R = shape->R;
+  a.H = shape->H;
+  a.hd = shape->head_dim;
+  a.nb = n_beams;
+  return a;
+}
+
 // Beams in and out of every step of a generation: n_0 = 1,
 // k_l = min(beam_width, n_l * vocab), n_{l+1} = k_l.
 struct GenLevels {
@@ -374,12 +459,9 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void
   if (!ws || ws_bytes < L.total) return GR_ERR_WORKSPACE;
   char *base = align_ptr(ws);
   void *o_buf = base + L.o_off;
-  float *z_buf = (float *)(base + L.z_off);
   void *part = L.part_bytes ? base + L.part_off : nullptr;
-  const int R = shape->R;
-  const int D = shape->H * shape->head_dim;
   const int lsm = (flags & GR_TOPK_LOG_SOFTMAX) ? 1 : 0;
-  const gr::SelectOut so = make_out(out_score, out_token, out_parent, part, R, n_beams, vocab, beam_width,
+  const gr::SelectOut so = make_out(out_score, out_token, out_parent, part, shape->R, n_beams, vocab, beam_width,
                                     use_mfma_logits(shape, vocab));
 
   gr::AttnArgs a = attn_args(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, dev_err);
@@ -400,44 +482,87 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void
     if (e != hipSuccess) return hip_status(e);
   }
   if (!run_select) return GR_OK;
+  return enqueue_scoring(shape, n_beams, W, vocab, prior, beam_width, lsm, cand_out, so, L, base,
+                         o_f32, stream);
+}
 
+gr_status gr_linear_state(const gr_shape *shape, const void *prompt_k, const void *prompt_v, float *state,
+                          float *norm, hipStream_t stream) {
+  gr_status st = check_shape(shape);
+  if (st) return st;
+  if (!prompt_k || !prompt_v || !state || !norm) return GR_ERR_NULL;
+  if (!aligned16(prompt_k) || !aligned16(prompt_v) || !aligned16(state)) return GR_ERR_UNSUPPORTED;
+  gr::LinearStateArgs a;
+  a.dtype = shape->dtype;
+  a.pk = prompt_k;
+  a.pv = prompt_v;
+  a.S = state;
+  a.z = norm;
+  a.R = shape->R;
+  a.H = shape->H;
+  a.hd = shape->head_dim;
+  a.Lp = shape->prompt_len;
+  a.Lw = prompt_window(shape);
+  clear_stale_error();
+  return hip_status(gr::launch_linear_state(a, stream));
+}
+
+gr_status gr_linear_attn(const gr_shape *shape, const float *state, const float *norm, const void *q,
+                         int32_t n_beams, const gr_trie *trie, const int32_t *beam_node, float *out,
+                         int32_t *dev_err, hipStream_t stream) {
+  gr_status st = linear_common(shape, state, norm, q, n_beams, trie, beam_node, dev_err);
+  if (st) return st;
+  if (!out) return GR_ERR_NULL;
+  if (!aligned16(out)) return GR_ERR_UNSUPPORTED;
+  gr::LinearAttnArgs a = linear_args(shape, state, norm, q, n_beams, trie, beam_node, dev_err);
+  a.out_f32 = out;
+  clear_stale_error();
+  return hip_status(gr::launch_linear_attn(a, stream));
+}
+
+gr_status gr_linear_decode_step(const gr_shape *shape, const float *state, const float *norm, const void *q,
+                                int32_t n_beams, const gr_trie *trie, const int32_t *beam_node, const void *W,
+                                int32_t vocab, const float *prior, int32_t beam_width, int32_t flags,
+                                float *out_score, int32_t *out_token, int32_t *out_parent, float *attn_out,
+                                float *cand_out, void *ws, size_t ws_bytes, int32_t *dev_err,
+                                hipStream_t stream) {
+  gr_status st = linear_common(shape, state, norm, q, n_beams, trie, beam_node, dev_err);
+  if (st) return st;
+  const int32_t stage = flags & (GR_STEP_ATTENTION | GR_STEP_SELECTION);
+  const bool run_attn = stage != GR_STEP_SELECTION;
+  const bool run_select = stage != GR_STEP_ATTENTION;
+  flags &= ~(GR_STEP_ATTENTION | GR_STEP_SELECTION);
+  st = check_select(shape->R, n_beams, vocab, beam_width, flags);
+  if (st) return st;
+  if (!W || !out_score || !out_token || !out_parent) return GR_ERR_NULL;
+  if (!aligned16(W) || (attn_out && !aligned16(attn_out)) || (cand_out && !aligned16(cand_out)))
+    return GR_ERR_UNSUPPORTED;
+  const DecodeLayout L = decode_layout(shape, n_beams, vocab, beam_width);
+  if (!ws || ws_bytes < L.total) return GR_ERR_WORKSPACE;
+  char *base = align_ptr(ws);
+  void *o_buf = base + L.o_off;
+  void *part = L.part_bytes ? base + L.part_off : nullptr;
+  const int lsm = (flags & GR_TOPK_LOG_SOFTMAX) ? 1 : 0;
+  const bool mfma_logits = use_mfma_logits(shape, vocab);
+  const gr::SelectOut so = make_out(out_score, out_token, out_parent, part, shape->R, n_beams, vocab, beam_width,
+                                    mfma_logits);
+  gr::LinearAttnArgs a = linear_args(shape, state, norm, q, n_beams, trie, beam_node, dev_err);
+  const float *o_f32 = nullptr;
   if (mfma_logits) {
-    gr::LogitsArgs l;
-    l.o = (const uint16_t *)o_buf;
-    l.W = (const uint16_t *)W;
-    l.prior = prior;
-    l.cand_out = cand_out;
-    l.R = R;
-    l.n_in = n_beams;
-    l.D = D;
-    l.hd = shape->head_dim;
-    l.k = beam_width;
-    l.log_softmax = lsm;
-    return hip_status(gr::launch_logits_select_bf16(l, so, stream));
+    a.out_lowp = o_buf;
+    a.out_f32 = attn_out;
+  } else {
+    a.out_f32 = attn_out ? attn_out : (float *)o_buf;
+    o_f32 = a.out_f32;
   }
-  gr::ProjArgs pj;
-  pj.dtype = shape->dtype;
-  pj.o = o_f32;
-  pj.W = W;
-  pj.prior = prior;
-  pj.z = z_buf;
-  pj.R = R;
-  pj.n = n_beams;
-  pj.D = D;
-  pj.vocab = vocab;
-  pj.add_prior = vocab == 1 ? 1 : 0;
-  e = gr::launch_project(pj, stream);
-  if (e != hipSuccess) return hip_status(e);
-  gr::ScoreSelectArgs sa;
-  sa.logits = z_buf;
-  sa.prior = vocab == 1 ? nullptr : prior;   // the scalar path added it already
-  sa.cand_out = cand_out;
-  sa.R = R;
-  sa.n_in = n_beams;
-  sa.vocab = vocab;
-  sa.k = beam_width;
-  sa.log_softmax = lsm;
-  return hip_status(gr::launch_score_select(sa, so, stream));
+  clear_stale_error();
+  if (run_attn) {
+    const hipError_t e = gr::launch_linear_attn(a, stream);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (!run_select) return GR_OK;
+  return enqueue_scoring(shape, n_beams, W, vocab, prior, beam_width, lsm, cand_out, so, L, base, o_f32,
+                         stream);
 }
 
 gr_status gr_code_table(const gr_shape *shape, int32_t levels, int32_t vocab, int32_t d_emb, const void *emb,

@@ -51,6 +51,27 @@ struct AppendArgs {
 };
 hipError_t launch_trie_append(const AppendArgs &a, hipStream_t s);
 
+// Linear-attention decoding (linear.hip).
+struct LinearStateArgs {
+  int dtype;
+  const void *pk, *pv;
+  float *S, *z;                // [R][H][hd][hd], [R][H][hd]
+  int R, H, hd, Lp, Lw;
+};
+hipError_t launch_linear_state(const LinearStateArgs &a, hipStream_t s);
+
+struct LinearAttnArgs {
+  int dtype;
+  const float *S, *z;
+  const void *q, *ak, *av;
+  const int32_t *parent, *beam_node;
+  int32_t *dev_err;
+  float *out_f32;              // [R][nb][H*hd] or NULL
+  void *out_lowp;              // bf16 head-major [R][H][nb][hd] or NULL
+  int R, H, hd, nb, cap, max_depth;
+};
+hipError_t launch_linear_attn(const LinearAttnArgs &a, hipStream_t s);
+
 // Whole-ID generation (generate.hip).  Levels of one generation call.
 constexpr int kMaxLevels = GR_MAX_DEPTH + 1;
 

@@ -1,0 +1,318 @@
+// Linear-attention decoding over one shared prompt state (OneLA, Abstract).
+//
+// With recurrent linear attention a beam's state is the sum of phi(k) v^T over
+// its history.  Every beam of a request shares the prompt, so its state is
+// one shared prompt-derived state plus the terms of its own append-only
+// records, found through the ancestry index; a step computes only what it
+// needs from them and never builds a per-beam state:
+//   S_p = sum_{prompt window} phi(k) v^T,   z_p = sum_{prompt window} phi(k)
+//   o_b = (phi(q)^T S_p + sum_{n in chain(b)} (phi(q).phi(k_n)) v_n)
+//       / (phi(q).z_p  + sum_{n in chain(b)}  phi(q).phi(k_n))
+// with phi(x) = elu(x) + 1 (positive, so the normaliser never vanishes).
+//
+// linear_state_bf16_kernel computes S_p, z_p once per (request, head):
+// Phi(K)^T V over the window is a dense contraction and runs on MFMA.
+// linear_attn_kernel reads S_p once per (request, head, 128 beams) into LDS
+// and gives each thread one beam: phi(q)^T S_p, then its chain records, in
+// fp32.  The scoring and selection after it are those of the softmax step.
+
+#include "gr_device.h"
+#include "gr_launch.h"
+
+namespace gr {
+namespace {
+
+__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+struct StateP {
+  const void *pk, *pv;
+  float *S, *z;
+  int R, H, Lp, Lw;
+};
+
+// One workgroup of 4 waves per (request, head), 64-key tiles through a
+// double-buffered LDS stage.  Wave w owns the 32 x 32 output tile
+// (d_k half w >> 1, d_v half w & 1) of S (for head dim 32 only wave 0 has a
+// tile).  A operand: phi(K)^T (row = d_k, k = key), split into two bf16
+// terms hi + lo (hi = phi rounded to bf16, lo = the rest rounded again) that
+// go through two MFMAs, so phi keeps about 16 mantissa bits instead of 8;
+// B operand: V (k = key, column = d_v), exact in bf16.  Lane (g, c) of an
+// MFMA k-step holds keys 8g .. 8g+7 of column c for both, read as single
+// bf16 elements.  z sums phi in fp32.
+// Window rows past the prompt end are zero in the tile and excluded from
+// phi (phi(0) = 1 would count them).
+template <int HD>
+__global__ __launch_bounds__(256) void linear_state_bf16_kernel(StateP p) {
+  constexpr int KT = 64, CH = HD / 8;                 // 16-byte chunks per row
+  constexpr int PER = KT * CH / 256;                  // chunks per thread per tile (K or V)
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * HD], Vs[2][KT * HD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, c = lane & 31;
+  const int h = blockIdx.x % p.H, r = blockIdx.x / p.H;
+  const size_t row = (size_t)p.H * HD;
+  const uint16_t *pk = (const uint16_t *)p.pk + (size_t)r * p.Lp * row + (size_t)h * HD;
+  const uint16_t *pv = (const uint16_t *)p.pv + (size_t)r * p.Lp * row + (size_t)h * HD;
+  const int k_begin = p.Lp - p.Lw;
+  const int n_tiles = (p.Lw + KT - 1) / KT;
+  constexpr int NT = (HD / 32) * (HD / 32);           // output tiles
+  const bool owner = wave < NT;
+  const int dk0 = (wave >> 1) * 32, dv0 = (wave & 1) * 32;
+
+  uint4 kr[PER], vr[PER];
+  auto load = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + 256 * i, kk = e / CH, ch = e % CH;
+      const int key = k_begin + t * KT + kk;
+      const bool in = key < p.Lp;
+      const uint4 zero = make_uint4(0, 0, 0, 0);
+      kr[i] = in ? *(const uint4 *)(pk + (size_t)key * row + ch * 8) : zero;
+      vr[i] = in ? *(const uint4 *)(pv + (size_t)key * row + ch * 8) : zero;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + 256 * i;
+      *(uint4 *)&Ks[buf][e * 8] = kr[i];
+      *(uint4 *)&Vs[buf][e * 8] = vr[i];
+    }
+  };
+
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  float zpart = 0.f;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) load(t + 1);
+    if (owner) {
+      const int valid = min(KT, p.Lp - (k_begin + t * KT));   // keys of this tile inside the prompt
+#pragma unroll
+      for (int ks = 0; ks < KT / 16; ++ks) {
+        bf16x8 a_hi, a_lo, b;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int kk = ks * 16 + 8 * g + u;
+          const float kv = bf16_to_f32(Ks[buf][kk * HD + dk0 + c]);
+          const float f = kk < valid ? phi(kv) : 0.f;
+          const __bf16 hi = (__bf16)f;
+          a_hi[u] = hi;
+          a_lo[u] = (__bf16)(f - (float)hi);
+          zpart += f;
+          b[u] = __builtin_bit_cast(__bf16, Vs[buf][kk * HD + dv0 + c]);
+        }
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi, b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_lo, b, acc, 0, 0, 0);
+      }
+    }
+    __syncthreads();                       // everyone is done with the other buffer
+    if (t + 1 < n_tiles) {
+      store(buf ^ 1);
+      __syncthreads();
+    }
+  }
+  if (!owner) return;
+  float *S = p.S + ((size_t)r * p.H + h) * HD * HD;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int m = 8 * (i >> 2) + 4 * g + (i & 3);
+    S[(size_t)(dk0 + m) * HD + dv0 + c] = acc[i];
+  }
+  // z: the two lane halves hold disjoint key sets of the same column
+  const float zsum = zpart + __shfl_xor(zpart, 32);
+  if ((wave & 1) == 0 && g == 0) p.z[((size_t)r * p.H + h) * HD + dk0 + c] = zsum;
+}
+
+// fp32 storage: one workgroup per (request, head); thread t owns entries
+// t, t + 256, ... of the HD x HD state; 32-key tiles with phi(k) staged in LDS.
+template <int HD>
+__global__ __launch_bounds__(256) void linear_state_f32_kernel(StateP p) {
+  constexpr int KT = 32, PER = HD * HD / 256;
+  __shared__ float Fk[KT][HD], Vs[KT][HD];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.x % p.H, r = blockIdx.x / p.H;
+  const size_t row = (size_t)p.H * HD;
+  const float *pk = (const float *)p.pk + (size_t)r * p.Lp * row + (size_t)h * HD;
+  const float *pv = (const float *)p.pv + (size_t)r * p.Lp * row + (size_t)h * HD;
+  float s[PER], zs = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) s[i] = 0.f;
+  for (int k0 = p.Lp - p.Lw; k0 < p.Lp; k0 += KT) {
+    const int nk = min(KT, p.Lp - k0);
+    __syncthreads();
+    for (int e = tid; e < KT * HD; e += 256) {
+      const int kk = e / HD, i = e % HD;
+      Fk[kk][i] = kk < nk ? phi(pk[(size_t)(k0 + kk) * row + i]) : 0.f;
+      Vs[kk][i] = kk < nk ? pv[(size_t)(k0 + kk) * row + i] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + 256 * i, a = e / HD, cc = e % HD;
+      for (int kk = 0; kk < KT; ++kk) s[i] = fmaf(Fk[kk][a], Vs[kk][cc], s[i]);
+    }
+    if (tid < HD)
+      for (int kk = 0; kk < KT; ++kk) zs += Fk[kk][tid];
+  }
+  float *S = p.S + ((size_t)r * p.H + h) * HD * HD;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) S[tid + 256 * i] = s[i];
+  if (tid < HD) p.z[((size_t)r * p.H + h) * HD + tid] = zs;
+}
+
+struct LinP {
+  const float *S, *z;
+  const void *q, *ak, *av;
+  const int32_t *parent, *beam_node;
+  int32_t *dev_err;
+  float *out_f32;
+  uint16_t *out_bf16;          // head-major [R][H][nb][HD]
+  int R, H, nb, cap, max_depth, n_chunk;
+};
+
+template <typename T>
+__device__ __forceinline__ void load8(const T *src, float *dst);
+template <>
+__device__ __forceinline__ void load8<float>(const float *src, float *dst) {
+  const float4 a = *(const float4 *)src, b = *(const float4 *)(src + 4);
+  dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
+  dst[4] = b.x; dst[5] = b.y; dst[6] = b.z; dst[7] = b.w;
+}
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t *src, float *dst) {
+  const uint4 a = *(const uint4 *)src;
+  dst[0] = bf16_lo(a.x); dst[1] = bf16_hi(a.x); dst[2] = bf16_lo(a.y); dst[3] = bf16_hi(a.y);
+  dst[4] = bf16_lo(a.z); dst[5] = bf16_hi(a.z); dst[6] = bf16_lo(a.w); dst[7] = bf16_hi(a.w);
+}
+
+// One workgroup of 128 threads per (request, head, 128 beams); S_p and z_p of
+// the (request, head) in LDS, read as broadcasts.  Thread = beam.
+template <typename T, int HD>
+__global__ __launch_bounds__(128) void linear_attn_kernel(LinP p) {
+  __shared__ __attribute__((aligned(16))) float Ss[HD * HD];
+  __shared__ float zs[HD];
+  int bid = blockIdx.x;
+  const int chunk = bid % p.n_chunk;
+  bid /= p.n_chunk;
+  const int h = bid % p.H, r = bid / p.H;
+  const float *Sg = p.S + ((size_t)r * p.H + h) * HD * HD;
+  for (int e = threadIdx.x * 4; e < HD * HD; e += 128 * 4) *(float4 *)&Ss[e] = *(const float4 *)&Sg[e];
+  if (threadIdx.x < HD) zs[threadIdx.x] = p.z[((size_t)r * p.H + h) * HD + threadIdx.x];
+  __syncthreads();
+  const int beam = chunk * 128 + threadIdx.x;
+  if (beam >= p.nb) return;
+  const size_t row = (size_t)p.H * HD;
+  const T *qp = (const T *)p.q + ((size_t)r * p.nb + beam) * row + (size_t)h * HD;
+  float fq[HD], num[HD], den = 0.f;
+#pragma unroll
+  for (int i = 0; i < HD; i += 8) load8<T>(qp + i, fq + i);
+#pragma unroll
+  for (int i = 0; i < HD; ++i) {
+    fq[i] = phi(fq[i]);
+    num[i] = 0.f;
+  }
+  // phi(q)^T S_p and phi(q) . z_p
+#pragma unroll 4
+  for (int a = 0; a < HD; ++a) {
+    const float f = fq[a];
+    den = fmaf(f, zs[a], den);
+#pragma unroll
+    for (int i = 0; i < HD; i += 4) {
+      const float4 s4 = *(const float4 *)&Ss[a * HD + i];
+      num[i] = fmaf(f, s4.x, num[i]);
+      num[i + 1] = fmaf(f, s4.y, num[i + 1]);
+      num[i + 2] = fmaf(f, s4.z, num[i + 2]);
+      num[i + 3] = fmaf(f, s4.w, num[i + 3]);
+    }
+  }
+  // the beam's own records, from its node up to the root
+  if (p.beam_node != nullptr) {
+    int n = p.beam_node[(size_t)r * p.nb + beam];
+    int err = 0;
+    const int32_t *par = p.parent + (size_t)r * p.cap;
+    for (int depth = 0; n != -1; ++depth) {
+      if (n < 0 || n >= p.cap) { err |= GR_DEVERR_PARENT_RANGE; break; }
+      if (depth >= p.max_depth) { err |= GR_DEVERR_DEPTH; break; }
+      const int pn = par[n];
+      const T *kn = (const T *)p.ak + ((size_t)r * p.cap + n) * row + (size_t)h * HD;
+      const T *vn = (const T *)p.av + ((size_t)r * p.cap + n) * row + (size_t)h * HD;
+      float w = 0.f;
+#pragma unroll
+      for (int i = 0; i < HD; i += 8) {
+        float kk[8];
+        load8<T>(kn + i, kk);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) w = fmaf(fq[i + u], phi(kk[u]), w);
+      }
+      den += w;
+#pragma unroll
+      for (int i = 0; i < HD; i += 8) {
+        float vv[8];
+        load8<T>(vn + i, vv);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) num[i + u] = fmaf(w, vv[u], num[i + u]);
+      }
+      if (pn < -1 || pn >= p.cap) { err |= GR_DEVERR_PARENT_RANGE; break; }
+      if (pn >= n) { err |= GR_DEVERR_PARENT_ORDER; break; }
+      n = pn;
+    }
+    if (err) atomicOr(p.dev_err, err);
+  }
+  const float inv = 1.f / den;
+  if (p.out_f32) {
+    float *op = p.out_f32 + ((size_t)r * p.nb + beam) * row + (size_t)h * HD;
+#pragma unroll
+    for (int i = 0; i < HD; i += 4) *(float4 *)(op + i) = make_float4(num[i] * inv, num[i + 1] * inv,
+                                                                       num[i + 2] * inv, num[i + 3] * inv);
+  }
+  if (p.out_bf16) {
+    uint16_t *op = p.out_bf16 + (((size_t)r * p.H + h) * p.nb + beam) * HD;
+#pragma unroll
+    for (int i = 0; i < HD; i += 8)
+      *(uint4 *)(op + i) = make_uint4(pack_bf16x2(num[i] * inv, num[i + 1] * inv),
+                                      pack_bf16x2(num[i + 2] * inv, num[i + 3] * inv),
+                                      pack_bf16x2(num[i + 4] * inv, num[i + 5] * inv),
+                                      pack_bf16x2(num[i + 6] * inv, num[i + 7] * inv));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_linear_state(const LinearStateArgs &a, hipStream_t s) {
+  StateP p;
+  p.pk = a.pk; p.pv = a.pv; p.S = a.S; p.z = a.z;
+  p.R = a.R; p.H = a.H; p.Lp = a.Lp; p.Lw = a.Lw;
+  const dim3 grid((unsigned)(a.R * a.H)), block(256);
+  if (a.dtype == GR_BF16) {
+    if (a.hd == 64) hipLaunchKernelGGL(linear_state_bf16_kernel<64>, grid, block, 0, s, p);
+    else hipLaunchKernelGGL(linear_state_bf16_kernel<32>, grid, block, 0, s, p);
+  } else {
+    if (a.hd == 64) hipLaunchKernelGGL(linear_state_f32_kernel<64>, grid, block, 0, s, p);
+    else hipLaunchKernelGGL(linear_state_f32_kernel<32>, grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_attn(const LinearAttnArgs &a, hipStream_t s) {
+  LinP p;
+  p.S = a.S; p.z = a.z; p.q = a.q; p.ak = a.ak; p.av = a.av;
+  p.parent = a.parent; p.beam_node = a.beam_node; p.dev_err = a.dev_err;
+  p.out_f32 = a.out_f32; p.out_bf16 = (uint16_t *)a.out_lowp;
+  p.R = a.R; p.H = a.H; p.nb = a.nb; p.cap = a.cap; p.max_depth = a.max_depth;
+  p.n_chunk = (a.nb + 127) / 128;
+  const dim3 grid((unsigned)((long long)a.R * a.H * p.n_chunk)), block(128);
+  if (a.dtype == GR_BF16) {
+    if (a.hd == 64) hipLaunchKernelGGL((linear_attn_kernel<uint16_t, 64>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((linear_attn_kernel<uint16_t, 32>), grid, block, 0, s, p);
+  } else {
+    if (a.hd == 64) hipLaunchKernelGGL((linear_attn_kernel<float, 64>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((linear_attn_kernel<float, 32>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gr

@@ -162,6 +162,21 @@ def decode_step(ds: DeviceStep, buf: DecodeBuffers, stream=None) -> None:
                      buf.cand, buf.ws, buf.ws_bytes, ds.dev_err, stream)
 
 
+def linear_state(ds: DeviceStep, stream=None):
+    """gr_linear_state of an uploaded step's prompt: (state, norm)."""
+    R, H, hd = ds.shape.R, ds.shape.H, ds.shape.head_dim
+    S = torch.empty((R, H, hd, hd), dtype=torch.float32, device=ds.q.device)
+    z = torch.empty((R, H, hd), dtype=torch.float32, device=ds.q.device)
+    L.gr_linear_state(ds.shape, ds.prompt_k, ds.prompt_v, S, z, stream)
+    return S, z
+
+
+def linear_decode_step(ds: DeviceStep, buf: DecodeBuffers, state, norm, stream=None) -> None:
+    L.gr_linear_decode_step(ds.shape, state, norm, ds.q, ds.n_beams, ds.trie, ds.beam_node, ds.W, ds.vocab,
+                            ds.prior, ds.k, ds.flags, buf.score, buf.token, buf.parent, buf.attn, buf.cand,
+                            buf.ws, buf.ws_bytes, ds.dev_err, stream)
+
+
 def beam_topk(logits: torch.Tensor, prior: Optional[torch.Tensor], k: int, flags: int, cand: bool = True):
     R, n_in, vocab = logits.shape
     dev = logits.device

@@ -206,6 +206,57 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k,
                          size_t ws_bytes, int32_t *dev_err,
                          hipStream_t stream);
 
+/* gr_linear_state -- the shared prompt-derived state of linear-attention
+ * decoding (OneLA, Abstract: one state derived from the shared prompt serves
+ * every beam).  For every request r and head h, over the prompt window rows
+ * j in [prompt_len - Lw, prompt_len):
+ *   state[r][h][a][c] = sum_j phi(k_j[h][a]) * v_j[h][c]
+ *   norm[r][h][a]     = sum_j phi(k_j[h][a])
+ * with the feature map phi(x) = elu(x) + 1 (x + 1 for x > 0, e^x otherwise).
+ *   prompt_k, prompt_v: [R][prompt_len][H][head_dim] dtype.  state:
+ *   [R][H][head_dim][head_dim] fp32, norm: [R][H][head_dim] fp32.  bf16:
+ *   the contraction runs on bf16 MFMA with fp32 accumulation, phi(k) split
+ *   into two bf16 terms (about 16 mantissa bits); norm sums phi(k) in fp32;
+ *   fp32: all fp32.
+ *   Host errors: NULL pointers, sizes <= 0, unsupported dtype/head_dim,
+ *   unaligned pointers. */
+gr_status gr_linear_state(const gr_shape *shape, const void *prompt_k,
+                          const void *prompt_v, float *state, float *norm,
+                          hipStream_t stream);
+
+/* gr_linear_attn -- linear attention of every beam over the shared prompt
+ * state plus its own chain of records (OneLA, Abstract: each beam is the
+ * shared state plus compact append-only records of its own transitions; only
+ * the state information a step needs is computed, no per-beam state):
+ *   num = phi(q)^T state[r][h] + sum_{n in chain} (phi(q).phi(k_n)) v_n
+ *   den = phi(q) . norm[r][h]  + sum_{n in chain}  phi(q).phi(k_n)
+ *   out[r][b][h*head_dim + i] = num[i] / den          (fp32 arithmetic)
+ *   state, norm: gr_linear_state's outputs.  q, trie, beam_node, out and
+ *   the device errors: as gr_prefix_attn (shape->scale is not used).
+ *   Host errors: NULL pointers, sizes <= 0, unsupported dtype/head_dim,
+ *   unaligned pointers, max_depth outside [1, GR_MAX_DEPTH]. */
+gr_status gr_linear_attn(const gr_shape *shape, const float *state,
+                         const float *norm, const void *q, int32_t n_beams,
+                         const gr_trie *trie, const int32_t *beam_node,
+                         float *out, int32_t *dev_err, hipStream_t stream);
+
+/* gr_linear_decode_step -- gr_decode_step with gr_linear_attn in place of
+ * the softmax attention: the same codebook projection, log-softmax, prior
+ * add and exact top-k on the linear-attention output, the same arguments
+ * (state and norm replace the prompt K/V), flags, outputs and errors.
+ *   ws: at least gr_decode_workspace_size(shape, n_beams, vocab, beam_width)
+ *   bytes. */
+gr_status gr_linear_decode_step(const gr_shape *shape, const float *state,
+                                const float *norm, const void *q,
+                                int32_t n_beams, const gr_trie *trie,
+                                const int32_t *beam_node, const void *W,
+                                int32_t vocab, const float *prior,
+                                int32_t beam_width, int32_t flags,
+                                float *out_score, int32_t *out_token,
+                                int32_t *out_parent, float *attn_out,
+                                float *cand_out, void *ws, size_t ws_bytes,
+                                int32_t *dev_err, hipStream_t stream);
+
 /* gr_code_table -- query, key and value of every code of each level
  * (Engineering Exploration of Generative Recall, 4.1: attention starts from
  * the per-token query, key and value; 4.2: each level has its own 256

@@ -141,13 +141,17 @@ def attend_linear_shared(prompt_k, prompt_v, q, parent=None, arena_k=None, arena
 
 
 def linear_decode_step(prompt_k, prompt_v, q, parent, arena_k, arena_v, beam_node, W, prior, k,
-                       window=0, max_depth=8):
+                       use_log_softmax=True, window=0, max_depth=8):
     """A decode step with linear attention: attend_linear_shared, then the
-    same codebook logits, log-softmax, prior add and exact top-k as the
-    softmax step.  Returns dict(score, token, parent, attn, cand)."""
-    from .beam import codebook_logits, candidate_scores, _select_all
+    same scoring as the softmax step (codebook logits, log-softmax, prior add,
+    exact top-k; with vocab == 1 and no log-softmax, scalar scores o . w).
+    Returns dict(score, token, parent, attn, cand)."""
+    from .beam import codebook_logits, candidate_scores, scalar_scores, _select_all
     o = attend_linear_shared(prompt_k, prompt_v, q, parent, arena_k, arena_v, beam_node, window,
                              max_depth)
-    c = candidate_scores(codebook_logits(o, W), prior, True)
+    if W.shape[0] == 1 and not use_log_softmax:
+        c = scalar_scores(o, W[0], prior)[..., None]
+    else:
+        c = candidate_scores(codebook_logits(o, W), prior, use_log_softmax)
     score, token, par = _select_all(c, k)
     return dict(score=score, token=token, parent=par, attn=o, cand=c)

@@ -235,3 +235,31 @@ def test_generate_workspace_size():
     assert L.gr_generate_workspace_size(sh, 0, 256, 100) == 0
     assert L.gr_generate_workspace_size(sh, 4, 1, 100) == 0
     assert L.gr_generate_workspace_size(sh, 4, 256, L.GR_MAX_K + 1) == 0
+
+
+def test_linear_host_errors():
+    sh, tr = shape(), trie()
+    st = lambda **kw: L._lib.gr_linear_state(ctypes.byref(kw.get("sh", sh)), kw.get("pk", FAKE), FAKE,
+                                             kw.get("S", FAKE), kw.get("z", FAKE), None)
+    assert st(pk=None) == L.GR_ERR_NULL
+    assert st(z=None) == L.GR_ERR_NULL
+    assert st(S=FAKE + 4) == L.GR_ERR_UNSUPPORTED
+    assert st(sh=shape(head_dim=16)) == L.GR_ERR_UNSUPPORTED
+    at = lambda **kw: L._lib.gr_linear_attn(
+        ctypes.byref(kw.get("sh", sh)), kw.get("S", FAKE), kw.get("z", FAKE), FAKE, kw.get("n", 100),
+        ctypes.byref(kw.get("tr", tr)), kw.get("bn", FAKE), kw.get("out", FAKE), kw.get("dev_err", FAKE), None)
+    assert at(S=None) == L.GR_ERR_NULL
+    assert at(out=None) == L.GR_ERR_NULL
+    assert at(dev_err=None) == L.GR_ERR_NULL
+    assert at(n=0) == L.GR_ERR_SHAPE
+    assert at(tr=trie(max_depth=9)) == L.GR_ERR_UNSUPPORTED
+    assert at(tr=trie(k=None)) == L.GR_ERR_NULL
+    need = L.gr_decode_workspace_size(sh, 100, 256, 100)
+    ds = lambda **kw: L._lib.gr_linear_decode_step(
+        ctypes.byref(sh), FAKE, FAKE, FAKE, 100, ctypes.byref(tr), FAKE, kw.get("W", FAKE), kw.get("vocab", 256),
+        None, kw.get("k", 100), 1, FAKE, FAKE, FAKE, None, None, kw.get("ws", FAKE), kw.get("ws_bytes", need),
+        FAKE, None)
+    assert ds(W=None) == L.GR_ERR_NULL
+    assert ds(vocab=3) == L.GR_ERR_UNSUPPORTED
+    assert ds(k=25601) == L.GR_ERR_K_TOO_LARGE
+    assert ds(ws_bytes=need - 1) == L.GR_ERR_WORKSPACE

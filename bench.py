@@ -61,6 +61,9 @@ def parse():
                     help="independent input copies rotated between steps (default: 2 per stream)")
     ap.add_argument("--streams", type=int, default=2,
                     help="HIP streams carrying independent batches concurrently (1 = one after another)")
+    ap.add_argument("--attention", choices=["softmax", "linear"], default="softmax",
+                    help="linear: linear-attention decoding over a shared prompt state (gr_linear_decode_step); "
+                         "the state is computed once per input set before timing, as a prefill would")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -113,6 +116,20 @@ def algorithmic(x):
                 prompt=prompt, q=q, records=records, n_chain_records=n_chain, flops=flops)
 
 
+def algorithmic_linear(x):
+    """Bytes of a linear-attention step: the shared state and normaliser of
+    every (request, head) once (fp32), then as the softmax step without the
+    prompt (queries, distinct chain records, codebook, priors, outputs)."""
+    cfg = x.cfg
+    a = algorithmic(x)
+    state = cfg.R * cfg.H * (cfg.d * cfg.d + cfg.d) * 4
+    step = a["step_bytes"] - a["prompt"] + state
+    attn_out = cfg.R * cfg.n_in * cfg.D * (2 if (cfg.dtype == "bf16" and cfg.vocab == 256) else 4)
+    flops = cfg.R * cfg.n_in * cfg.H * (2 * cfg.d * cfg.d + 4 * cfg.depth * cfg.d) + 2 * cfg.R * cfg.n_in * cfg.D * cfg.vocab
+    return dict(step_bytes=step, attn_kernel_bytes=state + a["q"] + a["records"] + attn_out, state=state,
+                flops=flops, n_chain_records=a["n_chain_records"])
+
+
 # ------------------------------------------------------------------ devices
 def clone_step(ds):
     """An independent device copy of one uploaded step (same values)."""
@@ -148,11 +165,14 @@ def traffic_from_counters(attn_bytes_alg):
     return int((c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024)
 
 
-def cpu_baseline(x, seconds):
+def cpu_baseline(x, seconds, linear=False):
     """The oracle (plain NumPy, one BLAS thread) on the first requests of the
-    same workload until `seconds` of work have accumulated."""
+    same workload until `seconds` of work have accumulated (for linear
+    attention the prompt state is computed outside the timed part, as on the
+    GPU)."""
     import numpy as np
     import oracle
+    from oracle import linear as LA
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:            # pragma: no cover
@@ -169,9 +189,17 @@ def cpu_baseline(x, seconds):
             for (pb, k, v) in x.levels:
                 ak, av, par, prev = oracle.trie_append(ak, av, par, base, k[r], v[r], sl(pb), prev)
                 base += k.shape[1]
-            t0 = time.perf_counter()
-            oracle.decode_step(x.prompt_k[r], x.prompt_v[r], x.q[r], par, ak, av, sl(x.beam_node), x.W,
-                               sl(x.prior), cfg.k, use_log_softmax=cfg.vocab > 1, window=cfg.window)
+            if linear:
+                state = LA.prompt_state(x.prompt_k[r], x.prompt_v[r], cfg.window)
+                t0 = time.perf_counter()
+                o = LA.attend_linear_shared(x.prompt_k[r], x.prompt_v[r], x.q[r], par, ak, av, sl(x.beam_node),
+                                            cfg.window, state=state)
+                c = oracle.candidate_scores(oracle.codebook_logits(o, x.W), sl(x.prior), True)
+                oracle.select_topk(c[0], cfg.k)
+            else:
+                t0 = time.perf_counter()
+                oracle.decode_step(x.prompt_k[r], x.prompt_v[r], x.q[r], par, ak, av, sl(x.beam_node), x.W,
+                                   sl(x.prior), cfg.k, use_log_softmax=cfg.vocab > 1, window=cfg.window)
             spent += time.perf_counter() - t0
             done += 1
             beams += cfg.n_in
@@ -355,8 +383,29 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] {len(sets)} input set(s) resident on the GPU", file=sys.stderr, flush=True)
 
+    linear = args.attention == "linear"
+    states = []
+    prefill_ms = None
+    if linear:
+        acc = algorithmic_linear(x)
+        HN.linear_state(sets[0])           # first launch (code object load) untimed
+        torch.cuda.synchronize()
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record()
+        for ds in sets:
+            states.append(HN.linear_state(ds))
+        p1.record()
+        torch.cuda.synchronize()
+        prefill_ms = p0.elapsed_time(p1) / len(sets)
+
     def step(i, flags_extra=0, stream=None):
         ds, buf = sets[i % len(sets)], bufs[i % len(bufs)]
+        if linear:
+            S, z = states[i % len(sets)]
+            L.gr_linear_decode_step(ds.shape, S, z, ds.q, ds.n_beams, ds.trie, ds.beam_node, ds.W, ds.vocab,
+                                    ds.prior, ds.k, ds.flags | flags_extra, buf.score, buf.token, buf.parent,
+                                    None, None, buf.ws, buf.ws_bytes, ds.dev_err, stream)
+            return
         L.gr_decode_step(ds.shape, ds.prompt_k, ds.prompt_v, ds.q, ds.n_beams, ds.trie, ds.beam_node, ds.W,
                          ds.vocab, ds.prior, ds.k, ds.flags | flags_extra, buf.score, buf.token, buf.parent,
                          None, None, buf.ws, buf.ws_bytes, ds.dev_err, stream)
@@ -445,12 +494,14 @@ def main():
     achieved = acc["attn_kernel_bytes"] / (attn_avg_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic_from_counters(acc["attn_kernel_bytes"]),
-                "kernel": "attn_bf16_kernel", "avg_launch_ms": round(attn_avg_ms, 5),
+                "traffic": None if linear else traffic_from_counters(acc["attn_kernel_bytes"]),
+                "kernel": "linear_attn_kernel" if linear else "attn_bf16_kernel",
+                "avg_launch_ms": round(attn_avg_ms, 5),
                 "algorithmic_bytes_per_launch": acc["attn_kernel_bytes"]}
     step_gbps = acc["step_bytes"] / (ms_step * 1e-3) / 1e9
     out = {
-        "metric": "beam decode steps/s & achieved HBM GB/s, beam=100, prompt=600 tok (1 GPU)",
+        "metric": ("linear-attention " if linear else "") +
+                  "beam decode steps/s & achieved HBM GB/s, beam=100, prompt=600 tok (1 GPU)",
         "value": round(steps_per_s, 2),
         "unit": "steps/s",
         "n_gpus": 1,
@@ -479,9 +530,12 @@ def main():
     }
     if copy_gbps is not None:
         out["copy_GBps"] = round(copy_gbps, 1)
+    if linear:
+        out["config"]["attention"] = "linear (elu+1 features, shared prompt state)"
+        out["prefill_state_ms"] = round(prefill_ms, 5)
     if not args.skip_cpu_baseline:
         print("[bench] timing the oracle on a sample of the same workload", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds, linear)
     print(json.dumps(out), flush=True)
 
 

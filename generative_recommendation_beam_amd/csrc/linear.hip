@@ -12,9 +12,11 @@
 //
 // linear_state_bf16_kernel computes S_p, z_p once per (request, head):
 // Phi(K)^T V over the window is a dense contraction and runs on MFMA.
-// linear_attn_kernel reads S_p once per (request, head, 128 beams) into LDS
-// and gives each thread one beam: phi(q)^T S_p, then its chain records, in
-// fp32.  The scoring and selection after it are those of the softmax step.
+// linear_attn_bf16_kernel reads S_p once per (request, head, 128 beams) into
+// LDS; phi(Q) S_p for the 128 beams is again a dense contraction (MFMA), and
+// each lane then folds its beam's chain records in fp32.  fp32 workloads use
+// VALU kernels throughout.  The scoring and selection after it are those of
+// the softmax step.
 
 #include "gr_device.h"
 #include "gr_launch.h"
@@ -39,8 +41,8 @@ struct StateP {
 // B operand: V (k = key, column = d_v), exact in bf16.  Lane (g, c) of an
 // MFMA k-step holds keys 8g .. 8g+7 of column c for both, read as single
 // bf16 elements.  z sums phi in fp32.
-// Window rows past the prompt end are zero in the tile and excluded from
-// phi (phi(0) = 1 would count them).
+// Tile rows past the prompt end re-read its last row and are excluded from
+// phi by the row count (their V rows then meet a zero A operand).
 template <int HD>
 __global__ __launch_bounds__(256) void linear_state_bf16_kernel(StateP p) {
   constexpr int KT = 64, CH = HD / 8;                 // 16-byte chunks per row
@@ -58,37 +60,46 @@ __global__ __launch_bounds__(256) void linear_state_bf16_kernel(StateP p) {
   const bool owner = wave < NT;
   const int dk0 = (wave >> 1) * 32, dv0 = (wave & 1) * 32;
 
-  uint4 kr[PER], vr[PER];
-  auto load = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = tid + 256 * i, kk = e / CH, ch = e % CH;
-      const int key = k_begin + t * KT + kk;
-      const bool in = key < p.Lp;
-      const uint4 zero = make_uint4(0, 0, 0, 0);
-      kr[i] = in ? *(const uint4 *)(pk + (size_t)key * row + ch * 8) : zero;
-      vr[i] = in ? *(const uint4 *)(pv + (size_t)key * row + ch * 8) : zero;
-    }
+  // tile t's chunks of this thread: e = tid + 256 i -> row e / CH, chunk e % CH
+  // (PER is 1 or 2; named registers rather than an array keep them out of
+  // scratch memory)
+  static_assert(PER == 1 || PER == 2, "chunks per thread");
+  uint4 kr0, vr0, kr1, vr1;
+  auto chunk_off = [&](int t, int i) -> size_t {
+    const int e = tid + 256 * i, key = k_begin + t * KT + e / CH;
+    return (size_t)min(key, p.Lp - 1) * row + (e % CH) * 8;
   };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = tid + 256 * i;
-      *(uint4 *)&Ks[buf][e * 8] = kr[i];
-      *(uint4 *)&Vs[buf][e * 8] = vr[i];
-    }
-  };
+#define GR_STATE_LOAD(t)                                                           \
+  {                                                                                \
+    const size_t o0 = chunk_off((t), 0);                                           \
+    kr0 = *(const uint4 *)(pk + o0);                                               \
+    vr0 = *(const uint4 *)(pv + o0);                                               \
+    if constexpr (PER == 2) {                                                      \
+      const size_t o1 = chunk_off((t), 1);                                         \
+      kr1 = *(const uint4 *)(pk + o1);                                             \
+      vr1 = *(const uint4 *)(pv + o1);                                             \
+    }                                                                              \
+  }
+#define GR_STATE_STORE(b)                                                          \
+  {                                                                                \
+    *(uint4 *)&Ks[b][tid * 8] = kr0;                                               \
+    *(uint4 *)&Vs[b][tid * 8] = vr0;                                               \
+    if constexpr (PER == 2) {                                                      \
+      *(uint4 *)&Ks[b][(tid + 256) * 8] = kr1;                                     \
+      *(uint4 *)&Vs[b][(tid + 256) * 8] = vr1;                                     \
+    }                                                                              \
+  }
 
   f32x16 acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
   float zpart = 0.f;
-  load(0);
-  store(0);
+  GR_STATE_LOAD(0)
+  GR_STATE_STORE(0)
   __syncthreads();
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < n_tiles) load(t + 1);
+    if (t + 1 < n_tiles) GR_STATE_LOAD(t + 1)
     if (owner) {
       const int valid = min(KT, p.Lp - (k_begin + t * KT));   // keys of this tile inside the prompt
 #pragma unroll
@@ -111,10 +122,12 @@ __global__ __launch_bounds__(256) void linear_state_bf16_kernel(StateP p) {
     }
     __syncthreads();                       // everyone is done with the other buffer
     if (t + 1 < n_tiles) {
-      store(buf ^ 1);
+      GR_STATE_STORE(buf ^ 1)
       __syncthreads();
     }
   }
+#undef GR_STATE_LOAD
+#undef GR_STATE_STORE
   if (!owner) return;
   float *S = p.S + ((size_t)r * p.H + h) * HD * HD;
 #pragma unroll
@@ -150,10 +163,12 @@ __global__ __launch_bounds__(256) void linear_state_f32_kernel(StateP p) {
       Vs[kk][i] = kk < nk ? pv[(size_t)(k0 + kk) * row + i] : 0.f;
     }
     __syncthreads();
+    // entry tid + 256 i is (a, cc) = (tid / HD + i * 256 / HD, tid % HD)
+#pragma unroll 2
+    for (int kk = 0; kk < KT; ++kk) {
+      const float v = Vs[kk][tid % HD];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = tid + 256 * i, a = e / HD, cc = e % HD;
-      for (int kk = 0; kk < KT; ++kk) s[i] = fmaf(Fk[kk][a], Vs[kk][cc], s[i]);
+      for (int i = 0; i < PER; ++i) s[i] = fmaf(Fk[kk][tid / HD + i * (256 / HD)], v, s[i]);
     }
     if (tid < HD)
       for (int kk = 0; kk < KT; ++kk) zs += Fk[kk][tid];
@@ -189,8 +204,10 @@ __device__ __forceinline__ void load8<uint16_t>(const uint16_t *src, float *dst)
   dst[4] = bf16_lo(a.z); dst[5] = bf16_hi(a.z); dst[6] = bf16_lo(a.w); dst[7] = bf16_hi(a.w);
 }
 
-// One workgroup of 128 threads per (request, head, 128 beams); S_p and z_p of
-// the (request, head) in LDS, read as broadcasts.  Thread = beam.
+// fp32 storage: one workgroup of 128 threads per (request, head, 128 beams);
+// S_p and z_p of the (request, head) in LDS, read as broadcasts, one thread
+// per beam, all fp32.  (Every lane reads all of S_p, so this form is LDS-bound
+// at scale; the bf16 path below uses MFMA.)
 template <typename T, int HD>
 __global__ __launch_bounds__(128) void linear_attn_kernel(LinP p) {
   __shared__ __attribute__((aligned(16))) float Ss[HD * HD];
@@ -215,8 +232,9 @@ __global__ __launch_bounds__(128) void linear_attn_kernel(LinP p) {
     fq[i] = phi(fq[i]);
     num[i] = 0.f;
   }
-  // phi(q)^T S_p and phi(q) . z_p
-#pragma unroll 4
+  // phi(q)^T S_p and phi(q) . z_p (fully unrolled: fq and num stay in
+  // registers)
+#pragma unroll
   for (int a = 0; a < HD; ++a) {
     const float f = fq[a];
     den = fmaf(f, zs[a], den);
@@ -280,6 +298,135 @@ __global__ __launch_bounds__(128) void linear_attn_kernel(LinP p) {
   }
 }
 
+// bf16: one workgroup of 4 waves per (request, head, 128 beams), wave w
+// owning beams 32w .. 32w+31.  The shared-state term is a dense contraction,
+// O^T = S_p^T Phi(Q)^T ([HD x HD] by [HD x 32] per wave), on
+// v_mfma_f32_32x32x16_bf16 with both operands split into bf16 hi + lo terms
+// (three MFMAs: hi.hi + hi.lo + lo.hi), which keeps about 16 mantissa bits:
+//   A = S_p^T (row = d_v, k = d_k) from S_p in LDS,
+//   B = Phi(Q)^T (k = d_k, column = beam): lane (g, c) holds phi of dims
+//       16 ks + 8g .. +8 of beam c, from one 16-byte load of its query.
+// Accumulator i of tile dt is o[beam c][32 dt + 8(i/4) + 4g + i%4].  Each
+// lane then folds its beam's records straight from global memory: the dot
+// phi(q).phi(k_n) over the lane's HD/2 query dims, completed across the lane
+// pair (c, c+32), updates the lane's HD/2 output rows and the normaliser.
+// (Staging the record rows through LDS tiles level by level, 8 threads per
+// row, was measured slower: it costs occupancy and a barrier per level.)
+template <int HD>
+__global__ __launch_bounds__(256) void linear_attn_bf16_kernel(LinP p) {
+  constexpr int DT = HD / 32, KS = HD / 16;
+  __shared__ __attribute__((aligned(16))) float Ss[HD * HD];
+  __shared__ float zs[HD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, c = lane & 31;
+  int bid = blockIdx.x;
+  const int chunk = bid % p.n_chunk;
+  bid /= p.n_chunk;
+  const int h = bid % p.H, r = bid / p.H;
+  const float *Sg = p.S + ((size_t)r * p.H + h) * HD * HD;
+  for (int e = tid * 4; e < HD * HD; e += 256 * 4) *(float4 *)&Ss[e] = *(const float4 *)&Sg[e];
+  if (tid < HD) zs[tid] = p.z[((size_t)r * p.H + h) * HD + tid];
+  const int beam = chunk * 128 + wave * 32 + c;
+  const bool valid = beam < p.nb;
+  const size_t row = (size_t)p.H * HD;
+  const uint16_t *qp = (const uint16_t *)p.q + ((size_t)r * p.nb + (valid ? beam : p.nb - 1)) * row +
+                       (size_t)h * HD;
+  // phi(q) of this lane's dims 16 ks + 8g + u, fp32 and as bf16 hi / lo
+  float fq[KS][8];
+  bf16x8 bhi[KS], blo[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    float v[8];
+    load8<uint16_t>(qp + 16 * ks + 8 * g, v);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      fq[ks][u] = phi(v[u]);
+      const __bf16 hi = (__bf16)fq[ks][u];
+      bhi[ks][u] = hi;
+      blo[ks][u] = (__bf16)(fq[ks][u] - (float)hi);
+    }
+  }
+  __syncthreads();
+  float den = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) den = fmaf(fq[ks][u], zs[16 * ks + 8 * g + u], den);
+  den = xor32_sum(den);
+  f32x16 O[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[dt][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 ahi, alo;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float sv = Ss[(16 * ks + 8 * g + u) * HD + 32 * dt + c];
+        const __bf16 hi = (__bf16)sv;
+        ahi[u] = hi;
+        alo[u] = (__bf16)(sv - (float)hi);
+      }
+      O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bhi[ks], O[dt], 0, 0, 0);
+      O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, blo[ks], O[dt], 0, 0, 0);
+      O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bhi[ks], O[dt], 0, 0, 0);
+    }
+  }
+  // the beam's own records, from its node up to the root
+  if (p.beam_node != nullptr && valid) {
+    int n = p.beam_node[(size_t)r * p.nb + beam];
+    int err = 0;
+    const int32_t *par = p.parent + (size_t)r * p.cap;
+    for (int depth = 0; n != -1; ++depth) {
+      if (n < 0 || n >= p.cap) { err |= GR_DEVERR_PARENT_RANGE; break; }
+      if (depth >= p.max_depth) { err |= GR_DEVERR_DEPTH; break; }
+      const int pn = par[n];
+      const uint16_t *kn = (const uint16_t *)p.ak + ((size_t)r * p.cap + n) * row + (size_t)h * HD;
+      const uint16_t *vn = (const uint16_t *)p.av + ((size_t)r * p.cap + n) * row + (size_t)h * HD;
+      float w = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        float kk[8];
+        load8<uint16_t>(kn + 16 * ks + 8 * g, kk);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) w = fmaf(fq[ks][u], phi(kk[u]), w);
+      }
+      w = xor32_sum(w);
+      den += w;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const uint2 v2 = *(const uint2 *)(vn + 32 * dt + 8 * q4 + 4 * g);
+          O[dt][4 * q4 + 0] = fmaf(w, bf16_lo(v2.x), O[dt][4 * q4 + 0]);
+          O[dt][4 * q4 + 1] = fmaf(w, bf16_hi(v2.x), O[dt][4 * q4 + 1]);
+          O[dt][4 * q4 + 2] = fmaf(w, bf16_lo(v2.y), O[dt][4 * q4 + 2]);
+          O[dt][4 * q4 + 3] = fmaf(w, bf16_hi(v2.y), O[dt][4 * q4 + 3]);
+        }
+      if (pn < -1 || pn >= p.cap) { err |= GR_DEVERR_PARENT_RANGE; break; }
+      if (pn >= n) { err |= GR_DEVERR_PARENT_ORDER; break; }
+      n = pn;
+    }
+    if (err) atomicOr(p.dev_err, err);
+  }
+  if (!valid) return;
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * dt + 8 * q4 + 4 * g;
+      const float o0 = O[dt][4 * q4] * inv, o1 = O[dt][4 * q4 + 1] * inv;
+      const float o2 = O[dt][4 * q4 + 2] * inv, o3 = O[dt][4 * q4 + 3] * inv;
+      if (p.out_f32)
+        *(float4 *)(p.out_f32 + ((size_t)r * p.nb + beam) * row + (size_t)h * HD + d0) = make_float4(o0, o1, o2, o3);
+      if (p.out_bf16)
+        *(uint2 *)(p.out_bf16 + (((size_t)r * p.H + h) * p.nb + beam) * HD + d0) =
+            make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+    }
+}
+
 }  // namespace
 
 hipError_t launch_linear_state(const LinearStateArgs &a, hipStream_t s) {
@@ -304,11 +451,12 @@ hipError_t launch_linear_attn(const LinearAttnArgs &a, hipStream_t s) {
   p.out_f32 = a.out_f32; p.out_bf16 = (uint16_t *)a.out_lowp;
   p.R = a.R; p.H = a.H; p.nb = a.nb; p.cap = a.cap; p.max_depth = a.max_depth;
   p.n_chunk = (a.nb + 127) / 128;
-  const dim3 grid((unsigned)((long long)a.R * a.H * p.n_chunk)), block(128);
+  const dim3 grid((unsigned)((long long)a.R * a.H * p.n_chunk));
   if (a.dtype == GR_BF16) {
-    if (a.hd == 64) hipLaunchKernelGGL((linear_attn_kernel<uint16_t, 64>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((linear_attn_kernel<uint16_t, 32>), grid, block, 0, s, p);
+    if (a.hd == 64) hipLaunchKernelGGL(linear_attn_bf16_kernel<64>, grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(linear_attn_bf16_kernel<32>, grid, dim3(256), 0, s, p);
   } else {
+    const dim3 block(128);
     if (a.hd == 64) hipLaunchKernelGGL((linear_attn_kernel<float, 64>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((linear_attn_kernel<float, 32>), grid, block, 0, s, p);
   }

@@ -94,6 +94,13 @@ gr_status check_select(int R, int n_in, int vocab, int k, int flags) {
 size_t attn_ids_bytes(const gr_shape *s, int n_beams) {
   return s->dtype == GR_BF16 ? align_up(gr::attn_ids_bytes(s->R, n_beams)) : 0;
 }
+// bf16 attention with few (request, head, beam group) units: the partial
+// states of the split prompt window
+size_t attn_split_ws_bytes(const gr_shape *s, int n_beams) {
+  if (s->dtype != GR_BF16) return 0;
+  const int Lw = (s->window <= 0 || s->window >= s->prompt_len) ? s->prompt_len : s->window;
+  return align_up(gr::attn_split_bytes(s->R, s->H, s->head_dim, n_beams, Lw));
+}
 
 // The bf16 codebook step feeds the attention output to the projection MFMA
 // in bf16.  Its rounding perturbs a logit by about 2^-9 |o| |W|; over a long
@@ -107,7 +114,7 @@ bool use_mfma_logits(const gr_shape *s, int vocab) {
 }
 
 struct DecodeLayout {
-  size_t o_off, o_bytes, z_off, z_bytes, part_off, part_bytes, ids_off, ids_bytes, total;
+  size_t o_off, o_bytes, z_off, z_bytes, part_off, part_bytes, ids_off, ids_bytes, split_off, split_bytes, total;
 };
 DecodeLayout decode_layout(const gr_shape *s, int n_beams, int vocab, int k) {
   DecodeLayout L;
@@ -125,7 +132,9 @@ DecodeLayout decode_layout(const gr_shape *s, int n_beams, int vocab, int k) {
   L.part_off = L.z_off + L.z_bytes;
   L.ids_bytes = attn_ids_bytes(s, n_beams);
   L.ids_off = L.part_off + L.part_bytes;
-  L.total = L.ids_off + L.ids_bytes + kAlign;  // slack for aligning ws
+  L.split_bytes = attn_split_ws_bytes(s, n_beams);
+  L.split_off = L.ids_off + L.ids_bytes;
+  L.total = L.split_off + L.split_bytes + kAlign;  // slack for aligning ws
   return L;
 }
 
@@ -346,7 +355,7 @@ const char *gr_status_string(gr_status s) {
 
 size_t gr_attn_workspace_size(const gr_shape *shape, int32_t n_beams) {
   if (check_shape(shape) || n_beams <= 0) return 0;
-  const size_t b = attn_ids_bytes(shape, n_beams);
+  const size_t b = attn_ids_bytes(shape, n_beams) + attn_split_ws_bytes(shape, n_beams);
   return b ? b + kAlign : 0;
 }
 
@@ -407,9 +416,11 @@ gr_status gr_prefix_attn(const gr_shape *shape, const void *prompt_k, const void
   if (!aligned16(out)) return GR_ERR_UNSUPPORTED;
   gr::AttnArgs a = attn_args(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, dev_err);
   a.out_f32 = out;
-  if (beam_node && attn_ids_bytes(shape, n_beams)) {
+  const size_t ids_bytes = attn_ids_bytes(shape, n_beams), split_bytes = attn_split_ws_bytes(shape, n_beams);
+  if ((beam_node && ids_bytes) || split_bytes) {
     if (!ws || ws_bytes < gr_attn_workspace_size(shape, n_beams)) return GR_ERR_WORKSPACE;
     a.chain_ids = (int32_t *)align_ptr(ws);
+    a.split_ws = split_bytes ? (float *)(align_ptr(ws) + ids_bytes) : nullptr;
   }
   clear_stale_error();
   return hip_status(gr::launch_attn(a, stream));
@@ -466,6 +477,7 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void
 
   gr::AttnArgs a = attn_args(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, dev_err);
   a.chain_ids = L.ids_bytes ? (int32_t *)(base + L.ids_off) : nullptr;
+  a.split_ws = L.split_bytes ? (float *)(base + L.split_off) : nullptr;
   const bool mfma_logits = use_mfma_logits(shape, vocab);
   const float *o_f32 = nullptr;
   if (mfma_logits) {

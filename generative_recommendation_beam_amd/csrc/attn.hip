@@ -108,6 +108,8 @@ struct AttnP {
   float *out_f32;
   uint16_t *out_bf16;
   int R, H, Lp, Lw, nb, cap, D, nb_pad, n_grp;
+  int n_split, tps;          // prompt runs per unit and 64-key tiles per run
+  float *part;               // n_split > 1: partial states (see attn_split_bytes)
   int ids_words, par_words;  // dynamic LDS: ids [ids_words], parents [par_words], beam nodes
   float sl2;                 // scale * log2(e)
 };
@@ -160,7 +162,6 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   int16_t *const ids16 = reinterpret_cast<int16_t *>(dyn_s);
   int32_t *const par_s = dyn_s + p.ids_words;
   int32_t *const bn_s = par_s + p.par_words;
-  const bool chains = p.ids != nullptr || p.parent != nullptr;
   auto chain_id = [&](int d, int b) -> int {
     return p.parent != nullptr ? (int)ids16[d * G::NB + b] : ids_s[d * G::NB + b];
   };
@@ -183,6 +184,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   // same time.
   int bid = blockIdx.x;
   if ((gridDim.x & 7) == 0) bid = (bid & 7) * (int)(gridDim.x >> 3) + (bid >> 3);
+  const int split = bid % p.n_split;           // run of the prompt window (0 unless it is split)
+  bid /= p.n_split;
   const int grp = bid % p.n_grp;
   bid /= p.n_grp;
   const int h = bid % p.H, r = bid / p.H;
@@ -193,8 +196,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   const uint32_t row32 = (uint32_t)row;
   const uint16_t *pk = p.pk + (size_t)r * p.Lp * row + (size_t)h * HD;
   const uint16_t *pv = p.pv + (size_t)r * p.Lp * row + (size_t)h * HD;
-  const int k_begin = p.Lp - p.Lw;
-  const int n_tiles = (p.Lw + G::KT - 1) / G::KT;
+  // this workgroup's run of the window: tiles [split * tps, ...); the chain
+  // records go with the last run
+  const int k_begin = p.Lp - p.Lw + split * p.tps * G::KT;
+  const int n_tiles = (min(p.tps * G::KT, p.Lw - split * p.tps * G::KT) + G::KT - 1) / G::KT;
+  const bool chains = (p.ids != nullptr || p.parent != nullptr) && split == p.n_split - 1;
   const int n_pre = max(n_tiles, NS - 1);       // prompt tiles, padded to fill the prologue
   int n_total = n_pre;                          // + chain-record tiles, known after tile 0
 
@@ -256,13 +262,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   // nodes (wave 0), the queries of the workgroup into the last stage (its K
   // half: beams 0..63, V half: beams 64..127, K-swizzled rows), then prompt
   // tiles 0..NS-2.
-  if (p.parent != nullptr && wave == 0) {
+  if (chains && p.parent != nullptr && wave == 0) {
     const int32_t *par = p.parent + (size_t)r * p.cap;
     for (int i = 0; i * 64 < p.cap; ++i) dma4(par + min(i * 64 + lane, p.cap - 1), par_s + i * 64);
     const int32_t *bnp = p.beam_node + (size_t)r * p.nb;
     for (int i = 0; i * 64 < G::NB; ++i) dma4(bnp + min(grp * G::NB + i * 64 + lane, p.nb - 1), bn_s + i * 64);
   }
-  if (p.ids != nullptr && wave == 0) {
+  if (chains && p.ids != nullptr && wave == 0) {
     const int words = p.D * G::NB;
     const int32_t *src0 = p.ids + (size_t)r * p.D * p.nb_pad + (size_t)grp * G::NB;
     for (int i = 0; i * 256 < words; ++i) {
@@ -340,7 +346,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
       if constexpr (st == 0) {
         if (tile == 0) {
           // queries and chain ids / parents have landed (they precede tile 0)
-          if (p.parent != nullptr && tid < G::NB) {
+          if (chains && p.parent != nullptr && tid < G::NB) {
             // resolve the chain of workgroup beam tid in LDS, checking range,
             // order and depth (heads of one request see the same chains; the
             // head-0 workgroup reports)
@@ -502,13 +508,50 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   // XOR-swizzled 16-byte chunks, then written with consecutive lanes covering
   // whole rows.
   const float l_tot = xor32_sum(l_run);
-  const float inv = valid ? 1.f / l_tot : 0.f;
   const size_t out_row0 = ((size_t)r * p.nb + (size_t)grp * G::NB) * row + (size_t)h * HD;
   const int n_rows = min(G::NB, p.nb - grp * G::NB);   // rows of this workgroup that exist
   // bf16 feed of the projection: head-major [R][H][nb][HD], so that this
   // workgroup's rows form one contiguous block
   const size_t lowp_row0 = (((size_t)r * p.H + h) * p.nb + (size_t)grp * G::NB) * HD;
   __syncthreads();                                      // every wave is past its last tile
+  // fp32 rows o * sc to dst0 + row_index * stride, staged in the first ring
+  // stage (64 rows at a time) and written with consecutive lanes per row
+  auto store_f32 = [&](float *dst0, size_t stride, float sc) {
+    constexpr int CPR = HD / 4;                         // 16-byte chunks per fp32 row
+    float *st = (float *)KV0;                           // 64 rows x HD fp32 (<= 16 KB)
+#pragma unroll
+    for (int half = 0; half < (G::NB + 63) / 64; ++half) {
+      if ((wb >> 6) == half) {                          // wave-uniform
+        const int lr = wb & 63;
+#pragma unroll
+        for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int pch = (8 * dt + 2 * q4 + g) ^ (lr & (CPR - 1));
+            *(float4 *)(st + lr * HD + pch * 4) = make_float4(O[dt][4 * q4] * sc, O[dt][4 * q4 + 1] * sc,
+                                                              O[dt][4 * q4 + 2] * sc, O[dt][4 * q4 + 3] * sc);
+          }
+      }
+      __syncthreads();
+      const int rows_h = min(64, n_rows - 64 * half);
+      for (int id = tid; id < rows_h * CPR; id += NW * 64) {
+        const int lr = id / CPR, ch = id % CPR;
+        const float4 v = *(const float4 *)(st + lr * HD + ((ch ^ (lr & (CPR - 1))) << 2));
+        *(float4 *)(dst0 + (size_t)(64 * half + lr) * stride + ch * 4) = v;
+      }
+      __syncthreads();
+    }
+  };
+  if (p.n_split > 1) {
+    // partial state of this run: unnormalised o rows, then (max, sum) per
+    // beam (the max in the exp2 domain of the scores times scale*log2(e))
+    const size_t slot = (((size_t)r * p.H + h) * p.n_split + split) * p.nb_pad + (size_t)grp * G::NB;
+    store_f32(p.part + slot * HD, HD, 1.f);
+    float2 *ml = reinterpret_cast<float2 *>(p.part + (size_t)p.R * p.H * p.n_split * p.nb_pad * HD);
+    if (g == 0 && valid) ml[slot + wb] = make_float2(m_run, l_tot);
+    return;
+  }
+  const float inv = valid ? 1.f / l_tot : 0.f;
   if (p.out_bf16 != nullptr) {
     constexpr int CPR = HD / 8;                         // 16-byte chunks per bf16 row
     uint16_t *st = KV0;                                 // NB rows x HD bf16 (<= 16 KB)
@@ -529,32 +572,53 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
     }
     __syncthreads();
   }
-  if (p.out_f32 != nullptr) {
-    constexpr int CPR = HD / 4;                         // 16-byte chunks per fp32 row
-    float *st = (float *)KV0;                           // 64 rows x HD fp32 (<= 16 KB)
-#pragma unroll
-    for (int half = 0; half < (G::NB + 63) / 64; ++half) {
-      if ((wb >> 6) == half) {                          // wave-uniform
-        const int lr = wb & 63;
-#pragma unroll
-        for (int dt = 0; dt < G::DT; ++dt)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int pch = (8 * dt + 2 * q4 + g) ^ (lr & (CPR - 1));
-            *(float4 *)(st + lr * HD + pch * 4) = make_float4(O[dt][4 * q4] * inv, O[dt][4 * q4 + 1] * inv,
-                                                              O[dt][4 * q4 + 2] * inv, O[dt][4 * q4 + 3] * inv);
-          }
-      }
-      __syncthreads();
-      const int rows_h = min(64, n_rows - 64 * half);
-      for (int id = tid; id < rows_h * CPR; id += NW * 64) {
-        const int lr = id / CPR, ch = id % CPR;
-        const float4 v = *(const float4 *)(st + lr * HD + ((ch ^ (lr & (CPR - 1))) << 2));
-        *(float4 *)(p.out_f32 + out_row0 + (size_t)(64 * half + lr) * row + ch * 4) = v;
-      }
-      __syncthreads();
-    }
+  if (p.out_f32 != nullptr) store_f32(p.out_f32 + out_row0, row, inv);
+}
+
+// The runs of a split window, merged per (request, head, beam) with their
+// log-sum-exp weights: m = max_s m_s, w_s = 2^(m_s - m),
+// o = sum_s w_s o_s / sum_s w_s l_s.  One thread per 16-byte chunk of a row.
+struct MergeP {
+  const float *part;
+  float *out_f32;
+  uint16_t *out_bf16;
+  int R, H, nb, nb_pad, n_split;
+};
+
+template <int HD>
+__global__ __launch_bounds__(256) void attn_merge_kernel(MergeP p) {
+  constexpr int CH = HD / 4;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)p.R * p.H * p.nb * CH) return;
+  const int ch = (int)(idx % CH);
+  long long t = idx / CH;
+  const int beam = (int)(t % p.nb);
+  t /= p.nb;
+  const int h = (int)(t % p.H), r = (int)(t / p.H);
+  const size_t unit = ((size_t)r * p.H + h) * p.n_split;
+  const float2 *ml = reinterpret_cast<const float2 *>(p.part + (size_t)p.R * p.H * p.n_split * p.nb_pad * HD);
+  float m = -__builtin_inff();
+  for (int sp = 0; sp < p.n_split; ++sp) m = fmaxf(m, ml[(unit + sp) * p.nb_pad + beam].x);
+  float l = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp = 0; sp < p.n_split; ++sp) {
+    const size_t slot = (unit + sp) * p.nb_pad + beam;
+    const float2 e = ml[slot];
+    const float w = fast_exp2(e.x - m);
+    const float4 v = *(const float4 *)(p.part + slot * HD + ch * 4);
+    l = fmaf(w, e.y, l);
+    o.x = fmaf(w, v.x, o.x);
+    o.y = fmaf(w, v.y, o.y);
+    o.z = fmaf(w, v.z, o.z);
+    o.w = fmaf(w, v.w, o.w);
   }
+  const float inv = 1.f / l;
+  if (p.out_f32)
+    *(float4 *)(p.out_f32 + ((size_t)r * p.nb + beam) * p.H * HD + (size_t)h * HD + ch * 4) =
+        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+  if (p.out_bf16)
+    *(uint2 *)(p.out_bf16 + (((size_t)r * p.H + h) * p.nb + beam) * HD + ch * 4) =
+        make_uint2(pack_bf16x2(o.x * inv, o.y * inv), pack_bf16x2(o.z * inv, o.w * inv));
 }
 
 // ------------------------------------------------------------------ fp32
@@ -702,9 +766,22 @@ hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
       p.ids_words = (a.max_depth * NB + 255) / 256 * 256;   // the ids arrive in 1 KB DMA blocks
     }
   }
+  const AttnSplit sp = attn_split(a.R, a.H, a.nb, a.Lw);
+  p.n_split = sp.n_split;
+  p.tps = sp.tiles_per_split;
+  p.part = a.split_ws;
+  if (sp.n_split > 1 && a.split_ws == nullptr) return hipErrorInvalidValue;   // the caller checks this
   const size_t dyn = (size_t)(p.ids_words + p.par_words + (p.parent ? (NB + 63) / 64 * 64 : 0)) * sizeof(int32_t);
-  const long long grid = (long long)a.R * a.H * p.n_grp;
+  const long long grid = (long long)a.R * a.H * p.n_grp * p.n_split;
   hipLaunchKernelGGL((attn_bf16_kernel<HD, NW, NS, OCC>), dim3((unsigned)grid), dim3(NW * 64), dyn, s, p);
+  if (sp.n_split == 1) return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  MergeP m;
+  m.part = a.split_ws; m.out_f32 = a.out_f32; m.out_bf16 = (uint16_t *)a.out_lowp;
+  m.R = a.R; m.H = a.H; m.nb = a.nb; m.nb_pad = p.nb_pad; m.n_split = sp.n_split;
+  const long long n = (long long)a.R * a.H * a.nb * (HD / 4);
+  hipLaunchKernelGGL(attn_merge_kernel<HD>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, m);
   return hipGetLastError();
 }
 

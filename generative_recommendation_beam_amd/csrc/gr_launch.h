@@ -17,6 +17,7 @@ struct AttnArgs {
   const int32_t *parent;           // [R][cap]
   const int32_t *beam_node;        // [R][nb] or null (prompt only)
   int32_t *chain_ids;              // bf16 path: workspace for the resolved chains, attn_ids_bytes(R, nb)
+  float *split_ws;                 // bf16 path with a split prompt: partial states, attn_split_bytes(...)
   float *out_f32;                  // optional [R][nb][H*hd]
   void *out_lowp;                  // optional head-major [R][H][nb][hd] in dtype (bf16 feed of the logits)
   int32_t *dev_err;
@@ -38,6 +39,40 @@ inline int attn_beam_pad(int nb) {
 }
 inline size_t attn_ids_bytes(int R, int nb) {
   return (size_t)R * GR_MAX_DEPTH * attn_beam_pad(nb) * sizeof(int32_t);
+}
+
+// Split of the prompt window (bf16 path).  With too few (request, head, beam
+// group) units to fill the GPU, each unit's window is cut into n_split runs
+// of tiles_per_split 64-key tiles, one workgroup each; every workgroup leaves
+// its partial online-softmax state (unnormalised o, running max, sum) in the
+// workspace and a merge pass combines them with their log-sum-exp weights.
+// The chain records go with the last run.
+constexpr int kAttnSplitBelow = 384;   // units below which the window is split
+constexpr int kAttnSplitTarget = 384;  // workgroups aimed at (measured: 6 to 12 runs of an 8192-key
+                                       // window, 4 requests x 8 heads, all within 3 %; 16 or more
+                                       // runs are slower, the partial states growing with them)
+constexpr int kAttnSplitMinTiles = 4;  // tiles (256 keys) per run at least
+struct AttnSplit {
+  int n_split, tiles_per_split;
+};
+inline AttnSplit attn_split(int R, int H, int nb, int Lw) {
+  const long long units = (long long)R * H * (attn_beam_pad(nb) / (attn_waves(nb) * 32));
+  const int n_tiles = (Lw + 63) / 64;
+  AttnSplit sp = {1, n_tiles};
+  if (units >= kAttnSplitBelow) return sp;
+  const long long want = (kAttnSplitTarget + units - 1) / units;
+  const int most = n_tiles / kAttnSplitMinTiles;
+  const int ns = (int)(want < most ? want : most);
+  if (ns < 2) return sp;
+  sp.tiles_per_split = (n_tiles + ns - 1) / ns;
+  sp.n_split = (n_tiles + sp.tiles_per_split - 1) / sp.tiles_per_split;
+  return sp;
+}
+// partial states: o [R][H][n_split][nb_pad][hd] fp32, then (max, sum) [R][H][n_split][nb_pad][2]
+inline size_t attn_split_bytes(int R, int H, int hd, int nb, int Lw) {
+  const AttnSplit sp = attn_split(R, H, nb, Lw);
+  if (sp.n_split == 1) return 0;
+  return (size_t)R * H * sp.n_split * attn_beam_pad(nb) * (hd + 2) * sizeof(float);
 }
 
 struct AppendArgs {

@@ -101,6 +101,10 @@ CONFIGS: Dict[str, Config] = {c.name: c for c in [
     Config("beam512_p2048_w512", 5, R=32, Lp=2048, window=512, H=16, d=64,
            n_in=512, k=512, depth=4, level_sizes=(256, 512, 512, 512),
            dtype="bf16", vocab=256, prior="cumsum"),
+    # long prompts, few requests: the regime of the split prompt window
+    Config("long8k_beam100", 8, R=4, Lp=8192, window=0, H=8, d=64, n_in=100,
+           k=100, depth=3, level_sizes=(100, 100, 100), dtype="bf16",
+           vocab=256, prior="cumsum"),
 ]}
 
 HEADLINE = "beam100_p600"

@@ -12,6 +12,10 @@ The top-k sweep draws requests, candidate counts (up to 120 000, several
 selection groups and the final merge), k (1 .. GR_MAX_K), the 256-code or
 scalar mode, the log-softmax, priors and exact ties, covering the counting
 rank, bucket, bitonic and merge orderings of the selection list.
+
+Twelve of the decode shapes also go through gr_linear_decode_step, and ten
+long-prompt shapes (500 .. 3000 keys, few requests and heads, so that the
+prompt window is split into runs) through gr_decode_step.
 """
 import numpy as np
 import pytest
@@ -87,3 +91,57 @@ def test_topk_random_shapes(seed):
     c = random_topk_case(seed)
     announce(f"gr_beam_topk random case {seed}: {c}")
     check_topk_case(f"random {seed}", c, np.random.default_rng(8000 + seed))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_linear_decode_random_shapes(seed):
+    """The same random shapes through gr_linear_decode_step."""
+    from oracle import linear as LA
+    from test_gpu_5_linear import arena_of
+    cfg = random_config(seed)
+    announce(f"gr_linear_decode_step random case {seed}: R={cfg.R} Lp={cfg.Lp} window={cfg.window} H={cfg.H} "
+             f"d={cfg.d} n_in={cfg.n_in} k={cfg.k} levels={cfg.level_sizes} {cfg.dtype}")
+    x = W.make_step_inputs(cfg, seed=9000 + seed)
+    ds = HN.upload_step(x)
+    S, z = HN.linear_state(ds)
+    buf = HN.decode_buffers(ds, debug_outputs=True)
+    HN.linear_decode_step(ds, buf, S, z)
+    torch.cuda.synchronize()
+    assert int(ds.dev_err.item()) == 0
+    got = HN.results_to_host(buf)
+    ak, av, par = arena_of(x)
+    ref = LA.linear_decode_step(x.prompt_k, x.prompt_v, x.q, par, ak, av, x.beam_node, x.W, x.prior, cfg.k,
+                                window=cfg.window)
+    compare(cfg, got, ref, list(range(cfg.R)), f"linear random {seed}")
+
+
+def random_long_config(seed: int) -> W.Config:
+    """Few requests and heads with prompts of 500 .. 3000 keys: the prompt
+    window is split into runs (bf16)."""
+    rng = np.random.default_rng(6000 + seed)
+    R = int(rng.integers(1, 3))
+    H = int(rng.integers(1, 4))
+    d = int(rng.choice([32, 64]))
+    Lp = int(rng.integers(500, 3001))
+    window = int(rng.choice([0, 0, int(rng.integers(300, Lp))]))
+    n_in = int(rng.choice([7, 50, 100, 129]))
+    depth = int(rng.integers(0, 4))
+    sizes = tuple(n_in for _ in range(depth))
+    k = int(min(n_in * 256, rng.choice([10, 100, 300])))
+    return W.reduced(W.CONFIGS["beam100_p600"], R=R, Lp=Lp, window=window, H=H, d=d, n_in=n_in, k=k,
+                     depth=depth, level_sizes=sizes, dtype="bf16", prior="cumsum")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_split_window_random_shapes(seed):
+    cfg = random_long_config(seed)
+    announce(f"gr_decode_step split-window random case {seed}: R={cfg.R} Lp={cfg.Lp} window={cfg.window} "
+             f"H={cfg.H} d={cfg.d} n_in={cfg.n_in} k={cfg.k} depth={cfg.depth}")
+    x = W.make_step_inputs(cfg, seed=9500 + seed)
+    ds = HN.upload_step(x)
+    buf = HN.decode_buffers(ds, debug_outputs=True)
+    HN.decode_step(ds, buf)
+    torch.cuda.synchronize()
+    assert int(ds.dev_err.item()) == 0
+    got = HN.results_to_host(buf)
+    compare(cfg, got, oracle_step(x), list(range(cfg.R)), f"split random {seed}")

@@ -394,16 +394,32 @@ __global__ __launch_bounds__(256) void linear_attn_bf16_kernel(LinP p) {
       }
       w = xor32_sum(w);
       den += w;
+      // v: the lane needs half g (4 elements) of every 16-byte chunk j =
+      // 4 dt + q4 of the row.  Lane g loads the chunks j = 2 jp + g whole,
+      // keeps its half and trades the other half for the partner's
+      // (one permlane32 swap per dword), so each lane issues HD/16 16-byte
+      // loads instead of HD/8 8-byte ones.
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const uint2 v2 = *(const uint2 *)(vn + 32 * dt + 8 * q4 + 4 * g);
-          O[dt][4 * q4 + 0] = fmaf(w, bf16_lo(v2.x), O[dt][4 * q4 + 0]);
-          O[dt][4 * q4 + 1] = fmaf(w, bf16_hi(v2.x), O[dt][4 * q4 + 1]);
-          O[dt][4 * q4 + 2] = fmaf(w, bf16_lo(v2.y), O[dt][4 * q4 + 2]);
-          O[dt][4 * q4 + 3] = fmaf(w, bf16_hi(v2.y), O[dt][4 * q4 + 3]);
-        }
+      for (int jp = 0; jp < HD / 16; ++jp) {
+        const uint4 cv = *(const uint4 *)(vn + 8 * (2 * jp + g));
+        const uint32_t give0 = g ? cv.x : cv.z, give1 = g ? cv.y : cv.w;
+        const uint32_t keep0 = g ? cv.z : cv.x, keep1 = g ? cv.w : cv.y;
+        const auto t0 = __builtin_amdgcn_permlane32_swap(give0, give0, false, false);
+        const auto t1 = __builtin_amdgcn_permlane32_swap(give1, give1, false, false);
+        const uint32_t got0 = g ? t0[0] : t0[1], got1 = g ? t1[0] : t1[1];   // the partner's give
+        // chunk 2 jp: half g is keep (g = 0) or got (g = 1); chunk 2 jp + 1: got (g = 0) or keep (g = 1)
+        const uint2 ca = g ? make_uint2(got0, got1) : make_uint2(keep0, keep1);
+        const uint2 cb = g ? make_uint2(keep0, keep1) : make_uint2(got0, got1);
+        const int ja = 2 * jp, jb = 2 * jp + 1;
+        O[ja >> 2][4 * (ja & 3) + 0] = fmaf(w, bf16_lo(ca.x), O[ja >> 2][4 * (ja & 3) + 0]);
+        O[ja >> 2][4 * (ja & 3) + 1] = fmaf(w, bf16_hi(ca.x), O[ja >> 2][4 * (ja & 3) + 1]);
+        O[ja >> 2][4 * (ja & 3) + 2] = fmaf(w, bf16_lo(ca.y), O[ja >> 2][4 * (ja & 3) + 2]);
+        O[ja >> 2][4 * (ja & 3) + 3] = fmaf(w, bf16_hi(ca.y), O[ja >> 2][4 * (ja & 3) + 3]);
+        O[jb >> 2][4 * (jb & 3) + 0] = fmaf(w, bf16_lo(cb.x), O[jb >> 2][4 * (jb & 3) + 0]);
+        O[jb >> 2][4 * (jb & 3) + 1] = fmaf(w, bf16_hi(cb.x), O[jb >> 2][4 * (jb & 3) + 1]);
+        O[jb >> 2][4 * (jb & 3) + 2] = fmaf(w, bf16_lo(cb.y), O[jb >> 2][4 * (jb & 3) + 2]);
+        O[jb >> 2][4 * (jb & 3) + 3] = fmaf(w, bf16_hi(cb.y), O[jb >> 2][4 * (jb & 3) + 3]);
+      }
       if (pn < -1 || pn >= p.cap) { err |= GR_DEVERR_PARENT_RANGE; break; }
       if (pn >= n) { err |= GR_DEVERR_PARENT_ORDER; break; }
       n = pn;

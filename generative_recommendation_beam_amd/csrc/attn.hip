@@ -28,6 +28,12 @@
 // for arenas too large to stage in LDS; its ids reach the attention kernel
 // through the workspace.
 //
+// With too few (request, head, beam group) units to fill the GPU (few
+// requests with long prompts), the window is cut into runs of tiles, one
+// workgroup per run; each leaves its partial online-softmax state in the
+// workspace (the chain records go with the last run) and attn_merge combines
+// the runs with their log-sum-exp weights.
+//
 // Scores are formed transposed, S^T = K Q^T (keys x beams), with
 // v_mfma_f32_32x32x16_bf16: the accumulator holds one beam per lane column,
 // so the softmax reductions are in-lane plus one lane^32 swap, and the

@@ -10,6 +10,10 @@
  *   3. log-softmax over those 256 codes;
  *   4. the running beam score is added;
  *   5. the best B of the B_in x 256 candidates are selected.
+ * Around the step: whole semantic-ID generation with every level enqueued on
+ * the device (gr_code_table, gr_append_codes, gr_generate), and the same step
+ * with linear attention over one shared prompt state (gr_linear_state,
+ * gr_linear_attn, gr_linear_decode_step).
  *
  * Sources (page title, section):
  *   - Engineering Exploration of Generative Recall (ASGR), 4.1 Superman

@@ -303,3 +303,21 @@ def test_generate_graph_replays():
         np.testing.assert_array_equal(got["ids"], eager["ids"], err_msg=f"replay {rep} ids")
         # eager work on the default stream between replays
         torch.matmul(torch.randn(256, 256, device="cuda"), torch.randn(256, 256, device="cuda")).sum().item()
+
+
+def test_generate_maximum_levels():
+    """GR_MAX_DEPTH + 1 levels: the last step's chains hold GR_MAX_DEPTH
+    records, and the trace-back walks nine levels."""
+    cfg = W.reduced(GC["gen_tiny_f32"], R=2, Lp=40, H=2, d=32, k=4, steps=L.GR_MAX_DEPTH + 1,
+                    level_sizes=(4,) * L.GR_MAX_DEPTH)
+    announce(f"gr_generate {cfg.steps} levels, beam 4, fp32")
+    x, g, tabs = setup(cfg)
+    assert g.trie.max_depth == L.GR_MAX_DEPTH
+    HN.generate(g)
+    torch.cuda.synchronize()
+    assert int(g.dev_err.item()) == 0
+    got = HN.generate_to_host(g)
+    res, ids, _ = OG.generate(x.prompt_k, x.prompt_v, x.q0, x.W, tabs, cfg.k)
+    followed = compare_free_running(cfg, got, res, ids)
+    print(f"[info] levels followed per request: {followed}")
+    assert got["ids"].shape == (cfg.R, cfg.k, cfg.steps)

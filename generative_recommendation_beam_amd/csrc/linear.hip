@@ -187,6 +187,7 @@ struct LinP {
   float *out_f32;
   uint16_t *out_bf16;          // head-major [R][H][nb][HD]
   int R, H, nb, cap, max_depth, n_chunk;
+  int par_words;               // ring kernel: parent words staged in LDS
 };
 
 template <typename T>
@@ -443,6 +444,227 @@ __global__ __launch_bounds__(256) void linear_attn_bf16_kernel(LinP p) {
     }
 }
 
+// Arenas of up to this many nodes per request take the ring kernel below.
+constexpr int kLinRingNodes = 4096;
+
+// bf16, ring form: the same computation as linear_attn_bf16_kernel, with the
+// record rows gathered by LDS DMA (global_load_lds) through a 3-stage ring of
+// 64-beam tiles, as the softmax kernel streams its records; the per-lane
+// loads of the plain form gather 128-byte rows with 16-byte pieces from 32
+// rows per instruction and cost about 15 us per chain level at the headline
+// shape.  Stream order, each wait an exact vmcnt: the parent array and the
+// workgroup's beam nodes (wave 0), S_p into stage 0 (and the queries, loaded
+// to registers); then, once the chains are resolved in LDS, record tile k
+// (level k / 2, beams 64 (k % 2) ..) into stage (k + 1) % 3, two tiles ahead.
+// Stage 0 is free for records once the shared-state MFMAs have read S_p.
+// Record rows are XOR-swizzled so that 16 lanes reading 16 consecutive rows
+// at one logical 16-byte chunk hit 16 distinct bank slots.
+template <int HD>
+__device__ __forceinline__ int lswz(int row) {
+  constexpr int RB = HD * 2, CPR = RB / 16;
+  return (row / (256 / RB)) & (CPR - 1);
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void linear_ring_bf16_kernel(LinP p) {
+  constexpr int DT = HD / 32, KS = HD / 16;
+  constexpr int NB = 128, KT = 64, NS = 3;
+  constexpr int RB = HD * 2, CPR = RB / 16;          // bytes and 16-byte chunks per record row
+  constexpr int TB = KT * RB;                        // bytes of the K (or V) half of a tile
+  constexpr int NBLK = 2 * TB / 1024, BPW = NBLK / 4;   // 1 KB DMA blocks per tile, per wave
+  constexpr int SBLK = HD * HD * 4 / 1024;           // 1 KB blocks of S_p
+  static_assert(HD * HD * 4 <= 2 * TB, "S_p fits one ring stage");
+  static_assert(NBLK % 4 == 0 && SBLK % 4 == 0, "every wave moves the same number of blocks");
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[NS][2 * TB];
+  __shared__ float zs[HD];
+  __shared__ int16_t ids16[GR_MAX_DEPTH][NB];
+  extern __shared__ __attribute__((aligned(16))) int32_t dyn_l[];   // parents [par_words], beam nodes [NB]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, c = lane & 31;
+  int bid = blockIdx.x;
+  const int chunk = bid % p.n_chunk;
+  bid /= p.n_chunk;
+  const int h = bid % p.H, r = bid / p.H;
+  const int wb = wave * 32 + c;
+  const int beam = chunk * NB + wb;
+  const bool valid = beam < p.nb;
+  const size_t row = (size_t)p.H * HD;
+  const bool chains = p.beam_node != nullptr;
+  int32_t *const par_s = dyn_l;
+  int32_t *const bn_s = dyn_l + p.par_words;
+
+  // ---- prologue: parents and beam nodes, S_p, z_p, queries
+  if (chains && wave == 0) {
+    const int32_t *par = p.parent + (size_t)r * p.cap;
+    for (int i = 0; i * 64 < p.cap; ++i) dma4(par + min(i * 64 + lane, p.cap - 1), par_s + i * 64);
+    const int32_t *bnp = p.beam_node + (size_t)r * p.nb;
+    for (int i = 0; i * 64 < NB; ++i) dma4(bnp + min(chunk * NB + i * 64 + lane, p.nb - 1), bn_s + i * 64);
+  }
+  const float *Sg = p.S + ((size_t)r * p.H + h) * HD * HD;
+#pragma unroll
+  for (int i = 0; i < SBLK / 4; ++i) {
+    const int blk = wave * (SBLK / 4) + i;
+    dma16((const char *)Sg + blk * 1024 + 16 * lane, ring[0] + blk * 1024);
+  }
+  if (tid < HD) zs[tid] = p.z[((size_t)r * p.H + h) * HD + tid];
+  const uint16_t *qp = (const uint16_t *)p.q + ((size_t)r * p.nb + (valid ? beam : p.nb - 1)) * row +
+                       (size_t)h * HD;
+  // phi(q) of this lane's dims 16 ks + 8g + u as bf16 hi + lo (about 16
+  // mantissa bits); the dots with z_p and the records use hi + lo as well
+  bf16x8 bhi[KS], blo[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    float v[8];
+    load8<uint16_t>(qp + 16 * ks + 8 * g, v);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float f = phi(v[u]);
+      const __bf16 hi = (__bf16)f;
+      bhi[ks][u] = hi;
+      blo[ks][u] = (__bf16)(f - (float)hi);
+    }
+  }
+  auto fq = [&](int ks, int u) -> float { return (float)bhi[ks][u] + (float)blo[ks][u]; };
+  GR_WAIT_VMCNT(0);
+  __syncthreads();
+
+  // ---- chains: one thread per beam walks its parent links in LDS
+  int depth = 0;
+  if (chains) {
+    if (tid < NB) {
+      int n = chunk * NB + tid < p.nb ? bn_s[tid] : -1;
+      int err = 0;
+      for (int d = 0; d < p.max_depth; ++d) {
+        int id = -1;
+        if (n != -1) {
+          if (n < 0 || n >= p.cap) {
+            err |= GR_DEVERR_PARENT_RANGE;
+            n = -1;
+          } else {
+            id = n;
+            const int pn = par_s[n];
+            if (pn < -1 || pn >= p.cap) { err |= GR_DEVERR_PARENT_RANGE; n = -1; }
+            else if (pn >= n) { err |= GR_DEVERR_PARENT_ORDER; n = -1; }
+            else n = pn;
+          }
+        }
+        ids16[d][tid] = (int16_t)id;
+      }
+      for (int d = p.max_depth; d < GR_MAX_DEPTH; ++d) ids16[d][tid] = -1;
+      if (n != -1) err |= GR_DEVERR_DEPTH;
+      if (err) atomicOr(p.dev_err, err);
+    }
+    __syncthreads();
+    for (int d = 0; d < p.max_depth; ++d)
+      if (__syncthreads_or(tid < NB && ids16[d][tid] >= 0)) depth = d + 1;
+  }
+  const int n_tiles = depth * (NB / KT);
+
+  // record tile k: row t of its K (V) half = the level k / 2 record of
+  // workgroup beam 64 (k % 2) + t (node 0 when the beam has none: unused)
+  auto issue = [&](int k, unsigned char *st) {
+    const int d = k / (NB / KT), bb = k % (NB / KT);
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int blk = wave * BPW + i;                  // blocks [0, NBLK/2): K, then V
+      const int half = blk / (NBLK / 2), hb = blk % (NBLK / 2);
+      const int byte = hb * 1024 + 16 * lane;
+      const int t = byte / RB, pch = (byte % RB) / 16;
+      const int id = ids16[d][bb * KT + t];
+      const uint16_t *src = (const uint16_t *)(half ? p.av : p.ak) +
+                            ((size_t)r * p.cap + (id >= 0 ? id : 0)) * row + (size_t)h * HD +
+                            (pch ^ lswz<HD>(t)) * 8;
+      dma16(src, st + half * TB + hb * 1024);
+    }
+  };
+  if (n_tiles > 0) issue(0, ring[1]);
+  if (n_tiles > 1) issue(1, ring[2]);
+
+  // ---- phi(q)^T S_p and phi(q) . z_p (S_p from stage 0)
+  const float *Ss = reinterpret_cast<const float *>(ring[0]);
+  float den = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) den = fmaf(fq(ks, u), zs[16 * ks + 8 * g + u], den);
+  den = xor32_sum(den);
+  f32x16 O[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[dt][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 ahi, alo;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float sv = Ss[(16 * ks + 8 * g + u) * HD + 32 * dt + c];
+        const __bf16 hi = (__bf16)sv;
+        ahi[u] = hi;
+        alo[u] = (__bf16)(sv - (float)hi);
+      }
+      O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bhi[ks], O[dt], 0, 0, 0);
+      O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, blo[ks], O[dt], 0, 0, 0);
+      O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bhi[ks], O[dt], 0, 0, 0);
+    }
+  }
+
+  // ---- records, tile by tile
+  const int my_bb = wb / KT, t_row = wb % KT;
+  for (int k = 0; k < n_tiles; ++k) {
+    // tile k has landed once at most the tiles issued after it (k + 1, the
+    // ring being NS - 1 = 2 tiles deep) are in flight: BPW DMAs per tile and wave
+    static_assert(NS == 3, "one tile ahead at each wait");
+    if (k + 1 < n_tiles) GR_WAIT_VMCNT(BPW);
+    else GR_WAIT_VMCNT(0);
+    ring_barrier();                            // tile k landed for all; stage of tile k-1 (or S_p) free
+    if (k + NS - 1 < n_tiles) issue(k + NS - 1, ring[(k + NS) % NS]);
+    const unsigned char *st = ring[(k + 1) % NS];
+    const int d = k / (NB / KT), bb = k % (NB / KT);
+    if (bb == my_bb && d < p.max_depth && ids16[d][wb] >= 0) {
+      const unsigned char *kr = st + t_row * RB, *vr = st + TB + t_row * RB;
+      float w = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 k4 = *(const uint4 *)(kr + (((2 * ks + g) ^ lswz<HD>(t_row)) << 4));
+        const float kk[8] = {bf16_lo(k4.x), bf16_hi(k4.x), bf16_lo(k4.y), bf16_hi(k4.y),
+                             bf16_lo(k4.z), bf16_hi(k4.z), bf16_lo(k4.w), bf16_hi(k4.w)};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) w = fmaf(fq(ks, u), phi(kk[u]), w);
+      }
+      w = xor32_sum(w);
+      den += w;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int j = 4 * dt + q4;                   // logical chunk of rows 8j .. 8j+7
+          const uint2 v2 = *(const uint2 *)(vr + ((j ^ lswz<HD>(t_row)) << 4) + 8 * g);
+          O[dt][4 * q4 + 0] = fmaf(w, bf16_lo(v2.x), O[dt][4 * q4 + 0]);
+          O[dt][4 * q4 + 1] = fmaf(w, bf16_hi(v2.x), O[dt][4 * q4 + 1]);
+          O[dt][4 * q4 + 2] = fmaf(w, bf16_lo(v2.y), O[dt][4 * q4 + 2]);
+          O[dt][4 * q4 + 3] = fmaf(w, bf16_hi(v2.y), O[dt][4 * q4 + 3]);
+        }
+    }
+  }
+  if (!valid) return;
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * dt + 8 * q4 + 4 * g;
+      const float o0 = O[dt][4 * q4] * inv, o1 = O[dt][4 * q4 + 1] * inv;
+      const float o2 = O[dt][4 * q4 + 2] * inv, o3 = O[dt][4 * q4 + 3] * inv;
+      if (p.out_f32)
+        *(float4 *)(p.out_f32 + ((size_t)r * p.nb + beam) * row + (size_t)h * HD + d0) = make_float4(o0, o1, o2, o3);
+      if (p.out_bf16)
+        *(uint2 *)(p.out_bf16 + (((size_t)r * p.H + h) * p.nb + beam) * HD + d0) =
+            make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+    }
+}
+
 }  // namespace
 
 hipError_t launch_linear_state(const LinearStateArgs &a, hipStream_t s) {
@@ -468,7 +690,13 @@ hipError_t launch_linear_attn(const LinearAttnArgs &a, hipStream_t s) {
   p.R = a.R; p.H = a.H; p.nb = a.nb; p.cap = a.cap; p.max_depth = a.max_depth;
   p.n_chunk = (a.nb + 127) / 128;
   const dim3 grid((unsigned)((long long)a.R * a.H * p.n_chunk));
-  if (a.dtype == GR_BF16) {
+  p.par_words = 0;
+  if (a.dtype == GR_BF16 && (a.beam_node == nullptr || a.cap <= kLinRingNodes)) {
+    p.par_words = a.beam_node ? (a.cap + 63) / 64 * 64 : 0;
+    const size_t dyn = (size_t)(p.par_words + 128) * sizeof(int32_t);
+    if (a.hd == 64) hipLaunchKernelGGL(linear_ring_bf16_kernel<64>, grid, dim3(256), dyn, s, p);
+    else hipLaunchKernelGGL(linear_ring_bf16_kernel<32>, grid, dim3(256), dyn, s, p);
+  } else if (a.dtype == GR_BF16) {
     if (a.hd == 64) hipLaunchKernelGGL(linear_attn_bf16_kernel<64>, grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL(linear_attn_bf16_kernel<32>, grid, dim3(256), 0, s, p);
   } else {

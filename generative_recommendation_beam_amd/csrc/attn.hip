@@ -582,8 +582,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
 }
 
 // The runs of a split window, merged per (request, head, beam) with their
-// log-sum-exp weights: m = max_s m_s, w_s = 2^(m_s - m),
-// o = sum_s w_s o_s / sum_s w_s l_s.  One thread per 16-byte chunk of a row.
+// log-sum-exp weights: m = max_s m_s, w_s = 2^(m_s - m) / sum_s' 2^(m_s' - m) l_s',
+// o = sum_s w_s o_s.  One workgroup per (request, head, MB beams); thread t
+// serves beam t / CH and, in turn, the runs t % CH, t % CH + CH, ... (the
+// weights, reduced across the CH threads of a beam and kept in LDS) and the
+// 16-byte chunk t % CH of the beam's row (summed over the runs, four runs'
+// loads at a time).
 struct MergeP {
   const float *part;
   float *out_f32;
@@ -593,38 +597,58 @@ struct MergeP {
 
 template <int HD>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeP p) {
-  constexpr int CH = HD / 4;
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long long)p.R * p.H * p.nb * CH) return;
-  const int ch = (int)(idx % CH);
-  long long t = idx / CH;
-  const int beam = (int)(t % p.nb);
-  t /= p.nb;
-  const int h = (int)(t % p.H), r = (int)(t / p.H);
+  constexpr int CH = HD / 4, MB = 256 / CH;           // chunks per row, beams per workgroup
+  __shared__ float wts[MB][kAttnSplitTarget];         // attn_split keeps the runs at or below this
+  const int n_bt = (p.nb + MB - 1) / MB;
+  int bid = blockIdx.x;
+  const int bt = bid % n_bt;
+  bid /= n_bt;
+  const int h = bid % p.H, r = bid / p.H;
+  const int tid = threadIdx.x, b = tid / CH, li = tid % CH;
+  const int beam = bt * MB + b;
+  const bool valid = beam < p.nb;
+  const int bq = valid ? beam : p.nb - 1;
   const size_t unit = ((size_t)r * p.H + h) * p.n_split;
   const float2 *ml = reinterpret_cast<const float2 *>(p.part + (size_t)p.R * p.H * p.n_split * p.nb_pad * HD);
   float m = -__builtin_inff();
-  for (int sp = 0; sp < p.n_split; ++sp) m = fmaxf(m, ml[(unit + sp) * p.nb_pad + beam].x);
+  for (int sp = li; sp < p.n_split; sp += CH) m = fmaxf(m, ml[(unit + sp) * p.nb_pad + bq].x);
+#pragma unroll
+  for (int o = CH / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   float l = 0.f;
+  for (int sp = li; sp < p.n_split; sp += CH) {
+    const float2 e = ml[(unit + sp) * p.nb_pad + bq];
+    l = fmaf(fast_exp2(e.x - m), e.y, l);
+  }
+#pragma unroll
+  for (int o = CH / 2; o > 0; o >>= 1) l += __shfl_xor(l, o);
+  const float inv = 1.f / l;
+  for (int sp = li; sp < p.n_split; sp += CH) wts[b][sp] = fast_exp2(ml[(unit + sp) * p.nb_pad + bq].x - m) * inv;
+  __syncthreads();
+  const size_t run = (size_t)p.nb_pad * HD;
+  const float *src = p.part + (unit * p.nb_pad + bq) * HD + li * 4;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int sp = 0; sp < p.n_split; ++sp) {
-    const size_t slot = (unit + sp) * p.nb_pad + beam;
-    const float2 e = ml[slot];
-    const float w = fast_exp2(e.x - m);
-    const float4 v = *(const float4 *)(p.part + slot * HD + ch * 4);
-    l = fmaf(w, e.y, l);
+  auto add = [&](float w, float4 v) {
     o.x = fmaf(w, v.x, o.x);
     o.y = fmaf(w, v.y, o.y);
     o.z = fmaf(w, v.z, o.z);
     o.w = fmaf(w, v.w, o.w);
+  };
+  int sp = 0;
+  for (; sp + 4 <= p.n_split; sp += 4) {
+    const float4 v0 = *(const float4 *)(src + sp * run), v1 = *(const float4 *)(src + (sp + 1) * run);
+    const float4 v2 = *(const float4 *)(src + (sp + 2) * run), v3 = *(const float4 *)(src + (sp + 3) * run);
+    add(wts[b][sp], v0);
+    add(wts[b][sp + 1], v1);
+    add(wts[b][sp + 2], v2);
+    add(wts[b][sp + 3], v3);
   }
-  const float inv = 1.f / l;
+  for (; sp < p.n_split; ++sp) add(wts[b][sp], *(const float4 *)(src + sp * run));
+  if (!valid) return;
   if (p.out_f32)
-    *(float4 *)(p.out_f32 + ((size_t)r * p.nb + beam) * p.H * HD + (size_t)h * HD + ch * 4) =
-        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    *(float4 *)(p.out_f32 + ((size_t)r * p.nb + beam) * p.H * HD + (size_t)h * HD + li * 4) = o;
   if (p.out_bf16)
-    *(uint2 *)(p.out_bf16 + (((size_t)r * p.H + h) * p.nb + beam) * HD + ch * 4) =
-        make_uint2(pack_bf16x2(o.x * inv, o.y * inv), pack_bf16x2(o.z * inv, o.w * inv));
+    *(uint2 *)(p.out_bf16 + (((size_t)r * p.H + h) * p.nb + beam) * HD + li * 4) =
+        make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
 }
 
 // ------------------------------------------------------------------ fp32
@@ -786,8 +810,8 @@ hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
   MergeP m;
   m.part = a.split_ws; m.out_f32 = a.out_f32; m.out_bf16 = (uint16_t *)a.out_lowp;
   m.R = a.R; m.H = a.H; m.nb = a.nb; m.nb_pad = p.nb_pad; m.n_split = sp.n_split;
-  const long long n = (long long)a.R * a.H * a.nb * (HD / 4);
-  hipLaunchKernelGGL(attn_merge_kernel<HD>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, m);
+  const long long n_wg = (long long)a.R * a.H * ((a.nb + 256 / (HD / 4) - 1) / (256 / (HD / 4)));
+  hipLaunchKernelGGL(attn_merge_kernel<HD>, dim3((unsigned)n_wg), dim3(256), 0, s, m);
   return hipGetLastError();
 }
 

@@ -13,6 +13,8 @@ gr_linear_decode_step) against the oracle (oracle/linear.py).
   sampled requests.
 * A chain longer than max_depth raises GR_DEVERR_DEPTH; two calls give
   bit-identical outputs.
+* Both bf16 forms: arenas of up to 4096 nodes (records through the LDS DMA
+  ring) and larger ones (per-lane loads).
 """
 import numpy as np
 import pytest
@@ -161,3 +163,24 @@ def test_linear_depth_error_and_determinism():
         outs.append(HN.results_to_host(buf))
     for key in ("score", "token", "parent", "attn", "cand"):
         np.testing.assert_array_equal(outs[0][key], outs[1][key])
+
+
+def test_linear_attn_large_arena():
+    """Arenas above 4096 nodes per request take the per-lane-load form of the
+    bf16 kernel instead of the ring form; same results."""
+    cfg = SMALL["beam100_small"]
+    announce("gr_linear_attn, 5000-node arena (per-lane loads)")
+    x = W.make_step_inputs(cfg)
+    outs = []
+    for capacity in (None, 5000):
+        ds = HN.upload_step(x, capacity=capacity)
+        S, z = HN.linear_state(ds)
+        out = torch.empty((cfg.R, cfg.n_in, cfg.D), dtype=torch.float32, device="cuda")
+        L.gr_linear_attn(ds.shape, S, z, ds.q, ds.n_beams, ds.trie, ds.beam_node, out, ds.dev_err)
+        torch.cuda.synchronize()
+        assert int(ds.dev_err.item()) == 0
+        outs.append(out.cpu().numpy())
+    ak, av, par = arena_of(x)
+    ref = LA.attend_linear_shared(x.prompt_k, x.prompt_v, x.q, par, ak, av, x.beam_node, cfg.window)
+    assert_close(outs[0], ref, cfg.dtype, "linear attention, ring form")
+    assert_close(outs[1], ref, cfg.dtype, "linear attention, per-lane form")

@@ -103,14 +103,21 @@ size_t attn_split_ws_bytes(const gr_shape *s, int n_beams) {
 }
 
 // The bf16 codebook step feeds the attention output to the projection MFMA
-// in bf16.  Its rounding perturbs a logit by about 2^-9 |o| |W|; over a long
-// window o is an average of many values and the perturbation stays far below
-// the near-tie scale of the selection, but with a handful of keys |o| can be
-// as large as one value row.  Windows shorter than this take the fp32 path
-// (fp32 o, fp32 projection, scoring from fp32 logits).
+// in bf16.  Its rounding perturbs a logit by about 2^-9 rms(W) |o| (RMS over
+// the codes).  o is an average of the window's value rows, so |o| grows like
+// sqrt(D / Lw) (D = H * head_dim): over a long window the perturbation stays
+// far below the near-tie scale of the selection, but with a handful of keys
+// |o| can be as large as one value row, and a wide model with a short window
+// (D = 4096, 80 keys) swaps picks 1.2e-3 apart.  The bf16 projection is kept
+// for windows of at least 64 keys and at least D / 8 keys (the ratio of a
+// 512-wide model at 64 keys); other shapes take the fp32 path (fp32 o, fp32
+// projection, scoring from fp32 logits).
 constexpr int kMfmaLogitsMinWindow = 64;
+constexpr int kMfmaLogitsWidthPerKey = 8;
 bool use_mfma_logits(const gr_shape *s, int vocab) {
-  return s->dtype == GR_BF16 && vocab == 256 && prompt_window(s) >= kMfmaLogitsMinWindow;
+  const int Lw = prompt_window(s);
+  return s->dtype == GR_BF16 && vocab == 256 && Lw >= kMfmaLogitsMinWindow &&
+         (long long)Lw * kMfmaLogitsWidthPerKey >= (long long)s->H * s->head_dim;
 }
 
 struct DecodeLayout {

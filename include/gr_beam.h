@@ -191,11 +191,13 @@ gr_status gr_beam_topk(int32_t R, int32_t n_in, int32_t vocab, int32_t k,
  *   W: [vocab][H*head_dim] dtype (row t = code t's projection vector).
  *   vocab = 1 is scalar scoring (TransRetrieval): score = o . W[0] (+ prior),
  *   flags must be 0.
- *   Precision: for bf16 with vocab = 256 and a prompt window of at least 64
- *   keys, o enters the projection (a bf16 MFMA) rounded to bf16, which moves
- *   a logit by about 2^-9 |o| |W|: negligible when o averages many keys.
- *   Shorter windows, where a few keys can dominate o, use fp32 o and an fp32
- *   projection instead (slower, same results up to fp32 rounding).
+ *   Precision: for bf16 with vocab = 256 and a prompt window Lw of at least
+ *   64 keys and at least H*head_dim / 8 keys, o enters the projection (a
+ *   bf16 MFMA) rounded to bf16, which moves a logit by about
+ *   2^-9 rms(W) |o|: negligible when o averages many keys.  Shorter windows,
+ *   where a few keys can dominate o (|o| grows like sqrt(H*head_dim / Lw)),
+ *   use fp32 o and an fp32 projection instead (slower, same results up to
+ *   fp32 rounding).
  *   attn_out: optional [R][n_beams][H*head_dim] fp32 copy of the attention
  *   output; cand_out: optional [R][n_beams][vocab] fp32 copy of c.
  *   ws: at least gr_decode_workspace_size(shape, n_beams, vocab, beam_width)

@@ -164,6 +164,29 @@ def test_workspace_sizes():
     assert L.status_string(L.GR_ERR_CAPACITY).startswith("append")
 
 
+def test_projection_path_by_window_and_width():
+    """The bf16 codebook MFMA (bf16 copy of o in the workspace) needs a window
+    of at least 64 keys and at least D / 8 keys; other bf16 shapes keep o and
+    the logits in fp32.  Seen through the workspace size, with 32 beams and
+    enough requests that the attention does not split its windows."""
+    def path(**kw):
+        H = kw.pop("H", 8)
+        sh = shape(R=-(-384 // H), H=H, **kw)
+        rows = sh.R * 32
+        D = sh.H * sh.head_dim
+        n = L.gr_decode_workspace_size(sh, 32, 256, 32)
+        fp32 = rows * D * 4 + rows * 256 * 4
+        return "fp32" if n >= fp32 else "bf16"
+    assert path(prompt_len=600) == "bf16"                        # D = 512
+    assert path(prompt_len=64) == "bf16"
+    assert path(prompt_len=63) == "fp32"
+    assert path(prompt_len=600, window=40) == "fp32"
+    assert path(H=64, prompt_len=600) == "bf16"                  # D = 4096, 600 >= 512 keys
+    assert path(H=64, prompt_len=511) == "fp32"
+    assert path(H=64, prompt_len=2048, window=512) == "bf16"
+    assert path(H=128, head_dim=32, prompt_len=80) == "fp32"
+
+
 def test_code_table_host_errors():
     sh = shape()
     call = lambda **kw: L._lib.gr_code_table(

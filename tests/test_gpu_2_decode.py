@@ -1,7 +1,8 @@
 """GPU parity of gr_decode_step (the whole hot path) against the oracle.
 
 * Reduced versions of every workload family (beam 50/100/512 with windows,
-  scalar scoring), compared in full: attention outputs, all candidate scores,
+  scalar scoring) and the widest model the boundary takes (D = 4096),
+  compared in full: attention outputs, all candidate scores,
   the selected scores (max|err|/RMS bar), the index rule and exact
   self-consistency of the selection with the GPU's own candidate scores.
 * The tiny fp32 workload run end to end for three chained steps, the trie grown
@@ -45,6 +46,17 @@ SMALL = {
     "one_token_prompt": W.reduced(CF["beam50_p600"], R=2, Lp=1, level_sizes=(30, 50)),
     "one_token_window": W.reduced(CF["beam50_p600"], R=2, Lp=100, window=1, level_sizes=(30, 50)),
     "single_beam": W.reduced(CF["beam50_p600"], R=3, Lp=64, n_in=1, k=1, level_sizes=(1, 1)),
+    # the widest model the boundary takes: D = H * d = 4096 (64 heads of 64,
+    # 128 heads of 32; bf16 and fp32).  Windows below D / 8 keys take the fp32
+    # projection; the 600-key window keeps the bf16 codebook MFMA.
+    "max_width_long_window": W.reduced(CF["beam100_p600"], R=1, Lp=600, H=64, d=64, n_in=32, k=32,
+                                       level_sizes=(20, 32)),
+    "max_width_h64_d64": W.reduced(CF["beam100_p600"], R=2, Lp=96, H=64, d=64, n_in=40, k=40,
+                                   level_sizes=(30, 40)),
+    "max_width_h128_d32": W.reduced(CF["beam100_p600"], R=2, Lp=80, H=128, d=32, n_in=24, k=24,
+                                    level_sizes=(20, 24, 24)),
+    "max_width_f32": W.reduced(CF["beam100_p600"], R=1, Lp=50, H=128, d=32, n_in=16, k=16,
+                               level_sizes=(9, 16), dtype="f32"),
 }
 
 

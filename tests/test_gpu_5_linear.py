@@ -7,10 +7,10 @@ gr_linear_decode_step) against the oracle (oracle/linear.py).
 * gr_linear_attn against the oracle's shared-state form, for bf16 and fp32
   workloads, chains of 0..8 records, a one-token prompt and window.
 * gr_linear_decode_step end to end on reduced versions of every workload
-  family, compared in full like the softmax step: attention outputs, all
-  candidate scores, selected scores (bar), the index rule and the exact
-  self-consistency of the selection; and the headline shape at full size on
-  sampled requests.
+  family and the widest model (D = 4096), compared in full like the softmax
+  step: attention outputs, all candidate scores, selected scores (bar), the
+  index rule and the exact self-consistency of the selection; and the
+  headline shape at full size on sampled requests.
 * A chain longer than max_depth raises GR_DEVERR_DEPTH; two calls give
   bit-identical outputs.
 * Both bf16 forms: arenas of up to 4096 nodes (records through the LDS DMA
@@ -100,7 +100,9 @@ def test_linear_attn(name):
 
 
 STEP_CASES = ["beam50_small", "beam100_small", "beam100_flat_prior", "beam512_window_small", "beam130_two_groups",
-              "scalar_small", "f32_beam16", "depth8_chains", "one_token_window", "single_beam"]
+              "scalar_small", "f32_beam16", "depth8_chains", "one_token_window", "single_beam",
+              "max_width_h64_d64", "max_width_h128_d32", "max_width_f32",
+              "max_width_long_window"]
 
 
 @pytest.mark.parametrize("name", STEP_CASES)

@@ -49,6 +49,10 @@ SMALL = {
     # the widest model the boundary takes: D = H * d = 4096 (64 heads of 64,
     # 128 heads of 32; bf16 and fp32).  Windows below D / 8 keys take the fp32
     # projection; the 600-key window keeps the bf16 codebook MFMA.
+    # the largest selection a decode step takes: 1024 beams (8 groups of 128)
+    # into k = GR_MAX_K = 2048, 8 x 2048 partial entries in the final merge
+    "max_k_1024_beams": W.reduced(CF["beam512_p2048_w512"], R=1, Lp=128, window=0, H=2, n_in=1024, k=2048,
+                                  depth=2, level_sizes=(256, 1024)),
     "max_width_long_window": W.reduced(CF["beam100_p600"], R=1, Lp=600, H=64, d=64, n_in=32, k=32,
                                        level_sizes=(20, 32)),
     "max_width_h64_d64": W.reduced(CF["beam100_p600"], R=2, Lp=96, H=64, d=64, n_in=40, k=40,

@@ -102,7 +102,7 @@ def test_linear_attn(name):
 STEP_CASES = ["beam50_small", "beam100_small", "beam100_flat_prior", "beam512_window_small", "beam130_two_groups",
               "scalar_small", "f32_beam16", "depth8_chains", "one_token_window", "single_beam",
               "max_width_h64_d64", "max_width_h128_d32", "max_width_f32",
-              "max_width_long_window"]
+              "max_width_long_window", "max_k_1024_beams"]
 
 
 @pytest.mark.parametrize("name", STEP_CASES)

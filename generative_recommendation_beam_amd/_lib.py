@@ -103,11 +103,17 @@ def status_string(status: int) -> str:
 
 
 def _ptr(t) -> Optional[int]:
-    """Device (or host) address of a tensor, an int address, or None."""
+    """Address of a device tensor, an int address (passed as is), or None.
+    Every pointer of the C ABI is a device address of dense data: a host
+    tensor or a strided view is refused here rather than handed to a kernel."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError(f"a device tensor is expected, got one on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"a contiguous tensor is expected, got strides {tuple(t.stride())}")
     return t.data_ptr()
 
 

@@ -5,6 +5,8 @@
   anything is enqueued (no HIP call is made, so these run without a GPU; the
   pointers passed are never dereferenced).
 * Workspace sizing is consistent with the documented layout.
+* The binding refuses host tensors (and, on a GPU, strided views) before
+  calling into the library.
 """
 import ctypes
 import os
@@ -286,3 +288,21 @@ def test_linear_host_errors():
     assert ds(vocab=3) == L.GR_ERR_UNSUPPORTED
     assert ds(k=25601) == L.GR_ERR_K_TOO_LARGE
     assert ds(ws_bytes=need - 1) == L.GR_ERR_WORKSPACE
+
+
+def test_binding_refuses_host_and_strided_tensors():
+    """The binding passes device addresses of dense data only: a host tensor
+    or a strided view raises before the C entry point is called."""
+    import torch
+    sh = shape()
+    host = torch.zeros(16, dtype=torch.float32)
+    with pytest.raises(ValueError, match="device tensor"):
+        L.gr_linear_state(sh, host, host, host, host)
+
+
+@pytest.mark.gpu
+def test_binding_refuses_strided_tensors():
+    import torch
+    dev = torch.zeros((4, 4), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="contiguous"):
+        L.gr_linear_state(shape(), dev.t(), dev, dev, dev)

@@ -11,7 +11,8 @@ gr_linear_decode_step) against the oracle (oracle/linear.py).
   step: attention outputs, all candidate scores, selected scores (bar), the
   index rule and the exact self-consistency of the selection; and the
   headline shape at full size on sampled requests.
-* A chain longer than max_depth raises GR_DEVERR_DEPTH; two calls give
+* A chain longer than max_depth raises GR_DEVERR_DEPTH, corrupt parents
+  GR_DEVERR_PARENT_ORDER / _RANGE (every form); two calls give
   bit-identical outputs.
 * Both bf16 forms: arenas of up to 4096 nodes (records through the LDS DMA
   ring) and larger ones (per-lane loads).
@@ -186,3 +187,29 @@ def test_linear_attn_large_arena():
     ref = LA.attend_linear_shared(x.prompt_k, x.prompt_v, x.q, par, ak, av, x.beam_node, cfg.window)
     assert_close(outs[0], ref, cfg.dtype, "linear attention, ring form")
     assert_close(outs[1], ref, cfg.dtype, "linear attention, per-lane form")
+
+
+@pytest.mark.parametrize("capacity,dtype", [(None, "bf16"), (5000, "bf16"), (None, "f32")])
+def test_linear_attn_device_errors(capacity, dtype):
+    """Corrupt ancestry in each form (ring, per-lane loads, fp32): a parent
+    newer than its child raises GR_DEVERR_PARENT_ORDER, a beam node outside
+    the arena GR_DEVERR_PARENT_RANGE; nothing is read out of bounds."""
+    cfg = W.reduced(CF["beam100_p600"], R=2, Lp=40, H=2, n_in=6, k=6, level_sizes=(3, 6, 6), dtype=dtype)
+    announce(f"gr_linear_attn device errors, capacity {capacity}, {dtype}")
+    x = W.make_step_inputs(cfg)
+    out = torch.empty((cfg.R, cfg.n_in, cfg.D), dtype=torch.float32, device="cuda")
+
+    def run(ds):
+        S, z = HN.linear_state(ds)
+        ds.dev_err.zero_()
+        L.gr_linear_attn(ds.shape, S, z, ds.q, ds.n_beams, ds.trie, ds.beam_node, out, ds.dev_err)
+        torch.cuda.synchronize()
+        return int(ds.dev_err.item())
+
+    ds = HN.upload_step(x, capacity=capacity)
+    assert run(ds) == 0
+    ds.parent[1, 9] = 12                         # a level-3 record gets a newer parent
+    assert run(ds) & L.GR_DEVERR_PARENT_ORDER
+    ds = HN.upload_step(x, capacity=capacity)
+    ds.beam_node[0, 2] = 100000                  # outside the arena
+    assert run(ds) == L.GR_DEVERR_PARENT_RANGE

@@ -12,6 +12,8 @@
   (no debug outputs), checked on sampled requests that the oracle computes in
   full, plus a second call with debug outputs for attention and candidates.
 * Determinism: two calls give bit-identical outputs.
+* The attention-only and selection-only stage bits, called one after the
+  other, give bit-identical results to one whole call.
 """
 import numpy as np
 import pytest
@@ -223,4 +225,27 @@ def test_determinism():
         torch.cuda.synchronize()
         outs.append(HN.results_to_host(buf))
     for key in outs[0]:
+        np.testing.assert_array_equal(outs[0][key], outs[1][key], err_msg=key)
+
+
+@pytest.mark.parametrize("name", ["beam100_small", "one_token_window", "scalar_small", "f32_beam16"])
+def test_stage_split_equals_whole(name):
+    """GR_STEP_ATTENTION then GR_STEP_SELECTION on the same workspace (the
+    split the benchmark times) gives bit-identical results to one whole call,
+    on the bf16 codebook MFMA, the fp32 projection and scalar scoring."""
+    cfg = SMALL[name]
+    announce(f"gr_decode_step stage split {name}")
+    x = W.make_step_inputs(cfg)
+    ds = HN.upload_step(x)
+    outs = []
+    for stages in ([0], [L.GR_STEP_ATTENTION, L.GR_STEP_SELECTION]):
+        buf = HN.decode_buffers(ds, debug_outputs=True)
+        for st in stages:
+            L.gr_decode_step(ds.shape, ds.prompt_k, ds.prompt_v, ds.q, ds.n_beams, ds.trie, ds.beam_node, ds.W,
+                             ds.vocab, ds.prior, ds.k, ds.flags | st, buf.score, buf.token, buf.parent, buf.attn,
+                             buf.cand, buf.ws, buf.ws_bytes, ds.dev_err)
+        torch.cuda.synchronize()
+        outs.append(HN.results_to_host(buf))
+    assert int(ds.dev_err.item()) == 0
+    for key in ("score", "token", "parent", "attn", "cand"):
         np.testing.assert_array_equal(outs[0][key], outs[1][key], err_msg=key)

@@ -12,8 +12,8 @@ gr_linear_decode_step) against the oracle (oracle/linear.py).
   index rule and the exact self-consistency of the selection; and the
   headline shape at full size on sampled requests.
 * A chain longer than max_depth raises GR_DEVERR_DEPTH, corrupt parents
-  GR_DEVERR_PARENT_ORDER / _RANGE (every form); two calls give
-  bit-identical outputs.
+  GR_DEVERR_PARENT_ORDER / _RANGE (every form); two calls, and a call split
+  by the stage bits, give bit-identical outputs.
 * Both bf16 forms: arenas of up to 4096 nodes (records through the LDS DMA
   ring) and larger ones (per-lane loads).
 """
@@ -213,3 +213,26 @@ def test_linear_attn_device_errors(capacity, dtype):
     ds = HN.upload_step(x, capacity=capacity)
     ds.beam_node[0, 2] = 100000                  # outside the arena
     assert run(ds) == L.GR_DEVERR_PARENT_RANGE
+
+
+@pytest.mark.parametrize("name", ["beam100_small", "one_token_window"])
+def test_linear_stage_split_equals_whole(name):
+    """The two stage bits of gr_linear_decode_step, called one after the
+    other, give bit-identical results to one whole call."""
+    cfg = SMALL[name]
+    announce(f"gr_linear_decode_step stage split {name}")
+    x = W.make_step_inputs(cfg)
+    ds = HN.upload_step(x)
+    S, z = HN.linear_state(ds)
+    outs = []
+    for stages in ([0], [L.GR_STEP_ATTENTION, L.GR_STEP_SELECTION]):
+        buf = HN.decode_buffers(ds, debug_outputs=True)
+        for st in stages:
+            L.gr_linear_decode_step(ds.shape, S, z, ds.q, ds.n_beams, ds.trie, ds.beam_node, ds.W, ds.vocab,
+                                    ds.prior, ds.k, ds.flags | st, buf.score, buf.token, buf.parent, buf.attn,
+                                    buf.cand, buf.ws, buf.ws_bytes, ds.dev_err)
+        torch.cuda.synchronize()
+        outs.append(HN.results_to_host(buf))
+    assert int(ds.dev_err.item()) == 0
+    for key in ("score", "token", "parent", "attn", "cand"):
+        np.testing.assert_array_equal(outs[0][key], outs[1][key], err_msg=key)

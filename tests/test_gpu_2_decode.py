@@ -12,6 +12,7 @@
   (no debug outputs), checked on sampled requests that the oracle computes in
   full, plus a second call with debug outputs for attention and candidates.
 * Determinism: two calls give bit-identical outputs.
+* Two batches in flight on two streams match one call alone, bit for bit.
 * The attention-only and selection-only stage bits, called one after the
   other, give bit-identical results to one whole call.
 """
@@ -249,3 +250,30 @@ def test_stage_split_equals_whole(name):
     assert int(ds.dev_err.item()) == 0
     for key in ("score", "token", "parent", "attn", "cand"):
         np.testing.assert_array_equal(outs[0][key], outs[1][key], err_msg=key)
+
+
+def test_two_streams_concurrent():
+    """Two batches in flight on two streams (each with its own workspace and
+    outputs, as the benchmark runs them) give the results of one call alone,
+    bit for bit: the library keeps no state between calls."""
+    cfg = SMALL["beam100_small"]
+    announce("gr_decode_step on two streams at once")
+    x = W.make_step_inputs(cfg)
+    ds = HN.upload_step(x)
+    ref = HN.decode_buffers(ds, debug_outputs=True)
+    HN.decode_step(ds, ref)
+    torch.cuda.synchronize()
+    want = HN.results_to_host(ref)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    bufs = [[HN.decode_buffers(ds, debug_outputs=True) for _ in range(3)] for _ in streams]
+    torch.cuda.synchronize()
+    for i in range(3):
+        for s, b in zip(streams, bufs):
+            HN.decode_step(ds, b[i], stream=s)
+    torch.cuda.synchronize()
+    assert int(ds.dev_err.item()) == 0
+    for b in bufs:
+        for buf in b:
+            got = HN.results_to_host(buf)
+            for key in ("score", "token", "parent", "attn", "cand"):
+                np.testing.assert_array_equal(got[key], want[key], err_msg=key)

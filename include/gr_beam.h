@@ -36,8 +36,10 @@
  *     caller.  The library never allocates, frees or synchronises; it keeps no
  *     global state and is re-entrant across streams.  Work is enqueued on
  *     `stream` and the call returns at once.
- *   - The return value reports host-checkable errors only.  When it is not
- *     GR_OK nothing was enqueued and no output was touched.
+ *   - The return value reports host-checkable errors, plus GR_ERR_HIP for a
+ *     launch the HIP runtime refused.  With any other status nothing was
+ *     enqueued and no output was touched; after GR_ERR_HIP, launches that
+ *     the same call made earlier may have been enqueued.
  *   - Data-dependent errors are found on the device and OR-ed into *dev_err
  *     (a device int32 the caller zeroes before the call and reads after
  *     synchronising).  Outputs are undefined when it is nonzero.

@@ -449,13 +449,18 @@ constexpr int kLinRingNodes = 4096;
 
 // bf16, ring form: the same computation as linear_attn_bf16_kernel, with the
 // record rows gathered by LDS DMA (global_load_lds) through a 3-stage ring of
-// 64-beam tiles, as the softmax kernel streams its records; the per-lane
-// loads of the plain form gather 128-byte rows with 16-byte pieces from 32
-// rows per instruction and cost about 15 us per chain level at the headline
-// shape.  Stream order, each wait an exact vmcnt: the parent array and the
+// tiles, as the softmax kernel streams its records; the per-lane loads of the
+// plain form gather 128-byte rows with 16-byte pieces from 32 rows per
+// instruction and cost about 15 us per chain level at the headline shape.
+// Stream order, each wait an exact vmcnt: the parent array and the
 // workgroup's beam nodes (wave 0), S_p into stage 0 (and the queries, loaded
 // to registers); then, once the chains are resolved in LDS, record tile k
-// (level k / 2, beams 64 (k % 2) ..) into stage (k + 1) % 3, two tiles ahead.
+// into stage (k + 1) % 3, two tiles ahead.  Tile k holds the key rows (k
+// even) or the value rows (k odd) of the level k / 2 records of all 128
+// beams, so that every wave folds every tile: a key tile gives each beam its
+// record's weight, the value tile after it adds the weighted values (tiles of
+// 64 beams holding both halves left half the waves idle at each tile and
+// took 6 % longer).
 // Stage 0 is free for records once the shared-state MFMAs have read S_p.
 // Record rows are XOR-swizzled so that 16 lanes reading 16 consecutive rows
 // at one logical 16-byte chunk hit 16 distinct bank slots.
@@ -561,21 +566,22 @@ __global__ __launch_bounds__(256) void linear_ring_bf16_kernel(LinP p) {
   }
   const int n_tiles = depth * (NB / KT);
 
-  // record tile k: row t of its K (V) half = the level k / 2 record of
-  // workgroup beam 64 (k % 2) + t (node 0 when the beam has none: unused)
+  // record tile k: the key (k even) or value (k odd) rows of the level k / 2
+  // records, row t for workgroup beam t (node 0 when the beam has none:
+  // unused), so that every wave folds every tile
+  static_assert(NB * RB == 2 * TB, "one half-record of every beam fills a stage");
   auto issue = [&](int k, unsigned char *st) {
-    const int d = k / (NB / KT), bb = k % (NB / KT);
+    const int d = k >> 1, half = k & 1;
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
-      const int blk = wave * BPW + i;                  // blocks [0, NBLK/2): K, then V
-      const int half = blk / (NBLK / 2), hb = blk % (NBLK / 2);
-      const int byte = hb * 1024 + 16 * lane;
+      const int blk = wave * BPW + i;
+      const int byte = blk * 1024 + 16 * lane;
       const int t = byte / RB, pch = (byte % RB) / 16;
-      const int id = ids16[d][bb * KT + t];
+      const int id = ids16[d][t];
       const uint16_t *src = (const uint16_t *)(half ? p.av : p.ak) +
                             ((size_t)r * p.cap + (id >= 0 ? id : 0)) * row + (size_t)h * HD +
                             (pch ^ lswz<HD>(t)) * 8;
-      dma16(src, st + half * TB + hb * 1024);
+      dma16(src, st + blk * 1024);
     }
   };
   if (n_tiles > 0) issue(0, ring[1]);
@@ -611,7 +617,7 @@ __global__ __launch_bounds__(256) void linear_ring_bf16_kernel(LinP p) {
   }
 
   // ---- records, tile by tile
-  const int my_bb = wb / KT, t_row = wb % KT;
+  float w_lev = 0.f;                           // weight of the level whose values come next
   for (int k = 0; k < n_tiles; ++k) {
     // tile k has landed once at most the tiles issued after it (k + 1, the
     // ring being NS - 1 = 2 tiles deep) are in flight: BPW DMAs per tile and wave
@@ -620,32 +626,35 @@ __global__ __launch_bounds__(256) void linear_ring_bf16_kernel(LinP p) {
     else GR_WAIT_VMCNT(0);
     ring_barrier();                            // tile k landed for all; stage of tile k-1 (or S_p) free
     if (k + NS - 1 < n_tiles) issue(k + NS - 1, ring[(k + NS) % NS]);
-    const unsigned char *st = ring[(k + 1) % NS];
-    const int d = k / (NB / KT), bb = k % (NB / KT);
-    if (bb == my_bb && d < p.max_depth && ids16[d][wb] >= 0) {
-      const unsigned char *kr = st + t_row * RB, *vr = st + TB + t_row * RB;
-      float w = 0.f;
+    const unsigned char *rr = ring[(k + 1) % NS] + wb * RB;
+    const int d = k >> 1;
+    if (d < p.max_depth && ids16[d][wb] >= 0) {
+      if ((k & 1) == 0) {                      // key row: the record's weight
+        float w = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 k4 = *(const uint4 *)(kr + (((2 * ks + g) ^ lswz<HD>(t_row)) << 4));
-        const float kk[8] = {bf16_lo(k4.x), bf16_hi(k4.x), bf16_lo(k4.y), bf16_hi(k4.y),
-                             bf16_lo(k4.z), bf16_hi(k4.z), bf16_lo(k4.w), bf16_hi(k4.w)};
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 k4 = *(const uint4 *)(rr + (((2 * ks + g) ^ lswz<HD>(wb)) << 4));
+          const float kk[8] = {bf16_lo(k4.x), bf16_hi(k4.x), bf16_lo(k4.y), bf16_hi(k4.y),
+                               bf16_lo(k4.z), bf16_hi(k4.z), bf16_lo(k4.w), bf16_hi(k4.w)};
 #pragma unroll
-        for (int u = 0; u < 8; ++u) w = fmaf(fq(ks, u), phi(kk[u]), w);
-      }
-      w = xor32_sum(w);
-      den += w;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int j = 4 * dt + q4;                   // logical chunk of rows 8j .. 8j+7
-          const uint2 v2 = *(const uint2 *)(vr + ((j ^ lswz<HD>(t_row)) << 4) + 8 * g);
-          O[dt][4 * q4 + 0] = fmaf(w, bf16_lo(v2.x), O[dt][4 * q4 + 0]);
-          O[dt][4 * q4 + 1] = fmaf(w, bf16_hi(v2.x), O[dt][4 * q4 + 1]);
-          O[dt][4 * q4 + 2] = fmaf(w, bf16_lo(v2.y), O[dt][4 * q4 + 2]);
-          O[dt][4 * q4 + 3] = fmaf(w, bf16_hi(v2.y), O[dt][4 * q4 + 3]);
+          for (int u = 0; u < 8; ++u) w = fmaf(fq(ks, u), phi(kk[u]), w);
         }
+        w = xor32_sum(w);
+        den += w;
+        w_lev = w;
+      } else {                                 // value row, weighted
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int j = 4 * dt + q4;                 // logical chunk of rows 8j .. 8j+7
+            const uint2 v2 = *(const uint2 *)(rr + ((j ^ lswz<HD>(wb)) << 4) + 8 * g);
+            O[dt][4 * q4 + 0] = fmaf(w_lev, bf16_lo(v2.x), O[dt][4 * q4 + 0]);
+            O[dt][4 * q4 + 1] = fmaf(w_lev, bf16_hi(v2.x), O[dt][4 * q4 + 1]);
+            O[dt][4 * q4 + 2] = fmaf(w_lev, bf16_lo(v2.y), O[dt][4 * q4 + 2]);
+            O[dt][4 * q4 + 3] = fmaf(w_lev, bf16_hi(v2.y), O[dt][4 * q4 + 3]);
+          }
+      }
     }
   }
   if (!valid) return;

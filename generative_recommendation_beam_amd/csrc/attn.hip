@@ -16,9 +16,10 @@
 // one NS-stage ring of 64-row tiles, NS-1 tiles in flight, in this order: the
 // request's parent ids and the workgroup's beam nodes, the queries, the prompt
 // window (read from HBM once per (request, head), never copied per beam), then
-// the chain records gathered row by row (one tile per chain level and 64
-// beams).  Vector loads complete in issue order, so keeping every load on this
-// one in-order stream makes each wait exact and keeps the ring full while the
+// the chain records gathered row by row (128-beam workgroups: per chain
+// level a tile of the key rows of all beams, then one of their value rows).
+// Vector loads complete in issue order, so keeping every load on this one
+// in-order stream makes each wait exact and keeps the ring full while the
 // chains are processed.  At the first tile each beam's chain is resolved in
 // LDS (parent links from the beam's own record to the root, with range, order
 // and depth checks) into level-major node ids: the ancestry index of the step.
@@ -235,17 +236,33 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
       dma16_stream(pv + (src + dma_v[i]), vst(S) + blk * 512);
     }
   };
-  // chain-record tile: row t holds the level-d record of workgroup beam
-  // 64*bb + t (a beam without one reads record 0 of the request, unused)
+  // chain-record tiles (a beam without a record at the level reads record 0
+  // of the request, unused).  128-beam workgroups: two tiles per chain level,
+  // the key rows (bb = 0), then the value rows (bb = 1) of all 128 beams,
+  // beams 0..63 in the stage's first half and 64..127 in its second, so that
+  // every wave folds every tile.  Smaller workgroups: one tile per level, row
+  // t holding beam t's key in the first half and its value in the second.
   auto issue_records = [&](int d, int bb, auto S) {
+    if constexpr (G::NRB == 2) {
+      const uint16_t *const base = bb ? p.av : p.ak;
 #pragma unroll
-    for (int i = 0; i < G::IPW; ++i) {
-      const int blk = wave * G::IPW + i;
-      const int b = bb * G::KT + dma_row[i];
-      const int id = b < G::NB ? chain_id(d, b) : -1;
-      const size_t src = ((size_t)r * p.cap + (id >= 0 ? id : 0)) * row + (size_t)h * HD;
-      dma16(p.ak + src + dma_k[i], kst(S) + blk * 512);
-      dma16(p.av + src + dma_v[i], vst(S) + blk * 512);
+      for (int i = 0; i < G::IPW; ++i) {
+        const int blk = wave * G::IPW + i;
+        const uint32_t sw = bb ? dma_v[i] : dma_k[i];
+        const int id0 = chain_id(d, dma_row[i]), id1 = chain_id(d, G::KT + dma_row[i]);
+        dma16(base + ((size_t)r * p.cap + (id0 >= 0 ? id0 : 0)) * row + (size_t)h * HD + sw, kst(S) + blk * 512);
+        dma16(base + ((size_t)r * p.cap + (id1 >= 0 ? id1 : 0)) * row + (size_t)h * HD + sw, vst(S) + blk * 512);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < G::IPW; ++i) {
+        const int blk = wave * G::IPW + i;
+        const int b = bb * G::KT + dma_row[i];
+        const int id = b < G::NB ? chain_id(d, b) : -1;
+        const size_t src = ((size_t)r * p.cap + (id >= 0 ? id : 0)) * row + (size_t)h * HD;
+        dma16(p.ak + src + dma_k[i], kst(S) + blk * 512);
+        dma16(p.av + src + dma_v[i], vst(S) + blk * 512);
+      }
     }
   };
   auto issue = [&](int tile, auto S) {
@@ -341,6 +358,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
     for (int i = 0; i < 16; ++i) O[t][i] = 0.f;
   bf16x8 qf[G::KSTEP];  // B operand of S^T: lane (g, c) holds head dims (HD/2)*g + 8j .. +8 of its beam
   int cnt = 0;          // chain records of this lane's beam
+  float rec_alpha = 1.f, rec_p = 0.f;   // a record's rescale and weight, from its key tile to its value tile
 
   auto step = [&](int t0, auto S) {
     constexpr int st = decltype(S)::value;
@@ -469,10 +487,39 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
           }
         }
       } else if (tile >= n_pre) {
-        // ---- one chain level of the beams of record tile bb
+        // ---- one chain level: its key tile, then its value tile
+        // (128-beam workgroups), or the beams of record tile bb
         const int k = tile - n_pre;
         const int d = k / G::NRB, bb = k % G::NRB;
-        if (bb == my_bb) {
+        if constexpr (G::NRB == 2) {
+          const char *const rb = my_bb ? vb : kb;      // this beam's row: the stage's first or second half
+          if (bb == 0) {
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < G::KSTEP; ++j)
+              s += dot8_bf16(__builtin_bit_cast(uint4, qf[j]), *(const uint4 *)(rb + roff_k[j]));
+            s = xor32_sum(s);
+            if (d < cnt) {
+              const float t = s * p.sl2;
+              const float m_new = fmaxf(m_run, t);
+              rec_alpha = fast_exp2(m_run - m_new);
+              rec_p = fast_exp2(t - m_new);
+              l_run = l_run * rec_alpha + (g == 0 ? rec_p : 0.f);
+              m_run = m_new;
+            }
+          } else if (d < cnt) {
+#pragma unroll
+            for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4) {
+                const uint2 vv = *(const uint2 *)(rb + roff_v[dt][q4]);
+                O[dt][4 * q4 + 0] = fmaf(rec_p, bf16_lo(vv.x), O[dt][4 * q4 + 0] * rec_alpha);
+                O[dt][4 * q4 + 1] = fmaf(rec_p, bf16_hi(vv.x), O[dt][4 * q4 + 1] * rec_alpha);
+                O[dt][4 * q4 + 2] = fmaf(rec_p, bf16_lo(vv.y), O[dt][4 * q4 + 2] * rec_alpha);
+                O[dt][4 * q4 + 3] = fmaf(rec_p, bf16_hi(vv.y), O[dt][4 * q4 + 3] * rec_alpha);
+              }
+          }
+        } else if (bb == my_bb) {
           float s = 0.f;
 #pragma unroll
           for (int j = 0; j < G::KSTEP; ++j)

@@ -10,19 +10,20 @@ add and top-100 of 100 x 256 per request.  Inputs are seeded synthetic data
 rotate between steps so that each step reads cold data (the working set of
 one copy exceeds the 256 MB last-level cache).
 
-The timed steps are independent batches.  By default they are spread over two
-HIP streams (step i on stream i % 2, each stream with its own input copies,
-outputs and workspace), as a serving process keeps two batches in flight:
-one batch's scoring, a latency-bound pass with one workgroup per request,
-overlaps the other's HBM-bound attention.  `value` is K steps over the time
-of the whole timed region; the same K steps run back to back on one stream
-give `ms_per_step_one_stream`, and a third pass with an event between the two
-stages of every step gives the stage times and the attention roofline.
-
-Printed: one JSON line with steps/s (value), beam-steps/s, algorithmic HBM
-GB/s of the step, the attention kernel's roofline (algorithmic bytes per
-launch / its event-timed average duration, against 8 TB/s), and the oracle
-timed on a bounded sample of the same workload on the host CPU.
+Order of a run:
+  1. the oracle on the host CPU, over the same workload (cpu_baseline), with
+     one worker process per host core (before the GPU is touched);
+  2. a plain device copy of 512 MiB each way, repeated for about 0.2 s and
+     then timed (copy bandwidth, the practical HBM figure the step is also
+     compared with; the GPU is at steady clocks afterwards);
+  3. W warm-up steps, then K steps back to back on one stream between two
+     events: `value` = 1 / step time, `ms_per_step`;
+  4. the same K steps, each split into its stages (the GR_STEP_ATTENTION and
+     GR_STEP_SELECTION calls) with an event between them: stage times, and the
+     attention kernel's roofline (its algorithmic bytes per launch over the
+     mean attention interval).
+With --streams S > 1 the K steps also run spread over S streams (independent
+batches in flight); that throughput is an extra field, never `value`.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 
@@ -54,20 +55,22 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first (the GPU takes some tens of ms to reach steady clocks)")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps first")
     ap.add_argument("--workload", default="beam100_p600")
     ap.add_argument("--sets", type=int, default=0,
                     help="independent input copies rotated between steps (default: 2 per stream)")
-    ap.add_argument("--streams", type=int, default=2,
-                    help="HIP streams carrying independent batches concurrently (1 = one after another)")
+    ap.add_argument("--streams", type=int, default=1,
+                    help="also time the steps spread over this many HIP streams (extra field)")
     ap.add_argument("--attention", choices=["softmax", "linear"], default="softmax",
                     help="linear: linear-attention decoding over a shared prompt state (gr_linear_decode_step); "
                          "the state is computed once per input set before timing, as a prefill would")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU sample")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run a plain 512 MiB device copy (counter calibration, copy bandwidth)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="bound on the oracle's wall time (requests beyond it are not run)")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle worker processes (default: the host cores this process may use, at most 16)")
+    ap.add_argument("--copy-seconds", type=float, default=0.2, help="device copy calibration time")
+    ap.add_argument("--gemm-seconds", type=float, default=0.3, help="dense bf16 GEMM calibration time")
     return ap.parse_args()
 
 
@@ -111,9 +114,13 @@ def algorithmic(x):
     outs = R * cfg.k * 12
     delta = cfg.depth
     flops = R * (4 * B * Lw * D + 4 * B * delta * D + 2 * B * D * cfg.vocab)
+    # the attention launch: what it must read (prompt window, queries, chain
+    # records with their parent ids, beam nodes); its output is handed on
+    # through the workspace and counted as traffic, not as algorithmic bytes
     return dict(step_bytes=prompt + q + records + W + prior + outs,
-                attn_kernel_bytes=prompt + q + records + attn_out,
-                prompt=prompt, q=q, records=records, n_chain_records=n_chain, flops=flops)
+                attn_kernel_bytes=prompt + q + records, attn_out_bytes=attn_out,
+                prompt=prompt, q=q, records=records, n_chain_records=n_chain, flops=flops,
+                prefix_flops=R * 4 * B * Lw * D)
 
 
 def algorithmic_linear(x):
@@ -126,8 +133,8 @@ def algorithmic_linear(x):
     step = a["step_bytes"] - a["prompt"] + state
     attn_out = cfg.R * cfg.n_in * cfg.D * (2 if (cfg.dtype == "bf16" and cfg.vocab == 256) else 4)
     flops = cfg.R * cfg.n_in * cfg.H * (2 * cfg.d * cfg.d + 4 * cfg.depth * cfg.d) + 2 * cfg.R * cfg.n_in * cfg.D * cfg.vocab
-    return dict(step_bytes=step, attn_kernel_bytes=state + a["q"] + a["records"] + attn_out, state=state,
-                flops=flops, n_chain_records=a["n_chain_records"])
+    return dict(step_bytes=step, attn_kernel_bytes=state + a["q"] + a["records"], attn_out_bytes=attn_out,
+                state=state, flops=flops, n_chain_records=a["n_chain_records"], prefix_flops=None)
 
 
 # ------------------------------------------------------------------ devices
@@ -152,7 +159,7 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_counters(attn_bytes_alg):
+def traffic_from_counters():
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summary, or None when absent or taken on another version of the kernel."""
     try:
@@ -165,52 +172,102 @@ def traffic_from_counters(attn_bytes_alg):
     return int((c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024)
 
 
-def cpu_baseline(x, seconds, linear=False):
-    """The oracle (plain NumPy, one BLAS thread) on the first requests of the
-    same workload until `seconds` of work have accumulated (for linear
-    attention the prompt state is computed outside the timed part, as on the
-    GPU)."""
-    import numpy as np
-    import oracle
-    from oracle import linear as LA
+# The oracle runs in worker processes forked before the GPU is touched; a
+# worker reads the workload from this module global (copy-on-write).
+_ORACLE_INPUT = None
+
+
+def host_cores(requested=0):
+    """Worker processes for the oracle: the cores this process may run on
+    (at most 16, the host share of one GPU), or the number asked for."""
+    n = len(os.sched_getaffinity(0))
+    return max(1, requested if requested > 0 else min(n, 16)), n
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _one_blas_thread():
     try:
         from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
     except ImportError:            # pragma: no cover
-        threadpool_limits = None
+        pass
+
+
+def _oracle_request(task):
+    """The oracle's decode step for one request of the shared workload
+    (its arena is built first, untimed).  Returns the step's seconds."""
+    import oracle
+    from oracle import linear as LA
+    r, linear = task
+    x = _ORACLE_INPUT
     cfg = x.cfg
-    done, spent, beams = 0, 0.0, 0
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    try:
-        while done < cfg.R and (spent < seconds or done < 2):
-            r = [done]
-            sl = lambda a: None if a is None else a[r]
-            ak, av, par = oracle.new_arena(1, max(cfg.capacity, 1), cfg.H, cfg.d)
-            prev, base = None, 0
-            for (pb, k, v) in x.levels:
-                ak, av, par, prev = oracle.trie_append(ak, av, par, base, k[r], v[r], sl(pb), prev)
-                base += k.shape[1]
-            if linear:
-                state = LA.prompt_state(x.prompt_k[r], x.prompt_v[r], cfg.window)
-                t0 = time.perf_counter()
-                o = LA.attend_linear_shared(x.prompt_k[r], x.prompt_v[r], x.q[r], par, ak, av, sl(x.beam_node),
-                                            cfg.window, state=state)
-                c = oracle.candidate_scores(oracle.codebook_logits(o, x.W), sl(x.prior), True)
-                oracle.select_topk(c[0], cfg.k)
-            else:
-                t0 = time.perf_counter()
-                oracle.decode_step(x.prompt_k[r], x.prompt_v[r], x.q[r], par, ak, av, sl(x.beam_node), x.W,
-                                   sl(x.prior), cfg.k, use_log_softmax=cfg.vocab > 1, window=cfg.window)
-            spent += time.perf_counter() - t0
-            done += 1
-            beams += cfg.n_in
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
-    steps_per_s = (done / cfg.R) / spent
-    return {"value": steps_per_s, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {done} of {cfg.R} requests ({done * cfg.n_in} beams), "
-                      f"{spent:.1f} s of oracle time, scaled to whole steps",
-            "beam_steps_per_s": beams / spent}
+    rr = [r]
+    sl = lambda a: None if a is None else a[rr]
+    ak, av, par = oracle.new_arena(1, max(cfg.capacity, 1), cfg.H, cfg.d)
+    prev, base = None, 0
+    for (pb, k, v) in x.levels:
+        ak, av, par, prev = oracle.trie_append(ak, av, par, base, k[rr], v[rr], sl(pb), prev)
+        base += k.shape[1]
+    if linear:
+        state = LA.prompt_state(x.prompt_k[rr], x.prompt_v[rr], cfg.window)
+        t0 = time.perf_counter()
+        o = LA.attend_linear_shared(x.prompt_k[rr], x.prompt_v[rr], x.q[rr], par, ak, av, sl(x.beam_node),
+                                    cfg.window, state=state)
+        c = oracle.candidate_scores(oracle.codebook_logits(o, x.W), sl(x.prior), True)
+        oracle.select_topk(c[0], cfg.k)
+    else:
+        t0 = time.perf_counter()
+        oracle.decode_step(x.prompt_k[rr], x.prompt_v[rr], x.q[rr], par, ak, av, sl(x.beam_node), x.W,
+                           sl(x.prior), cfg.k, use_log_softmax=cfg.vocab > 1, window=cfg.window)
+    return time.perf_counter() - t0
+
+
+def _noop(_):
+    return 0
+
+
+def cpu_baseline(x, seconds, workers, linear=False):
+    """The oracle (plain NumPy, fp64 accumulation) on the same workload, one
+    request per task over `workers` forked processes with one BLAS thread
+    each, in rounds of `workers` requests until every request is done or the
+    wall time passes `seconds`.  Steps/s = requests done / R / wall time of
+    the rounds (arena builds, and for linear attention the prompt state, are
+    inside the wall time; see `decode_only_value` for the decode calls
+    alone).  Must run before anything touches the GPU (the workers fork)."""
+    import multiprocessing as mp
+    global _ORACLE_INPUT
+    _ORACLE_INPUT = x
+    cfg = x.cfg
+    done, times = 0, []
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers, initializer=_one_blas_thread) as pool:
+        pool.map(_noop, range(workers))              # workers up (fork, imports) before the clock
+        pool.map(_oracle_request, [(0, linear)] * min(workers, cfg.R))   # first-call costs, untimed
+        t0 = time.perf_counter()
+        while done < cfg.R:
+            batch = [(r, linear) for r in range(done, min(cfg.R, done + workers))]
+            times += pool.map(_oracle_request, batch, chunksize=1)
+            done += len(batch)
+            if time.perf_counter() - t0 > seconds:
+                break
+        wall = time.perf_counter() - t0
+    _ORACLE_INPUT = None
+    return {"value": (done / cfg.R) / wall, "unit": "steps/s", "cores": workers, "kind": "oracle",
+            "sample": f"{done} of {cfg.R} requests ({done * cfg.n_in} beams), one per task over {workers} "
+                      f"processes x 1 BLAS thread, {wall:.2f} s wall, scaled to whole steps",
+            "beam_steps_per_s": done * cfg.n_in / wall,
+            "decode_only_value": (done / cfg.R) / (sum(times) / workers),
+            "cpu_model": cpu_model()}
 
 
 def gen_accounting(g, steps):
@@ -247,10 +304,15 @@ def bench_generate(args, cfg):
     import torch
     import workloads as W
     from generative_recommendation_beam_amd import harness as HN
-    torch.cuda.set_device(0)
     t0 = time.perf_counter()
     x = W.make_generate_inputs(cfg)
     print(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.skip_cpu_baseline:
+        workers, _ = host_cores(args.cpu_workers)
+        print(f"[bench] the oracle on {workers} host cores", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_generate(x, args.cpu_seconds, workers)
+    torch.cuda.set_device(0)
     sets = [HN.upload_generate(x) for _ in range(args.sets if args.sets > 0 else 2)]
     torch.cuda.synchronize()
     print(f"[bench] {len(sets)} input set(s) resident on the GPU", file=sys.stderr, flush=True)
@@ -272,6 +334,8 @@ def bench_generate(args, cfg):
             one(g)
         graphs.append(gr)
     torch.cuda.synchronize()
+    copy_gbps = copy_bandwidth(args.copy_seconds)
+    mfma_bandwidth(args.gemm_seconds)
     with torch.cuda.stream(s):
         for i in range(args.warmup):
             graphs[i % len(graphs)].replay()
@@ -316,38 +380,107 @@ def bench_generate(args, cfg):
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "whole generation (all launches of one graph replay)",
                      "prompt_bytes_per_generation": prompt_bytes},
+        "copy_GBps": round(copy_gbps, 1),
+        "frac_of_copy": round(gbps / copy_gbps, 4),
     }
-    if not args.skip_cpu_baseline:
-        print("[bench] timing the oracle on a sample of the same workload", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline_generate(x, args.cpu_seconds)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline_generate(x, seconds):
-    """The oracle's whole-ID generation (one BLAS thread) request by request
-    until `seconds` of work have accumulated, scaled to whole batches."""
+def _oracle_generate(r):
     from oracle import generate as OG
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:            # pragma: no cover
-        threadpool_limits = None
+    x, tables = _ORACLE_INPUT
+    rr = [r]
+    t0 = time.perf_counter()
+    OG.generate(x.prompt_k[rr], x.prompt_v[rr], x.q0[rr], x.W, tables, x.cfg.k)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline_generate(x, seconds, workers):
+    """The oracle's whole-ID generation, one request per task over `workers`
+    forked processes (one BLAS thread each), in rounds until every request
+    is done or `seconds` of wall time have passed; the code tables are
+    computed once beforehand (outside the wall time)."""
+    import multiprocessing as mp
+    from oracle import generate as OG
+    global _ORACLE_INPUT
     cfg = x.cfg
-    done, spent = 0, 0.0
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    try:
-        tables = [OG.code_table(e, x.w_qkv, cfg.H, cfg.d, cfg.dtype) for e in x.emb]
-        while done < cfg.R and (spent < seconds or done < 2):
-            r = [done]
-            t0 = time.perf_counter()
-            OG.generate(x.prompt_k[r], x.prompt_v[r], x.q0[r], x.W, tables, cfg.k)
-            spent += time.perf_counter() - t0
-            done += 1
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
-    return {"value": (done / cfg.R) / spent, "unit": "generations/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {done} of {cfg.R} requests, {spent:.1f} s of oracle time (code tables "
-                      f"excluded), scaled to whole batches"}
+    _one_blas_thread()
+    tables = [OG.code_table(e, x.w_qkv, cfg.H, cfg.d, cfg.dtype) for e in x.emb]
+    _ORACLE_INPUT = (x, tables)
+    done = 0
+    with mp.get_context("fork").Pool(workers, initializer=_one_blas_thread) as pool:
+        pool.map(_noop, range(workers))
+        t0 = time.perf_counter()
+        while done < cfg.R:
+            pool.map(_oracle_generate, list(range(done, min(cfg.R, done + workers))), chunksize=1)
+            done += min(workers, cfg.R - done)
+            if time.perf_counter() - t0 > seconds:
+                break
+        wall = time.perf_counter() - t0
+    _ORACLE_INPUT = None
+    return {"value": (done / cfg.R) / wall, "unit": "generations/s", "cores": workers, "kind": "oracle",
+            "sample": f"{done} of {cfg.R} requests, one per task over {workers} processes x 1 BLAS thread, "
+                      f"{wall:.2f} s wall (code tables excluded), scaled to whole batches",
+            "cpu_model": cpu_model()}
+
+
+def mfma_bandwidth(seconds):
+    """A dense bf16 GEMM (torch.matmul, 8192^3, hipBLASLt): repeated for
+    `seconds`, then 10 timed between events.  Returns TFLOP/s, the measured
+    counterpart of the published dense bf16 MFMA peak.  Running right before
+    the decode steps, it also brings the GPU to the clocks it holds under
+    sustained load: from an idle GPU the first ~200 decode steps run up to
+    30 % slower while the clocks rise."""
+    import torch
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(5):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    tf = 2 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    return tf
+
+
+def copy_bandwidth(seconds):
+    """A plain device copy, 512 MiB each way (torch's copy kernel): repeated
+    for `seconds`, then 20 copies timed between events.  Returns GB/s of
+    bytes read plus bytes written.  Running first, it also brings the GPU to
+    its steady clocks before the decode steps."""
+    import torch
+    n = 512 * 1024 * 1024 // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            b.copy_(a)
+        torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(20):
+        b.copy_(a)
+    c1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * n * 4 * 20 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return gbps
 
 
 def main():
@@ -368,11 +501,20 @@ def main():
         return
     cfg = W.CONFIGS[args.workload]
     assert cfg.steps == 1, "the benchmark times single-step workloads"
-    torch.cuda.set_device(0)
+    linear = args.attention == "linear"
     t0 = time.perf_counter()
     x = W.make_step_inputs(cfg)
     print(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
-    acc = algorithmic(x)
+    acc = algorithmic_linear(x) if linear else algorithmic(x)
+
+    # 1. the oracle on the host cores, before the GPU is touched (its workers fork)
+    cpu = None
+    if not args.skip_cpu_baseline:
+        workers, _ = host_cores(args.cpu_workers)
+        print(f"[bench] the oracle on {workers} host cores", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(x, args.cpu_seconds, workers, linear)
+
+    torch.cuda.set_device(0)
     n_streams = max(1, args.streams)
     n_sets = args.sets if args.sets > 0 else 2 * n_streams
     assert n_sets % n_streams == 0, "every stream needs its own input sets"
@@ -383,11 +525,9 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] {len(sets)} input set(s) resident on the GPU", file=sys.stderr, flush=True)
 
-    linear = args.attention == "linear"
     states = []
     prefill_ms = None
     if linear:
-        acc = algorithmic_linear(x)
         HN.linear_state(sets[0])           # first launch (code object load) untimed
         torch.cuda.synchronize()
         p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -397,6 +537,11 @@ def main():
         p1.record()
         torch.cuda.synchronize()
         prefill_ms = p0.elapsed_time(p1) / len(sets)
+
+    # 2. device copy bandwidth and a dense bf16 GEMM (measured counterparts of
+    # the published HBM and MFMA peaks), right before the decode steps
+    copy_gbps = copy_bandwidth(args.copy_seconds)
+    gemm_tflops = mfma_bandwidth(args.gemm_seconds)
 
     def step(i, flags_extra=0, stream=None):
         ds, buf = sets[i % len(sets)], bufs[i % len(bufs)]
@@ -410,58 +555,23 @@ def main():
                          ds.vocab, ds.prior, ds.k, ds.flags | flags_extra, buf.score, buf.token, buf.parent,
                          None, None, buf.ws, buf.ws_bytes, ds.dev_err, stream)
 
-    # Independent batches on several streams (a serving process keeping
-    # several batches in flight, as concurrent workers sharing one GPU do):
-    # step i runs on stream i % S with input set i % n_sets, so a stream
-    # only ever touches its own sets, outputs and workspaces.  One batch's
-    # scoring, a latency-bound pass with one workgroup per request, then
-    # overlaps another batch's HBM-bound attention.
-    main_stream = torch.cuda.current_stream()
-    streams = [main_stream] + [torch.cuda.Stream() for _ in range(n_streams - 1)]
-
-    def run_streams(k):
-        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record(main_stream)
-        for st in streams[1:]:
-            st.wait_event(start)
-        for i in range(k):
-            step(i, stream=streams[i % n_streams])
-        for st in streams[1:]:
-            e = torch.cuda.Event()
-            e.record(st)
-            main_stream.wait_event(e)
-        stop.record(main_stream)
-        return start, stop
-
+    # 3. W warm-up steps, then K whole steps back to back on one stream
     for i in range(args.warmup):
         step(i)
-    run_streams(args.warmup)
     torch.cuda.synchronize()
-
-    # timed region 1: K whole steps, one call each
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     ev0.record()
     for i in range(args.steps):
         step(i)
     ev1.record()
     torch.cuda.synchronize()
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step_one_stream = ms_total / args.steps
+    ms_step = ev0.elapsed_time(ev1) / args.steps
 
-    # timed region 1b: the same K steps spread over the streams
-    ms_step = ms_step_one_stream
-    if n_streams > 1:
-        torch.cuda.synchronize()
-        e0, e1 = run_streams(args.steps)
-        torch.cuda.synchronize()
-        ms_step = e0.elapsed_time(e1) / args.steps
-
-    # timed region 2: the same K steps, each split into its two stages with
-    # an event before, between and after them on the launch stream (same
-    # kernels, same arguments, same order as in region 1; the input sets
-    # still alternate, so every attention launch streams a prompt set the
-    # previous one evicted).  Stage time = mean event-to-event interval.
+    # 4. the same K steps, each split into its two stages with an event
+    # before, between and after them on the launch stream (same kernels,
+    # arguments and order as in 3; the input sets still alternate, so every
+    # attention launch streams a prompt set the previous one evicted).
+    # Stage time = mean event-to-event interval.
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
     torch.cuda.synchronize()
     ev[0].record()
@@ -473,31 +583,39 @@ def main():
     torch.cuda.synchronize()
     attn_avg_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)) / args.steps
     sel_avg_ms = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(args.steps)) / args.steps
+
+    # optional: the same K steps as independent batches spread over streams
+    ms_multi = None
+    if n_streams > 1:
+        main_stream = torch.cuda.current_stream()
+        streams = [main_stream] + [torch.cuda.Stream() for _ in range(n_streams - 1)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(main_stream)
+        for st in streams[1:]:
+            st.wait_event(start)
+        for i in range(args.steps):
+            step(i, stream=streams[i % n_streams])
+        for st in streams[1:]:
+            e = torch.cuda.Event()
+            e.record(st)
+            main_stream.wait_event(e)
+        stop.record(main_stream)
+        torch.cuda.synchronize()
+        ms_multi = start.elapsed_time(stop) / args.steps
     errs = [int(ds.dev_err.item()) for ds in sets]
     assert not any(errs), f"device error bits set: {errs}"
-
-    copy_gbps = None
-    if args.calibrate_copy:
-        n = 512 * 1024 * 1024 // 4
-        a = torch.ones(n, dtype=torch.float32, device="cuda")
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record()
-        for _ in range(10):
-            torch.mul(a, 1.0, out=b)
-        c1.record()
-        torch.cuda.synchronize()
-        copy_gbps = 2 * n * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
 
     steps_per_s = 1e3 / ms_step
     achieved = acc["attn_kernel_bytes"] / (attn_avg_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": None if linear else traffic_from_counters(acc["attn_kernel_bytes"]),
-                "kernel": "linear_attn_kernel" if linear else "attn_bf16_kernel",
+                "traffic": None if linear else traffic_from_counters(),
+                "kernel": "linear_ring_bf16_kernel" if linear else "attn_bf16_kernel",
                 "avg_launch_ms": round(attn_avg_ms, 5),
-                "algorithmic_bytes_per_launch": acc["attn_kernel_bytes"]}
+                "algorithmic_bytes_per_launch": acc["attn_kernel_bytes"],
+                "output_bytes_per_launch": acc["attn_out_bytes"],
+                "frac_of_copy": round(achieved / copy_gbps, 4)}
     step_gbps = acc["step_bytes"] / (ms_step * 1e-3) / 1e9
     out = {
         "metric": ("linear-attention " if linear else "") +
@@ -515,27 +633,35 @@ def main():
         "data": "synthetic (seeded N(0,1) K/V/Q, N(0,0.02) codebook, cumsum(-x^2) priors)",
         "config": {"workload": cfg.name, "requests": cfg.R, "prompt_len": cfg.Lp, "window": cfg.Lw,
                    "heads": cfg.H, "head_dim": cfg.d, "beams": cfg.n_in, "beam_width": cfg.k,
-                   "chain_records": cfg.depth, "codes_per_level": cfg.vocab, "input_sets": len(sets),
-                   "concurrent_batches": n_streams},
+                   "chain_records": cfg.depth, "codes_per_level": cfg.vocab, "input_sets": len(sets)},
         "beam_steps_per_s": round(steps_per_s * cfg.R * cfg.n_in, 0),
         "achieved_GBps": round(step_gbps, 1),
         "hbm_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "copy_GBps": round(copy_gbps, 1),
+        "hbm_frac_of_copy": round(step_gbps / copy_gbps, 4),
+        "gemm_bf16_TFLOPs": round(gemm_tflops, 1),
         "algorithmic_bytes_per_step": acc["step_bytes"],
         "flops_per_step": acc["flops"],
         "achieved_TFLOPs": round(acc["flops"] / (ms_step * 1e-3) / 1e12, 2),
-        "streams": n_streams,
-        "ms_per_step_one_stream": round(ms_step_one_stream, 5),
         "stage_ms": {"attention": round(attn_avg_ms, 5), "scoring_selection": round(sel_avg_ms, 5)},
         "roofline": roofline,
     }
-    if copy_gbps is not None:
-        out["copy_GBps"] = round(copy_gbps, 1)
+    if acc.get("prefix_flops"):
+        # the prompt part of the attention is a dense contraction on bf16 MFMA
+        tf = acc["prefix_flops"] / (attn_avg_ms * 1e-3) / 1e12
+        out["prefix_mfma"] = {"flops_per_launch": acc["prefix_flops"], "achieved_TFLOPs": round(tf, 1),
+                              "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                              "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "frac_of_gemm": round(tf / gemm_tflops, 4)}
+    if ms_multi is not None:
+        out["streams"] = n_streams
+        out["ms_per_step_streams"] = round(ms_multi, 5)
+        out["steps_per_s_streams"] = round(1e3 / ms_multi, 2)
     if linear:
         out["config"]["attention"] = "linear (elu+1 features, shared prompt state)"
         out["prefill_state_ms"] = round(prefill_ms, 5)
-    if not args.skip_cpu_baseline:
-        print("[bench] timing the oracle on a sample of the same workload", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds, linear)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

@@ -54,3 +54,26 @@ def test_bench_refuses_several_gpus():
                          text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_attention_launch_bytes_exclude_its_output():
+    """The attention launch's algorithmic bytes are what it must read (prompt
+    window, queries, distinct chain records with parent ids, beam nodes);
+    the bf16 output it hands to the scoring stage is traffic, not
+    algorithmic bytes."""
+    cfg = W.CONFIGS["beam100_p600"]
+    x = W.make_step_inputs(cfg)
+    acc = bench.algorithmic(x)
+    assert acc["attn_kernel_bytes"] == acc["prompt"] + acc["q"] + acc["records"]
+    assert acc["attn_out_bytes"] == 256 * 100 * 512 * 2
+    assert acc["records"] == acc["n_chain_records"] * (512 * 2 * 2 + 4) + 256 * 100 * 4
+
+
+def test_cpu_baseline_uses_worker_processes():
+    """The oracle baseline runs one request per task over several forked
+    workers and reports how many it used."""
+    cfg = W.reduced(W.CONFIGS["beam50_p600"], R=4, Lp=64, n_in=8, k=8, level_sizes=(8, 8))
+    x = W.make_step_inputs(cfg)
+    res = bench.cpu_baseline(x, 30.0, 2)
+    assert res["cores"] == 2 and res["kind"] == "oracle"
+    assert res["value"] > 0 and "4 of 4 requests" in res["sample"]

@@ -32,7 +32,7 @@ GR_MAX_DEPTH, GR_MAX_K = 8, 2048
 EXPORTED = ["gr_trie_append", "gr_prefix_attn", "gr_beam_topk", "gr_decode_step",
             "gr_linear_state", "gr_linear_attn", "gr_linear_decode_step",
             "gr_code_table", "gr_append_codes", "gr_generate",
-            "gr_attn_workspace_size", "gr_topk_workspace_size",
+            "gr_workspace_size", "gr_attn_workspace_size", "gr_topk_workspace_size",
             "gr_decode_workspace_size", "gr_generate_workspace_size", "gr_status_string"]
 
 
@@ -83,6 +83,7 @@ _sig = {
     "gr_generate": [ctypes.POINTER(Shape), _P, _P, _P, _I, _P, _P, _I, _I, ctypes.POINTER(Trie), _P, _P, _P, _P,
                     _P, _S, _P, _P],
     "gr_generate_workspace_size": [ctypes.POINTER(Shape), _I, _I, _I],
+    "gr_workspace_size": [ctypes.POINTER(Shape), _I, _I, _I],
     "gr_attn_workspace_size": [ctypes.POINTER(Shape), _I],
     "gr_topk_workspace_size": [_I, _I, _I, _I],
     "gr_decode_workspace_size": [ctypes.POINTER(Shape), _I, _I, _I],
@@ -92,7 +93,7 @@ for _name, _args in _sig.items():
     _f = getattr(_lib, _name)
     _f.argtypes = _args
     _f.restype = ctypes.c_int32
-for _name in ("gr_attn_workspace_size", "gr_topk_workspace_size", "gr_decode_workspace_size",
+for _name in ("gr_workspace_size", "gr_attn_workspace_size", "gr_topk_workspace_size", "gr_decode_workspace_size",
               "gr_generate_workspace_size"):
     getattr(_lib, _name).restype = ctypes.c_size_t
 _lib.gr_status_string.restype = ctypes.c_char_p
@@ -213,6 +214,10 @@ def gr_generate(shape, prompt_k, prompt_v, q0, levels, W, tables, vocab, beam_wi
 
 def gr_generate_workspace_size(shape, levels, vocab, beam_width) -> int:
     return int(_lib.gr_generate_workspace_size(_shape_ref(shape), int(levels), int(vocab), int(beam_width)))
+
+
+def gr_workspace_size(shape, n_beams, vocab, k) -> int:
+    return int(_lib.gr_workspace_size(_shape_ref(shape), int(n_beams), int(vocab), int(k)))
 
 
 def gr_attn_workspace_size(shape, n_beams) -> int:

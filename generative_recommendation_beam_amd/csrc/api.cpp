@@ -646,6 +646,13 @@ gr_status gr_append_codes(const gr_shape *shape, const gr_trie *trie, int32_t ba
   return hip_status(gr::launch_append_codes(a, stream));
 }
 
+size_t gr_workspace_size(const gr_shape *shape, int32_t n_beams, int32_t vocab, int32_t k) {
+  const size_t d = gr_decode_workspace_size(shape, n_beams, vocab, k);
+  const size_t a = gr_attn_workspace_size(shape, n_beams);
+  const size_t t = shape ? gr_topk_workspace_size(shape->R, n_beams, vocab, k) : 0;
+  return d > a ? (d > t ? d : t) : (a > t ? a : t);
+}
+
 size_t gr_generate_workspace_size(const gr_shape *shape, int32_t levels, int32_t vocab, int32_t beam_width) {
   if (check_shape(shape) || levels < 1 || levels > gr::kMaxLevels || vocab != 256 || beam_width <= 0 ||
       beam_width > GR_MAX_K)

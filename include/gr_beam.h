@@ -344,7 +344,14 @@ gr_status gr_generate(const gr_shape *shape, const void *prompt_k,
                       int32_t *out_parent, int32_t *out_ids, void *ws,
                       size_t ws_bytes, int32_t *dev_err, hipStream_t stream);
 
-/* Scratch sizes in bytes (0 when none is needed; sizes <= 0 give 0). */
+/* Scratch sizes in bytes (0 when none is needed; sizes <= 0 give 0).
+ * gr_workspace_size(shape, n_beams, vocab, k) is the scratch that is enough
+ * for every call of the step on these sizes: gr_prefix_attn(shape, n_beams),
+ * gr_beam_topk(shape->R, n_beams, vocab, k) and gr_decode_step(shape,
+ * n_beams, vocab, k) (equal to gr_decode_workspace_size, which covers the
+ * other two).  The per-call sizes below may be smaller. */
+size_t gr_workspace_size(const gr_shape *shape, int32_t n_beams,
+                         int32_t vocab, int32_t k);
 size_t gr_attn_workspace_size(const gr_shape *shape, int32_t n_beams);
 size_t gr_topk_workspace_size(int32_t R, int32_t n_in, int32_t vocab,
                               int32_t k);

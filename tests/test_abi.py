@@ -306,3 +306,17 @@ def test_binding_refuses_strided_tensors():
     dev = torch.zeros((4, 4), dtype=torch.float32, device="cuda")
     with pytest.raises(ValueError, match="contiguous"):
         L.gr_linear_state(shape(), dev.t(), dev, dev, dev)
+
+
+def test_workspace_size_covers_every_call_of_the_step():
+    """gr_workspace_size(shape, n_beams, vocab, k) is enough scratch for
+    gr_prefix_attn, gr_beam_topk and gr_decode_step on those sizes."""
+    for sh, nb, vocab, k in [(shape(), 100, 256, 100), (shape(R=256), 100, 256, 100),
+                             (shape(R=1, H=4, head_dim=32, prompt_len=256), 40000, 1, 2000),
+                             (shape(R=4, prompt_len=8192), 100, 256, 100),
+                             (shape(dtype=L.GR_F32, R=2, H=4, head_dim=32, prompt_len=64), 8, 256, 8)]:
+        need = L.gr_workspace_size(sh, nb, vocab, k)
+        assert need >= L.gr_decode_workspace_size(sh, nb, vocab, k) > 0
+        assert need >= L.gr_attn_workspace_size(sh, nb)
+        assert need >= L.gr_topk_workspace_size(sh.R, nb, vocab, k)
+    assert L.gr_workspace_size(shape(R=0), 100, 256, 100) == 0

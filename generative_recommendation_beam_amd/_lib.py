@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libgrbeam.so")
 
 GR_OK, GR_ERR_NULL, GR_ERR_SHAPE, GR_ERR_UNSUPPORTED = 0, 1, 2, 3
 GR_ERR_CAPACITY, GR_ERR_K_TOO_LARGE, GR_ERR_WORKSPACE, GR_ERR_HIP = 4, 5, 6, 7
+GR_ERR_SCRATCH_LIMIT = 8
+GR_NOALLOC_SCRATCH_BYTES = 48 << 20
 GR_F32, GR_BF16 = 0, 1
 GR_DEVERR_PARENT_RANGE, GR_DEVERR_PARENT_ORDER = 1, 2
 GR_DEVERR_DEPTH, GR_DEVERR_BEAM_RANGE, GR_DEVERR_TOKEN_RANGE = 4, 8, 16
@@ -29,7 +31,7 @@ GR_TOPK_LOG_SOFTMAX = 1
 GR_STEP_ATTENTION, GR_STEP_SELECTION = 2, 4
 GR_MAX_DEPTH, GR_MAX_K = 8, 2048
 
-EXPORTED = ["gr_trie_append", "gr_prefix_attn", "gr_beam_topk", "gr_decode_step",
+EXPORTED = ["gr_trie_append", "gr_prefix_attn", "gr_beam_topk", "gr_decode_step", "gr_decode_step_noalloc",
             "gr_linear_state", "gr_linear_attn", "gr_linear_decode_step",
             "gr_code_table", "gr_append_codes", "gr_generate",
             "gr_workspace_size", "gr_attn_workspace_size", "gr_topk_workspace_size",
@@ -73,6 +75,8 @@ _sig = {
     "gr_beam_topk": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P],
     "gr_decode_step": [ctypes.POINTER(Shape), _P, _P, _P, _I, ctypes.POINTER(Trie), _P, _P, _I, _P, _I, _I,
                        _P, _P, _P, _P, _P, _P, _S, _P, _P],
+    "gr_decode_step_noalloc": [ctypes.POINTER(Shape), _P, _P, _P, _I, ctypes.POINTER(Trie), _P, _P, _I, _P, _I,
+                               _I, _P, _P, _P, _P, _P, _P, _P],
     "gr_linear_state": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P],
     "gr_linear_attn": [ctypes.POINTER(Shape), _P, _P, _P, _I, ctypes.POINTER(Trie), _P, _P, _P, _P],
     "gr_linear_decode_step": [ctypes.POINTER(Shape), _P, _P, _P, _I, ctypes.POINTER(Trie), _P, _P, _I, _P, _I,
@@ -166,6 +170,15 @@ def gr_decode_step(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, W, vo
                                int(vocab), _ptr(prior), int(beam_width), int(flags), _ptr(out_score),
                                _ptr(out_token), _ptr(out_parent), _ptr(attn_out), _ptr(cand_out), _ptr(ws),
                                int(ws_bytes), _ptr(dev_err), _stream(stream)), "gr_decode_step")
+
+
+def gr_decode_step_noalloc(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, W, vocab, prior, beam_width,
+                           flags, out_score, out_token, out_parent, attn_out, cand_out, dev_err, stream=None):
+    _check(_lib.gr_decode_step_noalloc(_shape_ref(shape), _ptr(prompt_k), _ptr(prompt_v), _ptr(q), int(n_beams),
+                                       None if trie is None else ctypes.byref(trie), _ptr(beam_node), _ptr(W),
+                                       int(vocab), _ptr(prior), int(beam_width), int(flags), _ptr(out_score),
+                                       _ptr(out_token), _ptr(out_parent), _ptr(attn_out), _ptr(cand_out),
+                                       _ptr(dev_err), _stream(stream)), "gr_decode_step_noalloc")
 
 
 def gr_linear_state(shape, prompt_k, prompt_v, state, norm, stream=None):

@@ -356,6 +356,7 @@ const char *gr_status_string(gr_status s) {
     case GR_ERR_K_TOO_LARGE: return "k exceeds the candidate count or GR_MAX_K";
     case GR_ERR_WORKSPACE: return "workspace too small";
     case GR_ERR_HIP: return "a HIP launch failed";
+    case GR_ERR_SCRATCH_LIMIT: return "the step needs more scratch than the static no-alloc buffer holds";
     default: return "unknown status";
   }
 }

@@ -69,7 +69,9 @@ enum {
   GR_ERR_CAPACITY = 4,     /* base + n_new > capacity */
   GR_ERR_K_TOO_LARGE = 5,  /* k > n_in * vocab, or k above GR_MAX_K */
   GR_ERR_WORKSPACE = 6,    /* ws too small (see the *_workspace_size calls) */
-  GR_ERR_HIP = 7           /* a HIP launch failed */
+  GR_ERR_HIP = 7,          /* a HIP launch failed */
+  GR_ERR_SCRATCH_LIMIT = 8 /* gr_decode_step_noalloc: the step needs more
+                              scratch than GR_NOALLOC_SCRATCH_BYTES */
 };
 enum { GR_F32 = 0, GR_BF16 = 1 };
 
@@ -343,6 +345,34 @@ gr_status gr_generate(const gr_shape *shape, const void *prompt_k,
                       float *out_score, int32_t *out_token,
                       int32_t *out_parent, int32_t *out_ids, void *ws,
                       size_t ws_bytes, int32_t *dev_err, hipStream_t stream);
+
+/* gr_decode_step_noalloc -- gr_decode_step for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc.  Same arguments, semantics, outputs and errors as
+ * gr_decode_step, without ws / ws_bytes: the step's scratch is a static
+ * device array of GR_NOALLOC_SCRATCH_BYTES (48 MiB) that every GPU the
+ * library runs on holds from the library's first use on it until the
+ * process ends.  Its device address is looked up once per device
+ * (hipGetSymbolAddress, on the current device); the call allocates and
+ * frees nothing.
+ *   Limit: a step whose gr_decode_workspace_size() exceeds
+ *   GR_NOALLOC_SCRATCH_BYTES returns GR_ERR_SCRATCH_LIMIT before any device
+ *   call (the 256-request, beam-100, 600-token step needs 26 MiB).
+ *   Sharing: every call on one GPU uses that GPU's one array, which keeps
+ *   the last call's contents; no part of it needs to start at zero.  Calls
+ *   that overlap on one GPU (other streams, other threads) race on it and
+ *   must be serialised by the caller. */
+#define GR_NOALLOC_SCRATCH_BYTES (48u << 20)
+gr_status gr_decode_step_noalloc(const gr_shape *shape, const void *prompt_k,
+                                 const void *prompt_v, const void *q,
+                                 int32_t n_beams, const gr_trie *trie,
+                                 const int32_t *beam_node, const void *W,
+                                 int32_t vocab, const float *prior,
+                                 int32_t beam_width, int32_t flags,
+                                 float *out_score, int32_t *out_token,
+                                 int32_t *out_parent, float *attn_out,
+                                 float *cand_out, int32_t *dev_err,
+                                 hipStream_t stream);
 
 /* Scratch sizes in bytes (0 when none is needed; sizes <= 0 give 0).
  * gr_workspace_size(shape, n_beams, vocab, k) is the scratch that is enough

@@ -57,6 +57,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // s_waitcnt with only the vector-memory counter constrained to <= n.
 #define GR_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+// The same, and every LDS access of this wave completed (lgkmcnt 0).
+#define GR_WAIT_VMCNT_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4))
 
 // One global_load_lds_dwordx4: lane l's 16 bytes at src land at LDS byte
 // lds + 16*l (lds wave-uniform).  Written as inline asm so that the compiler

@@ -203,9 +203,10 @@ __device__ __forceinline__ void rank_sort_u64(uint64_t *arr, int L) {
   __syncthreads();
 }
 
-// The m-th smallest (m = 1 or 2, counting equal values) of one u32 per lane
-// across the wave: a butterfly that keeps each lane's two smallest.
-__device__ __forceinline__ uint32_t wave_small2_u32(uint32_t x, int m) {
+// The smallest and second smallest (counting equal values) of one u32 per
+// lane across the wave, in every lane: a butterfly that keeps each lane's two
+// smallest.
+__device__ __forceinline__ void wave_small2_pair_u32(uint32_t x, uint32_t &s1, uint32_t &s2) {
   uint32_t m1 = x, m2 = 0xFFFFFFFFu;
   auto merge = [&](uint32_t p1, uint32_t p2) {
     const uint32_t n2 = min(max(m1, p1), min(m2, p2));
@@ -223,7 +224,14 @@ __device__ __forceinline__ uint32_t wave_small2_u32(uint32_t x, int m) {
   xor_pair<32>(m1, a1, b1);
   xor_pair<32>(m2, a2, b2);
   merge(a1 == m1 ? b1 : a1, a2 == m2 ? b2 : a2);
-  return m == 1 ? m1 : m2;
+  s1 = m1;
+  s2 = m2;
+}
+// The m-th smallest (m = 1 or 2) of one u32 per lane across the wave.
+__device__ __forceinline__ uint32_t wave_small2_u32(uint32_t x, int m) {
+  uint32_t s1, s2;
+  wave_small2_pair_u32(x, s1, s2);
+  return m == 1 ? s1 : s2;
 }
 
 // Ascending sort of arr[0..NT E) (E = 2, 4 or 8; entries are unique): each

@@ -7,16 +7,18 @@
 // candidate selection runs on the device, next to scoring.
 //
 // logits_select_bf16: one workgroup (8 waves) per (request, group of <= 128
-// beams).  z^T = W o^T on v_mfma_f32_32x32x16_bf16 (codes x beams; wave w owns
-// beams 32*(w/2).. and codes 128*(w%2)..).  W and o stream HBM/L2 -> LDS
-// through a ring of 32-column chunks (global_load_lds, several chunks in
-// flight, each read once per workgroup).  Each lane then holds 64 codes of one
-// beam in registers: the log-softmax is in-lane plus one lane^32 swap and one
-// LDS exchange between the two code halves.  The selection first bounds the
-// k-th best score from lane minima and stages only the lanes that can reach
-// the bound, then runs the exact selection (gr_select.h) on the staged
-// candidates (on all registers when the bound prunes too little); scores never
-// leave the chip unless the caller asks for them.
+// beams).  z^T = W o^T on v_mfma_f32_32x32x16_bf16 (codes x beams; wave w
+// owns codes 32w.. for all beams).  o and W stream HBM/L2 -> LDS in 64-column
+// blocks (global_load_lds, two blocks in flight): o into a ring shared by the
+// workgroup, W into a ring of each wave's own rows.  Each lane then holds 16
+// codes of each of four beams: the log-softmax is in-lane plus one lane^32
+// swap and one LDS exchange between the 8 waves.  The selection bounds the
+// k-th best score from the lanes' per-beam minima, stages only the
+// candidates at or above the bound, finds the bin of the k-th among them in
+// one 256-bin histogram and orders the few candidates up to that bin by
+// counting ranks (the general radix selection of gr_select.h when the bound
+// prunes too little); scores never leave the chip unless the caller asks for
+// them.
 //
 // score_select: the same scoring and selection starting from fp32 logits in
 // global memory (the standalone top-k entry point, the fp32 path and scalar
@@ -34,33 +36,34 @@ namespace gr {
 namespace {
 
 constexpr int kNT = 512;
-constexpr int kOC = 32;                    // D columns per ring chunk (two MFMA k-steps)
-constexpr int kRS = 6;                     // ring stages (5 chunks in flight)
+constexpr int kCB = 64;                    // o columns per LDS block (four MFMA k-steps)
+constexpr int kFastK = 128;                // largest k of the bounded selection
+constexpr int kWaveStage = 512;            // staged candidates per wave, at most
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// One ring stage: a 32-column chunk of W (256 code rows) and of o (128 beam
-// rows), 64-byte rows whose 16-byte chunks are XOR-swizzled so that 16
-// consecutive rows read at one logical chunk hit 16 distinct 16-byte slots of
-// a 256-byte bank row (and any 8 of them distinct slots of a 128-byte one).
-struct LogitsStage {
-  uint16_t w[256 * kOC];                   // 16 KB
-  uint16_t o[kGroupBeams * kOC];           // 8 KB
-};
+// o column block in LDS: 128 beam rows x 64 columns bf16 (128-byte rows).
+// Logical 16-byte chunk q of row b sits at physical chunk q ^ swz(b): any 16
+// consecutive rows read at one logical chunk then touch 16 distinct 16-byte
+// slots of two 128-byte rows pairs, and any 8 of them distinct slots.
+__device__ __forceinline__ int swz_o(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+constexpr int kOS = 3;                     // ring slots: the block in use and two in flight
 struct LogitsSmem {
   union {
-    LogitsStage ring[kRS];                 // projection
-    SelectSmem<kNT> sel;                   // selection afterwards
+    struct {
+      uint16_t ob[kOS][kGroupBeams * kCB];          // o blocks (3 x 16 KB)
+      uint16_t wr[kNT / 64][kOS][32 * kCB];         // per wave: its 32 W rows of a block (8 x 3 x 4 KB)
+    } ring;
+    SelectSmem<kNT> sel;                   // selection afterwards (staging in sel.tmp)
   } u;
-  float red_max[4][2][32];
-  float red_sum[4][2][32];
-  uint32_t bound[kNT / 64];                // per-wave bound keys of the fast selection
-  uint32_t fast_cnt[kNT / 64];             // per-wave counts of staged lanes
+  float red_max[kNT / 64][kGroupBeams];    // per-wave partial max / sum of each beam's logits
+  float red_sum[kNT / 64][kGroupBeams];
+  uint4 wbest[kNT / 64];                   // per wave: its two best lane bounds, its best score (rank keys)
+  uint32_t wcnt[kNT / 64];                 // per wave: staged candidates
+  uint32_t n_final;                        // candidates gathered for the final ordering
 };
-// Fast selection: at most 8 staged candidates per thread, staged (scores
-// and the row bases of their lanes) in the then idle ring.
-constexpr int kFastList = 8 * kNT;
-static_assert(sizeof(LogitsStage) * kRS >= (sizeof(float) + sizeof(uint32_t)) * kFastList, "staging area");
+static_assert(kWaveStage * (kNT / 64) <= kListCap, "staging area");
 
 struct LP {
   const uint16_t *o, *W;
@@ -72,265 +75,323 @@ struct LP {
   int R, n_in, D, hd_log2, k, lsm, n_groups, kk;
 };
 
-__device__ __forceinline__ int swz64(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
-
+// NB: number of 64-column blocks of D when fixed at compile time (the
+// block loop is then unrolled, and the compiler's waits count the loads in
+// flight across blocks), 0 for any D.
+template <int NB>
 __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
   __shared__ LogitsSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, c = lane & 31;
-  const int r = blockIdx.x / p.n_groups, grp = blockIdx.x % p.n_groups;
+  // Consecutive workgroup ids go to the 8 XCDs in turn; XCD x takes the
+  // x-th eighth of the requests, the same eighth whose attention output its
+  // L2 received from the attention kernel (which maps its units alike).
+  int bid = blockIdx.x;
+  if ((gridDim.x & 7) == 0) bid = (bid & 7) * (int)(gridDim.x >> 3) + (bid >> 3);
+  const int r = bid / p.n_groups, grp = bid % p.n_groups;
   const int b_begin = grp * kGroupBeams;
   const int nbg = min(kGroupBeams, p.n_in - b_begin);
-  const int bb = wave >> 1, ch = wave & 1;
-  const int bl = bb * 32 + c;
-  const bool valid = bl < nbg;
-  const int beam = b_begin + bl;
-  const int n_chunks = p.D / kOC;
-
-  // ---- z^T = W o^T, W and o streamed HBM/L2 -> LDS through the ring.  A
-  // 1 KB DMA block is 16 rows x 64 B; lane l fetches row l/4 of its block at
-  // the logical chunk that the swizzle puts at physical chunk l%4.  Wave w
-  // moves W blocks 2w, 2w+1 and o block w of every chunk (3 DMAs per chunk).
-  // Chunks past the end re-read the last one (never used), so every step
-  // has the same number of chunks in flight.
-  // o is head-major ([R][H][n_in][hd]); a 32-column chunk lies inside one head.
-  const int drow = lane >> 2, dpc = lane & 3;
   const int hd = 1 << p.hd_log2, H = p.D >> p.hd_log2;
   const uint16_t *o_req = p.o + (size_t)r * H * p.n_in * hd;
-  auto issue = [&](int chunk, int st) {
-    const int col0 = min(chunk, n_chunks - 1) * kOC;
-    const int hc = col0 >> p.hd_log2, c_in = col0 & (hd - 1);
+  const int n_blk = NB > 0 ? NB : (p.D + kCB - 1) / kCB;
+
+  // priors of this lane's beams 32 t + c (read now, used after the projection)
+  float pr[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int bl = 32 * t + c;
+    pr[t] = (bl < nbg && p.prior) ? p.prior[(size_t)r * p.n_in + b_begin + bl] : 0.f;
+  }
+
+  // ---- z^T = W o^T on v_mfma_f32_32x32x16_bf16: wave w forms codes
+  // 32w .. 32w+31 (A: its own W rows) for all 128 beam rows (B: o, four
+  // 32-beam tiles), 64 columns of D per block.  Both operands stream
+  // HBM/L2 -> LDS by global_load_lds (whole 128-byte rows, two blocks ahead
+  // of the MFMAs, three ring slots): o blocks into a ring shared by the
+  // workgroup, W rows into a ring of the wave's own.  o is head-major
+  // ([R][H][n_in][hd]); a 16-byte chunk never straddles heads.  Rows past
+  // the group's beams repeat its last beam (never selected); columns past D
+  // (a last half block) repeat the last chunk (never read).
+  // Per wave and block: 2 o pieces + 4 W pieces of 1 KB (6 loads in flight
+  // per block).
+  constexpr int kDmaPerBlock = 6;
+  auto issue = [&](int cb) {
+    const int slot = cb % kOS;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int blk = wave * 2 + i, row = blk * 16 + drow;
-      const int lc = dpc ^ swz64(row);
-      dma16(p.W + (size_t)row * p.D + col0 + lc * 8, &sm.u.ring[st].w[blk * 512]);
-    }
-    {
-      const int row = wave * 16 + drow, lc = dpc ^ swz64(row);
+      const int j = 2 * wave + i, row = 8 * j + (lane >> 3);
+      const int col = min(cb * kCB + 8 * ((lane & 7) ^ swz_o(row)), p.D - 8);
+      const int h = col >> p.hd_log2, ci = col & (hd - 1);
       const int b = min(b_begin + row, p.n_in - 1);
-      dma16(o_req + ((size_t)hc * p.n_in + b) * hd + c_in + lc * 8, &sm.u.ring[st].o[wave * 512]);
+      dma16(o_req + ((size_t)h * p.n_in + b) * hd + ci, &sm.u.ring.ob[slot][j * 512]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int lr = 8 * i + (lane >> 3);
+      const int col = min(cb * kCB + 8 * ((lane & 7) ^ swz_o(lr)), p.D - 8);
+      dma16(p.W + (size_t)(32 * wave + lr) * p.D + col, &sm.u.ring.wr[wave][slot][i * 512]);
     }
   };
-  // per-lane LDS element offsets of the operand reads (logical chunk 2kk+g)
-  const int sw = swz64(c);                  // rows bl and ch*128+32m+c share bits 1..3 with c
-  int aoff[4][2], boff[2];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    boff[kk] = bl * kOC + (((2 * kk + g) ^ sw) << 3);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) aoff[m][kk] = (ch * 128 + 32 * m + c) * kOC + (((2 * kk + g) ^ sw) << 3);
-  }
-
   f32x16 acc[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
-
-  // Operands of chunk c+1 are read from LDS into registers while the MFMAs
-  // of chunk c run, so LDS reads, DMA fills and MFMAs overlap.
-  bf16x8 opa[2][2][4], opb[2][2];
-  auto read_ops = [&](int chunk, int buf) {
-    const LogitsStage &S = sm.u.ring[chunk % kRS];
+    for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+  const int swb = swz_o(c);                 // rows c and 32 t + c share the swizzle of c
+  // A block's operands (20 LDS reads) are all issued before its 16 MFMAs,
+  // so that the LDS latency is paid once per block, not once per MFMA.
+  auto mma = [&](int cb) {
+    const int slot = cb % kOS;
+    const bool full = NB > 0 || (p.D - cb * kCB) >= kCB;   // else a half block (2 k-steps)
+    const uint16_t *ob = &sm.u.ring.ob[slot][c * kCB];
+    const uint16_t *wb = &sm.u.ring.wr[wave][slot][c * kCB];
+    bf16x8 a[4], bo[4][4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      opb[buf][kk] = *(const bf16x8 *)&S.o[boff[kk]];
+    for (int ks = 0; ks < 4; ++ks) {
+      const int off = ((2 * ks + g) ^ swb) << 3;
+      a[ks] = *(const bf16x8 *)(wb + off);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) opa[buf][kk][m] = *(const bf16x8 *)&S.w[aoff[m][kk]];
+      for (int t = 0; t < 4; ++t) bo[ks][t] = *(const bf16x8 *)(ob + 32 * t * kCB + off);
     }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 2 || full) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], bo[ks][t], acc[t], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 20, 0);   // the LDS reads first,
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // then the MFMAs
   };
-  auto mfma_ops = [&](int buf) {
+  issue(0);
+  if (n_blk > 1) issue(1);
+  // Step cb: block cb has landed once at most the next block's loads are in
+  // flight, and this wave's reads of block cb - 1 have completed; after the
+  // barrier every wave is done with block cb - 1, whose slots receive block
+  // cb + 2.
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[buf][kk][m], opb[buf][kk], acc[m], 0, 0, 0);
-  };
-#pragma unroll
-  for (int c0 = 0; c0 < kRS - 1; ++c0) issue(c0, c0);
-  GR_WAIT_VMCNT(3 * (kRS - 2));             // this wave's pieces of chunk 0 landed
-  ring_barrier();                           // everyone's
-  read_ops(0, 0);
-  // Iteration c: chunk c+1 must have landed (chunks c+2 .. c+kRS-2 may still
-  // be in flight); after the barrier every wave has consumed chunk c-1, whose
-  // stage receives chunk c+kRS-1.  The loop runs in pairs so that the two
-  // register buffers are fixed; an odd last chunk leaves after the first half.
-  for (int chunk = 0; chunk < n_chunks; chunk += 2) {
-    GR_WAIT_VMCNT(3 * (kRS - 3));
+  for (int cb = 0; cb < n_blk; ++cb) {
+    if (cb + 1 < n_blk) GR_WAIT_VMCNT_LGKM0(kDmaPerBlock);
+    else GR_WAIT_VMCNT_LGKM0(0);
     ring_barrier();
-    issue(chunk + kRS - 1, (chunk + kRS - 1) % kRS);
-    read_ops(chunk + 1, 1);                 // past the end: a landed re-read, unused
-    mfma_ops(0);
-    if (chunk + 1 == n_chunks) break;
-    GR_WAIT_VMCNT(3 * (kRS - 3));
-    ring_barrier();
-    issue(chunk + kRS, (chunk + kRS) % kRS);
-    read_ops(chunk + 2, 0);
-    mfma_ops(1);
+    if (cb + 2 < n_blk) issue(cb + 2);
+    mma(cb);
   }
-  GR_WAIT_VMCNT(0);                         // the trailing re-reads landed
-  ring_barrier();                           // before the LDS is reused
+  // Lane (c, g) now holds, for beam row 32 t + c, the logits of codes
+  // 32 w + 8 (j >> 2) + 4 g + (j & 3) in acc[t][j].
 
-  // log-softmax over the 256 codes of each beam (two waves hold its halves)
-  float lse = 0.f;
-  float amax = acc[0][0];                   // this lane's largest logit
+  // ---- log-softmax over the 256 codes of each beam: partial max / sum over
+  // the lane's 16 codes, the lane 32 apart (same beam), then the 8 waves.
+  // The lane's smallest (NaN-propagating) and largest logit of each beam
+  // also bound its 16 candidate scores, rounding being monotonic.
+  float lo[4], hi[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int t = 0; t < 4; ++t) {
+    float mn = acc[t][0], mx = acc[t][0];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, acc[m][i]);
+    for (int j = 1; j < 16; ++j) {
+      mn = __builtin_elementwise_minimum(mn, acc[t][j]);
+      mx = fmaxf(mx, acc[t][j]);
+    }
+    lo[t] = mn;
+    hi[t] = mx;
+  }
+  float lse[4] = {0.f, 0.f, 0.f, 0.f};
   if (p.lsm) {
-    const float mx = fmaxf(amax, __shfl_xor(amax, 32));
-    if (lane < 32) sm.red_max[bb][ch][c] = mx;
-    __syncthreads();
-    const float M = fmaxf(sm.red_max[bb][0][c], sm.red_max[bb][1][c]);
-    const float Ml = M * kLog2e;
-    float se = 0.f;
+    float M[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) se += fast_exp2(fmaf(acc[m][i], kLog2e, -Ml));
-    se += __shfl_xor(se, 32);
-    if (lane < 32) sm.red_sum[bb][ch][c] = se;
+    for (int t = 0; t < 4; ++t) {
+      const float mx = xor32_max(hi[t]);
+      if (g == 0) sm.red_max[wave][32 * t + c] = mx;
+    }
     __syncthreads();
-    lse = M + __builtin_amdgcn_logf(sm.red_sum[bb][0][c] + sm.red_sum[bb][1][c]) * kLn2;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float mx = sm.red_max[0][32 * t + c];
+#pragma unroll
+      for (int w = 1; w < kNT / 64; ++w) mx = fmaxf(mx, sm.red_max[w][32 * t + c]);
+      M[t] = mx;
+      const float Ml = mx * kLog2e;
+      float se = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) se += fast_exp2(fmaf(acc[t][j], kLog2e, -Ml));
+      se = xor32_sum(se);
+      if (g == 0) sm.red_sum[wave][32 * t + c] = se;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float se = sm.red_sum[0][32 * t + c];
+#pragma unroll
+      for (int w = 1; w < kNT / 64; ++w) se += sm.red_sum[w][32 * t + c];
+      lse[t] = M[t] + __builtin_amdgcn_logf(se) * kLn2;
+    }
   }
 
-  // ---- selection.  Candidate score of register slot j = 16 m + 4 q4 + e:
-  // (acc[m][4 q4 + e] - lse) + prior.  Each lane holds 64 candidates of one
-  // beam, or none.
-  const float pr = (valid && p.prior) ? p.prior[(size_t)r * p.n_in + beam] : 0.f;
-  float *crow = (valid && p.cand) ? p.cand + ((size_t)r * p.n_in + beam) * 256 : nullptr;
-  const uint32_t row_base = (uint32_t)beam * 256u + ch * 128 + 4 * g;
-  auto idx_of = [&](int j) -> uint32_t {
-    return row_base + 32u * (uint32_t)(j >> 4) + 8u * (uint32_t)((j >> 2) & 3) + (uint32_t)(j & 3);
-  };
+  // ---- candidate scores (z - lse) + prior, in place
   const int n = nbg * 256;
   const int k_sel = min(p.k, n);
+  bool valid[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    valid[t] = 32 * t + c < nbg;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[t][j] = (acc[t][j] - lse[t]) + pr[t];
+    if (valid[t] && p.cand) {
+      float *crow = p.cand + ((size_t)r * p.n_in + b_begin + 32 * t + c) * 256 + 32 * wave + 4 * g;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(float4 *)(crow + 8 * q) = make_float4(acc[t][4 * q], acc[t][4 * q + 1], acc[t][4 * q + 2], acc[t][4 * q + 3]);
+    }
+  }
+  auto flat_of = [&](int t, int j) -> uint32_t {
+    return (uint32_t)(b_begin + 32 * t + c) * 256u + 32u * wave + 8u * (uint32_t)(j >> 2) + 4u * g + (uint32_t)(j & 3);
+  };
 
-  // Fast path.  If ml = ceil(k/64) lanes of one wave have no score below s,
-  // at least k candidates score >= s, so the k best all do.  s is the ml-th
-  // largest lane minimum of a wave (the largest such bound over the waves;
-  // lane extremes come from those of acc, the score being monotonic in it).
-  // Only lanes whose maximum reaches s can hold a selected candidate: they
-  // stage their 64 scores in LDS, and the exact selection runs over the
-  // staged candidates, 8 per thread.  If too many lanes qualify, or the bound
-  // is degenerate, it runs over all 64 register slots.  Every decision is
+  // ---- bounded selection (k <= 128).  A unit is the 16 scores one lane
+  // holds for one beam; its minimum u means 16 candidates score >= u.  The
+  // lane bound is its best unit minimum (a unit with a NaN score bounds
+  // nothing).  T is the ml-th best (ml = ceil(k/16)) of the waves' two best
+  // lane bounds: ml units hold 16 ml >= k candidates scoring >= T, so every
+  // selected candidate scores >= T, and only those are staged (by ballot,
+  // into one region per wave).  One 256-bin histogram of the staged rank
+  // keys over [best, T] finds the bin holding the k-th; the candidates up to
+  // that bin (at most 256, else the general path) are gathered and ordered
+  // by counting ranks.  Too many staged candidates or a degenerate bound go
+  // through the selection over all registers.  Every decision is
   // block-uniform.
-  bool cand_done = false, fast = false;
-  {
-    float amin = acc[0][0];
-    bool nan_in = false;                                // fminf / fmaxf skip NaN
-    if (p.lsm) {
+  bool done = false;
+  if (k_sel <= kFastK) {
+    const int ml = (k_sel + 15) >> 4;                   // <= 8
+    float lb = -__builtin_inff(), best = -__builtin_inff(), umax[4];
+    bool any = false;
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) amin = fminf(amin, acc[m][i]);
-    } else {
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          amin = fminf(amin, acc[m][i]);
-          nan_in = nan_in || acc[m][i] != acc[m][i];
-        }
+    for (int t = 0; t < 4; ++t) {
+      const float u = (lo[t] - lse[t]) + pr[t];
+      umax[t] = (hi[t] - lse[t]) + pr[t];
+      if (valid[t]) {
+        lb = fmaxf(lb, u != u ? -__builtin_inff() : u);
+        best = fmaxf(best, umax[t]);
+        any = true;
+      }
     }
-    // A lane with a NaN score (which ranks like -inf) bounds nothing.  With
-    // the log-softmax a NaN logit makes every score of its beam NaN, and so
-    // the lane minimum too.
-    const float lmin = nan_in ? -__builtin_inff() : (amin - lse) + pr, lmax = (amax - lse) + pr;
-    const uint32_t wkey = valid ? rank_key(lmin) : kInvalidKey;
-    const int ml = (k_sel + 63) >> 6;
-    uint32_t tw;                                        // ml-th smallest lane-minimum key of the wave
-    if (ml <= 2) {
-      tw = wave_small2_u32(wkey, ml);
-    } else {
-      uint64_t wv[1] = {((uint64_t)wkey << 32) | (uint32_t)lane};
-      wave_bitonic_sort_u64<1>(wv);                     // ascending keys: best lane minima first
-      tw = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(wv[0] >> 32), ml - 1);
-    }
-    if (lane == 0) sm.bound[wave] = tw;
-    __syncthreads();
-    uint32_t T = sm.bound[0];
-#pragma unroll
-    for (int w = 1; w < kNT / 64; ++w) T = min(T, sm.bound[w]);
-    const float Ts = key_score(T);
-    if (T != kInvalidKey && Ts > -__builtin_inff()) {
-      const bool has = valid && lmax >= Ts;
-      const uint64_t hm = __builtin_amdgcn_ballot_w64(has);
-      if (lane == 0) sm.fast_cnt[wave] = (uint32_t)__builtin_popcountll(hm);
-      __syncthreads();
-      int n_st = 0, base_w = 0;
+    uint32_t w1, w2;
+    wave_small2_pair_u32(any ? rank_key(lb) : kInvalidKey, w1, w2);
+    const uint32_t wh = wave_min_u32(any ? rank_key(best) : kInvalidKey);
+    if (lane == 0) sm.wbest[wave] = make_uint4(w1, w2, wh, 0u);
+    __syncthreads();                                    // also: the o buffers are no longer read
+    uint32_t kmin = kInvalidKey, T = kInvalidKey;
+    {
+      // lane i < 16 holds pick i; its rank among the 16 (ties by position)
+      uint32_t v = kInvalidKey;
+      int rank = 0;
 #pragma unroll
       for (int w = 0; w < kNT / 64; ++w) {
-        base_w += w < wave ? (int)sm.fast_cnt[w] : 0;
-        n_st += (int)sm.fast_cnt[w];
+        const uint4 b4 = sm.wbest[w];
+        kmin = min(kmin, b4.z);
+        if (lane == 2 * w) v = b4.x;
+        if (lane == 2 * w + 1) v = b4.y;
       }
-      const int S = n_st * 64;                           // staged candidates
-      if (S <= kFastList) {
-        fast = true;
-        cand_done = true;
-        float *st_v = reinterpret_cast<float *>(&sm.u.ring[0]);     // [n_st][64] scores
-        uint32_t *st_row = reinterpret_cast<uint32_t *>(st_v + kFastList);   // [n_st] row bases
-        const int s_idx = base_w + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(hm >> 32),
-                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)hm, 0u));
-        if (has || crow) {
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
+      for (int w = 0; w < kNT / 64; ++w) {
+        const uint4 b4 = sm.wbest[w];
+        rank += (b4.x < v || (b4.x == v && 2 * w < lane)) ? 1 : 0;
+        rank += (b4.y < v || (b4.y == v && 2 * w + 1 < lane)) ? 1 : 0;
+      }
+      const uint64_t m = __builtin_amdgcn_ballot_w64(lane < 16 && rank == ml - 1);
+      T = (uint32_t)__builtin_amdgcn_readlane((int)v, (int)__builtin_ctzll(m));
+    }
+    const float Ts = key_score(T);
+    if (T != kInvalidKey && Ts > -__builtin_inff()) {
+      uint64_t *reg = sm.u.sel.tmp + wave * kWaveStage;
+      uint32_t *hist = sm.u.sel.bstart;
+      uint32_t wc = 0;                                  // wave-uniform
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              float v[4];
+      for (int t = 0; t < 4; ++t) {
+        const bool ut = valid[t] && umax[t] >= Ts;
+        if (!__builtin_amdgcn_ballot_w64(ut)) continue;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = (acc[m][4 * q4 + e] - lse) + pr;
-              const float4 v4 = make_float4(v[0], v[1], v[2], v[3]);
-              if (crow) *(float4 *)(crow + ch * 128 + 32 * m + 8 * q4 + 4 * g) = v4;
-              if (has) *(float4 *)(st_v + s_idx * 64 + 16 * m + 4 * q4) = v4;
-            }
-          if (has) st_row[s_idx] = row_base;
+        for (int j = 0; j < 16; ++j) {
+          const bool q = ut && acc[t][j] >= Ts;
+          const uint64_t m = __builtin_amdgcn_ballot_w64(q);
+          if (m) {
+            // staged as (score, register slot and lane); keyed below, one entry a thread
+            const uint32_t pos = wc + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (q && pos < kWaveStage)
+              reg[pos] = ((uint64_t)(uint32_t)((16 * t + j) * 64 + lane) << 32) | __float_as_uint(acc[t][j]);
+            wc += (uint32_t)__builtin_popcountll(m);
+          }
+        }
+      }
+      if (tid < 256) hist[tid] = 0u;
+      if (lane == 0) sm.wcnt[wave] = wc;
+      if (tid == 0) sm.n_final = 0u;
+      __syncthreads();
+      int wmax = 0;
+#pragma unroll
+      for (int w = 0; w < kNT / 64; ++w) wmax = max(wmax, (int)sm.wcnt[w]);
+      if (wmax <= kWaveStage) {
+        // staged keys lie in [kmin, T]: digit = (key - kmin) >> shift < 256
+        const uint32_t range = T - kmin;
+        const int shift = range >> 8 ? 24 - __builtin_clz(range) : 0;
+        for (int i = lane; i < (int)wc; i += 64) {
+          const uint64_t e = reg[i];
+          const uint32_t sl = (uint32_t)(e >> 32), ln = sl & 63u, tj = sl >> 6;
+          const uint32_t key = rank_key(__uint_as_float((uint32_t)e));
+          const uint32_t flat = (uint32_t)(b_begin + 32 * (tj >> 4) + (ln & 31u)) * 256u + 32u * wave +
+                                8u * ((tj & 15u) >> 2) + 4u * (ln >> 5) + (tj & 3u);
+          reg[i] = ((uint64_t)key << 32) | flat;
+          atomicAdd(&hist[(key - kmin) >> shift], 1u);
         }
         __syncthreads();
-        // a bucket of at most pow2(k) + 1 - k members keeps the list within pow2(k)
-        const int cap = max(pow2_ceil(k_sel) + 1 - k_sel, 16);
-        // staged candidate t -> (key, flat index), NJ per thread (t = i kNT + tid)
-        auto select_staged = [&](auto nj) {
-          constexpr int NJ = decltype(nj)::value;
-          uint32_t keyj[NJ], idxj[NJ];
-#pragma unroll
-          for (int i = 0; i < NJ; ++i) {
-            const int t = i * kNT + tid, sl = t >> 6, j = t & 63;
-            keyj[i] = kInvalidKey;
-            idxj[i] = 0u;
-            if (t < S) {
-              keyj[i] = rank_key(st_v[t]);
-              idxj[i] = st_row[sl] + 32u * (uint32_t)(j >> 4) + 8u * (uint32_t)((j >> 2) & 3) + (uint32_t)(j & 3);
+        // the bin holding the k-th: every wave scans the 256 bins (4 a lane)
+        const uint4 h4 = reinterpret_cast<const uint4 *>(hist)[lane];
+        const uint32_t hs = h4.x + h4.y + h4.z + h4.w;
+        const uint32_t inc = wave_incl_scan_u32(hs), exc = inc - hs;
+        const bool mine = exc < (uint32_t)k_sel && inc >= (uint32_t)k_sel;
+        uint32_t bin = 0, below = exc, hb = h4.x;
+        if (mine) {
+          if (below + h4.x < (uint32_t)k_sel) {
+            below += h4.x; bin = 1; hb = h4.y;
+            if (below + h4.y < (uint32_t)k_sel) {
+              below += h4.y; bin = 2; hb = h4.z;
+              if (below + h4.z < (uint32_t)k_sel) { below += h4.z; bin = 3; hb = h4.w; }
             }
           }
-          __syncthreads();                                 // the staging area overlaps the selection state
-          select_regs<kNT, NJ>(keyj, [&](int i) -> uint32_t { return idxj[i]; }, S, k_sel, sm.u.sel, cap);
-        };
-        if (S <= kNT) select_staged(std::integral_constant<int, 1>{});
-        else select_staged(std::integral_constant<int, kFastList / kNT>{});
+        }
+        const int src = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(mine));
+        const uint32_t bstar = 4u * (uint32_t)src + (uint32_t)__builtin_amdgcn_readlane((int)bin, src);
+        const int L = __builtin_amdgcn_readlane((int)(below + hb), src);
+        if (L <= 256) {
+          done = true;
+          uint64_t *list = sm.u.sel.u.list;
+          for (int i0 = 0; i0 < (int)wc; i0 += 64) {
+            const int i = i0 + lane;
+            const uint64_t x = i < (int)wc ? reg[i] : ~0ull;
+            const bool q = i < (int)wc && (((uint32_t)(x >> 32) - kmin) >> shift) <= bstar;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(q);
+            if (m) {
+              uint32_t base = 0;
+              if (lane == 0) base = atomicAdd(&sm.n_final, (uint32_t)__builtin_popcountll(m));
+              base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+              if (q) list[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = x;
+            }
+          }
+          __syncthreads();
+          rank_sort_u64<kNT>(list, L);
+        }
       }
     }
   }
-  if (!fast) {
+  if (!done) {
     uint32_t key[64];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = (acc[m][4 * q4 + e] - lse) + pr;
-          key[16 * m + 4 * q4 + e] = valid ? rank_key(v[e]) : kInvalidKey;
-        }
-        if (crow && !cand_done)
-          *(float4 *)(crow + ch * 128 + 32 * m + 8 * q4 + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
-      }
-    __syncthreads();                                       // survivor regions may still be read
-    select_regs<kNT, 64>(key, idx_of, n, k_sel, sm.u.sel);
+      for (int j = 0; j < 16; ++j) key[16 * t + j] = valid[t] ? rank_key(acc[t][j]) : kInvalidKey;
+    __syncthreads();                                    // the o buffers / staging area are no longer read
+    select_regs<kNT, 64>(key, [&](int i) -> uint32_t { return flat_of(i >> 4, i & 15); }, n, k_sel, sm.u.sel);
   }
   emit_selection<kNT>(sm.u.sel, k_sel, r, grp, 256, p.score, p.token, p.parent, p.partial, p.n_groups, p.kk);
 }
@@ -520,7 +581,13 @@ hipError_t launch_logits_select_bf16(const LogitsArgs &a, const SelectOut &o, hi
   p.score = o.score; p.token = o.token; p.parent = o.parent; p.partial = o.partial;
   p.R = a.R; p.n_in = a.n_in; p.D = a.D; p.hd_log2 = __builtin_ctz((unsigned)a.hd); p.k = a.k;
   p.lsm = a.log_softmax; p.n_groups = o.n_groups; p.kk = o.kk;
-  hipLaunchKernelGGL(logits_select_bf16_kernel, dim3((unsigned)(a.R * o.n_groups)), dim3(kNT), 0, s, p);
+  const dim3 grid((unsigned)(a.R * o.n_groups));
+  if (a.D == 8 * kCB)
+    hipLaunchKernelGGL(logits_select_bf16_kernel<8>, grid, dim3(kNT), 0, s, p);
+  else if (a.D == 16 * kCB)
+    hipLaunchKernelGGL(logits_select_bf16_kernel<16>, grid, dim3(kNT), 0, s, p);
+  else
+    hipLaunchKernelGGL(logits_select_bf16_kernel<0>, grid, dim3(kNT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || o.n_groups == 1) return e;
   return launch_select_merge(o, a.R, a.k, 256, s);

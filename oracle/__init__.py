@@ -24,6 +24,9 @@ Modules:
   generate   whole-ID generation: the q/k/v table of each level's codes,
              every level's step with the chosen codes' records appended in
              between, and the final IDs traced back through the parents
+  broadcast  multi-layer broadcast scoring: a Pre-LN Transformer stack over
+             one user sequence (keys and values computed once) and many
+             single-token candidates, a scalar score each, exact top-k
 
 Pins: every function here is checked in tests/test_oracle_*.py against closed
 forms, library special cases, invariants and brute force (see the docstrings
@@ -36,11 +39,12 @@ from .attention import (attend_materialized, attend_masked, attend_split,
 from .beam import (codebook_logits, log_softmax, candidate_scores,
                    select_topk, decode_step, scalar_scores, beam_topk,
                    run_chained)
-from . import generate, linear
+from . import generate, linear, broadcast
 
 __all__ = [
     "trie_append", "chain", "TrieError", "new_arena", "attend_materialized",
     "attend_masked", "attend_split", "prefix_attn", "codebook_logits",
     "log_softmax", "candidate_scores", "select_topk", "decode_step",
     "scalar_scores", "beam_topk", "run_chained", "generate", "linear",
+    "broadcast",
 ]

@@ -40,6 +40,7 @@ __all__ = [
     "Config", "CONFIGS", "HEADLINE", "bf16_round", "make_step_inputs",
     "make_chained_inputs", "StepInputs", "ChainedInputs", "reduced",
     "GEN_CONFIGS", "GenInputs", "make_generate_inputs",
+    "XFConfig", "XF_CONFIGS", "XFInputs", "make_xf_inputs",
 ]
 
 
@@ -291,3 +292,102 @@ def make_generate_inputs(cfg: Config, d_emb: Optional[int] = None,
     w_qkv = _maybe_round(_normal(rng, (3 * D, d_emb), float(d_emb) ** -0.5), cfg.dtype)
     q0 = _maybe_round(_normal(rng, (R, 1, H, d)), cfg.dtype)
     return GenInputs(cfg, d_emb, pk, pv, q0, Wl, emb, w_qkv)
+
+
+# ---------------------------------------------------------------------------
+# Multi-layer broadcast scoring (TransRetrieval, Architecture Overview and
+# Model-based Retrieval: an xD-yL Pre-LN Transformer scoring ~4 x 10^4
+# single-token candidates per request against one user sequence; 128D-5L is
+# the largest configuration the page evaluates, Recall@2000 the cut).
+
+@dataclasses.dataclass(frozen=True)
+class XFConfig:
+    """R requests, each with Lu user tokens and N candidate tokens of width
+    D = 32 * heads, n_layers layers, k kept."""
+    name: str
+    index: int          # seed = 1000 + index
+    R: int
+    Lu: int
+    N: int
+    D: int
+    n_layers: int
+    k: int
+
+    @property
+    def H(self) -> int:
+        return self.D // 32
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.index
+
+
+XF_CONFIGS: Dict[str, XFConfig] = {c.name: c for c in [
+    XFConfig("xf128d5l_u256_c40k", 9, R=1, Lu=256, N=40000, D=128, n_layers=5, k=2000),
+]}
+
+
+@dataclasses.dataclass
+class XFInputs:
+    """Tokens and weights of a broadcast-scoring run, both as named arrays
+    (layers[l] is a dict: w_qkv [3D][D], b_qkv [3D], w_o [D][D], b_o [D],
+    w_1 [2D][D], b_1 [2D], w_2 [D][2D], b_2 [D], ln1_g, ln1_b, ln2_g, ln2_b
+    [D]; final lnf_g, lnf_b, w_score [D], b_score) and packed for the
+    device: w_mat bf16 values as float32, per layer w_qkv, w_o, w_1, w_2
+    (8 D^2 values); w_vec float32, per layer b_qkv, b_o, b_1, b_2, ln1_g,
+    ln1_b, ln2_g, ln2_b (11 D values), then lnf_g, lnf_b, w_score, b_score
+    (3 D + 1)."""
+    cfg: XFConfig
+    user: np.ndarray        # [R][Lu][D]
+    cand: np.ndarray        # [R][N][D]
+    layers: List[dict]
+    lnf_g: np.ndarray
+    lnf_b: np.ndarray
+    w_score: np.ndarray
+    b_score: float
+    w_mat: np.ndarray
+    w_vec: np.ndarray
+
+
+XF_MAT_KEYS = ("w_qkv", "w_o", "w_1", "w_2")
+XF_VEC_KEYS = ("b_qkv", "b_o", "b_1", "b_2", "ln1_g", "ln1_b", "ln2_g", "ln2_b")
+
+
+def make_xf_inputs(cfg: XFConfig, seed: Optional[int] = None, R: Optional[int] = None,
+                   N: Optional[int] = None) -> XFInputs:
+    """Draw order: user tokens, candidate tokens, then per layer w_qkv, w_o,
+    w_1, w_2, b_qkv, b_o, b_1, b_2, ln1_g, ln1_b, ln2_g, ln2_b, then lnf_g,
+    lnf_b, w_score, b_score.  Tokens ~ N(0, 1); weight matrices ~
+    N(0, 1/fan_in) (unit-variance activations through the stack); biases ~
+    N(0, 0.02); LayerNorm gains 1 + N(0, 0.1), biases N(0, 0.1).  Tokens and
+    weight matrices are rounded to bf16.  R and N override the request and
+    candidate counts (smaller parity runs draw the same way)."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    R = cfg.R if R is None else R
+    N = cfg.N if N is None else N
+    D = cfg.D
+    user = bf16_round(_normal(rng, (R, cfg.Lu, D)), inplace=True)
+    cand = bf16_round(_normal(rng, (R, N, D)), inplace=True)
+    layers = []
+    for _ in range(cfg.n_layers):
+        lp = {}
+        lp["w_qkv"] = bf16_round(_normal(rng, (3 * D, D), D ** -0.5), inplace=True)
+        lp["w_o"] = bf16_round(_normal(rng, (D, D), D ** -0.5), inplace=True)
+        lp["w_1"] = bf16_round(_normal(rng, (2 * D, D), D ** -0.5), inplace=True)
+        lp["w_2"] = bf16_round(_normal(rng, (D, 2 * D), (2 * D) ** -0.5), inplace=True)
+        lp["b_qkv"] = _normal(rng, (3 * D,), 0.02)
+        lp["b_o"] = _normal(rng, (D,), 0.02)
+        lp["b_1"] = _normal(rng, (2 * D,), 0.02)
+        lp["b_2"] = _normal(rng, (D,), 0.02)
+        for nm in ("ln1", "ln2"):
+            lp[nm + "_g"] = (1.0 + _normal(rng, (D,), 0.1)).astype(np.float32)
+            lp[nm + "_b"] = _normal(rng, (D,), 0.1)
+        layers.append(lp)
+    lnf_g = (1.0 + _normal(rng, (D,), 0.1)).astype(np.float32)
+    lnf_b = _normal(rng, (D,), 0.1)
+    w_score = _normal(rng, (D,), D ** -0.5)
+    b_score = float(_normal(rng, (1,), 0.02)[0])
+    w_mat = np.concatenate([lp[k].reshape(-1) for lp in layers for k in XF_MAT_KEYS]).astype(np.float32)
+    w_vec = np.concatenate([lp[k].reshape(-1) for lp in layers for k in XF_VEC_KEYS] +
+                           [lnf_g, lnf_b, w_score, np.array([b_score], np.float32)]).astype(np.float32)
+    return XFInputs(cfg, user, cand, layers, lnf_g, lnf_b, w_score, b_score, w_mat, w_vec)

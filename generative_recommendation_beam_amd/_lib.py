@@ -30,10 +30,12 @@ GR_DEVERR_DEPTH, GR_DEVERR_BEAM_RANGE, GR_DEVERR_TOKEN_RANGE = 4, 8, 16
 GR_TOPK_LOG_SOFTMAX = 1
 GR_STEP_ATTENTION, GR_STEP_SELECTION = 2, 4
 GR_MAX_DEPTH, GR_MAX_K = 8, 2048
+GR_XF_MAX_USER, GR_XF_MAX_LAYERS = 1024, 8
 
 EXPORTED = ["gr_trie_append", "gr_prefix_attn", "gr_beam_topk", "gr_decode_step", "gr_decode_step_noalloc",
             "gr_linear_state", "gr_linear_attn", "gr_linear_decode_step",
-            "gr_code_table", "gr_append_codes", "gr_generate",
+            "gr_code_table", "gr_append_codes", "gr_generate", "gr_broadcast_score",
+            "gr_broadcast_workspace_size",
             "gr_workspace_size", "gr_attn_workspace_size", "gr_topk_workspace_size",
             "gr_decode_workspace_size", "gr_generate_workspace_size", "gr_status_string"]
 
@@ -58,6 +60,14 @@ class Trie(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("parent", ctypes.c_void_p), ("capacity", ctypes.c_int32),
                 ("max_depth", ctypes.c_int32)]
+
+
+class XfShape(ctypes.Structure):
+    """gr_xf_shape: R requests of n_cand candidates and user_len user tokens,
+    d_model features, n_layers layers."""
+    _fields_ = [("R", ctypes.c_int32), ("n_cand", ctypes.c_int32),
+                ("user_len", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("n_layers", ctypes.c_int32)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -87,6 +97,8 @@ _sig = {
     "gr_generate": [ctypes.POINTER(Shape), _P, _P, _P, _I, _P, _P, _I, _I, ctypes.POINTER(Trie), _P, _P, _P, _P,
                     _P, _S, _P, _P],
     "gr_generate_workspace_size": [ctypes.POINTER(Shape), _I, _I, _I],
+    "gr_broadcast_score": [ctypes.POINTER(XfShape), _P, _P, _P, _P, _I, _P, _P, _P, _P, _S, _P],
+    "gr_broadcast_workspace_size": [ctypes.POINTER(XfShape), _I],
     "gr_workspace_size": [ctypes.POINTER(Shape), _I, _I, _I],
     "gr_attn_workspace_size": [ctypes.POINTER(Shape), _I],
     "gr_topk_workspace_size": [_I, _I, _I, _I],
@@ -98,7 +110,7 @@ for _name, _args in _sig.items():
     _f.argtypes = _args
     _f.restype = ctypes.c_int32
 for _name in ("gr_workspace_size", "gr_attn_workspace_size", "gr_topk_workspace_size", "gr_decode_workspace_size",
-              "gr_generate_workspace_size"):
+              "gr_generate_workspace_size", "gr_broadcast_workspace_size"):
     getattr(_lib, _name).restype = ctypes.c_size_t
 _lib.gr_status_string.restype = ctypes.c_char_p
 
@@ -227,6 +239,17 @@ def gr_generate(shape, prompt_k, prompt_v, q0, levels, W, tables, vocab, beam_wi
 
 def gr_generate_workspace_size(shape, levels, vocab, beam_width) -> int:
     return int(_lib.gr_generate_workspace_size(_shape_ref(shape), int(levels), int(vocab), int(beam_width)))
+
+
+def gr_broadcast_score(shape, user_tok, cand_tok, w_mat, w_vec, k, out_score, out_index, cand_scores, ws,
+                       ws_bytes, stream=None):
+    _check(_lib.gr_broadcast_score(ctypes.byref(shape), _ptr(user_tok), _ptr(cand_tok), _ptr(w_mat), _ptr(w_vec),
+                                   int(k), _ptr(out_score), _ptr(out_index), _ptr(cand_scores), _ptr(ws),
+                                   int(ws_bytes), _stream(stream)), "gr_broadcast_score")
+
+
+def gr_broadcast_workspace_size(shape, k) -> int:
+    return int(_lib.gr_broadcast_workspace_size(ctypes.byref(shape), int(k)))
 
 
 def gr_workspace_size(shape, n_beams, vocab, k) -> int:

@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgrbeam.so")
-SOURCES = ["api.cpp", "attn.hip", "score.hip", "trie.hip", "generate.hip", "linear.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "attn.hip", "score.hip", "trie.hip", "generate.hip", "linear.hip", "noalloc.hip", "xf.hip"]
 
 
 def hipcc() -> str:

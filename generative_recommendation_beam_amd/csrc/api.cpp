@@ -361,6 +361,89 @@ const char *gr_status_string(gr_status s) {
   }
 }
 
+// ---- multi-layer broadcast scoring
+
+namespace {
+
+gr_status check_xf(const gr_xf_shape *s, int32_t k) {
+  if (!s) return GR_ERR_NULL;
+  if (s->R <= 0 || s->n_cand <= 0 || s->user_len <= 0 || s->n_layers <= 0 || k <= 0) return GR_ERR_SHAPE;
+  if (s->d_model != 128 || s->user_len % 32 != 0 || s->user_len > GR_XF_MAX_USER ||
+      s->n_layers > GR_XF_MAX_LAYERS)
+    return GR_ERR_UNSUPPORTED;
+  if ((long long)s->R * s->n_cand * s->d_model > (1ll << 40) || s->n_cand > (1 << 30)) return GR_ERR_SHAPE;
+  return check_select(s->R, s->n_cand, 1, k, 0);
+}
+
+struct XfLayout {
+  size_t ukv_off, ukv_bytes, st_off, st_bytes, sc_off, sc_bytes, tok_off, tok_bytes, part_off, part_bytes, total;
+};
+XfLayout xf_layout(const gr_xf_shape *s, int32_t k) {
+  XfLayout L;
+  L.ukv_bytes = align_up(gr::xf_ukv_bytes(s->R, s->n_layers, s->user_len));
+  L.st_bytes = align_up(gr::xf_user_state_bytes(s->R, s->user_len));
+  L.sc_bytes = align_up((size_t)s->R * s->n_cand * sizeof(float));
+  L.tok_bytes = align_up((size_t)s->R * k * sizeof(int32_t));
+  L.part_bytes = sel_geo(s->R, s->n_cand, 1, k).bytes;
+  L.ukv_off = 0;
+  L.st_off = L.ukv_off + L.ukv_bytes;
+  L.sc_off = L.st_off + L.st_bytes;
+  L.tok_off = L.sc_off + L.sc_bytes;
+  L.part_off = L.tok_off + L.tok_bytes;
+  L.total = L.part_off + L.part_bytes + kAlign;
+  return L;
+}
+
+}  // namespace
+
+size_t gr_broadcast_workspace_size(const gr_xf_shape *shape, int32_t k) {
+  if (!shape || shape->R <= 0 || shape->n_cand <= 0 || shape->user_len <= 0 || shape->n_layers <= 0 || k <= 0)
+    return 0;
+  return xf_layout(shape, k).total;
+}
+
+gr_status gr_broadcast_score(const gr_xf_shape *shape, const void *user_tok, const void *cand_tok,
+                             const void *w_mat, const float *w_vec, int32_t k, float *out_score,
+                             int32_t *out_index, float *cand_scores, void *ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  gr_status st = check_xf(shape, k);
+  if (st) return st;
+  if (!user_tok || !cand_tok || !w_mat || !w_vec || !out_score || !out_index) return GR_ERR_NULL;
+  if (!aligned16(user_tok) || !aligned16(cand_tok) || !aligned16(w_mat) || !aligned16(w_vec) ||
+      (cand_scores && !aligned16(cand_scores)))
+    return GR_ERR_UNSUPPORTED;
+  const XfLayout L = xf_layout(shape, k);
+  if (!ws || ws_bytes < L.total) return GR_ERR_WORKSPACE;
+  char *base = align_ptr(ws);
+  gr::XfArgs a;
+  a.user = user_tok;
+  a.cand = cand_tok;
+  a.w_mat = w_mat;
+  a.w_vec = w_vec;
+  a.ukv = base + L.ukv_off;
+  a.user_state = base + L.st_off;
+  a.score = cand_scores ? cand_scores : (float *)(base + L.sc_off);
+  a.R = shape->R;
+  a.N = shape->n_cand;
+  a.Lu = shape->user_len;
+  a.L = shape->n_layers;
+  clear_stale_error();
+  hipError_t e = gr::launch_xf_scores(a, stream);
+  if (e != hipSuccess) return hip_status(e);
+  gr::ScoreSelectArgs sa;
+  sa.logits = a.score;
+  sa.prior = nullptr;
+  sa.cand_out = nullptr;
+  sa.R = shape->R;
+  sa.n_in = shape->n_cand;
+  sa.vocab = 1;
+  sa.k = k;
+  sa.log_softmax = 0;
+  const gr::SelectOut o = make_out(out_score, (int32_t *)(base + L.tok_off), out_index,
+                                   L.part_bytes ? base + L.part_off : nullptr, shape->R, shape->n_cand, 1, k);
+  return hip_status(gr::launch_score_select(sa, o, stream));
+}
+
 size_t gr_attn_workspace_size(const gr_shape *shape, int32_t n_beams) {
   if (check_shape(shape) || n_beams <= 0) return 0;
   const size_t b = attn_ids_bytes(shape, n_beams) + attn_split_ws_bytes(shape, n_beams);

@@ -138,6 +138,20 @@ struct TraceArgs {
 };
 hipError_t launch_trace_ids(const TraceArgs &a, hipStream_t s);
 
+// Multi-layer broadcast scoring (xf.hip): D = 128, 4 heads of 32, FFN 2D.
+struct XfArgs {
+  const void *user, *cand;     // [R][Lu][D], [R][N][D] bf16
+  const void *w_mat;           // [L][8 D^2] bf16: w_qkv [3D][D], w_o [D][D], w_1 [2D][D], w_2 [D][2D]
+  const float *w_vec;          // [L][11 D] fp32 (b_qkv, b_o, b_1, b_2, ln1 g/b, ln2 g/b), then lnf g/b, w_score, b_score
+  void *ukv;                   // workspace: the user keys/values of every layer, xf_ukv_bytes
+  void *user_state;            // workspace: the user tokens' x and queries between layers, xf_user_state_bytes
+  float *score;                // [R][N]
+  int R, N, Lu, L;
+};
+size_t xf_ukv_bytes(int R, int L, int Lu);
+size_t xf_user_state_bytes(int R, int Lu);
+hipError_t launch_xf_scores(const XfArgs &a, hipStream_t s);
+
 // Selection outputs / partial lists shared by the scoring kernels.
 struct SelectOut {
   float *score;

@@ -1,0 +1,689 @@
+// Multi-layer broadcast scoring: one user sequence and many single-token
+// candidates through a Pre-LN Transformer stack, one scalar score per
+// candidate.
+//
+// TransRetrieval, Architecture Overview (stage 4: N-layer Pre-LN Transformer
+// with a ReLU FFN; the user-side keys and values of a request are cached once
+// and reused by all of its candidates), the per-candidate cost paragraph
+// (each candidate has its own Q/K/V/output projections and FFN and attends to
+// the whole user sequence), Hardware-aware inference optimization (the one
+// user cache is broadcast to every candidate without copies; single-token
+// candidates are packed into batched products and kept apart) and GPU
+// retrieval (the selection stays on the device).
+//
+// Model: width D = 128 (4 heads of 32), FFN width 2D, LayerNorm eps 1e-5,
+// biases on every projection; a candidate attends to the layer's user keys
+// and to its own key; after the last layer a final LayerNorm and a linear
+// head give the score.
+//
+// Layout of a wave's tokens.  A wave owns 32 tokens (candidates, or user
+// tokens) and keeps everything about them in registers: the residual stream
+// x in fp32, and each product's output, in the accumulator layout of
+// v_mfma_f32_32x32x16_bf16 transposed (features x tokens: lane (c, g) holds
+// token c).  The A operand of every product is a weight (or user key /
+// value) row read from LDS, and its rows are taken in the order
+// pi(m) = m with bits 2 and 3 swapped: output row m of the tile then holds
+// feature 16 (i >> 3) + 8 g + (i & 7) at accumulator index i, i.e. eight
+// consecutive features per half of the tile, which are exactly the eight
+// k-values the lane supplies as the B operand of the next product.  No
+// activation ever goes through LDS; LayerNorm statistics are in-lane sums
+// plus one lane^32 swap.
+//
+// Weights, the per-layer vectors (biases, LayerNorm gains) and the user keys
+// and values stream HBM/L2 -> LDS through a ring of two 32 KB slots
+// (global_load_lds, one piece ahead of the products); all the workgroup's
+// waves read each piece.  Weight rows are stored with a 16-byte chunk
+// swizzle (chunk ^ row & 15) so that the 32 rows a read touches hit distinct
+// banks.  The user keys and values of a layer are written by the user pass
+// in exactly the ring's layout (per head, per 256 keys: K [key][32] with
+// chunk ^ (key >> 2) & 3, then V^T [32][key] with chunk ^ dim & 15), so the
+// candidates copy them as they are.
+//
+// xf_user_kernel: one launch per layer over the user tokens of every
+// request; launch l finishes layer l-1 (attention over the user keys of
+// l-1, output projection, FFN) and forms layer l's queries, keys and values.
+// xf_cand_kernel: all layers for 4 x 32 candidates per workgroup, then the
+// final LayerNorm and the score.
+
+#include "gr_device.h"
+#include "gr_launch.h"
+
+namespace gr {
+namespace {
+
+constexpr int kXD = 128;                // model width
+constexpr int kXHeads = 4;
+constexpr int kXHd = 32;                // head dim
+constexpr int kXFF = 2 * kXD;           // FFN width
+constexpr int kXSlot = 32768;           // ring slot bytes
+constexpr int kXVecBytes = 6144;        // per-layer vectors (11 D floats) or the final ones (3 D + 1)
+constexpr int kXLayerVec = 11 * kXD;    // floats per layer in the vector buffer
+constexpr int kXMat = 8 * kXD * kXD;    // bf16 values per layer in the matrix buffer
+// offsets inside a layer's vectors
+constexpr int kVbQKV = 0, kVbO = 3 * kXD, kVb1 = 4 * kXD, kVb2 = 6 * kXD, kVln1g = 7 * kXD, kVln1b = 8 * kXD,
+              kVln2g = 9 * kXD, kVln2b = 10 * kXD;
+// offsets inside a layer's matrices
+constexpr int kMqkv = 0, kMo = 3 * kXD * kXD, kM1 = 4 * kXD * kXD, kM2 = 6 * kXD * kXD;
+constexpr float kXLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int xpi(int m) { return (m & 0x13) | ((m & 8) >> 1) | ((m & 4) << 1); }
+
+// A copy of a lane value that the compiler must treat as changed here:
+// offsets derived from it are recomputed at each use instead of being
+// hoisted out of the piece loop and held in registers for the whole kernel.
+__device__ __forceinline__ int fresh(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+struct XfSmem {
+  unsigned char ring[2][kXSlot];
+  float vec[kXVecBytes / 4];
+};
+
+// ---- ring pieces -----------------------------------------------------------
+// Each DMA instruction moves 1 KB (64 lanes x 16 bytes) or, for vectors,
+// 256 bytes (dma4).  Pieces are split over the workgroup's NW waves.
+
+// nrows weight rows of 256 bytes (128 bf16) into a slot: row i comes from
+// src_row(i); LDS chunk ^ (i & 15).
+template <int NW, typename RowFn>
+__device__ __forceinline__ void dma_rows(unsigned char *slot, int nrows, RowFn src_row, int wave, int lane) {
+  const int nblk = nrows / 4;
+  lane = fresh(lane);
+  for (int b = wave; b < nblk; b += NW) {
+    const int row = 4 * b + (lane >> 4), pc = lane & 15;
+    const uint16_t *src = src_row(row) + 8 * (pc ^ (row & 15));
+    dma16(src, slot + b * 1024);
+  }
+}
+// the 32 columns 32 h .. of the 128 rows of W_o ([D][D]) into 64-byte rows
+// (chunk ^ (row >> 2) & 3)
+template <int NW>
+__device__ __forceinline__ void dma_wo_cols(unsigned char *dst, const uint16_t *wo, int h, int wave, int lane) {
+  lane = fresh(lane);
+  for (int b = wave; b < 8; b += NW) {
+    const int row = 16 * b + (lane >> 2), pc = lane & 3;
+    dma16(wo + (size_t)row * kXD + 32 * h + 8 * (pc ^ ((row >> 2) & 3)), dst + b * 1024);
+  }
+}
+// a contiguous run of bytes (a multiple of 1 KB)
+template <int NW>
+__device__ __forceinline__ void dma_copy(unsigned char *dst, const unsigned char *src, int bytes, int wave, int lane) {
+  lane = fresh(lane);
+  for (int b = wave; b < bytes / 1024; b += NW) dma16(src + b * 1024 + lane * 16, dst + b * 1024);
+}
+// n floats (dma4, 64 per instruction; the tail re-reads the last float)
+template <int NW>
+__device__ __forceinline__ void dma_floats(float *dst, const float *src, int n, int wave, int lane) {
+  lane = fresh(lane);
+  for (int b = wave; b < (n + 63) / 64; b += NW) dma4(src + min(64 * b + lane, n - 1), dst + 64 * b);
+}
+
+// ---- wave math ---------------------------------------------------------------
+typedef f32x16 Acc;
+
+__device__ __forceinline__ bf16x8 pack8(const Acc &a, int s) {
+  bf16x8 r;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) r[t] = (__bf16)a[8 * s + t];
+  return r;
+}
+
+// LayerNorm of the wave's 32 tokens (x: 4 tiles of 32 features), gains and
+// biases from LDS; writes the bf16 B operands h[ft][s].
+__device__ __forceinline__ void layer_norm_b(const Acc (&x)[4], const float *gain, const float *bias, int g,
+                                             bf16x8 (&h)[4][2]) {
+  g = fresh(g);
+  float s = 0.f;
+#pragma unroll
+  for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += x[ft][i];
+  const float mean = xor32_sum(s) * (1.f / kXD);
+  float v = 0.f;
+#pragma unroll
+  for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float d = x[ft][i] - mean;
+      v = fmaf(d, d, v);
+    }
+  const float rstd = 1.f / sqrtf(xor32_sum(v) * (1.f / kXD) + 1e-5f);
+#pragma unroll
+  for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int f0 = 32 * ft + 16 * s2 + 8 * g;
+      const float4 g0 = *(const float4 *)(gain + f0), g1 = *(const float4 *)(gain + f0 + 4);
+      const float4 b0 = *(const float4 *)(bias + f0), b1 = *(const float4 *)(bias + f0 + 4);
+      const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      bf16x8 r;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) r[t] = (__bf16)fmaf((x[ft][8 * s2 + t] - mean) * rstd, gg[t], bb[t]);
+      h[ft][s2] = r;
+    }
+}
+
+// acc += W[rows row0 + pi(c)] . h over K = 32 * NFT inputs; W rows of 256 bytes
+// in LDS (chunk-swizzled), input columns col0 .. of those rows.
+template <int NFT>
+__device__ __forceinline__ void gemm_tile(Acc &acc, const unsigned char *w, int row0, int c, int g,
+                                          const bf16x8 (&h)[NFT][2]) {
+  const int cf = fresh(c), gf = fresh(g);
+  const int row = row0 + xpi(cf);
+  const unsigned char *wr = w + row * 256;
+  const int sw = row & 15;
+#pragma unroll
+  for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 a = *(const bf16x8 *)(wr + 16 * ((4 * ft + 2 * s + gf) ^ sw));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, h[ft][s], acc, 0, 0, 0);
+    }
+}
+
+// x[ot] += W_o[32 ot + pi(c)][head h's 32 columns] . o_h: the head's column
+// block of W_o in LDS, 128 rows of 64 bytes (chunk ^ (row >> 2) & 3).
+__device__ __forceinline__ void oproj_head(Acc (&x)[4], const unsigned char *wo, int c, int g, const bf16x8 (&ob)[2]) {
+  const int cf = fresh(c), gf = fresh(g);
+#pragma unroll
+  for (int ot = 0; ot < 4; ++ot) {
+    const int row = 32 * ot + xpi(cf);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 a = *(const bf16x8 *)(wo + row * 64 + 16 * ((2 * s + gf) ^ ((row >> 2) & 3)));
+      x[ot] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ob[s], x[ot], 0, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void zero(Acc &a) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a[i] = 0.f;
+}
+// add the bias of features f0 + 16 s + 8 g + t
+__device__ __forceinline__ void add_bias(Acc &a, const float *b, int g) {
+  g = fresh(g);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const float4 b0 = *(const float4 *)(b + 16 * s + 8 * g), b1 = *(const float4 *)(b + 16 * s + 8 * g + 4);
+    a[8 * s + 0] += b0.x; a[8 * s + 1] += b0.y; a[8 * s + 2] += b0.z; a[8 * s + 3] += b0.w;
+    a[8 * s + 4] += b1.x; a[8 * s + 5] += b1.y; a[8 * s + 6] += b1.z; a[8 * s + 7] += b1.w;
+  }
+}
+
+// Online-softmax state of one head for the wave's 32 tokens.
+struct HeadState {
+  Acc o;          // output dims (accumulator layout), unnormalised
+  float m, l;     // running max (log2 units) and this lane's partial sum
+};
+
+// One piece of user keys/values (up to 256 keys; n_kt tiles of 32) folded
+// into the state: S^T = K q^T, p = exp2(S * sl2 - m), O^T += V^T P^T.
+__device__ __forceinline__ void attend_piece(HeadState &st, const unsigned char *piece, int n_kt, int c, int g,
+                                             const bf16x8 (&qb)[2], float sl2) {
+  const unsigned char *kp = piece, *vp = piece + 16384;
+  c = fresh(c);
+  g = fresh(g);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    Acc s;
+    zero(s);
+    const int key = 32 * kt + xpi(c);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const bf16x8 a = *(const bf16x8 *)(kp + key * 64 + 16 * ((2 * s2 + g) ^ ((key >> 2) & 3)));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[s2], s, 0, 0, 0);
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    const float m_new = fmaxf(st.m, xor32_max(mx) * sl2);
+    const float corr = fast_exp2(st.m - m_new);
+    st.l *= corr;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.o[i] *= corr;
+    st.m = m_new;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[i] = fast_exp2(fmaf(s[i], sl2, -m_new));
+      st.l += s[i];
+    }
+    const int dim = xpi(c);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int ch = 4 * kt + 2 * s2 + g;   // 16-byte chunk of the keys of this k-step
+      const bf16x8 a = *(const bf16x8 *)(vp + dim * 512 + 16 * (ch ^ (dim & 15)));
+      st.o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pack8(s, s2), st.o, 0, 0, 0);
+    }
+  }
+}
+
+// ---- candidate kernel --------------------------------------------------------
+struct XfCandP {
+  const uint16_t *cand;     // [R][N][D] bf16
+  const uint16_t *w_mat;    // [L][8 D^2] bf16
+  const float *w_vec;       // [L][11 D] + [3 D + 1]
+  const unsigned char *ukv; // user K/V pieces [R][L][H][n_kc][32 KB]
+  float *score;             // [R][N]
+  int R, N, L, n_kc, Lu;
+  float sl2;                // log2(e) / sqrt(32)
+};
+
+constexpr int kXCandWaves = 4;
+
+__global__ __launch_bounds__(kXCandWaves * 64, 2) void xf_cand_kernel(XfCandP p) {
+  constexpr int NW = kXCandWaves;
+  __shared__ __attribute__((aligned(1024))) XfSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, c = lane & 31;
+  const int tiles = (p.N + 32 * NW - 1) / (32 * NW);
+  const int r = blockIdx.x / tiles, tb = blockIdx.x % tiles;
+  const int n = (tb * NW + wave) * 32 + c;
+  const int nl = min(n, p.N - 1);
+
+  // the residual stream of this lane's token, features 32 ft + 16 s + 8 g + t
+  Acc x[4];
+  {
+    const uint16_t *src = p.cand + ((size_t)r * p.N + nl) * kXD + 8 * g;
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 v = *(const bf16x8 *)(src + 32 * ft + 16 * s);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) x[ft][8 * s + t] = (float)v[t];
+      }
+  }
+
+  // Pieces of a layer: per head h, its q, k, v weight rows (24 KB) with
+  // the W_o columns of head h - 1 (8 KB; the layer's vectors come with
+  // head 0), then its user keys/values (n_kc pieces); the W_o columns of the
+  // last head; two FFN halves (W1 rows, W2 columns).  After the last layer
+  // the final vectors.  The output projection is applied head by head, at
+  // the piece after the head's attention.
+  const int per_head = 1 + p.n_kc;
+  const int per_layer = kXHeads * per_head + 5;
+  const int n_pieces = p.L * per_layer + 1;
+  const unsigned char *ukv_r = p.ukv + (size_t)r * p.L * kXHeads * p.n_kc * kXSlot;
+  auto issue = [&](int pc) {
+    if (pc >= n_pieces) return;
+    unsigned char *slot = sm.ring[pc & 1];
+    if (pc == n_pieces - 1) {
+      dma_floats<NW>(sm.vec, p.w_vec + (size_t)p.L * kXLayerVec, 3 * kXD + 1, wave, lane);
+      return;
+    }
+    const int l = pc / per_layer, q = pc % per_layer;
+    const uint16_t *wm = p.w_mat + (size_t)l * kXMat;
+    if (q < kXHeads * per_head) {
+      const int h = q / per_head, j = q % per_head;
+      if (j == 0) {
+        if (h == 0) dma_floats<NW>(sm.vec, p.w_vec + (size_t)l * kXLayerVec, kXLayerVec, wave, lane);
+        else dma_wo_cols<NW>(slot + 24576, wm + kMo, h - 1, wave, lane);
+        dma_rows<NW>(slot, 96, [&](int i) { return wm + kMqkv + (size_t)((i >> 5) * kXD + 32 * h + (i & 31)) * kXD; },
+                     wave, lane);
+      } else {
+        dma_copy<NW>(slot, ukv_r + ((size_t)(l * kXHeads + h) * p.n_kc + (j - 1)) * kXSlot, kXSlot, wave, lane);
+      }
+      return;
+    }
+    const int e = q - kXHeads * per_head;
+    if (e == 0) {
+      dma_wo_cols<NW>(slot, wm + kMo, kXHeads - 1, wave, lane);
+    } else if ((e & 1) == 1) {
+      const int fh = e >> 1;
+      dma_rows<NW>(slot, 128, [&](int i) { return wm + kM1 + (size_t)(128 * fh + i) * kXD; }, wave, lane);
+    } else {
+      const int fh = (e >> 1) - 1;
+      dma_rows<NW>(slot, 128, [&](int i) { return wm + kM2 + (size_t)i * kXFF + 128 * fh; }, wave, lane);
+    }
+  };
+  // wait for piece pc (the only one in flight), make it visible, prefetch
+  // the next one into the other slot
+  auto step = [&](int pc) -> const unsigned char * {
+    GR_WAIT_VMCNT_LGKM0(0);
+    ring_barrier();
+    issue(pc + 1);
+    return sm.ring[pc & 1];
+  };
+
+  issue(0);
+  int pc = 0;
+  bf16x8 hB[4][2];
+  for (int l = 0; l < p.L; ++l) {
+    bf16x8 ob[2];                                      // the previous head's output
+    for (int h = 0; h < kXHeads; ++h) {
+      const unsigned char *w = step(pc++);
+      if (h == 0) {
+        layer_norm_b(x, sm.vec + kVln1g, sm.vec + kVln1b, g, hB);
+      } else {
+        oproj_head(x, w + 24576, c, g, ob);
+        if (h == 1) {
+#pragma unroll
+          for (int ot = 0; ot < 4; ++ot) add_bias(x[ot], sm.vec + kVbO + 32 * ot, g);
+        }
+      }
+      Acc qa, ka;
+      zero(qa); zero(ka);
+      gemm_tile<4>(qa, w, 0, c, g, hB);
+      gemm_tile<4>(ka, w, 32, c, g, hB);
+      add_bias(qa, sm.vec + kVbQKV + 32 * h, g);
+      add_bias(ka, sm.vec + kVbQKV + kXD + 32 * h, g);
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ss = fmaf(qa[i], ka[i], ss);
+      const float s_self = xor32_sum(ss) * p.sl2;     // own key, log2 units
+      const bf16x8 qb[2] = {pack8(qa, 0), pack8(qa, 1)};
+      Acc va;
+      zero(va);
+      gemm_tile<4>(va, w, 64, c, g, hB);
+      add_bias(va, sm.vec + kVbQKV + 2 * kXD + 32 * h, g);
+      HeadState st;
+      zero(st.o);
+      st.m = s_self;                                   // the own key starts the running max
+      st.l = 0.f;
+      for (int j = 0; j < p.n_kc; ++j) {
+        const unsigned char *kv = step(pc++);
+        attend_piece(st, kv, min(8, (p.Lu - 256 * j) >> 5), c, g, qb, p.sl2);
+      }
+      // own key: p_self = exp2(s_self - m), counted once in the sum
+      const float p_self = fast_exp2(s_self - st.m);
+      const float inv = 1.f / (xor32_sum(st.l) + p_self);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.o[i] = (st.o[i] + p_self * va[i]) * inv;
+      ob[0] = pack8(st.o, 0);
+      ob[1] = pack8(st.o, 1);
+    }
+    {
+      const unsigned char *w = step(pc++);
+      oproj_head(x, w, c, g, ob);
+      layer_norm_b(x, sm.vec + kVln2g, sm.vec + kVln2b, g, hB);
+    }
+    for (int fh = 0; fh < 2; ++fh) {
+      bf16x8 uB[4][2];
+      {
+        const unsigned char *w = step(pc++);
+#pragma unroll
+        for (int ot = 0; ot < 4; ++ot) {
+          Acc a;
+          zero(a);
+          gemm_tile<4>(a, w, 32 * ot, c, g, hB);
+          add_bias(a, sm.vec + kVb1 + 128 * fh + 32 * ot, g);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) a[i] = fmaxf(a[i], 0.f);
+          uB[ot][0] = pack8(a, 0);
+          uB[ot][1] = pack8(a, 1);
+        }
+      }
+      const unsigned char *w = step(pc++);
+#pragma unroll
+      for (int ot = 0; ot < 4; ++ot) {
+        gemm_tile<4>(x[ot], w, 32 * ot, c, g, uB);
+        if (fh == 0) add_bias(x[ot], sm.vec + kVb2 + 32 * ot, g);
+      }
+    }
+  }
+  // final LayerNorm and the score head
+  step(pc++);
+  {
+    const float *gain = sm.vec, *bias = sm.vec + kXD, *w = sm.vec + 2 * kXD;
+    float s = 0.f;
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s += x[ft][i];
+    const float mean = xor32_sum(s) * (1.f / kXD);
+    float v = 0.f;
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float d = x[ft][i] - mean;
+        v = fmaf(d, d, v);
+      }
+    const float rstd = 1.f / sqrtf(xor32_sum(v) * (1.f / kXD) + 1e-5f);
+    float dot = 0.f;
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int f = 32 * ft + 16 * (i >> 3) + 8 * g + (i & 7);
+        dot = fmaf(fmaf((x[ft][i] - mean) * rstd, gain[f], bias[f]), w[f], dot);
+      }
+    dot = xor32_sum(dot) + sm.vec[3 * kXD];
+    if (g == 0 && n < p.N) p.score[(size_t)r * p.N + n] = dot;
+  }
+}
+
+// ---- user kernel ---------------------------------------------------------------
+// Per (request, layer) launch over all user tokens of the request, one wave
+// per 32 tokens.  The wave's state between launches lives in the workspace:
+// x (fp32, the accumulator layout: 256 bytes a lane) and the queries of the
+// four heads (bf16 B operands: 128 bytes a lane).
+struct XfUserP {
+  const uint16_t *user;     // [R][Lu][D] bf16
+  const uint16_t *w_mat;
+  const float *w_vec;
+  unsigned char *ukv;       // user K/V pieces [R][L][H][n_kc][32 KB]
+  float *xs;                // [R][Lu/32][64 lanes][64] fp32
+  uint16_t *qs;             // [R][Lu/32][64 lanes][4 heads][16] bf16
+  int R, L, n_kc, Lu, layer;
+  float sl2;
+};
+
+constexpr int kXUserWaves = 8;
+
+__global__ __launch_bounds__(kXUserWaves * 64) void xf_user_kernel(XfUserP p) {
+  constexpr int NW = kXUserWaves;
+  __shared__ __attribute__((aligned(1024))) XfSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, c = lane & 31;
+  const int n_ut = p.Lu / 32;
+  const int wg_per_r = (n_ut + NW - 1) / NW;
+  const int r = blockIdx.x / wg_per_r;
+  const int ut = (blockIdx.x % wg_per_r) * NW + wave;    // this wave's token tile
+  const bool live = ut < n_ut;                           // waves past the last tile only help with the DMA
+  const int utl = min(ut, n_ut - 1);
+  const int l = p.layer;
+  float *xs = p.xs + (((size_t)r * n_ut + utl) * 64 + lane) * 64;
+  uint16_t *qs = p.qs + (((size_t)r * n_ut + utl) * 64 + lane) * 64;
+  unsigned char *ukv_r = p.ukv + (size_t)r * p.L * kXHeads * p.n_kc * kXSlot;
+
+  Acc x[4];
+  if (l == 0) {
+    const uint16_t *src = p.user + ((size_t)r * p.Lu + 32 * utl + c) * kXD + 8 * g;
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 v = *(const bf16x8 *)(src + 32 * ft + 16 * s);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) x[ft][8 * s + t] = (float)v[t];
+      }
+  } else {
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 v = *(const float4 *)(xs + 16 * ft + 4 * i4);
+        x[ft][4 * i4] = v.x; x[ft][4 * i4 + 1] = v.y; x[ft][4 * i4 + 2] = v.z; x[ft][4 * i4 + 3] = v.w;
+      }
+  }
+
+  // Pieces: (layer > 0) for each head the user K/V of layer l-1 (n_kc
+  // pieces) and the head's W_o columns (with the vectors of l-1 at head 0),
+  // the FFN halves of l-1; then the q/k/v rows of layer l per head (the
+  // vectors of l with head 0).
+  const int per_head = p.n_kc + 1;
+  const int n_fin = l > 0 ? kXHeads * per_head + 4 : 0;
+  const int n_pieces = n_fin + kXHeads;
+  auto issue = [&](int pc) {
+    if (pc >= n_pieces) return;
+    unsigned char *slot = sm.ring[pc & 1];
+    if (pc < n_fin) {
+      const int lp = l - 1;
+      const uint16_t *wm = p.w_mat + (size_t)lp * kXMat;
+      if (pc < kXHeads * per_head) {
+        const int h = pc / per_head, j = pc % per_head;
+        if (j < p.n_kc) {
+          dma_copy<NW>(slot, ukv_r + ((size_t)(lp * kXHeads + h) * p.n_kc + j) * kXSlot, kXSlot, wave, lane);
+        } else {
+          if (h == 0) dma_floats<NW>(sm.vec, p.w_vec + (size_t)lp * kXLayerVec, kXLayerVec, wave, lane);
+          dma_wo_cols<NW>(slot, wm + kMo, h, wave, lane);
+        }
+        return;
+      }
+      const int e = pc - kXHeads * per_head;          // 0..3: W1 half 0, W2 half 0, W1 half 1, W2 half 1
+      const int fh = e >> 1;
+      if ((e & 1) == 0)
+        dma_rows<NW>(slot, 128, [&](int i) { return wm + kM1 + (size_t)(128 * fh + i) * kXD; }, wave, lane);
+      else
+        dma_rows<NW>(slot, 128, [&](int i) { return wm + kM2 + (size_t)i * kXFF + 128 * fh; }, wave, lane);
+      return;
+    }
+    const int h = pc - n_fin;
+    const uint16_t *wm = p.w_mat + (size_t)l * kXMat;
+    if (h == 0) dma_floats<NW>(sm.vec, p.w_vec + (size_t)l * kXLayerVec, kXLayerVec, wave, lane);
+    dma_rows<NW>(slot, 96, [&](int i) { return wm + kMqkv + (size_t)((i >> 5) * kXD + 32 * h + (i & 31)) * kXD; },
+                 wave, lane);
+  };
+  auto step = [&](int pc) -> const unsigned char * {
+    GR_WAIT_VMCNT_LGKM0(0);
+    ring_barrier();
+    issue(pc + 1);
+    return sm.ring[pc & 1];
+  };
+
+  issue(0);
+  int pc = 0;
+  bf16x8 hB[4][2];
+  if (l > 0) {
+    // attention of layer l-1 over every user key (each token's own key is
+    // one of them), with the queries the previous launch left; the output
+    // projection head by head
+    for (int h = 0; h < kXHeads; ++h) {
+      bf16x8 qb[2];
+      qb[0] = *(const bf16x8 *)(qs + 16 * h);
+      qb[1] = *(const bf16x8 *)(qs + 16 * h + 8);
+      HeadState st;
+      zero(st.o);
+      st.m = -__builtin_inff();
+      st.l = 0.f;
+      for (int j = 0; j < p.n_kc; ++j) {
+        const unsigned char *kv = step(pc++);
+        attend_piece(st, kv, min(8, (p.Lu - 256 * j) >> 5), c, g, qb, p.sl2);
+      }
+      const float inv = 1.f / xor32_sum(st.l);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.o[i] *= inv;
+      const bf16x8 ob[2] = {pack8(st.o, 0), pack8(st.o, 1)};
+      const unsigned char *w = step(pc++);
+      oproj_head(x, w, c, g, ob);
+      if (h == 0) {
+#pragma unroll
+        for (int ot = 0; ot < 4; ++ot) add_bias(x[ot], sm.vec + kVbO + 32 * ot, g);
+      }
+    }
+    layer_norm_b(x, sm.vec + kVln2g, sm.vec + kVln2b, g, hB);
+    for (int fh = 0; fh < 2; ++fh) {
+      bf16x8 uB[4][2];
+      {
+        const unsigned char *w = step(pc++);
+#pragma unroll
+        for (int ot = 0; ot < 4; ++ot) {
+          Acc a;
+          zero(a);
+          gemm_tile<4>(a, w, 32 * ot, c, g, hB);
+          add_bias(a, sm.vec + kVb1 + 128 * fh + 32 * ot, g);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) a[i] = fmaxf(a[i], 0.f);
+          uB[ot][0] = pack8(a, 0);
+          uB[ot][1] = pack8(a, 1);
+        }
+      }
+      const unsigned char *w = step(pc++);
+#pragma unroll
+      for (int ot = 0; ot < 4; ++ot) {
+        gemm_tile<4>(x[ot], w, 32 * ot, c, g, uB);
+        if (fh == 0) add_bias(x[ot], sm.vec + kVb2 + 32 * ot, g);
+      }
+    }
+  }
+  // layer l: queries, keys and values of the user tokens
+  const int key = 32 * utl + c, kc = key >> 8, kl = key & 255;
+  for (int h = 0; h < kXHeads; ++h) {
+    const unsigned char *w = step(pc++);
+    if (h == 0) layer_norm_b(x, sm.vec + kVln1g, sm.vec + kVln1b, g, hB);
+    Acc qa, ka, va;
+    zero(qa); zero(ka); zero(va);
+    gemm_tile<4>(qa, w, 0, c, g, hB);
+    gemm_tile<4>(ka, w, 32, c, g, hB);
+    gemm_tile<4>(va, w, 64, c, g, hB);
+    add_bias(qa, sm.vec + kVbQKV + 32 * h, g);
+    add_bias(ka, sm.vec + kVbQKV + kXD + 32 * h, g);
+    add_bias(va, sm.vec + kVbQKV + 2 * kXD + 32 * h, g);
+    if (live) {
+      *(bf16x8 *)(qs + 16 * h) = pack8(qa, 0);
+      *(bf16x8 *)(qs + 16 * h + 8) = pack8(qa, 1);
+      unsigned char *piece = ukv_r + ((size_t)(l * kXHeads + h) * p.n_kc + kc) * kXSlot;
+      // K [key][32]: this lane's dims 16 s + 8 g .. +7 are one 16-byte chunk
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        *(bf16x8 *)(piece + kl * 64 + 16 * ((2 * s + g) ^ ((kl >> 2) & 3))) = pack8(ka, s);
+      // V^T [dim][key]: one bf16 per (dim, key)
+      uint16_t *vt = (uint16_t *)(piece + 16384);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int dim = 16 * (i >> 3) + 8 * g + (i & 7);
+        const __bf16 b = (__bf16)va[i];
+        vt[dim * 256 + 8 * ((kl >> 3) ^ (dim & 15)) + (kl & 7)] = *(const uint16_t *)&b;
+      }
+    }
+  }
+  if (live && l + 1 < p.L) {
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *(float4 *)(xs + 16 * ft + 4 * i4) =
+            make_float4(x[ft][4 * i4], x[ft][4 * i4 + 1], x[ft][4 * i4 + 2], x[ft][4 * i4 + 3]);
+  }
+}
+
+}  // namespace
+
+size_t xf_user_state_bytes(int R, int Lu) { return (size_t)R * (Lu / 32) * 64 * (64 * 4 + 64 * 2); }
+size_t xf_ukv_bytes(int R, int L, int Lu) { return (size_t)R * L * kXHeads * ((Lu + 255) / 256) * kXSlot; }
+
+hipError_t launch_xf_scores(const XfArgs &a, hipStream_t s) {
+  const int n_kc = (a.Lu + 255) / 256;
+  const int n_ut = a.Lu / 32;
+  XfUserP u;
+  u.user = (const uint16_t *)a.user; u.w_mat = (const uint16_t *)a.w_mat; u.w_vec = a.w_vec;
+  u.ukv = (unsigned char *)a.ukv;
+  u.xs = (float *)a.user_state;
+  u.qs = (uint16_t *)((char *)a.user_state + (size_t)a.R * n_ut * 64 * 64 * 4);
+  u.R = a.R; u.L = a.L; u.n_kc = n_kc; u.Lu = a.Lu;
+  u.sl2 = kXLog2e / sqrtf((float)kXHd);
+  const int wg_per_r = (n_ut + kXUserWaves - 1) / kXUserWaves;
+  for (int l = 0; l < a.L; ++l) {
+    u.layer = l;
+    hipLaunchKernelGGL(xf_user_kernel, dim3((unsigned)(a.R * wg_per_r)), dim3(kXUserWaves * 64), 0, s, u);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  XfCandP c;
+  c.cand = (const uint16_t *)a.cand; c.w_mat = (const uint16_t *)a.w_mat; c.w_vec = a.w_vec;
+  c.ukv = (const unsigned char *)a.ukv;
+  c.score = a.score;
+  c.R = a.R; c.N = a.N; c.L = a.L; c.n_kc = n_kc; c.Lu = a.Lu;
+  c.sl2 = u.sl2;
+  const int tiles = (a.N + 32 * kXCandWaves - 1) / (32 * kXCandWaves);
+  hipLaunchKernelGGL(xf_cand_kernel, dim3((unsigned)(a.R * tiles)), dim3(kXCandWaves * 64), 0, s, c);
+  return hipGetLastError();
+}
+
+}  // namespace gr

@@ -289,3 +289,44 @@ def generate_to_host(g: DeviceGen) -> dict:
     steps = [dict(score=g.level("out_score", lv).cpu().numpy(), token=g.level("out_token", lv).cpu().numpy(),
                   parent=g.level("out_parent", lv).cpu().numpy()) for lv in range(g.levels)]
     return dict(steps=steps, ids=g.out_ids.cpu().numpy())
+
+
+@dataclasses.dataclass
+class DeviceXf:
+    """A broadcast-scoring run on the device: tokens, packed weights,
+    outputs and workspace, ready for gr_broadcast_score."""
+    shape: L.XfShape
+    k: int
+    user: torch.Tensor         # [R][Lu][D] bf16
+    cand: torch.Tensor         # [R][N][D] bf16
+    w_mat: torch.Tensor        # bf16, per layer w_qkv, w_o, w_1, w_2
+    w_vec: torch.Tensor        # fp32, per layer vectors then the final ones
+    out_score: torch.Tensor    # [R][k]
+    out_index: torch.Tensor    # [R][k]
+    cand_scores: Optional[torch.Tensor]   # [R][N] or None
+    ws: torch.Tensor
+
+
+def upload_xf(x, k: Optional[int] = None, all_scores: bool = True, device="cuda") -> DeviceXf:
+    """Upload a workloads.XFInputs and allocate the outputs and workspace."""
+    cfg = x.cfg
+    R, N, D = x.cand.shape
+    k = cfg.k if k is None else int(k)
+    shape = L.XfShape(R, N, x.user.shape[1], D, len(x.layers))
+    ws_bytes = L.gr_broadcast_workspace_size(shape, k)
+    return DeviceXf(shape, k, to_dev(x.user, L.GR_BF16, device), to_dev(x.cand, L.GR_BF16, device),
+                    to_dev(x.w_mat, L.GR_BF16, device), to_dev(x.w_vec, L.GR_F32, device),
+                    torch.empty((R, k), dtype=torch.float32, device=device),
+                    torch.empty((R, k), dtype=torch.int32, device=device),
+                    torch.empty((R, N), dtype=torch.float32, device=device) if all_scores else None,
+                    torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device))
+
+
+def broadcast_score(d: DeviceXf, stream=None) -> None:
+    L.gr_broadcast_score(d.shape, d.user, d.cand, d.w_mat, d.w_vec, d.k, d.out_score, d.out_index, d.cand_scores,
+                         d.ws, d.ws.numel(), stream)
+
+
+def xf_to_host(d: DeviceXf) -> dict:
+    return dict(score=d.out_score.cpu().numpy(), index=d.out_index.cpu().numpy(),
+                all=None if d.cand_scores is None else d.cand_scores.cpu().numpy())

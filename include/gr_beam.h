@@ -346,6 +346,60 @@ gr_status gr_generate(const gr_shape *shape, const void *prompt_k,
                       int32_t *out_parent, int32_t *out_ids, void *ws,
                       size_t ws_bytes, int32_t *dev_err, hipStream_t stream);
 
+/* gr_broadcast_score -- multi-layer broadcast scoring of single-token
+ * candidates (TransRetrieval: Architecture Overview, stage 4: an N-layer
+ * Pre-LN Transformer with a ReLU FFN whose user-side keys and values are
+ * computed once per request and reused by every candidate; the
+ * per-candidate cost paragraph: each candidate has its own Q/K/V/output
+ * projections and FFN and attends to the whole user sequence;
+ * Hardware-aware inference optimization: the user cache is broadcast to all
+ * candidates without copies, single-token candidates are packed into batched
+ * products; GPU retrieval: the selection stays on the device).
+ *   Per request r: the user tokens user_tok[r] (L_u of them) pass through
+ *   the layers attending to one another; at each layer l their keys and
+ *   values K_l, V_l are kept.  Each candidate token cand_tok[r][i] passes
+ *   through the same layers attending to K_l, V_l and to its own key and
+ *   value only.  A layer is x += MHA(LN1(x)) W_o^T + b_o;
+ *   x += ReLU(LN2(x) W_1^T + b_1) W_2^T + b_2, with [q|k|v] = LN1(x)
+ *   w_qkv^T + b_qkv, heads of 32, scores scaled by 1/sqrt(32), LayerNorm
+ *   over the D features (biased variance, eps 1e-5, gain and bias).  The
+ *   score is s_i = LN_f(x_i) . w_score + b_score after the last layer, and
+ *   the call returns the k best of each request by (score desc, index asc).
+ *   The FFN width 2D follows the page's per-layer cost of 16 D^2 FLOPs per
+ *   candidate for the four D x D projections (8 D^2) and the FFN.
+ *   shape: R requests, n_cand candidates and user_len user tokens each
+ *   (user_len a multiple of 32, <= GR_XF_MAX_USER), d_model = 128,
+ *   n_layers <= GR_XF_MAX_LAYERS.
+ *   user_tok: [R][user_len][d_model] bf16.  cand_tok: [R][n_cand][d_model]
+ *   bf16.  w_mat: bf16, per layer (8 d_model^2 values, layer after layer):
+ *   w_qkv [3D][D] (rows: query, key, value output features; weights are
+ *   [out][in]), w_o [D][D], w_1 [2D][D], w_2 [D][2D].  w_vec: fp32, per
+ *   layer (11 D values): b_qkv [3D], b_o [D], b_1 [2D], b_2 [D], ln1_gain,
+ *   ln1_bias, ln2_gain, ln2_bias [D]; then lnf_gain, lnf_bias, w_score [D]
+ *   and b_score [1].
+ *   out_score [R][k] fp32, out_index [R][k] int32 (candidate index).
+ *   cand_scores: optional [R][n_cand] fp32, every candidate's score.
+ *   Products run in bf16 with fp32 accumulation (activations rounded to
+ *   bf16 where they enter a product), LayerNorm, softmax and the residual
+ *   stream in fp32; the selection is exact on those fp32 scores.
+ *   ws: gr_broadcast_workspace_size() bytes (caller-owned; holds the user
+ *   keys/values of every layer, broadcast in place to all candidates).
+ *   Host errors: NULL pointers (NULL), sizes <= 0 (SHAPE), d_model != 128,
+ *   user_len not a multiple of 32 or too long, too many layers, unaligned
+ *   pointers (UNSUPPORTED), k > n_cand or above GR_MAX_K (K_TOO_LARGE), a
+ *   small workspace (WORKSPACE).  No device errors. */
+#define GR_XF_MAX_USER 1024
+#define GR_XF_MAX_LAYERS 8
+typedef struct {
+  int32_t R, n_cand, user_len, d_model, n_layers;
+} gr_xf_shape;
+gr_status gr_broadcast_score(const gr_xf_shape *shape, const void *user_tok,
+                             const void *cand_tok, const void *w_mat,
+                             const float *w_vec, int32_t k, float *out_score,
+                             int32_t *out_index, float *cand_scores, void *ws,
+                             size_t ws_bytes, hipStream_t stream);
+size_t gr_broadcast_workspace_size(const gr_xf_shape *shape, int32_t k);
+
 /* gr_decode_step_noalloc -- gr_decode_step for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, hosts
  * that forbid hipMalloc.  Same arguments, semantics, outputs and errors as

@@ -27,6 +27,12 @@ batches in flight); that throughput is an extra field, never `value`.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 
+With a broadcast-scoring workload (--workload xf128d5l_u256_c40k) a step is
+one gr_broadcast_score call: the user pass over 256 user tokens, 40 000
+single-token candidates through 5 Pre-LN layers of width 128, their scores
+and the top-2000; its roofline is the bf16 MFMA peak (FLOPs per call over
+the call's time).
+
 With a whole-ID generation workload (--workload gen_beam100_p600) a step is
 one complete generation instead: the q/k/v tables of the chosen codes
 (one gr_code_table over the levels) and gr_generate (four decode steps with the chosen
@@ -388,6 +394,107 @@ def bench_generate(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+def xf_flops(cfg):
+    """FLOPs of one broadcast-scoring call, counted as the page counts a
+    candidate's cost (2 per multiply-add): per layer and token 16 D^2 for
+    the four projections and the FFN, plus 4 D per attended key (user
+    tokens attend to L_u keys, candidates to L_u + their own), plus the
+    score head (2 D per candidate).  Returns (total, candidate part)."""
+    D, Lu, N, L = cfg.D, cfg.Lu, cfg.N, cfg.n_layers
+    user = L * Lu * (16 * D * D + 4 * Lu * D)
+    cand = L * N * (16 * D * D + 4 * (Lu + 1) * D) + 2 * D * N
+    return cfg.R * (user + cand), cfg.R * cand
+
+
+def bench_broadcast(args, cfg):
+    import numpy as np
+    import torch
+    import workloads as W
+    from generative_recommendation_beam_amd import harness as HN
+    t0 = time.perf_counter()
+    x = W.make_xf_inputs(cfg)
+    print(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.skip_cpu_baseline:
+        cpu = cpu_baseline_broadcast(x, args.cpu_seconds)
+    torch.cuda.set_device(0)
+    n_sets = args.sets if args.sets > 0 else 2
+    sets = [HN.upload_xf(x, all_scores=False)]
+    for i in range(1, n_sets):
+        xi = W.make_xf_inputs(cfg, seed=cfg.seed + 100 * i)
+        sets.append(HN.upload_xf(xi, all_scores=False))
+    torch.cuda.synchronize()
+    print(f"[bench] {len(sets)} input set(s) resident on the GPU", file=sys.stderr, flush=True)
+    copy_gbps = copy_bandwidth(args.copy_seconds)
+    gemm_tflops = mfma_bandwidth(args.gemm_seconds)
+    for i in range(args.warmup):
+        HN.broadcast_score(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        HN.broadcast_score(sets[i % len(sets)])
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    flops, cand_flops = xf_flops(cfg)
+    tflops = flops / (ms * 1e-3) / 1e12
+    calls = 1e3 / ms
+    in_bytes = (x.user.size + x.cand.size + x.w_mat.size) * 2 + x.w_vec.size * 4
+    out = {
+        "metric": f"broadcast-scored candidates/s, {cfg.D}D-{cfg.n_layers}L, {cfg.N} candidates over "
+                  f"{cfg.Lu} user tokens, top-{cfg.k} (1 GPU)",
+        "value": round(calls * cfg.R * cfg.N, 0), "unit": "candidates/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) user and candidate tokens, N(0,1/fan_in) weights, N(0,0.02) biases, "
+                "LayerNorm gains 1+N(0,0.1))",
+        "config": {"workload": cfg.name, "requests": cfg.R, "candidates": cfg.N, "user_len": cfg.Lu,
+                   "d_model": cfg.D, "heads": cfg.H, "layers": cfg.n_layers, "ffn": 2 * cfg.D, "k": cfg.k,
+                   "input_sets": len(sets)},
+        "calls_per_s": round(calls, 2),
+        "flops_per_call": flops,
+        "candidate_flops_per_call": cand_flops,
+        "algorithmic_bytes_per_call": int(in_bytes + cfg.R * cfg.k * 8),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "gr_broadcast_score (user pass, candidate kernel, selection)"},
+        "gemm_bf16_TFLOPs": round(gemm_tflops, 1),
+        "frac_of_gemm": round(tflops / gemm_tflops, 4),
+        "copy_GBps": round(copy_gbps, 1),
+    }
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_broadcast(x, seconds):
+    """The oracle over chunks of 1000 candidates of request 0 (the user pass
+    once, outside the wall time) until `seconds` have passed, with NumPy's
+    BLAS on every host core; scaled to candidates/s."""
+    from oracle import broadcast as BC
+    cfg = x.cfg
+    layers = [BC.LayerParams(**{k: lp[k] for k in (
+        "w_qkv", "b_qkv", "w_o", "b_o", "w_1", "b_1", "w_2", "b_2",
+        "ln1_g", "ln1_b", "ln2_g", "ln2_b")}) for lp in x.layers]
+    P = BC.ModelParams(layers, x.lnf_g, x.lnf_b, x.w_score, x.b_score)
+    cores, _ = host_cores(0)
+    kv, _ = BC.user_forward(x.user[0], P, cfg.H)
+    done, chunk = 0, 1000
+    t0 = time.perf_counter()
+    while done < cfg.N:
+        n = min(chunk, cfg.N - done)
+        BC.score_head(BC.candidate_forward(x.cand[0][done:done + n], kv, P, cfg.H), P)
+        done += n
+        if time.perf_counter() - t0 > seconds:
+            break
+    wall = time.perf_counter() - t0
+    return {"value": round(done / wall, 1), "unit": "candidates/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {cfg.N} candidates of one request in chunks of {chunk}, user pass excluded, "
+                      f"{wall:.2f} s wall, NumPy BLAS threads over {cores} cores",
+            "cpu_model": cpu_model()}
+
+
 def _oracle_generate(r):
     from oracle import generate as OG
     x, tables = _ORACLE_INPUT
@@ -498,6 +605,9 @@ def main():
 
     if args.workload in W.GEN_CONFIGS:
         bench_generate(args, W.GEN_CONFIGS[args.workload])
+        return
+    if args.workload in W.XF_CONFIGS:
+        bench_broadcast(args, W.XF_CONFIGS[args.workload])
         return
     cfg = W.CONFIGS[args.workload]
     assert cfg.steps == 1, "the benchmark times single-step workloads"

@@ -166,37 +166,39 @@ __device__ __forceinline__ void layer_norm_b(const Acc (&x)[4], const float *gai
     }
 }
 
-// acc += W[rows row0 + pi(c)] . h over K = 32 * NFT inputs; W rows of 256 bytes
-// in LDS (chunk-swizzled), input columns col0 .. of those rows.
-template <int NFT>
-__device__ __forceinline__ void gemm_tile(Acc &acc, const unsigned char *w, int row0, int c, int g,
-                                          const bf16x8 (&h)[NFT][2]) {
-  const int cf = fresh(c), gf = fresh(g);
-  const int row = row0 + xpi(cf);
-  const unsigned char *wr = w + row * 256;
-  const int sw = row & 15;
-#pragma unroll
-  for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const bf16x8 a = *(const bf16x8 *)(wr + 16 * ((4 * ft + 2 * s + gf) ^ sw));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, h[ft][s], acc, 0, 0, 0);
-    }
-}
-
 // x[ot] += W_o[32 ot + pi(c)][head h's 32 columns] . o_h: the head's column
 // block of W_o in LDS, 128 rows of 64 bytes (chunk ^ (row >> 2) & 3).
 __device__ __forceinline__ void oproj_head(Acc (&x)[4], const unsigned char *wo, int c, int g, const bf16x8 (&ob)[2]) {
   const int cf = fresh(c), gf = fresh(g);
 #pragma unroll
-  for (int ot = 0; ot < 4; ++ot) {
-    const int row = 32 * ot + xpi(cf);
+  for (int s = 0; s < 2; ++s) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int ot = 0; ot < 4; ++ot) {
+      const int row = 32 * ot + xpi(cf);
       const bf16x8 a = *(const bf16x8 *)(wo + row * 64 + 16 * ((2 * s + gf) ^ ((row >> 2) & 3)));
       x[ot] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ob[s], x[ot], 0, 0, 0);
     }
   }
+}
+
+// acc[t] += W[rows row0 + 32 t + pi(c)] . h for t < NT (K = 128): the
+// k-steps outermost, so that the NT accumulation chains interleave on the
+// MFMA pipe instead of each waiting for its previous step.
+template <int NT>
+__device__ __forceinline__ void gemm_tiles(Acc (&acc)[NT], const unsigned char *w, int row0, int c, int g,
+                                           const bf16x8 (&h)[4][2]) {
+  const int cf = fresh(c), gf = fresh(g);
+  const int r0 = row0 + xpi(cf);
+  const int sw = r0 & 15;
+#pragma unroll
+  for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 a = *(const bf16x8 *)(w + (r0 + 32 * t) * 256 + 16 * ((4 * ft + 2 * s + gf) ^ sw));
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, h[ft][s], acc[t], 0, 0, 0);
+      }
 }
 
 __device__ __forceinline__ void zero(Acc &a) {
@@ -221,43 +223,74 @@ struct HeadState {
 };
 
 // One piece of user keys/values (up to 256 keys; n_kt tiles of 32) folded
-// into the state: S^T = K q^T, p = exp2(S * sl2 - m), O^T += V^T P^T.
+// into the state: S^T = K q^T, p = exp2(S * sl2 - m), O^T += V^T P^T.  Two
+// key tiles per round (one max, one rescale, two independent MFMA chains),
+// so that a round's dependent MFMA -> softmax -> MFMA chain covers twice
+// the keys.
+__device__ __forceinline__ void scores_tile(Acc &s, const unsigned char *kp, int kt, int c, int g,
+                                            const bf16x8 (&qb)[2]) {
+  zero(s);
+  const int key = 32 * kt + xpi(c);
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const bf16x8 a = *(const bf16x8 *)(kp + key * 64 + 16 * ((2 * s2 + g) ^ ((key >> 2) & 3)));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[s2], s, 0, 0, 0);
+  }
+}
+__device__ __forceinline__ void values_tile(Acc &o, const unsigned char *vp, int kt, int c, int g, const Acc &p) {
+  const int dim = xpi(c);
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const int ch = 4 * kt + 2 * s2 + g;   // 16-byte chunk of the keys of this k-step
+    const bf16x8 a = *(const bf16x8 *)(vp + dim * 512 + 16 * (ch ^ (dim & 15)));
+    o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pack8(p, s2), o, 0, 0, 0);
+  }
+}
 __device__ __forceinline__ void attend_piece(HeadState &st, const unsigned char *piece, int n_kt, int c, int g,
                                              const bf16x8 (&qb)[2], float sl2) {
   const unsigned char *kp = piece, *vp = piece + 16384;
   c = fresh(c);
   g = fresh(g);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    Acc s;
-    zero(s);
-    const int key = 32 * kt + xpi(c);
+  Acc o2;                                  // the second tile's chain, summed at the end
+  zero(o2);
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    const bool two = kt + 1 < n_kt;
+    Acc s0, s1;
+    scores_tile(s0, kp, kt, c, g, qb);
+    if (two) scores_tile(s1, kp, kt + 1, c, g, qb);
+    float mx = s0[0];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const bf16x8 a = *(const bf16x8 *)(kp + key * 64 + 16 * ((2 * s2 + g) ^ ((key >> 2) & 3)));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[s2], s, 0, 0, 0);
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s0[i]);
+    if (two) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s1[i]);
     }
-    float mx = s[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
     const float m_new = fmaxf(st.m, xor32_max(mx) * sl2);
     const float corr = fast_exp2(st.m - m_new);
     st.l *= corr;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) st.o[i] *= corr;
+    for (int i = 0; i < 16; ++i) {
+      st.o[i] *= corr;
+      o2[i] *= corr;
+    }
     st.m = m_new;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      s[i] = fast_exp2(fmaf(s[i], sl2, -m_new));
-      st.l += s[i];
+      s0[i] = fast_exp2(fmaf(s0[i], sl2, -m_new));
+      st.l += s0[i];
     }
-    const int dim = xpi(c);
+    values_tile(st.o, vp, kt, c, g, s0);
+    if (two) {
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int ch = 4 * kt + 2 * s2 + g;   // 16-byte chunk of the keys of this k-step
-      const bf16x8 a = *(const bf16x8 *)(vp + dim * 512 + 16 * (ch ^ (dim & 15)));
-      st.o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pack8(s, s2), st.o, 0, 0, 0);
+      for (int i = 0; i < 16; ++i) {
+        s1[i] = fast_exp2(fmaf(s1[i], sl2, -m_new));
+        st.l += s1[i];
+      }
+      values_tile(o2, vp, kt + 1, c, g, s1);
     }
   }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) st.o[i] += o2[i];
 }
 
 // ---- candidate kernel --------------------------------------------------------
@@ -365,21 +398,18 @@ __global__ __launch_bounds__(kXCandWaves * 64, 2) void xf_cand_kernel(XfCandP p)
           for (int ot = 0; ot < 4; ++ot) add_bias(x[ot], sm.vec + kVbO + 32 * ot, g);
         }
       }
-      Acc qa, ka;
-      zero(qa); zero(ka);
-      gemm_tile<4>(qa, w, 0, c, g, hB);
-      gemm_tile<4>(ka, w, 32, c, g, hB);
-      add_bias(qa, sm.vec + kVbQKV + 32 * h, g);
-      add_bias(ka, sm.vec + kVbQKV + kXD + 32 * h, g);
+      Acc qkv[3];
+      zero(qkv[0]); zero(qkv[1]); zero(qkv[2]);
+      gemm_tiles<3>(qkv, w, 0, c, g, hB);
+      add_bias(qkv[0], sm.vec + kVbQKV + 32 * h, g);
+      add_bias(qkv[1], sm.vec + kVbQKV + kXD + 32 * h, g);
+      add_bias(qkv[2], sm.vec + kVbQKV + 2 * kXD + 32 * h, g);
       float ss = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ss = fmaf(qa[i], ka[i], ss);
+      for (int i = 0; i < 16; ++i) ss = fmaf(qkv[0][i], qkv[1][i], ss);
       const float s_self = xor32_sum(ss) * p.sl2;     // own key, log2 units
-      const bf16x8 qb[2] = {pack8(qa, 0), pack8(qa, 1)};
-      Acc va;
-      zero(va);
-      gemm_tile<4>(va, w, 64, c, g, hB);
-      add_bias(va, sm.vec + kVbQKV + 2 * kXD + 32 * h, g);
+      const bf16x8 qb[2] = {pack8(qkv[0], 0), pack8(qkv[0], 1)};
+      const Acc va = qkv[2];
       HeadState st;
       zero(st.o);
       st.m = s_self;                                   // the own key starts the running max
@@ -405,23 +435,24 @@ __global__ __launch_bounds__(kXCandWaves * 64, 2) void xf_cand_kernel(XfCandP p)
       bf16x8 uB[4][2];
       {
         const unsigned char *w = step(pc++);
+        Acc a[4];
+#pragma unroll
+        for (int ot = 0; ot < 4; ++ot) zero(a[ot]);
+        gemm_tiles<4>(a, w, 0, c, g, hB);
 #pragma unroll
         for (int ot = 0; ot < 4; ++ot) {
-          Acc a;
-          zero(a);
-          gemm_tile<4>(a, w, 32 * ot, c, g, hB);
-          add_bias(a, sm.vec + kVb1 + 128 * fh + 32 * ot, g);
+          add_bias(a[ot], sm.vec + kVb1 + 128 * fh + 32 * ot, g);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) a[i] = fmaxf(a[i], 0.f);
-          uB[ot][0] = pack8(a, 0);
-          uB[ot][1] = pack8(a, 1);
+          for (int i = 0; i < 16; ++i) a[ot][i] = fmaxf(a[ot][i], 0.f);
+          uB[ot][0] = pack8(a[ot], 0);
+          uB[ot][1] = pack8(a[ot], 1);
         }
       }
       const unsigned char *w = step(pc++);
+      gemm_tiles<4>(x, w, 0, c, g, uB);
+      if (fh == 0) {
 #pragma unroll
-      for (int ot = 0; ot < 4; ++ot) {
-        gemm_tile<4>(x[ot], w, 32 * ot, c, g, uB);
-        if (fh == 0) add_bias(x[ot], sm.vec + kVb2 + 32 * ot, g);
+        for (int ot = 0; ot < 4; ++ot) add_bias(x[ot], sm.vec + kVb2 + 32 * ot, g);
       }
     }
   }
@@ -461,7 +492,11 @@ __global__ __launch_bounds__(kXCandWaves * 64, 2) void xf_cand_kernel(XfCandP p)
 // Per (request, layer) launch over all user tokens of the request, one wave
 // per 32 tokens.  The wave's state between launches lives in the workspace:
 // x (fp32, the accumulator layout: 256 bytes a lane) and the queries of the
-// four heads (bf16 B operands: 128 bytes a lane).
+// four heads (bf16 B operands: 128 bytes a lane).  A launch is a short
+// chain of pieces with little work each, so its ring is four slots deep
+// (three pieces in flight); every piece is exactly four 1 KB DMAs per wave
+// (short pieces add re-reads into a scratch block), which makes each wait a
+// fixed count.
 struct XfUserP {
   const uint16_t *user;     // [R][Lu][D] bf16
   const uint16_t *w_mat;
@@ -473,11 +508,24 @@ struct XfUserP {
   float sl2;
 };
 
-constexpr int kXUserWaves = 8;
+#ifndef GR_XF_USER_WAVES
+#define GR_XF_USER_WAVES 4
+#endif
+constexpr int kXUserWaves = GR_XF_USER_WAVES;
+constexpr int kXUserSlots = 4;
+constexpr int kXUserDma = 32 / kXUserWaves;   // DMAs per wave and piece (32 KB over the waves)
+static_assert(kXUserWaves >= 2 && kXUserWaves <= 8 && (kXUserSlots - 2) * kXUserDma < 64, "wait counts");
+
+struct XfUserSmem {
+  unsigned char ring[kXUserSlots][kXSlot];
+  unsigned char dummy[1024];
+  float vec_prev[kXVecBytes / 4];         // vectors of layer l - 1
+  float vec[kXVecBytes / 4];              // vectors of layer l
+};
 
 __global__ __launch_bounds__(kXUserWaves * 64) void xf_user_kernel(XfUserP p) {
   constexpr int NW = kXUserWaves;
-  __shared__ __attribute__((aligned(1024))) XfSmem sm;
+  __shared__ __attribute__((aligned(1024))) XfUserSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, c = lane & 31;
@@ -512,17 +560,26 @@ __global__ __launch_bounds__(kXUserWaves * 64) void xf_user_kernel(XfUserP p) {
         x[ft][4 * i4] = v.x; x[ft][4 * i4 + 1] = v.y; x[ft][4 * i4 + 2] = v.z; x[ft][4 * i4 + 3] = v.w;
       }
   }
+  // the vectors of both layers, ahead of every piece
+  if (l > 0) dma_floats<NW>(sm.vec_prev, p.w_vec + (size_t)(l - 1) * kXLayerVec, kXLayerVec, wave, lane);
+  dma_floats<NW>(sm.vec, p.w_vec + (size_t)l * kXLayerVec, kXLayerVec, wave, lane);
 
   // Pieces: (layer > 0) for each head the user K/V of layer l-1 (n_kc
-  // pieces) and the head's W_o columns (with the vectors of l-1 at head 0),
-  // the FFN halves of l-1; then the q/k/v rows of layer l per head (the
-  // vectors of l with head 0).
+  // pieces) and the head's W_o columns, the FFN halves of l-1; then the
+  // q/k/v rows of layer l per head.  Past the last piece, padding pieces
+  // of scratch re-reads keep the count of loads in flight fixed.
   const int per_head = p.n_kc + 1;
   const int n_fin = l > 0 ? kXHeads * per_head + 4 : 0;
   const int n_pieces = n_fin + kXHeads;
+  auto pad = [&](int n) {
+    for (int i = 0; i < n; ++i) dma16(p.w_mat + 8 * fresh(lane), sm.dummy);
+  };
   auto issue = [&](int pc) {
-    if (pc >= n_pieces) return;
-    unsigned char *slot = sm.ring[pc & 1];
+    if (pc >= n_pieces) {
+      pad(kXUserDma);
+      return;
+    }
+    unsigned char *slot = sm.ring[pc % kXUserSlots];
     if (pc < n_fin) {
       const int lp = l - 1;
       const uint16_t *wm = p.w_mat + (size_t)lp * kXMat;
@@ -531,8 +588,8 @@ __global__ __launch_bounds__(kXUserWaves * 64) void xf_user_kernel(XfUserP p) {
         if (j < p.n_kc) {
           dma_copy<NW>(slot, ukv_r + ((size_t)(lp * kXHeads + h) * p.n_kc + j) * kXSlot, kXSlot, wave, lane);
         } else {
-          if (h == 0) dma_floats<NW>(sm.vec, p.w_vec + (size_t)lp * kXLayerVec, kXLayerVec, wave, lane);
-          dma_wo_cols<NW>(slot, wm + kMo, h, wave, lane);
+          dma_wo_cols<NW>(slot, wm + kMo, h, wave, lane);     // 8 KB: a quarter of a piece
+          pad(kXUserDma - 8 / NW);
         }
         return;
       }
@@ -546,18 +603,24 @@ __global__ __launch_bounds__(kXUserWaves * 64) void xf_user_kernel(XfUserP p) {
     }
     const int h = pc - n_fin;
     const uint16_t *wm = p.w_mat + (size_t)l * kXMat;
-    if (h == 0) dma_floats<NW>(sm.vec, p.w_vec + (size_t)l * kXLayerVec, kXLayerVec, wave, lane);
     dma_rows<NW>(slot, 96, [&](int i) { return wm + kMqkv + (size_t)((i >> 5) * kXD + 32 * h + (i & 31)) * kXD; },
-                 wave, lane);
+                 wave, lane);                                 // 24 KB: three quarters of a piece
+    pad(kXUserDma - 24 / NW);
   };
-  auto step = [&](int pc) -> const unsigned char * {
-    GR_WAIT_VMCNT_LGKM0(0);
+  // piece pc has landed once the two issued after it may still be in
+  // flight; after the barrier every wave is done with piece pc - 1, whose
+  // slot receives piece pc + 3.  Once the wave has issued global stores
+  // (the layer's queries, keys and values), loads and stores share the
+  // counter and the wait drains it.
+  auto step = [&](int pc, bool stores) -> const unsigned char * {
+    if (stores) GR_WAIT_VMCNT_LGKM0(0);
+    else GR_WAIT_VMCNT_LGKM0((kXUserSlots - 2) * kXUserDma);
     ring_barrier();
-    issue(pc + 1);
-    return sm.ring[pc & 1];
+    issue(pc + kXUserSlots - 1);
+    return sm.ring[pc % kXUserSlots];
   };
 
-  issue(0);
+  for (int i = 0; i < kXUserSlots - 1; ++i) issue(i);
   int pc = 0;
   bf16x8 hB[4][2];
   if (l > 0) {
@@ -573,72 +636,83 @@ __global__ __launch_bounds__(kXUserWaves * 64) void xf_user_kernel(XfUserP p) {
       st.m = -__builtin_inff();
       st.l = 0.f;
       for (int j = 0; j < p.n_kc; ++j) {
-        const unsigned char *kv = step(pc++);
+        const unsigned char *kv = step(pc++, false);
         attend_piece(st, kv, min(8, (p.Lu - 256 * j) >> 5), c, g, qb, p.sl2);
       }
       const float inv = 1.f / xor32_sum(st.l);
 #pragma unroll
       for (int i = 0; i < 16; ++i) st.o[i] *= inv;
       const bf16x8 ob[2] = {pack8(st.o, 0), pack8(st.o, 1)};
-      const unsigned char *w = step(pc++);
+      const unsigned char *w = step(pc++, false);
       oproj_head(x, w, c, g, ob);
       if (h == 0) {
 #pragma unroll
-        for (int ot = 0; ot < 4; ++ot) add_bias(x[ot], sm.vec + kVbO + 32 * ot, g);
+        for (int ot = 0; ot < 4; ++ot) add_bias(x[ot], sm.vec_prev + kVbO + 32 * ot, g);
       }
     }
-    layer_norm_b(x, sm.vec + kVln2g, sm.vec + kVln2b, g, hB);
+    layer_norm_b(x, sm.vec_prev + kVln2g, sm.vec_prev + kVln2b, g, hB);
     for (int fh = 0; fh < 2; ++fh) {
       bf16x8 uB[4][2];
       {
-        const unsigned char *w = step(pc++);
+        const unsigned char *w = step(pc++, false);
 #pragma unroll
-        for (int ot = 0; ot < 4; ++ot) {
-          Acc a;
-          zero(a);
-          gemm_tile<4>(a, w, 32 * ot, c, g, hB);
-          add_bias(a, sm.vec + kVb1 + 128 * fh + 32 * ot, g);
+        for (int half = 0; half < 2; ++half) {
+          Acc a[2];
+          zero(a[0]); zero(a[1]);
+          gemm_tiles<2>(a, w, 64 * half, c, g, hB);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) a[i] = fmaxf(a[i], 0.f);
-          uB[ot][0] = pack8(a, 0);
-          uB[ot][1] = pack8(a, 1);
+          for (int t = 0; t < 2; ++t) {
+            const int ot = 2 * half + t;
+            add_bias(a[t], sm.vec_prev + kVb1 + 128 * fh + 32 * ot, g);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) a[t][i] = fmaxf(a[t][i], 0.f);
+            uB[ot][0] = pack8(a[t], 0);
+            uB[ot][1] = pack8(a[t], 1);
+          }
         }
       }
-      const unsigned char *w = step(pc++);
+      const unsigned char *w = step(pc++, false);
+      gemm_tiles<4>(x, w, 0, c, g, uB);
+      if (fh == 0) {
 #pragma unroll
-      for (int ot = 0; ot < 4; ++ot) {
-        gemm_tile<4>(x[ot], w, 32 * ot, c, g, uB);
-        if (fh == 0) add_bias(x[ot], sm.vec + kVb2 + 32 * ot, g);
+        for (int ot = 0; ot < 4; ++ot) add_bias(x[ot], sm.vec_prev + kVb2 + 32 * ot, g);
       }
     }
   }
   // layer l: queries, keys and values of the user tokens
   const int key = 32 * utl + c, kc = key >> 8, kl = key & 255;
   for (int h = 0; h < kXHeads; ++h) {
-    const unsigned char *w = step(pc++);
+    const unsigned char *w = step(pc++, h > 0);
     if (h == 0) layer_norm_b(x, sm.vec + kVln1g, sm.vec + kVln1b, g, hB);
-    Acc qa, ka, va;
-    zero(qa); zero(ka); zero(va);
-    gemm_tile<4>(qa, w, 0, c, g, hB);
-    gemm_tile<4>(ka, w, 32, c, g, hB);
-    gemm_tile<4>(va, w, 64, c, g, hB);
-    add_bias(qa, sm.vec + kVbQKV + 32 * h, g);
-    add_bias(ka, sm.vec + kVbQKV + kXD + 32 * h, g);
-    add_bias(va, sm.vec + kVbQKV + 2 * kXD + 32 * h, g);
+    unsigned char *piece = ukv_r + ((size_t)(l * kXHeads + h) * p.n_kc + kc) * kXSlot;
+    Acc a[1];
+    // q
+    zero(a[0]);
+    gemm_tiles<1>(a, w, 0, c, g, hB);
+    add_bias(a[0], sm.vec + kVbQKV + 32 * h, g);
     if (live) {
-      *(bf16x8 *)(qs + 16 * h) = pack8(qa, 0);
-      *(bf16x8 *)(qs + 16 * h + 8) = pack8(qa, 1);
-      unsigned char *piece = ukv_r + ((size_t)(l * kXHeads + h) * p.n_kc + kc) * kXSlot;
-      // K [key][32]: this lane's dims 16 s + 8 g .. +7 are one 16-byte chunk
+      *(bf16x8 *)(qs + 16 * h) = pack8(a[0], 0);
+      *(bf16x8 *)(qs + 16 * h + 8) = pack8(a[0], 1);
+    }
+    // k: K [key][32], this lane's dims 16 s + 8 g .. +7 are one 16-byte chunk
+    zero(a[0]);
+    gemm_tiles<1>(a, w, 32, c, g, hB);
+    add_bias(a[0], sm.vec + kVbQKV + kXD + 32 * h, g);
+    if (live) {
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        *(bf16x8 *)(piece + kl * 64 + 16 * ((2 * s + g) ^ ((kl >> 2) & 3))) = pack8(ka, s);
-      // V^T [dim][key]: one bf16 per (dim, key)
+        *(bf16x8 *)(piece + kl * 64 + 16 * ((2 * s + g) ^ ((kl >> 2) & 3))) = pack8(a[0], s);
+    }
+    // v: V^T [dim][key], one bf16 per (dim, key)
+    zero(a[0]);
+    gemm_tiles<1>(a, w, 64, c, g, hB);
+    add_bias(a[0], sm.vec + kVbQKV + 2 * kXD + 32 * h, g);
+    if (live) {
       uint16_t *vt = (uint16_t *)(piece + 16384);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int dim = 16 * (i >> 3) + 8 * g + (i & 7);
-        const __bf16 b = (__bf16)va[i];
+        const __bf16 b = (__bf16)a[0][i];
         vt[dim * 256 + 8 * ((kl >> 3) ^ (dim & 15)) + (kl & 7)] = *(const uint16_t *)&b;
       }
     }
@@ -651,6 +725,7 @@ __global__ __launch_bounds__(kXUserWaves * 64) void xf_user_kernel(XfUserP p) {
         *(float4 *)(xs + 16 * ft + 4 * i4) =
             make_float4(x[ft][4 * i4], x[ft][4 * i4 + 1], x[ft][4 * i4 + 2], x[ft][4 * i4 + 3]);
   }
+  GR_WAIT_VMCNT(0);                                      // the padding loads have landed
 }
 
 }  // namespace

@@ -29,6 +29,7 @@ GR_DEVERR_PARENT_RANGE, GR_DEVERR_PARENT_ORDER = 1, 2
 GR_DEVERR_DEPTH, GR_DEVERR_BEAM_RANGE, GR_DEVERR_TOKEN_RANGE = 4, 8, 16
 GR_TOPK_LOG_SOFTMAX = 1
 GR_STEP_ATTENTION, GR_STEP_SELECTION = 2, 4
+GR_W_DIM_MAJOR = 8
 GR_MAX_DEPTH, GR_MAX_K = 8, 2048
 GR_XF_MAX_USER, GR_XF_MAX_LAYERS = 1024, 8
 

@@ -121,7 +121,8 @@ bool use_mfma_logits(const gr_shape *s, int vocab) {
 }
 
 struct DecodeLayout {
-  size_t o_off, o_bytes, z_off, z_bytes, part_off, part_bytes, ids_off, ids_bytes, split_off, split_bytes, total;
+  size_t o_off, o_bytes, z_off, z_bytes, part_off, part_bytes, ids_off, ids_bytes, split_off, split_bytes, w_off,
+      w_bytes, total;
 };
 DecodeLayout decode_layout(const gr_shape *s, int n_beams, int vocab, int k) {
   DecodeLayout L;
@@ -141,7 +142,10 @@ DecodeLayout decode_layout(const gr_shape *s, int n_beams, int vocab, int k) {
   L.ids_off = L.part_off + L.part_bytes;
   L.split_bytes = attn_split_ws_bytes(s, n_beams);
   L.split_off = L.ids_off + L.ids_bytes;
-  L.total = L.split_off + L.split_bytes + kAlign;  // slack for aligning ws
+  // the code-major copy of a dimension-major W (GR_W_DIM_MAJOR)
+  L.w_bytes = align_up((size_t)vocab * D * elem_bytes(s->dtype));
+  L.w_off = L.split_off + L.split_bytes;
+  L.total = L.w_off + L.w_bytes + kAlign;  // slack for aligning ws
   return L;
 }
 
@@ -551,7 +555,8 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void
   const int32_t stage = flags & (GR_STEP_ATTENTION | GR_STEP_SELECTION);
   const bool run_attn = stage != GR_STEP_SELECTION;
   const bool run_select = stage != GR_STEP_ATTENTION;
-  flags &= ~(GR_STEP_ATTENTION | GR_STEP_SELECTION);
+  const bool w_dim_major = (flags & GR_W_DIM_MAJOR) != 0;
+  flags &= ~(GR_STEP_ATTENTION | GR_STEP_SELECTION | GR_W_DIM_MAJOR);
   st = check_select(shape->R, n_beams, vocab, beam_width, flags);
   if (st) return st;
   if (!W || !out_score || !out_token || !out_parent) return GR_ERR_NULL;
@@ -585,6 +590,13 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void
     if (e != hipSuccess) return hip_status(e);
   }
   if (!run_select) return GR_OK;
+  if (w_dim_major) {
+    // [D][vocab] -> [vocab][D] in the workspace
+    void *wt = base + L.w_off;
+    e = gr::launch_transpose(W, wt, shape->H * shape->head_dim, vocab, elem_bytes(shape->dtype), stream);
+    if (e != hipSuccess) return hip_status(e);
+    W = wt;
+  }
   return enqueue_scoring(shape, n_beams, W, vocab, prior, beam_width, lsm, cand_out, so, L, base,
                          o_f32, stream);
 }

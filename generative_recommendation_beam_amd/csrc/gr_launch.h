@@ -181,6 +181,9 @@ struct ScoreSelectArgs {
 };
 hipError_t launch_score_select(const ScoreSelectArgs &a, const SelectOut &o, hipStream_t s);
 
+// out[c][r] = in[r][c] for an in of rows x cols elements of elem_bytes (2 or 4).
+hipError_t launch_transpose(const void *in, void *out, int rows, int cols, int elem_bytes, hipStream_t s);
+
 // Final merge of per-group partial lists.
 hipError_t launch_select_merge(const SelectOut &o, int R, int k, int vocab, hipStream_t s);
 

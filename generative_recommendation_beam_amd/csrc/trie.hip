@@ -71,4 +71,34 @@ hipError_t launch_trie_append(const AppendArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---- transpose (a dimension-major codebook projection into code-major
+// rows): 32 x 32 tiles through LDS, reads and writes along rows.
+namespace {
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T *in, T *out, int rows, int cols) {
+  __shared__ T tile[32][33];
+  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int i = ty; i < 32; i += 8) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < rows && c < cols) tile[i][tx] = in[(size_t)r * cols + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8) {
+    const int c = c0 + i, r = r0 + tx;
+    if (r < rows && c < cols) out[(size_t)c * rows + r] = tile[tx][i];
+  }
+}
+}  // namespace
+
+hipError_t launch_transpose(const void *in, void *out, int rows, int cols, int elem_bytes, hipStream_t s) {
+  const dim3 grid((unsigned)((cols + 31) / 32), (unsigned)((rows + 31) / 32));
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t *)in, (uint16_t *)out,
+                       rows, cols);
+  else
+    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s, (const float *)in, (float *)out, rows, cols);
+  return hipGetLastError();
+}
+
 }  // namespace gr

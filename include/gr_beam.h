@@ -96,7 +96,12 @@ enum {
    * between the stages; the kernels and their arguments are the same as in
    * the single call. */
   GR_STEP_ATTENTION = 2,
-  GR_STEP_SELECTION = 4
+  GR_STEP_SELECTION = 4,
+  /* gr_decode_step only: W is given dimension-major, [H*head_dim][vocab]
+   * (the orientation of the pages' D x 256 projection), instead of the
+   * default code-major [vocab][H*head_dim].  The step then transposes it
+   * into its workspace first (one small extra launch). */
+  GR_W_DIM_MAJOR = 8
 };
 
 #define GR_MAX_DEPTH 8    /* longest ancestor chain a beam may have */
@@ -193,8 +198,15 @@ gr_status gr_beam_topk(int32_t R, int32_t n_in, int32_t vocab, int32_t k,
  * and selection with k = beam_width.  flags: GR_TOPK_LOG_SOFTMAX, plus the
  * optional stage bits GR_STEP_ATTENTION / GR_STEP_SELECTION.
  *   W: [vocab][H*head_dim] dtype (row t = code t's projection vector).
+ *   Layout note: this default is the TRANSPOSE of the D x 256 projection
+ *   matrix as the pages write it (Engineering Exploration of Generative
+ *   Recall, 4.2), i.e. of a [H*head_dim][vocab] array: code t's D weights
+ *   are contiguous, which makes each code one contiguous MFMA operand row.
+ *   A caller holding the [H*head_dim][vocab] array passes it as is with
+ *   flags | GR_W_DIM_MAJOR; passing it without that flag computes the
+ *   logits of the transposed matrix (wrong codes, no error).
  *   vocab = 1 is scalar scoring (TransRetrieval): score = o . W[0] (+ prior),
- *   flags must be 0.
+ *   flags must be 0 (GR_W_DIM_MAJOR aside).
  *   Precision: for bf16 with vocab = 256 and a prompt window Lw of at least
  *   64 keys and at least H*head_dim / 8 keys, o enters the projection (a
  *   bf16 MFMA) rounded to bf16, which moves a logit by about

@@ -142,10 +142,12 @@ def test_decode_step_host_errors():
 def test_workspace_sizes():
     sh = shape(R=256)
     # bf16 codebook path: bf16 copy of o and the chain ids, one selection
-    # group per request
+    # group per request, and room for a code-major copy of a dimension-major
+    # W (256 x 512 bf16)
     ids = 256 * 8 * 128 * 4
-    assert L.gr_decode_workspace_size(sh, 100, 256, 100) >= 256 * 100 * 512 * 2 + ids
-    assert L.gr_decode_workspace_size(sh, 100, 256, 100) < 256 * 100 * 512 * 2 + ids + 4096
+    wt = 256 * 512 * 2
+    assert L.gr_decode_workspace_size(sh, 100, 256, 100) >= 256 * 100 * 512 * 2 + ids + wt
+    assert L.gr_decode_workspace_size(sh, 100, 256, 100) < 256 * 100 * 512 * 2 + ids + wt + 4096
     # scalar path: fp32 o + one score per candidate + partial lists.  With a
     # single request, 40 000 candidates split into groups of 8192 (5 lists of
     # 2000) rather than 32768, as 5 x 2000 still fits the final merge.
@@ -176,7 +178,8 @@ def test_projection_path_by_window_and_width():
         sh = shape(R=-(-384 // H), H=H, **kw)
         rows = sh.R * 32
         D = sh.H * sh.head_dim
-        n = L.gr_decode_workspace_size(sh, 32, 256, 32)
+        # less the room for a code-major copy of a dimension-major W (bf16)
+        n = L.gr_decode_workspace_size(sh, 32, 256, 32) - 256 * D * 2
         fp32 = rows * D * 4 + rows * 256 * 4
         return "fp32" if n >= fp32 else "bf16"
     assert path(prompt_len=600) == "bf16"                        # D = 512
@@ -320,3 +323,25 @@ def test_workspace_size_covers_every_call_of_the_step():
         assert need >= L.gr_attn_workspace_size(sh, nb)
         assert need >= L.gr_topk_workspace_size(sh.R, nb, vocab, k)
     assert L.gr_workspace_size(shape(R=0), 100, 256, 100) == 0
+
+
+def test_codebook_layout_contract():
+    """The boundary's W contract as the header states it: code-major
+    [vocab][H*head_dim] by default, stated next to the pages' D x 256
+    orientation, which GR_W_DIM_MAJOR accepts as is; the one workspace-size
+    call of the step, gr_workspace_size(shape, n_beams, vocab, k), is
+    exported."""
+    import os
+    import re
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                            "gr_beam.h")).read()
+    assert "W: [vocab][H*head_dim] dtype (row t = code t's projection vector)." in hdr
+    assert "TRANSPOSE of the D x 256" in hdr and "[H*head_dim][vocab]" in hdr
+    m = re.search(r"GR_W_DIM_MAJOR\s*=\s*(\d+)", hdr)
+    assert m and int(m.group(1)) == L.GR_W_DIM_MAJOR
+    assert re.search(r"size_t gr_workspace_size\(const gr_shape \*shape, int32_t n_beams,\s*int32_t vocab, int32_t k\);",
+                     hdr)
+    assert hasattr(L._lib, "gr_workspace_size")
+    # the flag is accepted by gr_decode_step's host checks (no other flag is)
+    sh = L.Shape(1, 2, 64, 8, 0, L.GR_BF16, 0.0)
+    assert L.gr_workspace_size(sh, 4, 256, 4) >= L.gr_decode_workspace_size(sh, 4, 256, 4) > 0

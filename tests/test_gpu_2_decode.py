@@ -25,6 +25,7 @@ import workloads as W
 from generative_recommendation_beam_amd import _lib as L
 from generative_recommendation_beam_amd import harness as HN
 from parity import (announce, assert_close, check_index_rule, check_self_consistent)
+from oracle_pool import oracle_many
 
 pytestmark = pytest.mark.gpu
 
@@ -186,8 +187,11 @@ def test_chained_fp32_three_steps():
     print(f"teacher-forced steps: {forced}")
 
 
-FULL = [("beam50_p600", None), ("beam100_p600", [0, 97, 255]),
-        ("broadcast40k_u256", None), ("beam512_p2048_w512", [17])]
+# every request of the headline, the beam-50 and the scalar workloads, 8 of
+# the 32 large-beam requests, and the 8192-key split-window workload in full
+FULL = [("beam50_p600", None), ("beam100_p600", None),
+        ("broadcast40k_u256", None), ("beam512_p2048_w512", [0, 5, 9, 13, 17, 22, 27, 31]),
+        ("long8k_beam100", None)]
 
 
 @pytest.mark.parametrize("name,rsel", FULL, ids=[n for n, _ in FULL])
@@ -202,7 +206,8 @@ def test_decode_full_size_sampled(name, rsel):
     assert int(ds.dev_err.item()) == 0
     got = HN.results_to_host(buf)
     rs = list(range(cfg.R)) if rsel is None else rsel
-    ref = oracle_step(x, rs)
+    # the oracle over the requests in worker processes (one request each)
+    ref = oracle_many(name, rs) if len(rs) > 1 else oracle_step(x, rs)
     compare(cfg, got, ref, rs, name, debug=False)
     # same call with the debug outputs: attention and every candidate score
     buf2 = HN.decode_buffers(ds, debug_outputs=True)
@@ -245,6 +250,29 @@ def test_stage_split_equals_whole(name):
             L.gr_decode_step(ds.shape, ds.prompt_k, ds.prompt_v, ds.q, ds.n_beams, ds.trie, ds.beam_node, ds.W,
                              ds.vocab, ds.prior, ds.k, ds.flags | st, buf.score, buf.token, buf.parent, buf.attn,
                              buf.cand, buf.ws, buf.ws_bytes, ds.dev_err)
+        torch.cuda.synchronize()
+        outs.append(HN.results_to_host(buf))
+    assert int(ds.dev_err.item()) == 0
+    for key in ("score", "token", "parent", "attn", "cand"):
+        np.testing.assert_array_equal(outs[0][key], outs[1][key], err_msg=key)
+
+
+@pytest.mark.parametrize("name", ["beam100_small", "f32_beam16", "scalar_small"])
+def test_dim_major_codebook_equals_code_major(name):
+    """W given dimension-major ([H*d][vocab], the pages' D x 256 orientation)
+    with GR_W_DIM_MAJOR gives bit-identical results to the default
+    code-major [vocab][H*d]."""
+    cfg = SMALL[name]
+    announce(f"gr_decode_step dimension-major W {name}")
+    x = W.make_step_inputs(cfg)
+    ds = HN.upload_step(x)
+    wt = ds.W.t().contiguous()
+    outs = []
+    for w, fl in ((ds.W, 0), (wt, L.GR_W_DIM_MAJOR)):
+        buf = HN.decode_buffers(ds, debug_outputs=True)
+        L.gr_decode_step(ds.shape, ds.prompt_k, ds.prompt_v, ds.q, ds.n_beams, ds.trie, ds.beam_node, w,
+                         ds.vocab, ds.prior, ds.k, ds.flags | fl, buf.score, buf.token, buf.parent, buf.attn,
+                         buf.cand, buf.ws, buf.ws_bytes, ds.dev_err)
         torch.cuda.synchronize()
         outs.append(HN.results_to_host(buf))
     assert int(ds.dev_err.item()) == 0

@@ -39,9 +39,10 @@
 // chunk ^ (key >> 2) & 3, then V^T [32][key] with chunk ^ dim & 15), so the
 // candidates copy them as they are.
 //
-// xf_user_kernel: one launch per layer over the user tokens of every
-// request; launch l finishes layer l-1 (attention over the user keys of
-// l-1, output projection, FFN) and forms layer l's queries, keys and values.
+// xf_user_kernel: one launch per layer, one workgroup per 32 user tokens of
+// a request; launch l finishes layer l-1 (attention over the user keys of
+// l-1, output projection, FFN) and forms layer l's queries, keys and values,
+// its four waves splitting every product by head or by output features.
 // xf_cand_kernel: all layers for 4 x 32 candidates per workgroup, then the
 // final LayerNorm and the score.
 
@@ -489,14 +490,19 @@ __global__ __launch_bounds__(kXCandWaves * 64, 2) void xf_cand_kernel(XfCandP p)
 }
 
 // ---- user kernel ---------------------------------------------------------------
-// Per (request, layer) launch over all user tokens of the request, one wave
-// per 32 tokens.  The wave's state between launches lives in the workspace:
-// x (fp32, the accumulator layout: 256 bytes a lane) and the queries of the
-// four heads (bf16 B operands: 128 bytes a lane).  A launch is a short
-// chain of pieces with little work each, so its ring is four slots deep
-// (three pieces in flight); every piece is exactly four 1 KB DMAs per wave
-// (short pieces add re-reads into a scratch block), which makes each wait a
-// fixed count.
+// Per (request, layer) launch, one workgroup per 32 user tokens.  The four
+// waves split every product of the layer instead of each wave running the
+// whole layer for tokens of its own: wave h attends for head h (its user
+// keys and values staged in its own 32 KB of LDS), wave w forms output
+// features 32w .. 32w+31 of the output projection and of the second FFN
+// product, hidden units 64w .. 64w+63 of the first, and head w's queries,
+// keys and values.  Between the products the waves exchange their slices
+// of the activations through LDS (the heads' outputs, the residual stream,
+// the hidden units), in the same accumulator layout the products use.  The
+// weight rows a wave multiplies are its own, so they come from L2 straight
+// into registers.  Every wave holds the whole residual stream of the 32
+// tokens (for the LayerNorms); between launches it waits in the workspace
+// with the queries.
 struct XfUserP {
   const uint16_t *user;     // [R][Lu][D] bf16
   const uint16_t *w_mat;
@@ -508,41 +514,52 @@ struct XfUserP {
   float sl2;
 };
 
-#ifndef GR_XF_USER_WAVES
-#define GR_XF_USER_WAVES 4
-#endif
-constexpr int kXUserWaves = GR_XF_USER_WAVES;
-constexpr int kXUserSlots = 4;
-constexpr int kXUserDma = 32 / kXUserWaves;   // DMAs per wave and piece (32 KB over the waves)
-static_assert(kXUserWaves >= 2 && kXUserWaves <= 8 && (kXUserSlots - 2) * kXUserDma < 64, "wait counts");
+constexpr int kXUserNW = kXHeads;          // one wave per head / per output slice
+static_assert(kXD == 32 * kXUserNW, "one 32-feature tile per wave");
 
 struct XfUserSmem {
-  unsigned char ring[kXUserSlots][kXSlot];
-  unsigned char dummy[1024];
+  unsigned char kv[kXUserNW][kXSlot];     // wave w: head w's user K/V piece, then its exchange slices
   float vec_prev[kXVecBytes / 4];         // vectors of layer l - 1
   float vec[kXVecBytes / 4];              // vectors of layer l
 };
+// exchange slices inside a wave's kv region (after its attention): two
+// buffers, used in turn, so that a slice is never rewritten while another
+// wave may still read the previous one
+constexpr int kXchg = 8192;
 
-__global__ __launch_bounds__(kXUserWaves * 64) void xf_user_kernel(XfUserP p) {
-  constexpr int NW = kXUserWaves;
+// A operand rows of a product read from global memory: row `row` of a
+// row-major bf16 matrix with `ld` elements per row, k-step (ft, s) of the
+// lane's half g: elements 32 ft + 16 s + 8 g .. +7 (the B operand layout).
+__device__ __forceinline__ bf16x8 wrow8(const uint16_t *w, int row, int ld, int ft, int s, int g) {
+  return *(const bf16x8 *)(w + (size_t)row * ld + 32 * ft + 16 * s + 8 * g);
+}
+
+__global__ __launch_bounds__(kXUserNW * 64) void xf_user_kernel(XfUserP p) {
   __shared__ __attribute__((aligned(1024))) XfUserSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, c = lane & 31;
   const int n_ut = p.Lu / 32;
-  const int wg_per_r = (n_ut + NW - 1) / NW;
-  const int r = blockIdx.x / wg_per_r;
-  const int ut = (blockIdx.x % wg_per_r) * NW + wave;    // this wave's token tile
-  const bool live = ut < n_ut;                           // waves past the last tile only help with the DMA
-  const int utl = min(ut, n_ut - 1);
+  const int r = blockIdx.x / n_ut, ut = blockIdx.x % n_ut;
   const int l = p.layer;
-  float *xs = p.xs + (((size_t)r * n_ut + utl) * 64 + lane) * 64;
-  uint16_t *qs = p.qs + (((size_t)r * n_ut + utl) * 64 + lane) * 64;
+  float *xs = p.xs + (((size_t)r * n_ut + ut) * 64 + lane) * 64;
+  uint16_t *qs = p.qs + (((size_t)r * n_ut + ut) * 64 + lane) * 64;
   unsigned char *ukv_r = p.ukv + (size_t)r * p.L * kXHeads * p.n_kc * kXSlot;
+  unsigned char *mine = sm.kv[wave];
+  const int pr = xpi(c);                   // this lane's row within a 32-row weight tile
 
+  // ---- in stream order: the vectors of both layers (shared), this wave's
+  // head's first user K/V piece of layer l - 1 (its own region)
+  if (l > 0) {
+    dma_floats<kXUserNW>(sm.vec_prev, p.w_vec + (size_t)(l - 1) * kXLayerVec, kXLayerVec, wave, lane);
+    dma_copy<1>(mine, ukv_r + ((size_t)((l - 1) * kXHeads + wave) * p.n_kc) * kXSlot, kXSlot, 0, lane);
+  }
+  dma_floats<kXUserNW>(sm.vec, p.w_vec + (size_t)l * kXLayerVec, kXLayerVec, wave, lane);
+
+  // the residual stream of token c (features 32 ft + 16 (i >> 3) + 8 g + (i & 7))
   Acc x[4];
   if (l == 0) {
-    const uint16_t *src = p.user + ((size_t)r * p.Lu + 32 * utl + c) * kXD + 8 * g;
+    const uint16_t *src = p.user + ((size_t)r * p.Lu + 32 * ut + c) * kXD + 8 * g;
 #pragma unroll
     for (int ft = 0; ft < 4; ++ft)
 #pragma unroll
@@ -560,164 +577,178 @@ __global__ __launch_bounds__(kXUserWaves * 64) void xf_user_kernel(XfUserP p) {
         x[ft][4 * i4] = v.x; x[ft][4 * i4 + 1] = v.y; x[ft][4 * i4 + 2] = v.z; x[ft][4 * i4 + 3] = v.w;
       }
   }
-  // the vectors of both layers, ahead of every piece
-  if (l > 0) dma_floats<NW>(sm.vec_prev, p.w_vec + (size_t)(l - 1) * kXLayerVec, kXLayerVec, wave, lane);
-  dma_floats<NW>(sm.vec, p.w_vec + (size_t)l * kXLayerVec, kXLayerVec, wave, lane);
+  GR_WAIT_VMCNT(0);
+  ring_barrier();
 
-  // Pieces: (layer > 0) for each head the user K/V of layer l-1 (n_kc
-  // pieces) and the head's W_o columns, the FFN halves of l-1; then the
-  // q/k/v rows of layer l per head.  Past the last piece, padding pieces
-  // of scratch re-reads keep the count of loads in flight fixed.
-  const int per_head = p.n_kc + 1;
-  const int n_fin = l > 0 ? kXHeads * per_head + 4 : 0;
-  const int n_pieces = n_fin + kXHeads;
-  auto pad = [&](int n) {
-    for (int i = 0; i < n; ++i) dma16(p.w_mat + 8 * fresh(lane), sm.dummy);
+  int xb = 0;                              // exchange buffer in use
+  // write this wave's slice (n16 16-byte pieces a lane) and read every wave's
+  auto publish = [&](const uint4 *v, int n16) {
+    uint4 *dst = (uint4 *)(mine + xb * kXchg) + lane * n16;
+    for (int i = 0; i < n16; ++i) dst[i] = v[i];
   };
-  auto issue = [&](int pc) {
-    if (pc >= n_pieces) {
-      pad(kXUserDma);
-      return;
-    }
-    unsigned char *slot = sm.ring[pc % kXUserSlots];
-    if (pc < n_fin) {
-      const int lp = l - 1;
-      const uint16_t *wm = p.w_mat + (size_t)lp * kXMat;
-      if (pc < kXHeads * per_head) {
-        const int h = pc / per_head, j = pc % per_head;
-        if (j < p.n_kc) {
-          dma_copy<NW>(slot, ukv_r + ((size_t)(lp * kXHeads + h) * p.n_kc + j) * kXSlot, kXSlot, wave, lane);
-        } else {
-          dma_wo_cols<NW>(slot, wm + kMo, h, wave, lane);     // 8 KB: a quarter of a piece
-          pad(kXUserDma - 8 / NW);
-        }
-        return;
+  auto slice_of = [&](int w) -> const uint4 * { return (const uint4 *)(sm.kv[w] + xb * kXchg); };
+  // x[ft] += the update slice wave ft published (every wave sums alike)
+  auto add_slices = [&](Acc(&xx)[4]) {
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft) {
+      const uint4 *d4 = slice_of(ft) + lane * 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = d4[q];
+        xx[ft][4 * q] += __uint_as_float(v.x); xx[ft][4 * q + 1] += __uint_as_float(v.y);
+        xx[ft][4 * q + 2] += __uint_as_float(v.z); xx[ft][4 * q + 3] += __uint_as_float(v.w);
       }
-      const int e = pc - kXHeads * per_head;          // 0..3: W1 half 0, W2 half 0, W1 half 1, W2 half 1
-      const int fh = e >> 1;
-      if ((e & 1) == 0)
-        dma_rows<NW>(slot, 128, [&](int i) { return wm + kM1 + (size_t)(128 * fh + i) * kXD; }, wave, lane);
-      else
-        dma_rows<NW>(slot, 128, [&](int i) { return wm + kM2 + (size_t)i * kXFF + 128 * fh; }, wave, lane);
-      return;
     }
-    const int h = pc - n_fin;
-    const uint16_t *wm = p.w_mat + (size_t)l * kXMat;
-    dma_rows<NW>(slot, 96, [&](int i) { return wm + kMqkv + (size_t)((i >> 5) * kXD + 32 * h + (i & 31)) * kXD; },
-                 wave, lane);                                 // 24 KB: three quarters of a piece
-    pad(kXUserDma - 24 / NW);
-  };
-  // piece pc has landed once the two issued after it may still be in
-  // flight; after the barrier every wave is done with piece pc - 1, whose
-  // slot receives piece pc + 3.  Once the wave has issued global stores
-  // (the layer's queries, keys and values), loads and stores share the
-  // counter and the wait drains it.
-  auto step = [&](int pc, bool stores) -> const unsigned char * {
-    if (stores) GR_WAIT_VMCNT_LGKM0(0);
-    else GR_WAIT_VMCNT_LGKM0((kXUserSlots - 2) * kXUserDma);
-    ring_barrier();
-    issue(pc + kXUserSlots - 1);
-    return sm.ring[pc % kXUserSlots];
   };
 
-  for (int i = 0; i < kXUserSlots - 1; ++i) issue(i);
-  int pc = 0;
   bf16x8 hB[4][2];
   if (l > 0) {
-    // attention of layer l-1 over every user key (each token's own key is
-    // one of them), with the queries the previous launch left; the output
-    // projection head by head
-    for (int h = 0; h < kXHeads; ++h) {
-      bf16x8 qb[2];
-      qb[0] = *(const bf16x8 *)(qs + 16 * h);
-      qb[1] = *(const bf16x8 *)(qs + 16 * h + 8);
-      HeadState st;
-      zero(st.o);
-      st.m = -__builtin_inff();
-      st.l = 0.f;
-      for (int j = 0; j < p.n_kc; ++j) {
-        const unsigned char *kv = step(pc++, false);
-        attend_piece(st, kv, min(8, (p.Lu - 256 * j) >> 5), c, g, qb, p.sl2);
+    const uint16_t *wm = p.w_mat + (size_t)(l - 1) * kXMat;
+    // ---- attention of head `wave` of layer l - 1 over every user key
+    bf16x8 qb[2];
+    qb[0] = *(const bf16x8 *)(qs + 16 * wave);
+    qb[1] = *(const bf16x8 *)(qs + 16 * wave + 8);
+    HeadState st;
+    zero(st.o);
+    st.m = -__builtin_inff();
+    st.l = 0.f;
+    for (int j = 0; j < p.n_kc; ++j) {
+      if (j > 0) {
+        // this wave's reads of the previous piece are done; the region is its own
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        dma_copy<1>(mine, ukv_r + ((size_t)((l - 1) * kXHeads + wave) * p.n_kc + j) * kXSlot, kXSlot, 0, lane);
+        GR_WAIT_VMCNT(0);
+        asm volatile("" ::: "memory");
       }
-      const float inv = 1.f / xor32_sum(st.l);
+      attend_piece(st, mine, min(8, (p.Lu - 256 * j) >> 5), c, g, qb, p.sl2);
+    }
+    const float inv = 1.f / xor32_sum(st.l);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) st.o[i] *= inv;
+    for (int i = 0; i < 16; ++i) st.o[i] *= inv;
+    {
       const bf16x8 ob[2] = {pack8(st.o, 0), pack8(st.o, 1)};
-      const unsigned char *w = step(pc++, false);
-      oproj_head(x, w, c, g, ob);
-      if (h == 0) {
-#pragma unroll
-        for (int ot = 0; ot < 4; ++ot) add_bias(x[ot], sm.vec_prev + kVbO + 32 * ot, g);
-      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);     // done reading the K/V piece
+      publish((const uint4 *)ob, 2);
     }
+    // output projection rows of this wave's features, prefetched
+    bf16x8 wo[4][2];
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) wo[h][s] = wrow8(wm + kMo, 32 * wave + pr, kXD, h, s, g);
+    __syncthreads();
+    // ---- update slice of the wave's features: W_o[features] . o (all heads) + b_o
+    {
+      Acc d;
+      zero(d);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint4 *o4 = slice_of(h) + lane * 2;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wo[h][s], __builtin_bit_cast(bf16x8, o4[s]), d, 0, 0, 0);
+      }
+      add_bias(d, sm.vec_prev + kVbO + 32 * wave, g);
+      xb ^= 1;
+      publish((const uint4 *)&d, 4);
+    }
+    // first FFN product rows of this wave's hidden units, prefetched
+    bf16x8 w1[2][4][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) w1[t][ft][s] = wrow8(wm + kM1, 64 * wave + 32 * t + pr, kXD, ft, s, g);
+    // ---- every wave adds every wave's slice of the update
+    __syncthreads();
+    add_slices(x);
+    // ---- FFN: hidden units 64 wave .. of ReLU(W1 LN2(x) + b1)
     layer_norm_b(x, sm.vec_prev + kVln2g, sm.vec_prev + kVln2b, g, hB);
-    for (int fh = 0; fh < 2; ++fh) {
-      bf16x8 uB[4][2];
-      {
-        const unsigned char *w = step(pc++, false);
+    {
+      bf16x8 ub[2][2];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          Acc a[2];
-          zero(a[0]); zero(a[1]);
-          gemm_tiles<2>(a, w, 64 * half, c, g, hB);
+      for (int t = 0; t < 2; ++t) {
+        Acc a;
+        zero(a);
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int ot = 2 * half + t;
-            add_bias(a[t], sm.vec_prev + kVb1 + 128 * fh + 32 * ot, g);
+        for (int ft = 0; ft < 4; ++ft)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) a[t][i] = fmaxf(a[t][i], 0.f);
-            uB[ot][0] = pack8(a[t], 0);
-            uB[ot][1] = pack8(a[t], 1);
-          }
-        }
+          for (int s = 0; s < 2; ++s) a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w1[t][ft][s], hB[ft][s], a, 0, 0, 0);
+        add_bias(a, sm.vec_prev + kVb1 + 64 * wave + 32 * t, g);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a[i] = fmaxf(a[i], 0.f);
+        ub[t][0] = pack8(a, 0);
+        ub[t][1] = pack8(a, 1);
       }
-      const unsigned char *w = step(pc++, false);
-      gemm_tiles<4>(x, w, 0, c, g, uB);
-      if (fh == 0) {
-#pragma unroll
-        for (int ot = 0; ot < 4; ++ot) add_bias(x[ot], sm.vec_prev + kVb2 + 32 * ot, g);
-      }
+      xb ^= 1;
+      publish((const uint4 *)ub, 4);
     }
+    // second FFN product rows of this wave's features, prefetched
+    bf16x8 w2[8][2];
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) w2[tt][s] = wrow8(wm + kM2, 32 * wave + pr, kXFF, tt, s, g);
+    __syncthreads();
+    // ---- update slice of the wave's features: W2[features] . hidden (all 256) + b2
+    {
+      Acc d;
+      zero(d);
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const uint4 *u4 = slice_of(tt >> 1) + lane * 4 + 2 * (tt & 1);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w2[tt][s], __builtin_bit_cast(bf16x8, u4[s]), d, 0, 0, 0);
+      }
+      add_bias(d, sm.vec_prev + kVb2 + 32 * wave, g);
+      xb ^= 1;
+      publish((const uint4 *)&d, 4);
+    }
+    __syncthreads();
+    add_slices(x);
   }
-  // layer l: queries, keys and values of the user tokens
-  const int key = 32 * utl + c, kc = key >> 8, kl = key & 255;
-  for (int h = 0; h < kXHeads; ++h) {
-    const unsigned char *w = step(pc++, h > 0);
-    if (h == 0) layer_norm_b(x, sm.vec + kVln1g, sm.vec + kVln1b, g, hB);
-    unsigned char *piece = ukv_r + ((size_t)(l * kXHeads + h) * p.n_kc + kc) * kXSlot;
-    Acc a[1];
-    // q
-    zero(a[0]);
-    gemm_tiles<1>(a, w, 0, c, g, hB);
-    add_bias(a[0], sm.vec + kVbQKV + 32 * h, g);
-    if (live) {
-      *(bf16x8 *)(qs + 16 * h) = pack8(a[0], 0);
-      *(bf16x8 *)(qs + 16 * h + 8) = pack8(a[0], 1);
-    }
-    // k: K [key][32], this lane's dims 16 s + 8 g .. +7 are one 16-byte chunk
-    zero(a[0]);
-    gemm_tiles<1>(a, w, 32, c, g, hB);
-    add_bias(a[0], sm.vec + kVbQKV + kXD + 32 * h, g);
-    if (live) {
+  // ---- layer l: head `wave`'s queries, keys and values of the 32 tokens
+  {
+    const uint16_t *wq = p.w_mat + (size_t)l * kXMat + kMqkv;
+    bf16x8 wa[3][4][2];
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+      for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) wa[m][ft][s] = wrow8(wq, m * kXD + 32 * wave + pr, kXD, ft, s, g);
+    layer_norm_b(x, sm.vec + kVln1g, sm.vec + kVln1b, g, hB);
+    Acc a[3];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) zero(a[m]);
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft)
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        *(bf16x8 *)(piece + kl * 64 + 16 * ((2 * s + g) ^ ((kl >> 2) & 3))) = pack8(a[0], s);
-    }
-    // v: V^T [dim][key], one bf16 per (dim, key)
-    zero(a[0]);
-    gemm_tiles<1>(a, w, 64, c, g, hB);
-    add_bias(a[0], sm.vec + kVbQKV + 2 * kXD + 32 * h, g);
-    if (live) {
-      uint16_t *vt = (uint16_t *)(piece + 16384);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int dim = 16 * (i >> 3) + 8 * g + (i & 7);
-        const __bf16 b = (__bf16)a[0][i];
-        vt[dim * 256 + 8 * ((kl >> 3) ^ (dim & 15)) + (kl & 7)] = *(const uint16_t *)&b;
-      }
+        for (int m = 0; m < 3; ++m) a[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[m][ft][s], hB[ft][s], a[m], 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < 3; ++m) add_bias(a[m], sm.vec + kVbQKV + m * kXD + 32 * wave, g);
+    const int key = 32 * ut + c, kc = key >> 8, kl = key & 255;
+    unsigned char *piece = ukv_r + ((size_t)(l * kXHeads + wave) * p.n_kc + kc) * kXSlot;
+    // q: the B operand of the next launch's scores
+    *(bf16x8 *)(qs + 16 * wave) = pack8(a[0], 0);
+    *(bf16x8 *)(qs + 16 * wave + 8) = pack8(a[0], 1);
+    // k: K [key][32], this lane's dims 16 s + 8 g .. +7 are one 16-byte chunk
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      *(bf16x8 *)(piece + kl * 64 + 16 * ((2 * s + g) ^ ((kl >> 2) & 3))) = pack8(a[1], s);
+    // v: V^T [dim][key], one bf16 per (dim, key)
+    uint16_t *vt = (uint16_t *)(piece + 16384);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int dim = 16 * (i >> 3) + 8 * g + (i & 7);
+      const __bf16 b = (__bf16)a[2][i];
+      vt[dim * 256 + 8 * ((kl >> 3) ^ (dim & 15)) + (kl & 7)] = *(const uint16_t *)&b;
     }
   }
-  if (live && l + 1 < p.L) {
+  // the residual stream for the next launch (every wave holds all of it)
+  if (wave == 0 && l + 1 < p.L) {
 #pragma unroll
     for (int ft = 0; ft < 4; ++ft)
 #pragma unroll
@@ -725,7 +756,6 @@ __global__ __launch_bounds__(kXUserWaves * 64) void xf_user_kernel(XfUserP p) {
         *(float4 *)(xs + 16 * ft + 4 * i4) =
             make_float4(x[ft][4 * i4], x[ft][4 * i4 + 1], x[ft][4 * i4 + 2], x[ft][4 * i4 + 3]);
   }
-  GR_WAIT_VMCNT(0);                                      // the padding loads have landed
 }
 
 }  // namespace
@@ -743,10 +773,9 @@ hipError_t launch_xf_scores(const XfArgs &a, hipStream_t s) {
   u.qs = (uint16_t *)((char *)a.user_state + (size_t)a.R * n_ut * 64 * 64 * 4);
   u.R = a.R; u.L = a.L; u.n_kc = n_kc; u.Lu = a.Lu;
   u.sl2 = kXLog2e / sqrtf((float)kXHd);
-  const int wg_per_r = (n_ut + kXUserWaves - 1) / kXUserWaves;
   for (int l = 0; l < a.L; ++l) {
     u.layer = l;
-    hipLaunchKernelGGL(xf_user_kernel, dim3((unsigned)(a.R * wg_per_r)), dim3(kXUserWaves * 64), 0, s, u);
+    hipLaunchKernelGGL(xf_user_kernel, dim3((unsigned)(a.R * n_ut)), dim3(kXUserNW * 64), 0, s, u);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

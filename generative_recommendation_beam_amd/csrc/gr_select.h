@@ -227,6 +227,21 @@ __device__ __forceinline__ void wave_small2_pair_u32(uint32_t x, uint32_t &s1, u
   s1 = m1;
   s2 = m2;
 }
+// The m-th smallest (1 <= m <= 64, counting equal values) of one u32 per
+// lane across the wave, in every lane: a binary search over the bits, each
+// step one compare and one ballot (the answer is the largest value with
+// fewer than m lanes below it).
+__device__ __forceinline__ uint32_t wave_kth_smallest_u32(uint32_t x, int m) {
+  uint32_t ans = 0u;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = ans | (1u << bit);
+    const int below = __builtin_popcountll(__builtin_amdgcn_ballot_w64(x < cand));
+    if (below < m) ans = cand;
+  }
+  return ans;
+}
+
 // The m-th smallest (m = 1 or 2) of one u32 per lane across the wave.
 __device__ __forceinline__ uint32_t wave_small2_u32(uint32_t x, int m) {
   uint32_t s1, s2;

@@ -258,8 +258,9 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
   // into one region per wave).  One 256-bin histogram of the staged rank
   // keys over [best, T] finds the bin holding the k-th; the candidates up to
   // that bin (at most 256, else the general path) are gathered and ordered
-  // by counting ranks.  Too many staged candidates or a degenerate bound go
-  // through the selection over all registers.  Every decision is
+  // by counting ranks.  A second bound, from the waves' best lane maxima,
+  // tightens T when it can.  Too many staged candidates or a degenerate
+  // bound go through the selection over all registers.  Every decision is
   // block-uniform.
   bool done = false;
   if (k_sel <= kFastK) {
@@ -279,7 +280,14 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
     uint32_t w1, w2;
     wave_small2_pair_u32(any ? rank_key(lb) : kInvalidKey, w1, w2);
     const uint32_t wh = wave_min_u32(any ? rank_key(best) : kInvalidKey);
-    if (lane == 0) sm.wbest[wave] = make_uint4(w1, w2, wh, 0u);
+    // A second bound from the lanes' best candidates: the mw-th best lane
+    // maximum of a wave (mw = ceil(k/8)) has mw candidates of that wave at or
+    // above it, so the worst of the eight waves' values has 8 mw >= k
+    // candidates at or above it.  It is the tighter one when the beams'
+    // running scores lie close together (many beams share the best
+    // candidates, and a unit's minimum says little).
+    const uint32_t wv = wave_kth_smallest_u32(any ? rank_key(best) : kInvalidKey, (k_sel + 7) >> 3);
+    if (lane == 0) sm.wbest[wave] = make_uint4(w1, w2, wh, wv);
     __syncthreads();                                    // also: the o buffers are no longer read
     uint32_t kmin = kInvalidKey, T = kInvalidKey;
     {
@@ -301,6 +309,10 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
       }
       const uint64_t m = __builtin_amdgcn_ballot_w64(lane < 16 && rank == ml - 1);
       T = (uint32_t)__builtin_amdgcn_readlane((int)v, (int)__builtin_ctzll(m));
+      uint32_t T2 = 0u;
+#pragma unroll
+      for (int w = 0; w < kNT / 64; ++w) T2 = max(T2, sm.wbest[w].w);
+      T = min(T, T2);
     }
     const float Ts = key_score(T);
     if (T != kInvalidKey && Ts > -__builtin_inff()) {

@@ -227,6 +227,20 @@ __device__ __forceinline__ void wave_small2_pair_u32(uint32_t x, uint32_t &s1, u
   s1 = m1;
   s2 = m2;
 }
+// The four smallest (counting equal values) of one u32 per lane across the
+// wave, ascending, in every lane: four wave minima, each time taking one lane
+// that holds the minimum out.
+__device__ __forceinline__ void wave_smallest4_u32(uint32_t x, uint32_t (&out)[4]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t mn = wave_min_u32(x);
+    out[i] = mn;
+    const uint64_t at = __builtin_amdgcn_ballot_w64(x == mn);
+    if (lane == (int)__builtin_ctzll(at)) x = kInvalidKey;
+  }
+}
+
 // The m-th smallest (1 <= m <= 64, counting equal values) of one u32 per
 // lane across the wave, in every lane: a binary search over the bits, each
 // step one compare and one ballot (the answer is the largest value with
@@ -384,6 +398,30 @@ __device__ __forceinline__ bool bucket_sort_u64(SelectSmem<NT> &sm, int L, uint6
   return true;
 }
 
+// Ascending order of the unique composites sm.u.list[0..L) (L <= kListCap),
+// all in [lo, hi], of which the first k are wanted: counting ranks up to 256
+// entries, else one bucket pass, else (ties crowd a bucket) a bitonic or
+// merge sort of the list padded to a power of two.  Every thread takes the
+// barriers.
+template <int NT>
+__device__ __forceinline__ void order_list(SelectSmem<NT> &sm, int L, int k, uint64_t lo, uint64_t hi) {
+  const int tid = threadIdx.x;
+  const int P = pow2_ceil(max(L, k));
+  if (L <= 256) {
+    rank_sort_u64<NT>(sm.u.list, L);
+  } else if (bucket_sort_u64<NT>(sm, L, lo, hi)) {
+  } else if (P <= NT) {
+    block_bitonic_sort_u64<NT>(sm.u.list, L, P);
+  } else {
+    for (int i = L + tid; i < P; i += NT) sm.u.list[i] = ~0ull;
+    __syncthreads();
+    if (P == 2 * NT) merge_sort_u64<NT, 2>(sm.u.list, sm.tmp);
+    else if (P == 4 * NT) merge_sort_u64<NT, 4>(sm.u.list, sm.tmp);
+    else if (P == 8 * NT) merge_sort_u64<NT, 8>(sm.u.list, sm.tmp);
+    else bitonic_sort_u64<NT>(sm.u.list, P);
+  }
+}
+
 // Appends every register candidate j with sel(j) to list (composites, in no
 // particular order): per-lane counts, one wave prefix sum and one LDS atomic
 // per wave reserve the slots, so the per-candidate work is VALU only.
@@ -518,21 +556,7 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[J], IdxFn idx_
     }, sm.n_list, sm.u.list);
   }
   __syncthreads();
-  const int L = min(sm.n_list, kListCap);
-  const int P = pow2_ceil(max(L, k));
-  if (L <= 256) {
-    rank_sort_u64<NT>(sm.u.list, L);
-  } else if (bucket_sort_u64<NT>(sm, L, (uint64_t)a << 32, hi_bound)) {
-  } else if (P <= NT) {
-    block_bitonic_sort_u64<NT>(sm.u.list, L, P);
-  } else {
-    for (int i = L + tid; i < P; i += NT) sm.u.list[i] = ~0ull;
-    __syncthreads();
-    if (P == 2 * NT) merge_sort_u64<NT, 2>(sm.u.list, sm.tmp);
-    else if (P == 4 * NT) merge_sort_u64<NT, 4>(sm.u.list, sm.tmp);
-    else if (P == 8 * NT) merge_sort_u64<NT, 8>(sm.u.list, sm.tmp);
-    else bitonic_sort_u64<NT>(sm.u.list, P);
-  }
+  order_list<NT>(sm, min(sm.n_list, kListCap), k, (uint64_t)a << 32, hi_bound);
 }
 
 // Writes the sorted selection of k_sel candidates: the final outputs (one

@@ -37,7 +37,7 @@ namespace {
 
 constexpr int kNT = 512;
 constexpr int kCB = 64;                    // o columns per LDS block (four MFMA k-steps)
-constexpr int kFastK = 128;                // largest k of the bounded selection
+constexpr int kFastK = 512;                // largest k of the bounded selection
 constexpr int kWaveStage = 512;            // staged candidates per wave, at most
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -59,7 +59,8 @@ struct LogitsSmem {
   } u;
   float red_max[kNT / 64][kGroupBeams];    // per-wave partial max / sum of each beam's logits
   float red_sum[kNT / 64][kGroupBeams];
-  uint4 wbest[kNT / 64];                   // per wave: its two best lane bounds, its best score (rank keys)
+  uint4 wbest[kNT / 64];                   // per wave: (unused, unused, its best score, its lane-maximum bound) as rank keys
+  uint32_t wpick[kNT / 64][4];             // per wave: its four best lane bounds (rank keys)
   uint32_t wcnt[kNT / 64];                 // per wave: staged candidates
   uint32_t n_final;                        // candidates gathered for the final ordering
 };
@@ -249,22 +250,22 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
     return (uint32_t)(b_begin + 32 * t + c) * 256u + 32u * wave + 8u * (uint32_t)(j >> 2) + 4u * g + (uint32_t)(j & 3);
   };
 
-  // ---- bounded selection (k <= 128).  A unit is the 16 scores one lane
+  // ---- bounded selection (k <= 512).  A unit is the 16 scores one lane
   // holds for one beam; its minimum u means 16 candidates score >= u.  The
   // lane bound is its best unit minimum (a unit with a NaN score bounds
   // nothing).  T is the ml-th best (ml = ceil(k/16)) of the waves' two best
-  // lane bounds: ml units hold 16 ml >= k candidates scoring >= T, so every
+  // lane bounds (four when ml > 16): ml units hold 16 ml >= k candidates scoring >= T, so every
   // selected candidate scores >= T, and only those are staged (by ballot,
   // into one region per wave).  One 256-bin histogram of the staged rank
   // keys over [best, T] finds the bin holding the k-th; the candidates up to
-  // that bin (at most 256, else the general path) are gathered and ordered
-  // by counting ranks.  A second bound, from the waves' best lane maxima,
+  // that bin are gathered and ordered (counting ranks up to 256 entries,
+  // else a bucket pass or a sort).  A second bound, from the waves' best lane maxima,
   // tightens T when it can.  Too many staged candidates or a degenerate
   // bound go through the selection over all registers.  Every decision is
   // block-uniform.
   bool done = false;
   if (k_sel <= kFastK) {
-    const int ml = (k_sel + 15) >> 4;                   // <= 8
+    const int ml = (k_sel + 15) >> 4;                   // <= 32
     float lb = -__builtin_inff(), best = -__builtin_inff(), umax[4];
     bool any = false;
 #pragma unroll
@@ -277,8 +278,12 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
         any = true;
       }
     }
-    uint32_t w1, w2;
-    wave_small2_pair_u32(any ? rank_key(lb) : kInvalidKey, w1, w2);
+    // picks: each wave's two best lane bounds, or its four best when the
+    // bound needs more than 16 units (k > 256)
+    const int np = ml > 16 ? 4 : 2;
+    uint32_t w4[4] = {kInvalidKey, kInvalidKey, kInvalidKey, kInvalidKey};
+    if (np == 4) wave_smallest4_u32(any ? rank_key(lb) : kInvalidKey, w4);
+    else wave_small2_pair_u32(any ? rank_key(lb) : kInvalidKey, w4[0], w4[1]);
     const uint32_t wh = wave_min_u32(any ? rank_key(best) : kInvalidKey);
     // A second bound from the lanes' best candidates: the mw-th best lane
     // maximum of a wave (mw = ceil(k/8)) has mw candidates of that wave at or
@@ -287,27 +292,33 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
     // running scores lie close together (many beams share the best
     // candidates, and a unit's minimum says little).
     const uint32_t wv = wave_kth_smallest_u32(any ? rank_key(best) : kInvalidKey, (k_sel + 7) >> 3);
-    if (lane == 0) sm.wbest[wave] = make_uint4(w1, w2, wh, wv);
+    if (lane < 4) sm.wpick[wave][lane] = lane == 0 ? w4[0] : lane == 1 ? w4[1] : lane == 2 ? w4[2] : w4[3];
+    if (lane == 0) sm.wbest[wave] = make_uint4(0u, 0u, wh, wv);
     __syncthreads();                                    // also: the o buffers are no longer read
     uint32_t kmin = kInvalidKey, T = kInvalidKey;
     {
-      // lane i < 16 holds pick i; its rank among the 16 (ties by position)
+      // lane i < 8 np holds pick i (wave i / np's (i % np)-th best lane
+      // bound); its rank among the 8 np picks (ties by position)
       uint32_t v = kInvalidKey;
       int rank = 0;
 #pragma unroll
-      for (int w = 0; w < kNT / 64; ++w) {
-        const uint4 b4 = sm.wbest[w];
-        kmin = min(kmin, b4.z);
-        if (lane == 2 * w) v = b4.x;
-        if (lane == 2 * w + 1) v = b4.y;
-      }
+      for (int w = 0; w < kNT / 64; ++w) kmin = min(kmin, sm.wbest[w].z);
+      const int npk = 8 * np;
+      if (lane < npk) v = np == 4 ? sm.wpick[lane >> 2][lane & 3] : sm.wpick[lane >> 1][lane & 1];
+      if (np == 4) {
 #pragma unroll
-      for (int w = 0; w < kNT / 64; ++w) {
-        const uint4 b4 = sm.wbest[w];
-        rank += (b4.x < v || (b4.x == v && 2 * w < lane)) ? 1 : 0;
-        rank += (b4.y < v || (b4.y == v && 2 * w + 1 < lane)) ? 1 : 0;
+        for (int i = 0; i < 32; ++i) {
+          const uint32_t pi = sm.wpick[i >> 2][i & 3];
+          rank += (pi < v || (pi == v && i < lane)) ? 1 : 0;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t pi = sm.wpick[i >> 1][i & 1];
+          rank += (pi < v || (pi == v && i < lane)) ? 1 : 0;
+        }
       }
-      const uint64_t m = __builtin_amdgcn_ballot_w64(lane < 16 && rank == ml - 1);
+      const uint64_t m = __builtin_amdgcn_ballot_w64(lane < npk && rank == ml - 1);
       T = (uint32_t)__builtin_amdgcn_readlane((int)v, (int)__builtin_ctzll(m));
       uint32_t T2 = 0u;
 #pragma unroll
@@ -375,7 +386,7 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
         const int src = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(mine));
         const uint32_t bstar = 4u * (uint32_t)src + (uint32_t)__builtin_amdgcn_readlane((int)bin, src);
         const int L = __builtin_amdgcn_readlane((int)(below + hb), src);
-        if (L <= 256) {
+        {
           done = true;
           uint64_t *list = sm.u.sel.u.list;
           for (int i0 = 0; i0 < (int)wc; i0 += 64) {
@@ -391,7 +402,9 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
             }
           }
           __syncthreads();
-          rank_sort_u64<kNT>(list, L);
+          // all gathered keys lie in [kmin, the top of bin bstar]
+          const uint64_t top = min((uint64_t)T, (uint64_t)kmin + ((uint64_t)(bstar + 1u) << shift) - 1ull);
+          order_list<kNT>(sm.u.sel, L, k_sel, (uint64_t)kmin << 32, (top << 32) | 0xFFFFFFFFull);
         }
       }
     }

@@ -41,6 +41,14 @@ SMALL = {
     "beam130_two_groups": W.reduced(CF["beam100_p600"], R=2, Lp=90, n_in=130, k=130,
                                     level_sizes=(100, 130, 130), H=4),
     "scalar_small": W.reduced(CF["broadcast40k_u256"], n_in=3000, k=333, level_sizes=(3000,)),
+    # the bounded selection at larger k: four picks per wave (k > 256), the
+    # lane-maximum bound with near-equal running scores, lists above 256
+    # entries ordered by the bucket pass
+    "k300_four_picks": W.reduced(CF["beam100_p600"], R=2, Lp=90, n_in=128, k=300, level_sizes=(100, 128, 128), H=4),
+    "k512_flat_prior": W.reduced(CF["beam100_p600"], R=2, Lp=90, n_in=128, k=512, level_sizes=(100, 128, 128), H=4,
+                                 prior="flat"),
+    "k200_zero_prior": W.reduced(CF["beam100_p600"], R=2, Lp=90, n_in=100, k=200, level_sizes=(100, 100, 100), H=4,
+                                 prior="zero"),
     "f32_beam16": W.reduced(CF["beam100_p600"], R=2, Lp=40, H=4, d=32, n_in=16, k=16,
                             level_sizes=(9, 16, 16), dtype="f32"),
     # edge cases: chains of the maximum depth (8 records), a one-token prompt,

@@ -360,14 +360,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   int cnt = 0;          // chain records of this lane's beam
   float rec_alpha = 1.f, rec_p = 0.f;   // a record's rescale and weight, from its key tile to its value tile
 
-  auto step = [&](int t0, auto S) {
+  // Per tile: wait until its stage has landed, then refill the stage of
+  // tile - 1.  The prompt loop's stage-0 head also does the tile-0 work.
+  auto head = [&](int tile, auto S, auto in_prompt) {
     constexpr int st = decltype(S)::value;
-    const int tile = t0 + st;
-    if (tile < n_total) {
+    {
       // at tile 0 the prologue has put exactly NS-2 tiles behind it
       wait_tiles(tile == 0 ? NS - 2 : min(NS - 2, n_total - 1 - tile));
       ring_barrier();
-      if constexpr (st == 0) {
+      if constexpr (st == 0 && decltype(in_prompt)::value) {
         if (tile == 0) {
           // queries and chain ids / parents have landed (they precede tile 0)
           if (chains && p.parent != nullptr && tid < G::NB) {
@@ -421,10 +422,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
       }
       // every wave is past tile-1: its stage can be refilled
       if (tile + NS - 1 < n_total) issue(tile + NS - 1, Stage<(st + NS - 1) % NS>{});
-      const char *kb = (const char *)kst(S);
-      const char *vb = (const char *)vst(S);
-
-      if (tile < n_tiles) {
+    }
+  };
+  auto prompt_tile = [&](int tile, auto S) {
+    const char *kb = (const char *)kst(S);
+    const char *vb = (const char *)vst(S);
+    {
+      {
         // ---- shared prompt window
         f32x16 S0, S1;
 #pragma unroll
@@ -486,7 +490,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
             O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, O[dt], 0, 0, 0);
           }
         }
-      } else if (tile >= n_pre) {
+      }
+    }
+  };
+  auto record_tile = [&](int tile, auto S) {
+    const char *kb = (const char *)kst(S);
+    const char *vb = (const char *)vst(S);
+    {
+      {
         // ---- one chain level: its key tile, then its value tile
         // (128-beam workgroups), or the beams of record tile bb
         const int k = tile - n_pre;
@@ -547,11 +558,34 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
       }
     }
   };
-  for (int t0 = 0; t0 < n_total; t0 += NS) {
-    step(t0, Stage<0>{});
-    step(t0, Stage<1>{});
-    if constexpr (NS > 2) step(t0, Stage<2>{});
-    if constexpr (NS > 3) step(t0, Stage<3>{});
+  // The prompt tiles [0, n_pre) and the chain-record tiles [n_pre, n_total)
+  // run in loops of their own: with both kinds in one loop body the register
+  // allocator moves the O accumulators between register ranges at every tile.
+  auto pstep = [&](int t0, auto S) {
+    const int tile = t0 + decltype(S)::value;
+    if (tile < n_pre) {
+      head(tile, S, std::true_type{});
+      if (tile < n_tiles) prompt_tile(tile, S);
+    }
+  };
+  auto rstep = [&](int t0, auto S) {
+    const int tile = t0 + decltype(S)::value;
+    if (tile >= n_pre && tile < n_total) {
+      head(tile, S, std::false_type{});
+      record_tile(tile, S);
+    }
+  };
+  for (int t0 = 0; t0 < n_pre; t0 += NS) {
+    pstep(t0, Stage<0>{});
+    pstep(t0, Stage<1>{});
+    if constexpr (NS > 2) pstep(t0, Stage<2>{});
+    if constexpr (NS > 3) pstep(t0, Stage<3>{});
+  }
+  for (int t0 = n_pre - n_pre % NS; t0 < n_total; t0 += NS) {
+    rstep(t0, Stage<0>{});
+    rstep(t0, Stage<1>{});
+    if constexpr (NS > 2) rstep(t0, Stage<2>{});
+    if constexpr (NS > 3) rstep(t0, Stage<3>{});
   }
 
   // ---- epilogue.  o leaves through LDS: each lane holds 4-element pieces of

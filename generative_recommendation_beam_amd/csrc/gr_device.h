@@ -68,9 +68,11 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // vmcnt wait and a barrier (ring_barrier below).  No VGPR is written, so
 // nothing is left for the compiler to misjudge.  M0 (reserved by the
 // compiler) is saved and restored around the load, and needs one wait state
-// before the load reads it.
+// before the load reads it.  The LDS address goes through readfirstlane: it
+// is wave-uniform, but the compiler cannot always prove it and would then
+// hold it in a vector register, which the scalar move cannot take.
 __device__ __forceinline__ void dma16(const void *src, const void *lds) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)GR_LDS(lds);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)GR_LDS(lds));
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -84,7 +86,7 @@ __device__ __forceinline__ void dma16(const void *src, const void *lds) {
 }
 // Streaming variant (read once): non-temporal cache policy.
 __device__ __forceinline__ void dma16_stream(const void *src, const void *lds) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)GR_LDS(lds);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)GR_LDS(lds));
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -99,7 +101,7 @@ __device__ __forceinline__ void dma16_stream(const void *src, const void *lds) {
 // The same for one dword per lane (global_load_lds_dword): lane l's 4 bytes
 // land at LDS byte lds + 4*l.
 __device__ __forceinline__ void dma4(const void *src, const void *lds) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)GR_LDS(lds);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)GR_LDS(lds));
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"

@@ -450,15 +450,20 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
           }
         }
         // IEEE maximum (v_maximum3_f32): no operand canonicalisation needed
-        float mx = __builtin_elementwise_maximum(S0[0], S1[0]);
+        // two chains of v_maximum3, each folding two scores per instruction
+        float mx0 = __builtin_elementwise_maximum(S0[0], S1[0]);
+        float mx1 = __builtin_elementwise_maximum(S0[1], S1[1]);
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(S0[i], S1[i]));
-        mx = xor32_max(mx) * p.sl2;
+        for (int i = 2; i < 16; i += 2) {
+          mx0 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx0, S0[i]), S1[i]);
+          mx1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx1, S0[i + 1]), S1[i + 1]);
+        }
+        float mx = xor32_max(__builtin_elementwise_maximum(mx0, mx1)) * p.sl2;
         // Exact running max: the key that sets it gets weight exactly 1, which
         // bf16 holds exactly (it dominates a peaked softmax).  The rescale is
         // skipped only when no lane's max grew (then alpha would be 1).
         if (__ballot(mx > m_run)) {
-          const float m_new = fmaxf(m_run, mx);
+          const float m_new = __builtin_elementwise_maximum(m_run, mx);
           const float alpha = fast_exp2(m_run - m_new);
           m_run = m_new;
           l_run *= alpha;

@@ -242,7 +242,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   // beams 0..63 in the stage's first half and 64..127 in its second, so that
   // every wave folds every tile.  Smaller workgroups: one tile per level, row
   // t holding beam t's key in the first half and its value in the second.
-  auto issue_records = [&](int d, int bb, auto S) {
+  auto issue_records = [&](int d, int bb, uint16_t *ks, uint16_t *vs) {
     if constexpr (G::NRB == 2) {
       const uint16_t *const base = bb ? p.av : p.ak;
 #pragma unroll
@@ -250,8 +250,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
         const int blk = wave * G::IPW + i;
         const uint32_t sw = bb ? dma_v[i] : dma_k[i];
         const int id0 = chain_id(d, dma_row[i]), id1 = chain_id(d, G::KT + dma_row[i]);
-        dma16(base + ((size_t)r * p.cap + (id0 >= 0 ? id0 : 0)) * row + (size_t)h * HD + sw, kst(S) + blk * 512);
-        dma16(base + ((size_t)r * p.cap + (id1 >= 0 ? id1 : 0)) * row + (size_t)h * HD + sw, vst(S) + blk * 512);
+        dma16(base + ((size_t)r * p.cap + (id0 >= 0 ? id0 : 0)) * row + (size_t)h * HD + sw, ks + blk * 512);
+        dma16(base + ((size_t)r * p.cap + (id1 >= 0 ? id1 : 0)) * row + (size_t)h * HD + sw, vs + blk * 512);
       }
     } else {
 #pragma unroll
@@ -260,8 +260,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
         const int b = bb * G::KT + dma_row[i];
         const int id = b < G::NB ? chain_id(d, b) : -1;
         const size_t src = ((size_t)r * p.cap + (id >= 0 ? id : 0)) * row + (size_t)h * HD;
-        dma16(p.ak + src + dma_k[i], kst(S) + blk * 512);
-        dma16(p.av + src + dma_v[i], vst(S) + blk * 512);
+        dma16(p.ak + src + dma_k[i], ks + blk * 512);
+        dma16(p.av + src + dma_v[i], vs + blk * 512);
       }
     }
   };
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
       issue_prompt(tile, S);
     } else {
       const int k = tile - n_pre;
-      issue_records(k / G::NRB, k % G::NRB, S);
+      issue_records(k / G::NRB, k % G::NRB, kst(S), vst(S));
     }
   };
   // wait until this wave's DMAs of all but the `ahead` most recent tiles landed
@@ -359,6 +359,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   bf16x8 qf[G::KSTEP];  // B operand of S^T: lane (g, c) holds head dims (HD/2)*g + 8j .. +8 of its beam
   int cnt = 0;          // chain records of this lane's beam
   float rec_alpha = 1.f, rec_p = 0.f;   // a record's rescale and weight, from its key tile to its value tile
+  // The B operand of a record value product: in k-step st, lane (c, g) holds
+  // rows 16 st + 8 (e >> 2) + 4 g + (e & 3) of column c at element e (the
+  // order the prompt's P and V operands use), so beam c's weight sits in the
+  // lanes with g = bit 2 of c, k-step c >> 4, element e below.
+  const int rec_e = 4 * ((c >> 3) & 1) + (c & 3);
+  const int rec_bi = g == ((c >> 2) & 1) ? 4 * (c >> 4) + (rec_e >> 1) : 8;   // 32-bit word of bd[], or none
+  const int rec_sh = 16 * (rec_e & 1);
 
   // Per tile: wait until its stage has landed, then refill the stage of
   // tile - 1.  The prompt loop's stage-0 head also does the tile-0 work.
@@ -498,69 +505,87 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
       }
     }
   };
+  // Chain levels of 128-beam workgroups: the key tile folds each beam's
+  // record score into its running max and sum, the value tile its value row
+  // into O.  rb is the half of the stage holding this wave's beams.
+  auto rec_key = [&](int d, const char *rb) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < G::KSTEP; ++j)
+      s += dot8_bf16(__builtin_bit_cast(uint4, qf[j]), *(const uint4 *)(rb + roff_k[j]));
+    s = xor32_sum(s);
+    rec_alpha = 1.f;                     // a level the beam's chain does not reach adds nothing
+    rec_p = 0.f;
+    if (d < cnt) {
+      const float t = s * p.sl2;
+      const float m_new = __builtin_elementwise_maximum(m_run, t);
+      rec_alpha = fast_exp2(m_run - m_new);
+      // rounded to bf16, as it enters the value product as an MFMA operand
+      rec_p = bf16_to_f32(f32_to_bf16(fast_exp2(t - m_new)));
+      l_run = l_run * rec_alpha + (g == 0 ? rec_p : 0.f);
+      m_run = m_new;
+    }
+  };
+  // O^T = alpha O^T + V^T diag(p) on the MFMA.  A is the value rows of this
+  // wave's 32 beams, read transposed like the prompt's value tile; B holds
+  // each beam's weight at its own row and column and zeros elsewhere.  alpha
+  // is 1 in every lane unless a record raised some beam's running max.
+  auto rec_value = [&](const char *rb) {
+    if (__ballot(rec_alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) O[dt][i] *= rec_alpha;
+    }
+    const uint32_t pw = (uint32_t)f32_to_bf16(rec_p) << rec_sh;
+    bf16x8 bd[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const uint4 w = make_uint4(rec_bi == 4 * st ? pw : 0u, rec_bi == 4 * st + 1 ? pw : 0u,
+                                 rec_bi == 4 * st + 2 ? pw : 0u, rec_bi == 4 * st + 3 ? pw : 0u);
+      bd[st] = __builtin_bit_cast(bf16x8, w);
+    }
+    const char *const ab = rb + 32 * (wave & 1) * G::RB;   // this wave's 32 rows
+#pragma unroll
+    for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GR_LDS4(ab + st * 16 * G::RB + voff[dt][0][0]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GR_LDS4(ab + st * 16 * G::RB + voff[dt][0][1]));
+        const i16x4 a8[2] = {lo, hi};
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), bd[st], O[dt], 0, 0, 0);
+      }
+  };
+  // Smaller workgroups: one tile per chain level, beam t's key in row t of
+  // the stage's first half and its value in the second.
   auto record_tile = [&](int tile, auto S) {
     const char *kb = (const char *)kst(S);
     const char *vb = (const char *)vst(S);
-    {
-      {
-        // ---- one chain level: its key tile, then its value tile
-        // (128-beam workgroups), or the beams of record tile bb
-        const int k = tile - n_pre;
-        const int d = k / G::NRB, bb = k % G::NRB;
-        if constexpr (G::NRB == 2) {
-          const char *const rb = my_bb ? vb : kb;      // this beam's row: the stage's first or second half
-          if (bb == 0) {
-            float s = 0.f;
+    const int k = tile - n_pre;
+    const int d = k / G::NRB, bb = k % G::NRB;
+    if (bb != my_bb) return;
+    float s = 0.f;
 #pragma unroll
-            for (int j = 0; j < G::KSTEP; ++j)
-              s += dot8_bf16(__builtin_bit_cast(uint4, qf[j]), *(const uint4 *)(rb + roff_k[j]));
-            s = xor32_sum(s);
-            if (d < cnt) {
-              const float t = s * p.sl2;
-              const float m_new = fmaxf(m_run, t);
-              rec_alpha = fast_exp2(m_run - m_new);
-              rec_p = fast_exp2(t - m_new);
-              l_run = l_run * rec_alpha + (g == 0 ? rec_p : 0.f);
-              m_run = m_new;
-            }
-          } else if (d < cnt) {
+    for (int j = 0; j < G::KSTEP; ++j)
+      s += dot8_bf16(__builtin_bit_cast(uint4, qf[j]), *(const uint4 *)(kb + roff_k[j]));
+    s = xor32_sum(s);
+    if (d < cnt) {
+      const float t = s * p.sl2;
+      const float m_new = fmaxf(m_run, t);
+      const float alpha = fast_exp2(m_run - m_new);
+      const float pr = fast_exp2(t - m_new);
+      l_run = l_run * alpha + (g == 0 ? pr : 0.f);
 #pragma unroll
-            for (int dt = 0; dt < G::DT; ++dt)
+      for (int dt = 0; dt < G::DT; ++dt)
 #pragma unroll
-              for (int q4 = 0; q4 < 4; ++q4) {
-                const uint2 vv = *(const uint2 *)(rb + roff_v[dt][q4]);
-                O[dt][4 * q4 + 0] = fmaf(rec_p, bf16_lo(vv.x), O[dt][4 * q4 + 0] * rec_alpha);
-                O[dt][4 * q4 + 1] = fmaf(rec_p, bf16_hi(vv.x), O[dt][4 * q4 + 1] * rec_alpha);
-                O[dt][4 * q4 + 2] = fmaf(rec_p, bf16_lo(vv.y), O[dt][4 * q4 + 2] * rec_alpha);
-                O[dt][4 * q4 + 3] = fmaf(rec_p, bf16_hi(vv.y), O[dt][4 * q4 + 3] * rec_alpha);
-              }
-          }
-        } else if (bb == my_bb) {
-          float s = 0.f;
-#pragma unroll
-          for (int j = 0; j < G::KSTEP; ++j)
-            s += dot8_bf16(__builtin_bit_cast(uint4, qf[j]), *(const uint4 *)(kb + roff_k[j]));
-          s = xor32_sum(s);
-          if (d < cnt) {
-            const float t = s * p.sl2;
-            const float m_new = fmaxf(m_run, t);
-            const float alpha = fast_exp2(m_run - m_new);
-            const float pr = fast_exp2(t - m_new);
-            l_run = l_run * alpha + (g == 0 ? pr : 0.f);
-#pragma unroll
-            for (int dt = 0; dt < G::DT; ++dt)
-#pragma unroll
-              for (int q4 = 0; q4 < 4; ++q4) {
-                const uint2 vv = *(const uint2 *)(vb + roff_v[dt][q4]);
-                O[dt][4 * q4 + 0] = fmaf(pr, bf16_lo(vv.x), O[dt][4 * q4 + 0] * alpha);
-                O[dt][4 * q4 + 1] = fmaf(pr, bf16_hi(vv.x), O[dt][4 * q4 + 1] * alpha);
-                O[dt][4 * q4 + 2] = fmaf(pr, bf16_lo(vv.y), O[dt][4 * q4 + 2] * alpha);
-                O[dt][4 * q4 + 3] = fmaf(pr, bf16_hi(vv.y), O[dt][4 * q4 + 3] * alpha);
-              }
-            m_run = m_new;
-          }
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const uint2 vv = *(const uint2 *)(vb + roff_v[dt][q4]);
+          O[dt][4 * q4 + 0] = fmaf(pr, bf16_lo(vv.x), O[dt][4 * q4 + 0] * alpha);
+          O[dt][4 * q4 + 1] = fmaf(pr, bf16_hi(vv.x), O[dt][4 * q4 + 1] * alpha);
+          O[dt][4 * q4 + 2] = fmaf(pr, bf16_lo(vv.y), O[dt][4 * q4 + 2] * alpha);
+          O[dt][4 * q4 + 3] = fmaf(pr, bf16_hi(vv.y), O[dt][4 * q4 + 3] * alpha);
         }
-      }
+      m_run = m_new;
     }
   };
   // The prompt tiles [0, n_pre) and the chain-record tiles [n_pre, n_total)
@@ -586,11 +611,46 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
     if constexpr (NS > 2) pstep(t0, Stage<2>{});
     if constexpr (NS > 3) pstep(t0, Stage<3>{});
   }
-  for (int t0 = n_pre - n_pre % NS; t0 < n_total; t0 += NS) {
-    rstep(t0, Stage<0>{});
-    rstep(t0, Stage<1>{});
-    if constexpr (NS > 2) rstep(t0, Stage<2>{});
-    if constexpr (NS > 3) rstep(t0, Stage<3>{});
+  if constexpr (G::NRB == 2) {
+    // One chain level per iteration, its key tile then its value tile: the
+    // levels do not follow the ring's period, so the stage is picked at run
+    // time (the DMAs are asm the compiler does not track, and every wait is
+    // explicit, so a run-time stage costs only its address).
+    auto stage_at = [&](int st) -> uint16_t * {
+      if constexpr (NS > 3) if (st == 3) return KV3;
+      if constexpr (NS > 2) if (st == 2) return KV2;
+      return st == 1 ? KV1 : KV0;
+    };
+    auto rec_head = [&](int tile) {
+      wait_tiles(min(NS - 2, n_total - 1 - tile));
+      ring_barrier();
+      const int nt = tile + NS - 1;      // every wave is past tile - 1: refill its stage
+      if (nt < n_total) {
+        uint16_t *const ks = stage_at(nt % NS);
+        const int k = nt - n_pre;
+        issue_records(k / G::NRB, k % G::NRB, ks, ks + G::TB / 2);
+      }
+    };
+    for (int tile = n_pre; tile < n_total; tile += 2) {
+      const int d = (tile - n_pre) >> 1;
+      rec_head(tile);
+      {
+        const char *const sb = (const char *)stage_at(tile % NS);
+        rec_key(d, my_bb ? sb + G::TB : sb);
+      }
+      rec_head(tile + 1);
+      {
+        const char *const sb = (const char *)stage_at((tile + 1) % NS);
+        rec_value(my_bb ? sb + G::TB : sb);
+      }
+    }
+  } else {
+    for (int t0 = n_pre - n_pre % NS; t0 < n_total; t0 += NS) {
+      rstep(t0, Stage<0>{});
+      rstep(t0, Stage<1>{});
+      if constexpr (NS > 2) rstep(t0, Stage<2>{});
+      if constexpr (NS > 3) rstep(t0, Stage<3>{});
+    }
   }
 
   // ---- epilogue.  o leaves through LDS: each lane holds 4-element pieces of

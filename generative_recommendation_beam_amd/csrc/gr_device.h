@@ -34,16 +34,13 @@ __device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
 }
 
-// Dot product of 8 bf16 pairs held as two uint4 (fp32 accumulate).
+// Dot product of 8 bf16 pairs held as two uint4 (fp32 accumulate, four
+// v_dot2_f32_bf16).
 __device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b) {
-  float s = bf16_lo(a.x) * bf16_lo(b.x);
-  s = fmaf(bf16_hi(a.x), bf16_hi(b.x), s);
-  s = fmaf(bf16_lo(a.y), bf16_lo(b.y), s);
-  s = fmaf(bf16_hi(a.y), bf16_hi(b.y), s);
-  s = fmaf(bf16_lo(a.z), bf16_lo(b.z), s);
-  s = fmaf(bf16_hi(a.z), bf16_hi(b.z), s);
-  s = fmaf(bf16_lo(a.w), bf16_lo(b.w), s);
-  s = fmaf(bf16_hi(a.w), bf16_hi(b.w), s);
+  float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, b.x), 0.f, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, b.y), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, b.z), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, b.w), s, false);
   return s;
 }
 

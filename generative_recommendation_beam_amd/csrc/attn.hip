@@ -69,6 +69,9 @@ struct Stage {
   static constexpr int value = I;
 };
 #define GR_LDS4(p) ((__attribute__((address_space(3))) i16x4 *)(p))
+// Every lambda of the attention kernel is inlined: a call would put the
+// by-reference captures (offset tables, the queries) in scratch memory.
+#define GR_INLINE __attribute__((always_inline))
 
 // ------------------------------------------------------------ chain resolve
 struct ChainP {
@@ -169,17 +172,17 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   int16_t *const ids16 = reinterpret_cast<int16_t *>(dyn_s);
   int32_t *const par_s = dyn_s + p.ids_words;
   int32_t *const bn_s = par_s + p.par_words;
-  auto chain_id = [&](int d, int b) -> int {
+  auto chain_id = [&](int d, int b) GR_INLINE -> int {
     return p.parent != nullptr ? (int)ids16[d * G::NB + b] : ids_s[d * G::NB + b];
   };
-  auto kst = [&](auto S) -> uint16_t * {
+  auto kst = [&](auto S) GR_INLINE -> uint16_t * {
     constexpr int st = decltype(S)::value;
     if constexpr (st == 0) return KV0;
     else if constexpr (st == 1) return KV1;
     else if constexpr (st == 2) return KV2;
     else return KV3;
   };
-  auto vst = [&](auto S) -> uint16_t * { return kst(S) + G::TB / 2; };
+  auto vst = [&](auto S) GR_INLINE -> uint16_t * { return kst(S) + G::TB / 2; };
   uint16_t *const K3 = kst(Stage<NS - 1>{}), *const V3 = vst(Stage<NS - 1>{});
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   }
   // prompt tile: rows past the window end read the last prompt row (masked
   // or never used)
-  auto issue_prompt = [&](int tile, auto S) {
+  auto issue_prompt = [&](int tile, auto S) GR_INLINE {
     const int key0 = k_begin + tile * G::KT;
 #pragma unroll
     for (int i = 0; i < G::IPW; ++i) {
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   // beams 0..63 in the stage's first half and 64..127 in its second, so that
   // every wave folds every tile.  Smaller workgroups: one tile per level, row
   // t holding beam t's key in the first half and its value in the second.
-  auto issue_records = [&](int d, int bb, uint16_t *ks, uint16_t *vs) {
+  auto issue_records = [&](int d, int bb, uint16_t *ks, uint16_t *vs) GR_INLINE {
     if constexpr (G::NRB == 2) {
       const uint16_t *const base = bb ? p.av : p.ak;
 #pragma unroll
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
       }
     }
   };
-  auto issue = [&](int tile, auto S) {
+  auto issue = [&](int tile, auto S) GR_INLINE {
     if (tile < n_pre) {
       issue_prompt(tile, S);
     } else {
@@ -274,7 +277,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
     }
   };
   // wait until this wave's DMAs of all but the `ahead` most recent tiles landed
-  auto wait_tiles = [&](int ahead) {
+  auto wait_tiles = [&](int ahead) GR_INLINE {
     constexpr int per = 2 * G::IPW;
     if (ahead >= 2) GR_WAIT_VMCNT(2 * per);
     else if (ahead == 1) GR_WAIT_VMCNT(per);
@@ -369,7 +372,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
 
   // Per tile: wait until its stage has landed, then refill the stage of
   // tile - 1.  The prompt loop's stage-0 head also does the tile-0 work.
-  auto head = [&](int tile, auto S, auto in_prompt) {
+  auto head = [&](int tile, auto S, auto in_prompt) GR_INLINE {
     constexpr int st = decltype(S)::value;
     {
       // at tile 0 the prologue has put exactly NS-2 tiles behind it
@@ -431,7 +434,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
       if (tile + NS - 1 < n_total) issue(tile + NS - 1, Stage<(st + NS - 1) % NS>{});
     }
   };
-  auto prompt_tile = [&](int tile, auto S) {
+  auto prompt_tile = [&](int tile, auto S) GR_INLINE {
     const char *kb = (const char *)kst(S);
     const char *vb = (const char *)vst(S);
     {
@@ -508,7 +511,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   // Chain levels of 128-beam workgroups: the key tile folds each beam's
   // record score into its running max and sum, the value tile its value row
   // into O.  rb is the half of the stage holding this wave's beams.
-  auto rec_key = [&](int d, const char *rb) {
+  auto rec_key = [&](int d, const char *rb) GR_INLINE {
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < G::KSTEP; ++j)
@@ -530,7 +533,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   // wave's 32 beams, read transposed like the prompt's value tile; B holds
   // each beam's weight at its own row and column and zeros elsewhere.  alpha
   // is 1 in every lane unless a record raised some beam's running max.
-  auto rec_value = [&](const char *rb) {
+  auto rec_value = [&](const char *rb) GR_INLINE {
     if (__ballot(rec_alpha != 1.f)) {
 #pragma unroll
       for (int dt = 0; dt < G::DT; ++dt)
@@ -558,7 +561,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   };
   // Smaller workgroups: one tile per chain level, beam t's key in row t of
   // the stage's first half and its value in the second.
-  auto record_tile = [&](int tile, auto S) {
+  auto record_tile = [&](int tile, auto S) GR_INLINE {
     const char *kb = (const char *)kst(S);
     const char *vb = (const char *)vst(S);
     const int k = tile - n_pre;
@@ -591,14 +594,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   // The prompt tiles [0, n_pre) and the chain-record tiles [n_pre, n_total)
   // run in loops of their own: with both kinds in one loop body the register
   // allocator moves the O accumulators between register ranges at every tile.
-  auto pstep = [&](int t0, auto S) {
+  auto pstep = [&](int t0, auto S) GR_INLINE {
     const int tile = t0 + decltype(S)::value;
     if (tile < n_pre) {
       head(tile, S, std::true_type{});
       if (tile < n_tiles) prompt_tile(tile, S);
     }
   };
-  auto rstep = [&](int t0, auto S) {
+  auto rstep = [&](int t0, auto S) GR_INLINE {
     const int tile = t0 + decltype(S)::value;
     if (tile >= n_pre && tile < n_total) {
       head(tile, S, std::false_type{});
@@ -616,12 +619,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
     // levels do not follow the ring's period, so the stage is picked at run
     // time (the DMAs are asm the compiler does not track, and every wait is
     // explicit, so a run-time stage costs only its address).
-    auto stage_at = [&](int st) -> uint16_t * {
+    auto stage_at = [&](int st) GR_INLINE -> uint16_t * {
       if constexpr (NS > 3) if (st == 3) return KV3;
       if constexpr (NS > 2) if (st == 2) return KV2;
       return st == 1 ? KV1 : KV0;
     };
-    auto rec_head = [&](int tile) {
+    auto rec_head = [&](int tile) GR_INLINE {
       wait_tiles(min(NS - 2, n_total - 1 - tile));
       ring_barrier();
       const int nt = tile + NS - 1;      // every wave is past tile - 1: refill its stage
@@ -668,7 +671,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   __syncthreads();                                      // every wave is past its last tile
   // fp32 rows o * sc to dst0 + row_index * stride, staged in the first ring
   // stage (64 rows at a time) and written with consecutive lanes per row
-  auto store_f32 = [&](float *dst0, size_t stride, float sc) {
+  auto store_f32 = [&](float *dst0, size_t stride, float sc) GR_INLINE {
     constexpr int CPR = HD / 4;                         // 16-byte chunks per fp32 row
     float *st = (float *)KV0;                           // 64 rows x HD fp32 (<= 16 KB)
 #pragma unroll

@@ -78,8 +78,10 @@ struct LP {
 
 // NB: number of 64-column blocks of D when fixed at compile time (the
 // block loop is then unrolled, and the compiler's waits count the loads in
-// flight across blocks), 0 for any D.
-template <int NB>
+// flight across blocks), 0 for any D.  BT: 32-beam tiles formed per group,
+// 4 (up to 128 beams) or 2 (up to 64: half the products, exps and
+// selection work for small beams).
+template <int NB, int BT>
 __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
   __shared__ LogitsSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -98,9 +100,9 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
   const int n_blk = NB > 0 ? NB : (p.D + kCB - 1) / kCB;
 
   // priors of this lane's beams 32 t + c (read now, used after the projection)
-  float pr[4];
+  float pr[BT];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < BT; ++t) {
     const int bl = 32 * t + c;
     pr[t] = (bl < nbg && p.prior) ? p.prior[(size_t)r * p.n_in + b_begin + bl] : 0.f;
   }
@@ -134,9 +136,9 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
       dma16(p.W + (size_t)(32 * wave + lr) * p.D + col, &sm.u.ring.wr[wave][slot][i * 512]);
     }
   };
-  f32x16 acc[4];
+  f32x16 acc[BT];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < BT; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
   const int swb = swz_o(c);                 // rows c and 32 t + c share the swizzle of c
@@ -147,23 +149,23 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
     const bool full = NB > 0 || (p.D - cb * kCB) >= kCB;   // else a half block (2 k-steps)
     const uint16_t *ob = &sm.u.ring.ob[slot][c * kCB];
     const uint16_t *wb = &sm.u.ring.wr[wave][slot][c * kCB];
-    bf16x8 a[4], bo[4][4];
+    bf16x8 a[4], bo[4][BT];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int off = ((2 * ks + g) ^ swb) << 3;
       a[ks] = *(const bf16x8 *)(wb + off);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) bo[ks][t] = *(const bf16x8 *)(ob + 32 * t * kCB + off);
+      for (int t = 0; t < BT; ++t) bo[ks][t] = *(const bf16x8 *)(ob + 32 * t * kCB + off);
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (ks < 2 || full) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], bo[ks][t], acc[t], 0, 0, 0);
+        for (int t = 0; t < BT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], bo[ks][t], acc[t], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 20, 0);   // the LDS reads first,
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // then the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 + 4 * BT, 0);   // the LDS reads first,
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * BT, 0);       // then the MFMAs
   };
   issue(0);
   if (n_blk > 1) issue(1);
@@ -186,9 +188,9 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
   // the lane's 16 codes, the lane 32 apart (same beam), then the 8 waves.
   // The lane's smallest (NaN-propagating) and largest logit of each beam
   // also bound its 16 candidate scores, rounding being monotonic.
-  float lo[4], hi[4];
+  float lo[BT], hi[BT];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < BT; ++t) {
     float mn = acc[t][0], mx = acc[t][0];
 #pragma unroll
     for (int j = 1; j < 16; ++j) {
@@ -198,17 +200,19 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
     lo[t] = mn;
     hi[t] = mx;
   }
-  float lse[4] = {0.f, 0.f, 0.f, 0.f};
-  if (p.lsm) {
-    float M[4];
+  float lse[BT];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < BT; ++t) lse[t] = 0.f;
+  if (p.lsm) {
+    float M[BT];
+#pragma unroll
+    for (int t = 0; t < BT; ++t) {
       const float mx = xor32_max(hi[t]);
       if (g == 0) sm.red_max[wave][32 * t + c] = mx;
     }
     __syncthreads();
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < BT; ++t) {
       float mx = sm.red_max[0][32 * t + c];
 #pragma unroll
       for (int w = 1; w < kNT / 64; ++w) mx = fmaxf(mx, sm.red_max[w][32 * t + c]);
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
     }
     __syncthreads();
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < BT; ++t) {
       float se = sm.red_sum[0][32 * t + c];
 #pragma unroll
       for (int w = 1; w < kNT / 64; ++w) se += sm.red_sum[w][32 * t + c];
@@ -233,9 +237,9 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
   // ---- candidate scores (z - lse) + prior, in place
   const int n = nbg * 256;
   const int k_sel = min(p.k, n);
-  bool valid[4];
+  bool valid[BT];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < BT; ++t) {
     valid[t] = 32 * t + c < nbg;
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[t][j] = (acc[t][j] - lse[t]) + pr[t];
@@ -266,10 +270,10 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
   bool done = false;
   if (k_sel <= kFastK) {
     const int ml = (k_sel + 15) >> 4;                   // <= 32
-    float lb = -__builtin_inff(), best = -__builtin_inff(), umax[4];
+    float lb = -__builtin_inff(), best = -__builtin_inff(), umax[BT];
     bool any = false;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < BT; ++t) {
       const float u = (lo[t] - lse[t]) + pr[t];
       umax[t] = (hi[t] - lse[t]) + pr[t];
       if (valid[t]) {
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
       uint32_t *hist = sm.u.sel.bstart;
       uint32_t wc = 0;                                  // wave-uniform
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < BT; ++t) {
         const bool ut = valid[t] && umax[t] >= Ts;
         if (!__builtin_amdgcn_ballot_w64(ut)) continue;
 #pragma unroll
@@ -410,13 +414,13 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
     }
   }
   if (!done) {
-    uint32_t key[64];
+    uint32_t key[16 * BT];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < BT; ++t)
 #pragma unroll
       for (int j = 0; j < 16; ++j) key[16 * t + j] = valid[t] ? rank_key(acc[t][j]) : kInvalidKey;
     __syncthreads();                                    // the o buffers / staging area are no longer read
-    select_regs<kNT, 64>(key, [&](int i) -> uint32_t { return flat_of(i >> 4, i & 15); }, n, k_sel, sm.u.sel);
+    select_regs<kNT, 16 * BT>(key, [&](int i) -> uint32_t { return flat_of(i >> 4, i & 15); }, n, k_sel, sm.u.sel);
   }
   emit_selection<kNT>(sm.u.sel, k_sel, r, grp, 256, p.score, p.token, p.parent, p.partial, p.n_groups, p.kk);
 }
@@ -607,12 +611,17 @@ hipError_t launch_logits_select_bf16(const LogitsArgs &a, const SelectOut &o, hi
   p.R = a.R; p.n_in = a.n_in; p.D = a.D; p.hd_log2 = __builtin_ctz((unsigned)a.hd); p.k = a.k;
   p.lsm = a.log_softmax; p.n_groups = o.n_groups; p.kk = o.kk;
   const dim3 grid((unsigned)(a.R * o.n_groups));
-  if (a.D == 8 * kCB)
-    hipLaunchKernelGGL(logits_select_bf16_kernel<8>, grid, dim3(kNT), 0, s, p);
-  else if (a.D == 16 * kCB)
-    hipLaunchKernelGGL(logits_select_bf16_kernel<16>, grid, dim3(kNT), 0, s, p);
-  else
-    hipLaunchKernelGGL(logits_select_bf16_kernel<0>, grid, dim3(kNT), 0, s, p);
+  const bool half = a.n_in <= kGroupBeams / 2;           // every group holds at most 64 beams
+  if (a.D == 8 * kCB) {
+    if (half) hipLaunchKernelGGL((logits_select_bf16_kernel<8, 2>), grid, dim3(kNT), 0, s, p);
+    else hipLaunchKernelGGL((logits_select_bf16_kernel<8, 4>), grid, dim3(kNT), 0, s, p);
+  } else if (a.D == 16 * kCB) {
+    if (half) hipLaunchKernelGGL((logits_select_bf16_kernel<16, 2>), grid, dim3(kNT), 0, s, p);
+    else hipLaunchKernelGGL((logits_select_bf16_kernel<16, 4>), grid, dim3(kNT), 0, s, p);
+  } else {
+    if (half) hipLaunchKernelGGL((logits_select_bf16_kernel<0, 2>), grid, dim3(kNT), 0, s, p);
+    else hipLaunchKernelGGL((logits_select_bf16_kernel<0, 4>), grid, dim3(kNT), 0, s, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || o.n_groups == 1) return e;
   return launch_select_merge(o, a.R, a.k, 256, s);

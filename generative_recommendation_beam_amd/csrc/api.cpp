@@ -53,7 +53,8 @@ float eff_scale(const gr_shape *s) {
 }
 
 // Partial-list geometry of a selection over n_in x vocab candidates.  The
-// MFMA codebook path selects per group of 128 beams (32768 candidates).
+// MFMA codebook path selects per group of 128 beams (32768 candidates), or of
+// 64 beams when several 128-beam groups per request still leave CUs idle.
 // score_select uses the same groups unless they leave most CUs idle (few
 // requests, many candidates each): then groups of 8192, as long as their
 // partial lists still fit the final merge.
@@ -71,7 +72,14 @@ SelGeo make_geo(int R, int n_in, int vocab, int k, int gpos) {
 }
 SelGeo sel_geo(int R, int n_in, int vocab, int k, bool mfma_logits = false) {
   const SelGeo big = make_geo(R, n_in, vocab, k, gr::kGroupPositions);
-  if (mfma_logits || (long long)R * big.n_groups >= gr::kSelectCUs) return big;
+  if ((long long)R * big.n_groups >= gr::kSelectCUs) return big;
+  if (mfma_logits) {
+    // groups of 64 beams when 128-beam groups already need the merge and
+    // leave CUs idle (many beams, few requests)
+    const SelGeo half = make_geo(R, n_in, vocab, k, gr::kGroupPositions / 2);
+    if (big.n_groups > 1 && (long long)half.n_groups * half.kk <= gr::kMergeCapacity) return half;
+    return big;
+  }
   const SelGeo small = make_geo(R, n_in, vocab, k, gr::kSmallGroupPositions);
   if (small.n_groups > big.n_groups && (long long)small.n_groups * small.kk <= gr::kMergeCapacity) return small;
   return big;

@@ -158,7 +158,7 @@ struct SelectOut {
   int32_t *token, *parent;
   uint64_t *partial;               // [R][n_groups][kk] when n_groups > 1
   int n_groups, kk;
-  int gpos;                        // candidates per group of score_select (kSmallGroupPositions or kGroupPositions)
+  int gpos;                        // candidates per group: kGroupPositions, or kGroupPositions / 2 (MFMA scoring) or kSmallGroupPositions (score_select) when groups that size leave CUs idle
 };
 
 // Codebook projection on MFMA (bf16 o, bf16 W [256][D]), log-softmax, prior,

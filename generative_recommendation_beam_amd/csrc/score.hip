@@ -78,9 +78,10 @@ struct LP {
 
 // NB: number of 64-column blocks of D when fixed at compile time (the
 // block loop is then unrolled, and the compiler's waits count the loads in
-// flight across blocks), 0 for any D.  BT: 32-beam tiles formed per group,
-// 4 (up to 128 beams) or 2 (up to 64: half the products, exps and
-// selection work for small beams).
+// flight across blocks), 0 for any D.  BT: 32-beam tiles per group, 4
+// (groups of 128 beams) or 2 (groups of 64: half the products, exps and
+// selection work of a workgroup, for small beams or to spread many beams of
+// few requests over more CUs).
 template <int NB, int BT>
 __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
   __shared__ LogitsSmem sm;
@@ -93,8 +94,8 @@ __global__ __launch_bounds__(kNT) void logits_select_bf16_kernel(LP p) {
   int bid = blockIdx.x;
   if ((gridDim.x & 7) == 0) bid = (bid & 7) * (int)(gridDim.x >> 3) + (bid >> 3);
   const int r = bid / p.n_groups, grp = bid % p.n_groups;
-  const int b_begin = grp * kGroupBeams;
-  const int nbg = min(kGroupBeams, p.n_in - b_begin);
+  const int b_begin = grp * 32 * BT;                   // groups of 32 BT beams
+  const int nbg = min(32 * BT, p.n_in - b_begin);
   const int hd = 1 << p.hd_log2, H = p.D >> p.hd_log2;
   const uint16_t *o_req = p.o + (size_t)r * H * p.n_in * hd;
   const int n_blk = NB > 0 ? NB : (p.D + kCB - 1) / kCB;
@@ -611,7 +612,7 @@ hipError_t launch_logits_select_bf16(const LogitsArgs &a, const SelectOut &o, hi
   p.R = a.R; p.n_in = a.n_in; p.D = a.D; p.hd_log2 = __builtin_ctz((unsigned)a.hd); p.k = a.k;
   p.lsm = a.log_softmax; p.n_groups = o.n_groups; p.kk = o.kk;
   const dim3 grid((unsigned)(a.R * o.n_groups));
-  const bool half = a.n_in <= kGroupBeams / 2;           // every group holds at most 64 beams
+  const bool half = o.gpos == kGroupPositions / 2 || a.n_in <= kGroupBeams / 2;   // groups of at most 64 beams
   if (a.D == 8 * kCB) {
     if (half) hipLaunchKernelGGL((logits_select_bf16_kernel<8, 2>), grid, dim3(kNT), 0, s, p);
     else hipLaunchKernelGGL((logits_select_bf16_kernel<8, 4>), grid, dim3(kNT), 0, s, p);

@@ -49,6 +49,12 @@ SMALL = {
                                  prior="flat"),
     "k200_zero_prior": W.reduced(CF["beam100_p600"], R=2, Lp=90, n_in=100, k=200, level_sizes=(100, 100, 100), H=4,
                                  prior="zero"),
+    # 64-beam scoring groups with k above the bounded selection's 512: the
+    # register-wide selection over 32 slots a lane, alone (at most 64 input
+    # beams) and with a merge of four 64-beam groups (the last one of 8 beams)
+    "k600_beam60_exact": W.reduced(CF["beam100_p600"], R=2, Lp=90, n_in=60, k=600, level_sizes=(40, 60, 60), H=4),
+    "k600_beam200_groups64": W.reduced(CF["beam100_p600"], R=2, Lp=90, n_in=200, k=600,
+                                       level_sizes=(100, 200, 200), H=4),
     "f32_beam16": W.reduced(CF["beam100_p600"], R=2, Lp=40, H=4, d=32, n_in=16, k=16,
                             level_sizes=(9, 16, 16), dtype="f32"),
     # edge cases: chains of the maximum depth (8 records), a one-token prompt,

@@ -464,6 +464,9 @@ constexpr int kLinRingNodes = 4096;
 // Stage 0 is free for records once the shared-state MFMAs have read S_p.
 // Record rows are XOR-swizzled so that 16 lanes reading 16 consecutive rows
 // at one logical 16-byte chunk hit 16 distinct bank slots.
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+#define LIN_LDS4(p) ((__attribute__((address_space(3))) i16x4 *)(p))
+
 template <int HD>
 __device__ __forceinline__ int lswz(int row) {
   constexpr int RB = HD * 2, CPR = RB / 16;
@@ -617,20 +620,48 @@ __global__ __launch_bounds__(256) void linear_ring_bf16_kernel(LinP p) {
   }
 
   // ---- records, tile by tile
-  float w_lev = 0.f;                           // weight of the level whose values come next
-  for (int k = 0; k < n_tiles; ++k) {
-    // tile k has landed once at most the tiles issued after it (k + 1, the
-    // ring being NS - 1 = 2 tiles deep) are in flight: BPW DMAs per tile and wave
-    static_assert(NS == 3, "one tile ahead at each wait");
+  float w_lev = 0.f;                           // weight of the level whose values come next (0: no record)
+  // The value tile adds O^T += V^T diag(w) on the MFMA.  A: the value rows of
+  // this wave's 32 beams, read transposed; per 16-row k-step, lane (c, g)
+  // holds element e of rows 8 (e >> 2) + 4 g + (e & 3).  The row swizzle
+  // depends only on a row's low four bits, so the offsets within a k-step
+  // are the lane's own.  B: each beam's weight at its own row and column
+  // (beam c's in the lanes with g = bit 2 of c, k-step c >> 4, element
+  // rec_e), as bf16 hi + lo in two products.
+  int rvo[DT][2];
+  {
+    const int q16 = lane >> 4, j16 = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int tr = 8 * hh + 4 * g + (j16 >> 2);
+        const int dd = 32 * dt + 16 * (q16 & 1) + 4 * (j16 & 3);
+        rvo[dt][hh] = tr * RB + (((dd >> 3) ^ lswz<HD>(tr)) << 4) + ((dd & 7) << 1);
+      }
+  }
+  const int rec_e = 4 * ((c >> 3) & 1) + (c & 3);
+  const int rec_bi = g == ((c >> 2) & 1) ? 4 * (c >> 4) + (rec_e >> 1) : 8;   // 32-bit word of the B operand, or none
+  const int rec_sh = 16 * (rec_e & 1);
+  // tile k has landed once at most the tiles issued after it (k + 1, the
+  // ring being NS - 1 = 2 tiles deep) are in flight: BPW DMAs per tile and wave
+  static_assert(NS == 3, "one tile ahead at each wait");
+  auto tile_head = [&](int k) {
     if (k + 1 < n_tiles) GR_WAIT_VMCNT(BPW);
     else GR_WAIT_VMCNT(0);
     ring_barrier();                            // tile k landed for all; stage of tile k-1 (or S_p) free
     if (k + NS - 1 < n_tiles) issue(k + NS - 1, ring[(k + NS) % NS]);
-    const unsigned char *rr = ring[(k + 1) % NS] + wb * RB;
+  };
+  // one chain level per iteration, its key tile then its value tile (with
+  // both kinds in one loop body the register allocator moves O around the
+  // value product at every tile)
+  for (int k = 0; k < n_tiles; k += 2) {
     const int d = k >> 1;
-    if (d < p.max_depth && ids16[d][wb] >= 0) {
-      if ((k & 1) == 0) {                      // key row: the record's weight
-        float w = 0.f;
+    tile_head(k);
+    {                                          // key rows: each beam's record weight
+      const unsigned char *rr = ring[(k + 1) % NS] + wb * RB;
+      float w = 0.f;
+      if (d < p.max_depth && ids16[d][wb] >= 0) {   // the same for both lanes of a beam
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const uint4 k4 = *(const uint4 *)(rr + (((2 * ks + g) ^ lswz<HD>(wb)) << 4));
@@ -641,20 +672,36 @@ __global__ __launch_bounds__(256) void linear_ring_bf16_kernel(LinP p) {
         }
         w = xor32_sum(w);
         den += w;
-        w_lev = w;
-      } else {                                 // value row, weighted
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int j = 4 * dt + q4;                 // logical chunk of rows 8j .. 8j+7
-            const uint2 v2 = *(const uint2 *)(rr + ((j ^ lswz<HD>(wb)) << 4) + 8 * g);
-            O[dt][4 * q4 + 0] = fmaf(w_lev, bf16_lo(v2.x), O[dt][4 * q4 + 0]);
-            O[dt][4 * q4 + 1] = fmaf(w_lev, bf16_hi(v2.x), O[dt][4 * q4 + 1]);
-            O[dt][4 * q4 + 2] = fmaf(w_lev, bf16_lo(v2.y), O[dt][4 * q4 + 2]);
-            O[dt][4 * q4 + 3] = fmaf(w_lev, bf16_hi(v2.y), O[dt][4 * q4 + 3]);
-          }
       }
+      w_lev = w;
+    }
+    tile_head(k + 1);
+    {                                          // value rows, weighted, for the whole wave
+      const unsigned char *stage = ring[(k + 2) % NS];
+      const __bf16 whi = (__bf16)w_lev;
+      const __bf16 wlo = (__bf16)(w_lev - (float)whi);
+      const uint32_t ph = (uint32_t)__builtin_bit_cast(uint16_t, whi) << rec_sh;
+      const uint32_t pl = (uint32_t)__builtin_bit_cast(uint16_t, wlo) << rec_sh;
+      bf16x8 bh[2], bl[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        bh[st] = __builtin_bit_cast(bf16x8, make_uint4(rec_bi == 4 * st ? ph : 0u, rec_bi == 4 * st + 1 ? ph : 0u,
+                                                       rec_bi == 4 * st + 2 ? ph : 0u, rec_bi == 4 * st + 3 ? ph : 0u));
+        bl[st] = __builtin_bit_cast(bf16x8, make_uint4(rec_bi == 4 * st ? pl : 0u, rec_bi == 4 * st + 1 ? pl : 0u,
+                                                       rec_bi == 4 * st + 2 ? pl : 0u, rec_bi == 4 * st + 3 ? pl : 0u));
+      }
+      const unsigned char *ab = stage + 32 * wave * RB;   // this wave's 32 rows
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LIN_LDS4(ab + st * 16 * RB + rvo[dt][0]));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LIN_LDS4(ab + st * 16 * RB + rvo[dt][1]));
+          const i16x4 a8[2] = {lo, hi};
+          const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
+          O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[st], O[dt], 0, 0, 0);
+          O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[st], O[dt], 0, 0, 0);
+        }
     }
   }
   if (!valid) return;

@@ -213,6 +213,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   const bool chains = (p.ids != nullptr || p.parent != nullptr) && split == p.n_split - 1;
   const int n_pre = max(n_tiles, NS - 1);       // prompt tiles, padded to fill the prologue
   int n_total = n_pre;                          // + chain-record tiles, known after tile 0
+  int rec_fill = 0;     // a written record, gathered for the rows of beams without one at a level
 
   // Per-lane tile row and (swizzled) element offsets of this lane's DMA
   // pieces: wave w moves 1 KB blocks w*IPW..; lane l lands at byte 16*l of its
@@ -239,22 +240,35 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
       dma16_stream(pv + (src + dma_v[i]), vst(S) + blk * 512);
     }
   };
-  // chain-record tiles (a beam without a record at the level reads record 0
-  // of the request, unused).  128-beam workgroups: two tiles per chain level,
+  // chain-record tiles.  128-beam workgroups: two tiles per chain level,
   // the key rows (bb = 0), then the value rows (bb = 1) of all 128 beams,
   // beams 0..63 in the stage's first half and 64..127 in its second, so that
   // every wave folds every tile.  Smaller workgroups: one tile per level, row
-  // t holding beam t's key in the first half and its value in the second.
+  // t holding beam t's key in the first half and its value in the second (a
+  // beam without a record at the level reads record 0 of the request,
+  // unused: these fold each beam's own row only).
   auto issue_records = [&](int d, int bb, uint16_t *ks, uint16_t *vs) GR_INLINE {
     if constexpr (G::NRB == 2) {
+      // A beam without a record at level d gathers `rec_fill`, a record of
+      // the workgroup: the value product multiplies every row of the tile, by 0
+      // for such a beam, so every row must be written data.  It is the
+      // deepest record of the first beam that has a chain (any written record
+      // would do), found when the first level is issued: mid-stream, off the
+      // unit's first wait.
+      if (d == 0 && bb == 0) {
+        const uint64_t m0 = __builtin_amdgcn_ballot_w64(chain_id(0, lane) >= 0);
+        const uint64_t m1 = __builtin_amdgcn_ballot_w64(chain_id(0, G::KT + lane) >= 0);
+        const int fb = m0 ? (int)__builtin_ctzll(m0) : (m1 ? G::KT + (int)__builtin_ctzll(m1) : 0);
+        rec_fill = __builtin_amdgcn_readfirstlane(max(chain_id(0, fb), 0));
+      }
       const uint16_t *const base = bb ? p.av : p.ak;
 #pragma unroll
       for (int i = 0; i < G::IPW; ++i) {
         const int blk = wave * G::IPW + i;
         const uint32_t sw = bb ? dma_v[i] : dma_k[i];
         const int id0 = chain_id(d, dma_row[i]), id1 = chain_id(d, G::KT + dma_row[i]);
-        dma16(base + ((size_t)r * p.cap + (id0 >= 0 ? id0 : 0)) * row + (size_t)h * HD + sw, ks + blk * 512);
-        dma16(base + ((size_t)r * p.cap + (id1 >= 0 ? id1 : 0)) * row + (size_t)h * HD + sw, vs + blk * 512);
+        dma16(base + ((size_t)r * p.cap + (id0 >= 0 ? id0 : rec_fill)) * row + (size_t)h * HD + sw, ks + blk * 512);
+        dma16(base + ((size_t)r * p.cap + (id1 >= 0 ? id1 : rec_fill)) * row + (size_t)h * HD + sw, vs + blk * 512);
       }
     } else {
 #pragma unroll

@@ -568,13 +568,24 @@ __global__ __launch_bounds__(256) void linear_ring_bf16_kernel(LinP p) {
       if (__syncthreads_or(tid < NB && ids16[d][tid] >= 0)) depth = d + 1;
   }
   const int n_tiles = depth * (NB / KT);
+  // the deepest record of the first beam that has a chain (any written record
+  // would do; with none, no level is issued)
+  int rec_fill = 0;
+  if (n_tiles > 0) {
+    const uint64_t m0 = __builtin_amdgcn_ballot_w64(ids16[0][lane] >= 0);
+    const uint64_t m1 = __builtin_amdgcn_ballot_w64(ids16[0][64 + lane] >= 0);
+    const int fb = m0 ? (int)__builtin_ctzll(m0) : (m1 ? 64 + (int)__builtin_ctzll(m1) : 0);
+    rec_fill = __builtin_amdgcn_readfirstlane(max((int)ids16[0][fb], 0));
+  }
 
   // record tile k: the key (k even) or value (k odd) rows of the level k / 2
-  // records, row t for workgroup beam t (node 0 when the beam has none:
-  // unused), so that every wave folds every tile
+  // records, row t for workgroup beam t, so that every wave folds every tile
   static_assert(NB * RB == 2 * TB, "one half-record of every beam fills a stage");
   auto issue = [&](int k, unsigned char *st) {
     const int d = k >> 1, half = k & 1;
+    // a beam without a record at level d gathers `rec_fill`, a record of
+    // the workgroup: the value product multiplies every row, by 0 for such a
+    // beam, so every row must be written data
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
       const int blk = wave * BPW + i;
@@ -582,7 +593,7 @@ __global__ __launch_bounds__(256) void linear_ring_bf16_kernel(LinP p) {
       const int t = byte / RB, pch = (byte % RB) / 16;
       const int id = ids16[d][t];
       const uint16_t *src = (const uint16_t *)(half ? p.av : p.ak) +
-                            ((size_t)r * p.cap + (id >= 0 ? id : 0)) * row + (size_t)h * HD +
+                            ((size_t)r * p.cap + (id >= 0 ? id : rec_fill)) * row + (size_t)h * HD +
                             (pch ^ lswz<HD>(t)) * 8;
       dma16(src, st + blk * 1024);
     }

@@ -8,6 +8,8 @@ and 64; device error bits for corrupt parents and chains past max_depth.
 gr_beam_topk: scores within the bar, the index rule, exact self-consistency,
 exact ties, multi-group merges, scalar (vocab 1) selection of 2000 of 40000.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -124,6 +126,73 @@ def test_prefix_attn_parity_large_arena():
     ak, av, par = oracle_arena(x)
     ref = oracle.prefix_attn(x.prompt_k, x.prompt_v, x.q, par, ak, av, x.beam_node, window=cfg.window)
     assert_close(out.cpu().numpy(), ref, cfg.dtype, "bf16_large_arena")
+
+
+def relocated(ds, off):
+    """The same step with its arena moved up by `off` slots (node ids and
+    parent links shift by off) and the slots below it holding NaN."""
+    R, cap = ds.parent.shape
+    ak = torch.full((R, cap + off) + tuple(ds.arena_k.shape[2:]), float("nan"), dtype=ds.arena_k.dtype,
+                    device=ds.arena_k.device)
+    av = ak.clone()
+    ak[:, off:] = ds.arena_k
+    av[:, off:] = ds.arena_v
+    par = torch.full((R, cap + off), -1, dtype=torch.int32, device=ds.parent.device)
+    par[:, off:] = torch.where(ds.parent >= 0, ds.parent + off, ds.parent)
+    trie = L.Trie(k=ak.data_ptr(), v=av.data_ptr(), parent=par.data_ptr(), capacity=cap + off,
+                  max_depth=ds.trie.max_depth)
+    trie._tensors = (ak, av, par)
+    bn = torch.where(ds.beam_node >= 0, ds.beam_node + off, ds.beam_node)
+    return dataclasses.replace(ds, arena_k=ak, arena_v=av, parent=par, trie=trie, beam_node=bn)
+
+
+# 128-beam workgroups fold each chain level as one product over the tile of
+# all their beams' rows; beams without a record at a level must not bring in
+# arena slots that hold no record.  Mixed chain depths (prompt-only beams,
+# one-record chains, full chains) over an arena whose unused slots hold NaN.
+MIXED_DEPTHS = W.reduced(W.CONFIGS["beam100_p600"], R=2, Lp=90, n_in=100, level_sizes=(60, 100, 100), H=4)
+
+
+def mixed_depth_step(capacity):
+    x = W.make_step_inputs(MIXED_DEPTHS)
+    ds = HN.upload_step(x, capacity=capacity)
+    ds.beam_node[:, ::5] = -1                    # prompt only
+    ds.beam_node[:, 1::5] = 7                    # a level-1 node: a one-record chain
+    return ds
+
+
+@pytest.mark.parametrize("capacity", [None, LARGE_ARENA])
+def test_decode_step_never_reads_unused_arena_slots(capacity):
+    announce(f"decode step, mixed chain depths, arena moved over NaN slots, capacity {capacity}")
+    ds = mixed_depth_step(capacity)
+    outs = []
+    for d in (ds, relocated(ds, 37)):
+        buf = HN.decode_buffers(d, debug_outputs=True)
+        HN.decode_step(d, buf)
+        torch.cuda.synchronize()
+        outs.append(buf)
+    assert int(ds.dev_err.item()) == 0
+    a, b = outs
+    assert torch.isfinite(b.attn).all() and torch.isfinite(b.score).all()
+    for name in ("attn", "cand", "score", "token", "parent"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+
+
+def test_linear_step_never_reads_unused_arena_slots():
+    announce("linear decode step, mixed chain depths, arena moved over NaN slots")
+    ds = mixed_depth_step(None)
+    S, z = HN.linear_state(ds)
+    outs = []
+    for d in (ds, relocated(ds, 37)):
+        buf = HN.decode_buffers(d, debug_outputs=True)
+        HN.linear_decode_step(d, buf, S, z)
+        torch.cuda.synchronize()
+        outs.append(buf)
+    assert int(ds.dev_err.item()) == 0
+    a, b = outs
+    assert torch.isfinite(b.attn).all() and torch.isfinite(b.score).all()
+    for name in ("attn", "cand", "score", "token", "parent"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
 
 
 @pytest.mark.parametrize("capacity", [None, LARGE_ARENA])

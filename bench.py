@@ -7,8 +7,10 @@ A step is one gr_decode_step over the whole batch of the headline workload
 prompt plus its own ancestor chain, codebook projection, log-softmax, prior
 add and top-100 of 100 x 256 per request.  Inputs are seeded synthetic data
 (workloads module), uploaded once and resident in HBM; independent copies
-rotate between steps so that each step reads cold data (the working set of
-one copy exceeds the 256 MB last-level cache).
+rotate between steps so that each step reads cold data (as many copies as
+span 512 MiB of algorithmic bytes, twice the 256 MB last-level cache: two
+for the headline, six for beam50_p600, eighteen for the 40 000-candidate
+scalar workload).
 
 Order of a run:
   1. the oracle on the host CPU, over the same workload (cpu_baseline), with
@@ -55,6 +57,7 @@ HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0    # dense bf16 MFMA, published peak
 COUNTERS = os.path.join(ROOT, "profiles", "attn_bf16_beam100_p600_counters.json")
 ATTN_SOURCE = os.path.join(ROOT, "generative_recommendation_beam_amd", "csrc", "attn.hip")
+COLD_BYTES = 512 * 1024 * 1024    # input rotation span: twice the 256 MB last-level cache
 
 
 def parse():
@@ -64,7 +67,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20, help="untimed steps first")
     ap.add_argument("--workload", default="beam100_p600")
     ap.add_argument("--sets", type=int, default=0,
-                    help="independent input copies rotated between steps (default: 2 per stream)")
+                    help="independent input copies rotated between steps (default: enough to span 512 MiB of "
+                         "algorithmic bytes, at least 2, per stream)")
     ap.add_argument("--streams", type=int, default=1,
                     help="also time the steps spread over this many HIP streams (extra field)")
     ap.add_argument("--attention", choices=["softmax", "linear"], default="softmax",
@@ -626,7 +630,11 @@ def main():
 
     torch.cuda.set_device(0)
     n_streams = max(1, args.streams)
-    n_sets = args.sets if args.sets > 0 else 2 * n_streams
+    # enough independent sets that the rotation spans more than twice the
+    # 256 MB last-level cache: each step then reads data no earlier step left
+    # there (at least two sets per stream)
+    n_cold = -(-COLD_BYTES // max(1, acc["step_bytes"]))
+    n_sets = args.sets if args.sets > 0 else max(2, n_cold) * n_streams
     assert n_sets % n_streams == 0, "every stream needs its own input sets"
     sets = [HN.upload_step(x)]
     for _ in range(n_sets - 1):

@@ -388,137 +388,131 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   // tile - 1.  The prompt loop's stage-0 head also does the tile-0 work.
   auto head = [&](int tile, auto S, auto in_prompt) GR_INLINE {
     constexpr int st = decltype(S)::value;
-    {
-      // at tile 0 the prologue has put exactly NS-2 tiles behind it
-      wait_tiles(tile == 0 ? NS - 2 : min(NS - 2, n_total - 1 - tile));
-      ring_barrier();
-      if constexpr (st == 0 && decltype(in_prompt)::value) {
-        if (tile == 0) {
-          // queries and chain ids / parents have landed (they precede tile 0)
-          if (chains && p.parent != nullptr && tid < G::NB) {
-            // resolve the chain of workgroup beam tid in LDS, checking range,
-            // order and depth (heads of one request see the same chains; the
-            // head-0 workgroup reports)
-            int n = grp * G::NB + tid < p.nb ? bn_s[tid] : -1;
-            int err = 0;
-            for (int d = 0; d < p.D; ++d) {
-              int id = -1;
-              if (n != -1) {
-                if (n < 0 || n >= p.cap) {
-                  err |= GR_DEVERR_PARENT_RANGE;
-                  n = -1;
-                } else {
-                  id = n;
-                  const int pn = par_s[n];
-                  if (pn < -1 || pn >= p.cap) { err |= GR_DEVERR_PARENT_RANGE; n = -1; }
-                  else if (pn >= n) { err |= GR_DEVERR_PARENT_ORDER; n = -1; }
-                  else n = pn;
-                }
+    // at tile 0 the prologue has put exactly NS-2 tiles behind it
+    wait_tiles(tile == 0 ? NS - 2 : min(NS - 2, n_total - 1 - tile));
+    ring_barrier();
+    if constexpr (st == 0 && decltype(in_prompt)::value) {
+      if (tile == 0) {
+        // queries and chain ids / parents have landed (they precede tile 0)
+        if (chains && p.parent != nullptr && tid < G::NB) {
+          // resolve the chain of workgroup beam tid in LDS, checking range,
+          // order and depth (heads of one request see the same chains; the
+          // head-0 workgroup reports)
+          int n = grp * G::NB + tid < p.nb ? bn_s[tid] : -1;
+          int err = 0;
+          for (int d = 0; d < p.D; ++d) {
+            int id = -1;
+            if (n != -1) {
+              if (n < 0 || n >= p.cap) {
+                err |= GR_DEVERR_PARENT_RANGE;
+                n = -1;
+              } else {
+                id = n;
+                const int pn = par_s[n];
+                if (pn < -1 || pn >= p.cap) { err |= GR_DEVERR_PARENT_RANGE; n = -1; }
+                else if (pn >= n) { err |= GR_DEVERR_PARENT_ORDER; n = -1; }
+                else n = pn;
               }
-              ids16[d * G::NB + tid] = (int16_t)id;
             }
-            if (n != -1) err |= GR_DEVERR_DEPTH;
-            if (err && h == 0) atomicOr(p.dev_err, err);
+            ids16[d * G::NB + tid] = (int16_t)id;
           }
-          if (wave * 32 < G::KT) {
+          if (n != -1) err |= GR_DEVERR_DEPTH;
+          if (err && h == 0) atomicOr(p.dev_err, err);
+        }
+        if (wave * 32 < G::KT) {
 #pragma unroll
-            for (int j = 0; j < G::KSTEP; ++j) qf[j] = *(const bf16x8 *)((const char *)K3 + roff_k[j]);
-          } else {
+          for (int j = 0; j < G::KSTEP; ++j) qf[j] = *(const bf16x8 *)((const char *)K3 + roff_k[j]);
+        } else {
 #pragma unroll
-            for (int j = 0; j < G::KSTEP; ++j) qf[j] = *(const bf16x8 *)((const char *)V3 + roff_k[j]);
+          for (int j = 0; j < G::KSTEP; ++j) qf[j] = *(const bf16x8 *)((const char *)V3 + roff_k[j]);
+        }
+        // every wave holds its queries before the last stage is refilled,
+        // and the chain ids are visible to all
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        ring_barrier();
+        if (chains) {
+          int depth = 0;
+          for (int d = 0; d < p.D; ++d) {
+            const int own = chain_id(d, wb);
+            cnt += own >= 0 ? 1 : 0;
+            bool any = lane < G::NB && chain_id(d, lane) >= 0;
+            if constexpr (G::NB > 64) any = any || chain_id(d, 64 + lane) >= 0;
+            if (__ballot(any)) depth = d + 1;
           }
-          // every wave holds its queries before the last stage is refilled,
-          // and the chain ids are visible to all
-          __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-          ring_barrier();
-          if (chains) {
-            int depth = 0;
-            for (int d = 0; d < p.D; ++d) {
-              const int own = chain_id(d, wb);
-              cnt += own >= 0 ? 1 : 0;
-              bool any = lane < G::NB && chain_id(d, lane) >= 0;
-              if constexpr (G::NB > 64) any = any || chain_id(d, 64 + lane) >= 0;
-              if (__ballot(any)) depth = d + 1;
-            }
-            n_total = n_pre + depth * G::NRB;
-          }
+          n_total = n_pre + depth * G::NRB;
         }
       }
-      // every wave is past tile-1: its stage can be refilled
-      if (tile + NS - 1 < n_total) issue(tile + NS - 1, Stage<(st + NS - 1) % NS>{});
     }
+    // every wave is past tile-1: its stage can be refilled
+    if (tile + NS - 1 < n_total) issue(tile + NS - 1, Stage<(st + NS - 1) % NS>{});
   };
   auto prompt_tile = [&](int tile, auto S) GR_INLINE {
     const char *kb = (const char *)kst(S);
     const char *vb = (const char *)vst(S);
-    {
-      {
-        // ---- shared prompt window
-        f32x16 S0, S1;
+    // ---- shared prompt window
+    f32x16 S0, S1;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { S0[i] = 0.f; S1[i] = 0.f; }
+    for (int i = 0; i < 16; ++i) { S0[i] = 0.f; S1[i] = 0.f; }
 #pragma unroll
-        for (int j = 0; j < G::KSTEP; ++j) {
-          const bf16x8 a0 = *(const bf16x8 *)(kb + koff[0][j]);
-          const bf16x8 a1 = *(const bf16x8 *)(kb + koff[1][j]);
-          S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[j], S0, 0, 0, 0);
-          S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[j], S1, 0, 0, 0);
-        }
-        const int key0 = k_begin + tile * G::KT;
-        if (key0 + G::KT > p.Lp) {
+    for (int j = 0; j < G::KSTEP; ++j) {
+      const bf16x8 a0 = *(const bf16x8 *)(kb + koff[0][j]);
+      const bf16x8 a1 = *(const bf16x8 *)(kb + koff[1][j]);
+      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[j], S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[j], S1, 0, 0, 0);
+    }
+    const int key0 = k_begin + tile * G::KT;
+    if (key0 + G::KT > p.Lp) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kk = 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key0 + kk >= p.Lp) S0[i] = -__builtin_inff();
-            if (key0 + 32 + kk >= p.Lp) S1[i] = -__builtin_inff();
-          }
-        }
-        // IEEE maximum (v_maximum3_f32): no operand canonicalisation needed
-        // two chains of v_maximum3, each folding two scores per instruction
-        float mx0 = __builtin_elementwise_maximum(S0[0], S1[0]);
-        float mx1 = __builtin_elementwise_maximum(S0[1], S1[1]);
+      for (int i = 0; i < 16; ++i) {
+        const int kk = 8 * (i >> 2) + 4 * g + (i & 3);
+        if (key0 + kk >= p.Lp) S0[i] = -__builtin_inff();
+        if (key0 + 32 + kk >= p.Lp) S1[i] = -__builtin_inff();
+      }
+    }
+    // IEEE maximum (v_maximum3_f32): no operand canonicalisation needed
+    // two chains of v_maximum3, each folding two scores per instruction
+    float mx0 = __builtin_elementwise_maximum(S0[0], S1[0]);
+    float mx1 = __builtin_elementwise_maximum(S0[1], S1[1]);
 #pragma unroll
-        for (int i = 2; i < 16; i += 2) {
-          mx0 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx0, S0[i]), S1[i]);
-          mx1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx1, S0[i + 1]), S1[i + 1]);
-        }
-        float mx = xor32_max(__builtin_elementwise_maximum(mx0, mx1)) * p.sl2;
-        // Exact running max: the key that sets it gets weight exactly 1, which
-        // bf16 holds exactly (it dominates a peaked softmax).  The rescale is
-        // skipped only when no lane's max grew (then alpha would be 1).
-        if (__ballot(mx > m_run)) {
-          const float m_new = __builtin_elementwise_maximum(m_run, mx);
-          const float alpha = fast_exp2(m_run - m_new);
-          m_run = m_new;
-          l_run *= alpha;
+    for (int i = 2; i < 16; i += 2) {
+      mx0 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx0, S0[i]), S1[i]);
+      mx1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx1, S0[i + 1]), S1[i + 1]);
+    }
+    float mx = xor32_max(__builtin_elementwise_maximum(mx0, mx1)) * p.sl2;
+    // Exact running max: the key that sets it gets weight exactly 1, which
+    // bf16 holds exactly (it dominates a peaked softmax).  The rescale is
+    // skipped only when no lane's max grew (then alpha would be 1).
+    if (__ballot(mx > m_run)) {
+      const float m_new = __builtin_elementwise_maximum(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-          for (int dt = 0; dt < G::DT; ++dt)
+      for (int dt = 0; dt < G::DT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) O[dt][i] *= alpha;
-        }
-        uint32_t pw[16];
+        for (int i = 0; i < 16; ++i) O[dt][i] *= alpha;
+    }
+    uint32_t pw[16];
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          pw[i >> 1] = pack_bf16x2(fast_exp2(fmaf(S0[i], p.sl2, -m_run)), fast_exp2(fmaf(S0[i + 1], p.sl2, -m_run)));
-          pw[8 + (i >> 1)] =
-              pack_bf16x2(fast_exp2(fmaf(S1[i], p.sl2, -m_run)), fast_exp2(fmaf(S1[i + 1], p.sl2, -m_run)));
-        }
-        // row sums of the rounded weights the PV product uses
+    for (int i = 0; i < 16; i += 2) {
+      pw[i >> 1] = pack_bf16x2(fast_exp2(fmaf(S0[i], p.sl2, -m_run)), fast_exp2(fmaf(S0[i + 1], p.sl2, -m_run)));
+      pw[8 + (i >> 1)] =
+          pack_bf16x2(fast_exp2(fmaf(S1[i], p.sl2, -m_run)), fast_exp2(fmaf(S1[i + 1], p.sl2, -m_run)));
+    }
+    // row sums of the rounded weights the PV product uses
 #pragma unroll
-        for (int i = 0; i < 16; ++i) l_run = add_bf16x2(pw[i], l_run);
+    for (int i = 0; i < 16; ++i) l_run = add_bf16x2(pw[i], l_run);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint4 pk4 = make_uint4(pw[4 * t], pw[4 * t + 1], pw[4 * t + 2], pw[4 * t + 3]);
-          const bf16x8 pf = __builtin_bit_cast(bf16x8, pk4);
+    for (int t = 0; t < 4; ++t) {
+      const uint4 pk4 = make_uint4(pw[4 * t], pw[4 * t + 1], pw[4 * t + 2], pw[4 * t + 3]);
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pk4);
 #pragma unroll
-          for (int dt = 0; dt < G::DT; ++dt) {
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GR_LDS4(vb + voff[dt][t][0]));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GR_LDS4(vb + voff[dt][t][1]));
-            const i16x4 a8[2] = {lo, hi};
-            const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
-            O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, O[dt], 0, 0, 0);
-          }
-        }
+      for (int dt = 0; dt < G::DT; ++dt) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GR_LDS4(vb + voff[dt][t][0]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GR_LDS4(vb + voff[dt][t][1]));
+        const i16x4 a8[2] = {lo, hi};
+        const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, O[dt], 0, 0, 0);
       }
     }
   };

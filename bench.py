@@ -286,11 +286,15 @@ def gen_accounting(g, steps):
     v, parent id), the level's codebook, priors and outputs; per append, the
     written records, queries and node ids; the code tables (embeddings and
     projections read, tables written).  Distinct chain records are counted
-    from the parents the run selected."""
+    from the parents the run selected.  Where the records stay in the code
+    tables (bf16, arenas of at most 4096 nodes) a chain node costs its parent
+    id and table row index, each distinct table row (level, code) is read
+    once for all requests, and an append writes the query, not the record."""
     import numpy as np
     sh = g.shape
     es = 2 if sh.dtype == 1 else 4
     R, D, V = sh.R, sh.H * sh.head_dim, g.vocab
+    tab = sh.dtype == 1 and g.trie is not None and g.trie.capacity <= 4096
     Lw = sh.prompt_len if sh.window <= 0 else min(sh.window, sh.prompt_len)
     total, attn_prompt = 0, 0
     for lv, (n, k) in enumerate(g.sizes):
@@ -301,10 +305,14 @@ def gen_accounting(g, steps):
             live = np.tile(np.arange(n), (R, 1))
             for up in range(lv - 1, -1, -1):
                 recs = sum(len(np.unique(live[r])) for r in range(R))
-                total += recs * (D * 2 * es + 4)
+                if tab:
+                    codes = np.unique(np.take_along_axis(steps[up]["token"], live, axis=1))
+                    total += recs * 8 + codes.size * D * 2 * es
+                else:
+                    total += recs * (D * 2 * es + 4)
                 live = np.take_along_axis(steps[up]["parent"], live, axis=1)
         if lv + 1 < len(g.sizes):
-            total += R * k * (3 * D * es + 4 + 8)
+            total += R * k * ((1 if tab else 3) * D * es + 4 + 8 + (4 if tab else 0))
     total += (g.levels - 1) * (V * g.d_emb * es + 3 * D * g.d_emb * es + V * 3 * D * es)
     return total, attn_prompt
 

@@ -332,10 +332,11 @@ GenLevels gen_levels(int levels, int vocab, int beam_width) {
 }
 
 // Workspace of a generation: the decode workspace (the largest step), the
-// queries of the next step [R][k_max][D], and two node-id buffers [R][k_max]
-// (the nodes of a step's input beams, and of its output beams once appended).
+// queries of the next step [R][k_max][D], two node-id buffers [R][k_max]
+// (the nodes of a step's input beams, and of its output beams once appended)
+// and the code-table row of every node [R][records].
 struct GenLayout {
-  size_t dec_bytes, q_off, node_off[2], total;
+  size_t dec_bytes, q_off, node_off[2], row_off, total;
 };
 GenLayout gen_layout(const gr_shape *s, int levels, int vocab, int beam_width) {
   const GenLevels g = gen_levels(levels, vocab, beam_width);
@@ -350,7 +351,8 @@ GenLayout gen_layout(const gr_shape *s, int levels, int vocab, int beam_width) {
   L.q_off = L.dec_bytes;
   L.node_off[0] = L.q_off + align_up(rows * s->H * s->head_dim * elem_bytes(s->dtype));
   L.node_off[1] = L.node_off[0] + align_up(rows * sizeof(int32_t));
-  L.total = L.node_off[1] + align_up(rows * sizeof(int32_t)) + kAlign;
+  L.row_off = L.node_off[1] + align_up(rows * sizeof(int32_t));
+  L.total = L.row_off + align_up((size_t)s->R * (g.records > 0 ? g.records : 1) * sizeof(int32_t)) + kAlign;
   return L;
 }
 
@@ -553,11 +555,23 @@ gr_status gr_beam_topk(int32_t R, int32_t n_in, int32_t vocab, int32_t k, int32_
   return hip_status(gr::launch_score_select(a, o, stream));
 }
 
-gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void *prompt_v, const void *q,
-                         int32_t n_beams, const gr_trie *trie, const int32_t *beam_node, const void *W,
-                         int32_t vocab, const float *prior, int32_t beam_width, int32_t flags, float *out_score,
-                         int32_t *out_token, int32_t *out_parent, float *attn_out, float *cand_out, void *ws,
-                         size_t ws_bytes, int32_t *dev_err, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Chain records left in the code tables of a generation (bf16, small
+// arenas): node n of request r is row row[r][n] of tab, n < rows.
+struct RecTable {
+  const void *tab;
+  int32_t *row;
+  int rows;
+};
+
+gr_status decode_step_impl(const gr_shape *shape, const void *prompt_k, const void *prompt_v, const void *q,
+                           int32_t n_beams, const gr_trie *trie, const int32_t *beam_node, const void *W,
+                           int32_t vocab, const float *prior, int32_t beam_width, int32_t flags, float *out_score,
+                           int32_t *out_token, int32_t *out_parent, float *attn_out, float *cand_out, void *ws,
+                           size_t ws_bytes, int32_t *dev_err, hipStream_t stream, const RecTable *rt) {
   gr_status st = attn_common(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, dev_err);
   if (st) return st;
   const int32_t stage = flags & (GR_STEP_ATTENTION | GR_STEP_SELECTION);
@@ -580,6 +594,11 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void
                                     use_mfma_logits(shape, vocab));
 
   gr::AttnArgs a = attn_args(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, dev_err);
+  if (rt && beam_node) {
+    a.rec_tab = rt->tab;
+    a.rec_row = rt->row;
+    a.rec_rows = rt->rows;
+  }
   a.chain_ids = L.ids_bytes ? (int32_t *)(base + L.ids_off) : nullptr;
   a.split_ws = L.split_bytes ? (float *)(base + L.split_off) : nullptr;
   const bool mfma_logits = use_mfma_logits(shape, vocab);
@@ -607,6 +626,20 @@ gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void
   }
   return enqueue_scoring(shape, n_beams, W, vocab, prior, beam_width, lsm, cand_out, so, L, base,
                          o_f32, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+gr_status gr_decode_step(const gr_shape *shape, const void *prompt_k, const void *prompt_v, const void *q,
+                         int32_t n_beams, const gr_trie *trie, const int32_t *beam_node, const void *W,
+                         int32_t vocab, const float *prior, int32_t beam_width, int32_t flags, float *out_score,
+                         int32_t *out_token, int32_t *out_parent, float *attn_out, float *cand_out, void *ws,
+                         size_t ws_bytes, int32_t *dev_err, hipStream_t stream) {
+  return decode_step_impl(shape, prompt_k, prompt_v, q, n_beams, trie, beam_node, W, vocab, prior, beam_width,
+                          flags, out_score, out_token, out_parent, attn_out, cand_out, ws, ws_bytes, dev_err, stream,
+                          nullptr);
 }
 
 gr_status gr_linear_state(const gr_shape *shape, const void *prompt_k, const void *prompt_v, float *state,
@@ -710,10 +743,16 @@ gr_status gr_code_table(const gr_shape *shape, int32_t levels, int32_t vocab, in
   return hip_status(gr::launch_code_table(a, stream));
 }
 
-gr_status gr_append_codes(const gr_shape *shape, const gr_trie *trie, int32_t base, int32_t n_new,
-                          const void *table, int32_t vocab, const int32_t *token, const int32_t *parent_beam,
-                          const int32_t *prev_nodes, int32_t n_prev, void *q_out, int32_t *node_out,
-                          int32_t *dev_err, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// rt: the records stay in the code tables, whose row row0 + code each new
+// node gets in rt->row; the arena's keys and values are not written.
+gr_status append_codes_impl(const gr_shape *shape, const gr_trie *trie, int32_t base, int32_t n_new,
+                            const void *table, int32_t vocab, const int32_t *token, const int32_t *parent_beam,
+                            const int32_t *prev_nodes, int32_t n_prev, void *q_out, int32_t *node_out,
+                            int32_t *dev_err, hipStream_t stream, const RecTable *rt, int32_t row0) {
   gr_status st = check_shape(shape);
   if (st) return st;
   if (!trie || !table || !token || !dev_err) return GR_ERR_NULL;
@@ -746,8 +785,26 @@ gr_status gr_append_codes(const gr_shape *shape, const gr_trie *trie, int32_t ba
   a.n_new = n_new;
   a.n_prev = prev_nodes ? n_prev : 0;
   a.V = vocab;
+  if (rt) {
+    if ((long long)base + n_new > rt->rows) return GR_ERR_CAPACITY;
+    a.rec_row = rt->row;
+    a.row_n = rt->rows;
+    a.row0 = row0;
+  }
   clear_stale_error();
   return hip_status(gr::launch_append_codes(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+gr_status gr_append_codes(const gr_shape *shape, const gr_trie *trie, int32_t base, int32_t n_new,
+                          const void *table, int32_t vocab, const int32_t *token, const int32_t *parent_beam,
+                          const int32_t *prev_nodes, int32_t n_prev, void *q_out, int32_t *node_out,
+                          int32_t *dev_err, hipStream_t stream) {
+  return append_codes_impl(shape, trie, base, n_new, table, vocab, token, parent_beam, prev_nodes, n_prev, q_out,
+                           node_out, dev_err, stream, nullptr, 0);
 }
 
 size_t gr_workspace_size(const gr_shape *shape, int32_t n_beams, int32_t vocab, int32_t k) {
@@ -802,6 +859,15 @@ gr_status gr_generate(const gr_shape *shape, const void *prompt_k, const void *p
   const size_t eb = elem_bytes(shape->dtype);
   const size_t w_level = (size_t)vocab * D * eb;
   const size_t t_level = (size_t)vocab * 3 * D * eb;
+  // bf16 chains small enough to resolve inside the attention kernel read
+  // their records straight from the tables (a few hundred KB per level, held
+  // in L2), so the arena's keys and values are never written.
+  RecTable rt;
+  rt.tab = tables;
+  rt.row = (int32_t *)(base + L.row_off);
+  rt.rows = (int)g.records;
+  const RecTable *rtp =
+      levels > 1 && shape->dtype == GR_BF16 && trie->capacity <= gr::kLdsChainNodes ? &rt : nullptr;
 
   gr::TraceArgs tr;
   tr.R = R;
@@ -814,17 +880,17 @@ gr_status gr_generate(const gr_shape *shape, const void *prompt_k, const void *p
     int32_t *token = out_token + off;
     int32_t *parent = out_parent + off;
     const int32_t *beam_node = l > 0 ? nodes[(l - 1) & 1] : nullptr;
-    st = gr_decode_step(shape, prompt_k, prompt_v, l > 0 ? qbuf : q0, g.n[l], l > 0 ? trie : nullptr, beam_node,
-                        (const char *)W + l * w_level, vocab, l > 0 ? out_score + tr.off[l - 1] : nullptr,
-                        g.k[l], GR_TOPK_LOG_SOFTMAX, score, token, parent, nullptr, nullptr, dec_ws, L.dec_bytes,
-                        dev_err, stream);
+    st = decode_step_impl(shape, prompt_k, prompt_v, l > 0 ? qbuf : q0, g.n[l], l > 0 ? trie : nullptr,
+                          beam_node, (const char *)W + l * w_level, vocab,
+                          l > 0 ? out_score + tr.off[l - 1] : nullptr, g.k[l], GR_TOPK_LOG_SOFTMAX, score, token,
+                          parent, nullptr, nullptr, dec_ws, L.dec_bytes, dev_err, stream, rtp);
     if (st) return st;
     if (l + 1 < levels) {
       // the chosen codes become the next step's beams: records at nodes
       // [rec_base, rec_base + k_l), their queries into qbuf
-      st = gr_append_codes(shape, trie, (int32_t)rec_base, g.k[l], (const char *)tables + l * t_level, vocab,
-                           token, l > 0 ? parent : nullptr, l > 0 ? beam_node : nullptr, g.n[l], qbuf,
-                           nodes[l & 1], dev_err, stream);
+      st = append_codes_impl(shape, trie, (int32_t)rec_base, g.k[l], (const char *)tables + l * t_level, vocab,
+                             token, l > 0 ? parent : nullptr, l > 0 ? beam_node : nullptr, g.n[l], qbuf,
+                             nodes[l & 1], dev_err, stream, rtp, l * vocab);
       if (st) return st;
       rec_base += g.k[l];
     }

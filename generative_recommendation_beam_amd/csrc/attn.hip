@@ -120,8 +120,11 @@ struct AttnP {
   int R, H, Lp, Lw, nb, cap, D, nb_pad, n_grp;
   int n_split, tps;          // prompt runs per unit and 64-key tiles per run
   float *part;               // n_split > 1: partial states (see attn_split_bytes)
-  int ids_words, par_words;  // dynamic LDS: ids [ids_words], parents [par_words], beam nodes
+  int ids_words, par_words;  // dynamic LDS: ids [ids_words], parents [par_words], beam nodes, table rows
   float sl2;                 // scale * log2(e)
+  const uint16_t *rtab;      // records from code tables: [rows][3][H][HD] (q, k, v), or null
+  const int32_t *rrow;       // [R][rrow_n]: the table row of each node
+  int rrow_n;
 };
 
 template <int HD, int NW, int NS>
@@ -151,7 +154,9 @@ __device__ __forceinline__ int swz_v(int row) {
   return HD == 64 ? 2 * (row & 3) : 2 * ((row >> 1) & 1);
 }
 
-template <int HD, int NW, int NS, int OCC>
+// TAB: the chain records are rows of code tables (p.rtab, one row index per
+// node in p.rrow, staged in LDS with the parents); else rows of the arena.
+template <int HD, int NW, int NS, int OCC, bool TAB>
 __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   using G = Geo<HD, NW, NS>;
   static_assert(NS >= 2 && NS <= 4, "ring depth: the last stage carries the queries until it is first refilled");
@@ -172,6 +177,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   int16_t *const ids16 = reinterpret_cast<int16_t *>(dyn_s);
   int32_t *const par_s = dyn_s + p.ids_words;
   int32_t *const bn_s = par_s + p.par_words;
+  int32_t *const row_s = bn_s + (G::NB + 63) / 64 * 64;   // TAB: the request's table row per node
   auto chain_id = [&](int d, int b) GR_INLINE -> int {
     return p.parent != nullptr ? (int)ids16[d * G::NB + b] : ids_s[d * G::NB + b];
   };
@@ -247,6 +253,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   // t holding beam t's key in the first half and its value in the second (a
   // beam without a record at the level reads record 0 of the request,
   // unused: these fold each beam's own row only).
+  // the key (kv = 1) or value (kv = 2) row of record `id` for this head, at
+  // element offset sw: in the arena, or the node's row of the code tables
+  auto rec_src = [&](int id, int kv, uint32_t sw) GR_INLINE -> const uint16_t * {
+    if constexpr (TAB) return p.rtab + ((size_t)row_s[id] * 3 + kv) * row + (size_t)h * HD + sw;
+    else return (kv == 1 ? p.ak : p.av) + ((size_t)r * p.cap + id) * row + (size_t)h * HD + sw;
+  };
   auto issue_records = [&](int d, int bb, uint16_t *ks, uint16_t *vs) GR_INLINE {
     if constexpr (G::NRB == 2) {
       // A beam without a record at level d gathers `rec_fill`, a record of
@@ -261,14 +273,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
         const int fb = m0 ? (int)__builtin_ctzll(m0) : (m1 ? G::KT + (int)__builtin_ctzll(m1) : 0);
         rec_fill = __builtin_amdgcn_readfirstlane(max(chain_id(0, fb), 0));
       }
-      const uint16_t *const base = bb ? p.av : p.ak;
 #pragma unroll
       for (int i = 0; i < G::IPW; ++i) {
         const int blk = wave * G::IPW + i;
         const uint32_t sw = bb ? dma_v[i] : dma_k[i];
         const int id0 = chain_id(d, dma_row[i]), id1 = chain_id(d, G::KT + dma_row[i]);
-        dma16(base + ((size_t)r * p.cap + (id0 >= 0 ? id0 : rec_fill)) * row + (size_t)h * HD + sw, ks + blk * 512);
-        dma16(base + ((size_t)r * p.cap + (id1 >= 0 ? id1 : rec_fill)) * row + (size_t)h * HD + sw, vs + blk * 512);
+        dma16(rec_src(id0 >= 0 ? id0 : rec_fill, 1 + bb, sw), ks + blk * 512);
+        dma16(rec_src(id1 >= 0 ? id1 : rec_fill, 1 + bb, sw), vs + blk * 512);
       }
     } else {
 #pragma unroll
@@ -276,9 +287,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
         const int blk = wave * G::IPW + i;
         const int b = bb * G::KT + dma_row[i];
         const int id = b < G::NB ? chain_id(d, b) : -1;
-        const size_t src = ((size_t)r * p.cap + (id >= 0 ? id : 0)) * row + (size_t)h * HD;
-        dma16(p.ak + src + dma_k[i], ks + blk * 512);
-        dma16(p.av + src + dma_v[i], vs + blk * 512);
+        dma16(rec_src(id >= 0 ? id : 0, 1, dma_k[i]), ks + blk * 512);
+        dma16(rec_src(id >= 0 ? id : 0, 2, dma_v[i]), vs + blk * 512);
       }
     }
   };
@@ -307,6 +317,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
     for (int i = 0; i * 64 < p.cap; ++i) dma4(par + min(i * 64 + lane, p.cap - 1), par_s + i * 64);
     const int32_t *bnp = p.beam_node + (size_t)r * p.nb;
     for (int i = 0; i * 64 < G::NB; ++i) dma4(bnp + min(grp * G::NB + i * 64 + lane, p.nb - 1), bn_s + i * 64);
+    if constexpr (TAB) {
+      const int32_t *rr = p.rrow + (size_t)r * p.rrow_n;
+      for (int i = 0; i * 64 < p.rrow_n; ++i) dma4(rr + min(i * 64 + lane, p.rrow_n - 1), row_s + i * 64);
+    }
   }
   if (chains && p.ids != nullptr && wave == 0) {
     const int words = p.D * G::NB;
@@ -403,7 +417,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
           for (int d = 0; d < p.D; ++d) {
             int id = -1;
             if (n != -1) {
-              if (n < 0 || n >= p.cap) {
+              if (n < 0 || n >= (TAB ? p.rrow_n : p.cap)) {   // TAB: only nodes with a table row
                 err |= GR_DEVERR_PARENT_RANGE;
                 n = -1;
               } else {
@@ -904,10 +918,6 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnPF p) {
   for (int i = 0; i < HD; ++i) op[i] = o[i] * inv;
 }
 
-// Arenas up to this many nodes per request have their parent array staged in
-// LDS and the chains resolved inside the attention kernel; larger ones go
-// through the chain_resolve pre-pass.
-constexpr int kLdsChainNodes = 4096;
 
 template <int HD, int NW>
 hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
@@ -916,6 +926,7 @@ hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
   AttnP p;
   p.pk = (const uint16_t *)a.pk; p.pv = (const uint16_t *)a.pv; p.q = (const uint16_t *)a.q;
   p.ak = (const uint16_t *)a.ak; p.av = (const uint16_t *)a.av;
+  p.rtab = (const uint16_t *)a.rec_tab; p.rrow = a.rec_row; p.rrow_n = a.rec_rows;
   p.ids = nullptr; p.parent = nullptr; p.beam_node = nullptr; p.dev_err = a.dev_err;
   p.out_f32 = a.out_f32; p.out_bf16 = (uint16_t *)a.out_lowp;
   p.R = a.R; p.H = a.H; p.Lp = a.Lp; p.Lw = a.Lw; p.nb = a.nb; p.cap = a.cap;
@@ -935,8 +946,12 @@ hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
   const size_t prepass_dyn = (size_t)(a.max_depth * NB + 255) / 256 * 256 * 4;
   const bool inkernel_fits = (static_lds + inkernel_dyn) * OCC <= lds_per_cu;
   const bool prepass_fits = (static_lds + prepass_dyn) * OCC <= lds_per_cu;
+  const bool tab = a.rec_tab != nullptr;
+  if (tab && (a.beam_node == nullptr || a.rec_row == nullptr || a.cap > kLdsChainNodes || a.rec_rows < 1 ||
+              a.rec_rows > a.cap))
+    return hipErrorInvalidValue;
   if (a.beam_node != nullptr) {
-    if (a.cap <= kLdsChainNodes && (inkernel_fits || !prepass_fits || a.chain_ids == nullptr)) {
+    if (tab || (a.cap <= kLdsChainNodes && (inkernel_fits || !prepass_fits || a.chain_ids == nullptr))) {
       p.parent = a.parent;
       p.beam_node = a.beam_node;
       p.ids_words = (a.max_depth * NB + 1) / 2;           // int16 ids, two per word
@@ -958,9 +973,13 @@ hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
   p.tps = sp.tiles_per_split;
   p.part = a.split_ws;
   if (sp.n_split > 1 && a.split_ws == nullptr) return hipErrorInvalidValue;   // the caller checks this
-  const size_t dyn = (size_t)(p.ids_words + p.par_words + (p.parent ? (NB + 63) / 64 * 64 : 0)) * sizeof(int32_t);
+  const size_t dyn = (size_t)(p.ids_words + p.par_words + (p.parent ? (NB + 63) / 64 * 64 : 0) +
+                              (tab ? p.par_words : 0)) * sizeof(int32_t);
   const long long grid = (long long)a.R * a.H * p.n_grp * p.n_split;
-  hipLaunchKernelGGL((attn_bf16_kernel<HD, NW, NS, OCC>), dim3((unsigned)grid), dim3(NW * 64), dyn, s, p);
+  if (tab)
+    hipLaunchKernelGGL((attn_bf16_kernel<HD, NW, NS, OCC, true>), dim3((unsigned)grid), dim3(NW * 64), dyn, s, p);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<HD, NW, NS, OCC, false>), dim3((unsigned)grid), dim3(NW * 64), dyn, s, p);
   if (sp.n_split == 1) return hipGetLastError();
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

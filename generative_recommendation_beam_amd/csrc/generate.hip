@@ -93,8 +93,9 @@ struct CodeAP {
   const uint4 *table;          // [V][3][cpr]: q, k, v rows of each code
   const int32_t *token, *parent_beam, *prev_nodes;
   int32_t *node_out, *dev_err;
+  int32_t *rec_row;            // or [R][row_n]: the table row of each node, in place of ak / av
   long long total;             // R * n_new * cpr
-  int cpr, cap, base, n_new, n_prev, V;
+  int cpr, cap, base, n_new, n_prev, V, row_n, row0;
 };
 
 // One thread per 16-byte chunk of a record; the chunk-0 thread also links the
@@ -111,10 +112,13 @@ __global__ __launch_bounds__(256) void append_codes_kernel(CodeAP p) {
   const uint4 *src = p.table + (size_t)t * 3 * p.cpr;
   const long long dst = ((long long)r * p.cap + p.base + j) * p.cpr + ch;
   if (p.q_out) p.q_out[idx] = src[ch];
-  p.ak[dst] = src[p.cpr + ch];
-  p.av[dst] = src[2 * p.cpr + ch];
+  if (p.rec_row == nullptr) {
+    p.ak[dst] = src[p.cpr + ch];
+    p.av[dst] = src[2 * p.cpr + ch];
+  }
   if (ch != 0) return;
   const int n = p.base + j;
+  if (p.rec_row != nullptr) p.rec_row[(long long)r * p.row_n + n] = p.row0 + t;
   int par = -1, err = bad_code ? GR_DEVERR_TOKEN_RANGE : 0;
   if (p.parent_beam != nullptr) {
     const int pb = p.parent_beam[rowi];
@@ -177,6 +181,7 @@ hipError_t launch_append_codes(const AppendCodesArgs &a, hipStream_t s) {
   p.cpr = a.H * a.hd * a.elem_bytes / 16;
   p.total = (long long)a.R * a.n_new * p.cpr;
   p.cap = a.cap; p.base = a.base; p.n_new = a.n_new; p.n_prev = a.n_prev; p.V = a.V;
+  p.rec_row = a.rec_row; p.row_n = a.row_n; p.row0 = a.row0;
   const long long blocks = (p.total + 255) / 256;
   hipLaunchKernelGGL(append_codes_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();

@@ -23,8 +23,20 @@ struct AttnArgs {
   int32_t *dev_err;
   int R, H, hd, Lp, Lw, nb, cap, max_depth;
   float scale;
+  // Records read from code tables instead of the arena (whole-ID generation,
+  // bf16, arenas of at most kLdsChainNodes nodes): node n's key and value are
+  // row rec_row[r][n] of rec_tab ([rows][3][H][hd]: q, k, v), for the nodes
+  // n < rec_rows <= cap that chains reach.  Null: the arena.
+  const void *rec_tab = nullptr;
+  const int32_t *rec_row = nullptr;   // [R][rec_rows]
+  int rec_rows = 0;
 };
 hipError_t launch_attn(const AttnArgs &a, hipStream_t s);
+
+// Arenas up to this many nodes per request have their parent array staged in
+// LDS and the chains resolved inside the bf16 attention kernel; larger ones go
+// through the chain-resolve pre-pass (and cannot read records from tables).
+constexpr int kLdsChainNodes = 4096;
 
 // bf16 attention geometry: a workgroup holds NW waves of 32 beams; the chain
 // ids of a request are stored level-major, [max_depth][beams padded to whole
@@ -126,6 +138,11 @@ struct AppendCodesArgs {
   const int32_t *token, *parent_beam, *prev_nodes;
   int32_t *node_out, *dev_err;
   int R, H, hd, cap, base, n_new, n_prev, V;
+  // Records left in the code tables: node n's table row (row0 + its code) is
+  // written to rec_row[r][n] ([R][row_n], n < row_n) and ak / av are not
+  // touched.  Null: the rows are copied into the arena.
+  int32_t *rec_row = nullptr;
+  int row_n = 0, row0 = 0;
 };
 hipError_t launch_append_codes(const AppendCodesArgs &a, hipStream_t s);
 

@@ -246,9 +246,10 @@ class DeviceGen:
         return getattr(self, name)[off:off + R * k].view(R, k)
 
 
-def upload_generate(x, device="cuda") -> DeviceGen:
+def upload_generate(x, device="cuda", capacity: Optional[int] = None) -> DeviceGen:
     """Upload a workloads.GenInputs and allocate everything gr_generate needs
-    (the code tables are left empty: code_tables() fills them)."""
+    (the code tables are left empty: code_tables() fills them).  `capacity`
+    (default: exactly the appended records) sizes the trie arena."""
     cfg = x.cfg
     dt = dtype_code(cfg.dtype)
     R = x.prompt_k.shape[0]
@@ -258,7 +259,7 @@ def upload_generate(x, device="cuda") -> DeviceGen:
     total = R * sum(k for _, k in sizes)
     trie, tables, emb = None, None, None
     if levels > 1:
-        cap = sum(k for _, k in sizes[:-1])
+        cap = max(sum(k for _, k in sizes[:-1]), capacity or 0)
         trie = new_arena(shape, cap, max_depth=max(levels - 1, 1), device=device)[3]
         emb = to_dev(np.stack(x.emb), dt, device)
         tables = torch.empty((levels - 1, V, 3, cfg.H, cfg.d), dtype=_TORCH[dt], device=device)

@@ -338,7 +338,10 @@ gr_status gr_append_codes(const gr_shape *shape, const gr_trie *trie,
  *   level; NULL when levels == 1).  trie: arena for the appended records,
  *   capacity >= k_0 + ... + k_{levels-2} and max_depth >= levels - 1 (NULL
  *   when levels == 1); nodes [0, k_0) hold level-1 records, the next k_1
- *   level-2 records, and so on.
+ *   level-2 records, and so on.  Their parent links are always written; in
+ *   bf16 with capacity <= 4096 the attention reads each record's key and
+ *   value straight from its row of `tables`, and the arena's k and v are
+ *   left unwritten (otherwise they receive the records' rows).
  *   out_score / out_token / out_parent: per-step results packed step after
  *   step; step l's block is [R][k_l] and starts at element
  *   R * (k_0 + ... + k_{l-1}) (for beam_width <= 256 simply

@@ -16,7 +16,9 @@ gr_generate against the oracle (oracle/generate.py).
   requests: every level's candidate scores, selected scores and picks against
   the oracle, so levels after a bf16 near-tie are still checked.
 * gr_generate equals, bit for bit, the same chain of single-step entry points
-  run from the host (its orchestration: buffers, offsets, priors, nodes).
+  run from the host (its orchestration: buffers, offsets, priors, nodes; in
+  bf16 its records read from the code tables against the arena copies), also
+  with an arena too large for the table path and at the maximum depth.
 * Beam width above 256 (the first step keeps 256, later steps more) and a
   single-level generation.
 * One HIP graph holding the tables and the whole generation, replayed three
@@ -47,9 +49,9 @@ def oracle_tables(x):
     return [OG.code_table(e, x.w_qkv, cfg.H, cfg.d, cfg.dtype) for e in x.emb]
 
 
-def setup(cfg, seed=None, tables="oracle"):
+def setup(cfg, seed=None, tables="oracle", capacity=None):
     x = W.make_generate_inputs(cfg, seed=seed, R=cfg.R)
-    g = HN.upload_generate(x)
+    g = HN.upload_generate(x, capacity=capacity)
     tabs = oracle_tables(x)
     if g.levels > 1:
         if tables == "oracle":
@@ -236,10 +238,20 @@ def host_chain(g):
     return [tuple(t.cpu().numpy() for t in s) for s in steps]
 
 
-@pytest.mark.parametrize("cfg", [MID, WIDE], ids=["bf16", "wide"])
-def test_generate_equals_host_driven_chain(cfg):
-    announce(f"gr_generate vs host-driven chain {cfg.name}")
-    x, g, _ = setup(cfg)
+DEEP_BF16 = W.reduced(GC["gen_tiny_f32"], R=2, Lp=40, H=2, d=64, k=40, steps=L.GR_MAX_DEPTH + 1,
+                      level_sizes=(40,) * L.GR_MAX_DEPTH, dtype="bf16")
+NARROW = W.reduced(MID, k=20, level_sizes=(20, 20, 20))
+
+
+# In bf16 with an arena of at most 4096 nodes gr_generate's attention reads the
+# chain records from the code tables, while the single-step entry points read
+# the copies gr_append_codes wrote into the arena: the two must agree bit for
+# bit.  Capacity 5000 keeps gr_generate on the arena (chain pre-pass) path.
+@pytest.mark.parametrize("cfg,capacity", [(MID, None), (WIDE, None), (NARROW, None), (MID, 5000), (DEEP_BF16, None)],
+                         ids=["bf16", "wide", "bf16_beam20", "bf16_arena5000", "bf16_max_levels"])
+def test_generate_equals_host_driven_chain(cfg, capacity):
+    announce(f"gr_generate vs host-driven chain {cfg.name} capacity={capacity}")
+    x, g, _ = setup(cfg, capacity=capacity)
     chain = host_chain(g)
     HN.generate(g)
     torch.cuda.synchronize()

@@ -289,7 +289,8 @@ def gen_accounting(g, steps):
     from the parents the run selected.  Where the records stay in the code
     tables (bf16, arenas of at most 4096 nodes) a chain node costs its parent
     id and table row index, each distinct table row (level, code) is read
-    once for all requests, and an append writes the query, not the record."""
+    once for all requests (the queries of later steps too), and an append
+    writes the node's row index instead of the query and the record."""
     import numpy as np
     sh = g.shape
     es = 2 if sh.dtype == 1 else 4
@@ -298,7 +299,10 @@ def gen_accounting(g, steps):
     Lw = sh.prompt_len if sh.window <= 0 else min(sh.window, sh.prompt_len)
     total, attn_prompt = 0, 0
     for lv, (n, k) in enumerate(g.sizes):
-        total += R * Lw * D * 2 * es + R * n * D * es + V * D * es + R * k * 12 + (R * n * 4 if lv else 0)
+        q_bytes = R * n * D * es
+        if tab and lv:
+            q_bytes = np.unique(steps[lv - 1]["token"]).size * D * es
+        total += R * Lw * D * 2 * es + q_bytes + V * D * es + R * k * 12 + (R * n * 4 if lv else 0)
         attn_prompt += R * Lw * D * 2 * es
         # records on the chains of step lv's n beams: levels lv, lv-1, .., 1
         if lv:
@@ -312,7 +316,7 @@ def gen_accounting(g, steps):
                     total += recs * (D * 2 * es + 4)
                 live = np.take_along_axis(steps[up]["parent"], live, axis=1)
         if lv + 1 < len(g.sizes):
-            total += R * k * ((1 if tab else 3) * D * es + 4 + 8 + (4 if tab else 0))
+            total += R * k * (4 + 8 + 4 if tab else 3 * D * es + 4 + 8)
     total += (g.levels - 1) * (V * g.d_emb * es + 3 * D * g.d_emb * es + V * 3 * D * es)
     return total, attn_prompt
 

@@ -559,12 +559,13 @@ gr_status gr_beam_topk(int32_t R, int32_t n_in, int32_t vocab, int32_t k, int32_
 
 namespace {
 
-// Chain records left in the code tables of a generation (bf16, small
-// arenas): node n of request r is row row[r][n] of tab, n < rows.
+// Chain records and queries left in the code tables of a generation (bf16,
+// small arenas): node n of request r is row row[r][n] of tab
+// ([tab_rows][3][H][head_dim]), n < rows.
 struct RecTable {
   const void *tab;
   int32_t *row;
-  int rows;
+  int rows, tab_rows;
 };
 
 gr_status decode_step_impl(const gr_shape *shape, const void *prompt_k, const void *prompt_v, const void *q,
@@ -598,6 +599,7 @@ gr_status decode_step_impl(const gr_shape *shape, const void *prompt_k, const vo
     a.rec_tab = rt->tab;
     a.rec_row = rt->row;
     a.rec_rows = rt->rows;
+    a.rec_tab_rows = rt->tab_rows;
   }
   a.chain_ids = L.ids_bytes ? (int32_t *)(base + L.ids_off) : nullptr;
   a.split_ws = L.split_bytes ? (float *)(base + L.split_off) : nullptr;
@@ -860,12 +862,14 @@ gr_status gr_generate(const gr_shape *shape, const void *prompt_k, const void *p
   const size_t w_level = (size_t)vocab * D * eb;
   const size_t t_level = (size_t)vocab * 3 * D * eb;
   // bf16 chains small enough to resolve inside the attention kernel read
-  // their records straight from the tables (a few hundred KB per level, held
-  // in L2), so the arena's keys and values are never written.
+  // their records and queries straight from the tables (a few hundred KB per
+  // level, held in L2), so neither the arena's keys and values nor the next
+  // queries are written.
   RecTable rt;
   rt.tab = tables;
   rt.row = (int32_t *)(base + L.row_off);
   rt.rows = (int)g.records;
+  rt.tab_rows = (levels - 1) * vocab;
   const RecTable *rtp =
       levels > 1 && shape->dtype == GR_BF16 && trie->capacity <= gr::kLdsChainNodes ? &rt : nullptr;
 
@@ -889,8 +893,8 @@ gr_status gr_generate(const gr_shape *shape, const void *prompt_k, const void *p
       // the chosen codes become the next step's beams: records at nodes
       // [rec_base, rec_base + k_l), their queries into qbuf
       st = append_codes_impl(shape, trie, (int32_t)rec_base, g.k[l], (const char *)tables + l * t_level, vocab,
-                             token, l > 0 ? parent : nullptr, l > 0 ? beam_node : nullptr, g.n[l], qbuf,
-                             nodes[l & 1], dev_err, stream, rtp, l * vocab);
+                             token, l > 0 ? parent : nullptr, l > 0 ? beam_node : nullptr, g.n[l],
+                             rtp ? nullptr : qbuf, nodes[l & 1], dev_err, stream, rtp, l * vocab);
       if (st) return st;
       rec_base += g.k[l];
     }

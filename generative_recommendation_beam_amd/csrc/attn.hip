@@ -124,7 +124,7 @@ struct AttnP {
   float sl2;                 // scale * log2(e)
   const uint16_t *rtab;      // records from code tables: [rows][3][H][HD] (q, k, v), or null
   const int32_t *rrow;       // [R][rrow_n]: the table row of each node
-  int rrow_n;
+  int rrow_n, rtab_rows;
 };
 
 template <int HD, int NW, int NS>
@@ -154,8 +154,9 @@ __device__ __forceinline__ int swz_v(int row) {
   return HD == 64 ? 2 * (row & 3) : 2 * ((row >> 1) & 1);
 }
 
-// TAB: the chain records are rows of code tables (p.rtab, one row index per
-// node in p.rrow, staged in LDS with the parents); else rows of the arena.
+// TAB: the chain records and the queries are rows of code tables (p.rtab,
+// one row index per node in p.rrow, staged in LDS with the parents; a beam's
+// query is the row of its node); else the arena and p.q.
 template <int HD, int NW, int NS, int OCC, bool TAB>
 __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   using G = Geo<HD, NW, NS>;
@@ -256,7 +257,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
   // the key (kv = 1) or value (kv = 2) row of record `id` for this head, at
   // element offset sw: in the arena, or the node's row of the code tables
   auto rec_src = [&](int id, int kv, uint32_t sw) GR_INLINE -> const uint16_t * {
-    if constexpr (TAB) return p.rtab + ((size_t)row_s[id] * 3 + kv) * row + (size_t)h * HD + sw;
+    if constexpr (TAB) {
+      const uint32_t tr = min((uint32_t)row_s[id], (uint32_t)p.rtab_rows - 1);
+      return p.rtab + ((size_t)tr * 3 + kv) * row + (size_t)h * HD + sw;
+    }
     else return (kv == 1 ? p.ak : p.av) + ((size_t)r * p.cap + id) * row + (size_t)h * HD + sw;
   };
   auto issue_records = [&](int d, int bb, uint16_t *ks, uint16_t *vs) GR_INLINE {
@@ -308,6 +312,22 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
     else GR_WAIT_VMCNT(0);
   };
 
+  // TAB: this lane's query pieces are the query part of the table row of
+  // each beam's node
+  size_t q_tab[TAB ? G::IPW : 1][2];
+  if constexpr (TAB) {
+#pragma unroll
+    for (int i = 0; i < G::IPW; ++i) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int b = min(grp * G::NB + dma_row[i] + u * G::KT, p.nb - 1);
+        const int node = min(max(p.beam_node[(size_t)r * p.nb + b], 0), p.rrow_n - 1);
+        const uint32_t tr = min((uint32_t)p.rrow[(size_t)r * p.rrow_n + node], (uint32_t)p.rtab_rows - 1);
+        q_tab[i][u] = (size_t)tr * 3 * row + (size_t)h * HD;
+      }
+    }
+  }
+
   // ---- prologue, in stream order: chain ids or the parent array and beam
   // nodes (wave 0), the queries of the workgroup into the last stage (its K
   // half: beams 0..63, V half: beams 64..127, K-swizzled rows), then prompt
@@ -334,12 +354,17 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bf16_kernel(AttnP p) {
 #pragma unroll
   for (int i = 0; i < G::IPW; ++i) {
     const int blk = wave * G::IPW + i;
-    const int b0 = grp * G::NB + dma_row[i];
-    const size_t s0 = ((size_t)r * p.nb + min(b0, p.nb - 1)) * row + (size_t)h * HD;
-    dma16(p.q + s0 + dma_k[i], K3 + blk * 512);
-    if constexpr (G::NB > G::KT) {
-      const size_t s1 = ((size_t)r * p.nb + min(b0 + G::KT, p.nb - 1)) * row + (size_t)h * HD;
-      dma16(p.q + s1 + dma_k[i], V3 + blk * 512);
+    if constexpr (TAB) {
+      dma16(p.rtab + q_tab[i][0] + dma_k[i], K3 + blk * 512);
+      if constexpr (G::NB > G::KT) dma16(p.rtab + q_tab[i][1] + dma_k[i], V3 + blk * 512);
+    } else {
+      const int b0 = grp * G::NB + dma_row[i];
+      const size_t s0 = ((size_t)r * p.nb + min(b0, p.nb - 1)) * row + (size_t)h * HD;
+      dma16(p.q + s0 + dma_k[i], K3 + blk * 512);
+      if constexpr (G::NB > G::KT) {
+        const size_t s1 = ((size_t)r * p.nb + min(b0 + G::KT, p.nb - 1)) * row + (size_t)h * HD;
+        dma16(p.q + s1 + dma_k[i], V3 + blk * 512);
+      }
     }
   }
   issue_prompt(0, Stage<0>{});
@@ -926,7 +951,7 @@ hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
   AttnP p;
   p.pk = (const uint16_t *)a.pk; p.pv = (const uint16_t *)a.pv; p.q = (const uint16_t *)a.q;
   p.ak = (const uint16_t *)a.ak; p.av = (const uint16_t *)a.av;
-  p.rtab = (const uint16_t *)a.rec_tab; p.rrow = a.rec_row; p.rrow_n = a.rec_rows;
+  p.rtab = (const uint16_t *)a.rec_tab; p.rrow = a.rec_row; p.rrow_n = a.rec_rows; p.rtab_rows = a.rec_tab_rows;
   p.ids = nullptr; p.parent = nullptr; p.beam_node = nullptr; p.dev_err = a.dev_err;
   p.out_f32 = a.out_f32; p.out_bf16 = (uint16_t *)a.out_lowp;
   p.R = a.R; p.H = a.H; p.Lp = a.Lp; p.Lw = a.Lw; p.nb = a.nb; p.cap = a.cap;
@@ -948,7 +973,7 @@ hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
   const bool prepass_fits = (static_lds + prepass_dyn) * OCC <= lds_per_cu;
   const bool tab = a.rec_tab != nullptr;
   if (tab && (a.beam_node == nullptr || a.rec_row == nullptr || a.cap > kLdsChainNodes || a.rec_rows < 1 ||
-              a.rec_rows > a.cap))
+              a.rec_rows > a.cap || a.rec_tab_rows < 1))
     return hipErrorInvalidValue;
   if (a.beam_node != nullptr) {
     if (tab || (a.cap <= kLdsChainNodes && (inkernel_fits || !prepass_fits || a.chain_ids == nullptr))) {

@@ -94,24 +94,25 @@ struct CodeAP {
   const int32_t *token, *parent_beam, *prev_nodes;
   int32_t *node_out, *dev_err;
   int32_t *rec_row;            // or [R][row_n]: the table row of each node, in place of ak / av
-  long long total;             // R * n_new * cpr
-  int cpr, cap, base, n_new, n_prev, V, row_n, row0;
+  long long total;             // R * n_new * cpt
+  int cpr, cpt, cap, base, n_new, n_prev, V, row_n, row0;   // cpt: threads per node (cpr, or 1 with nothing to copy)
 };
 
-// One thread per 16-byte chunk of a record; the chunk-0 thread also links the
-// parent (as in trie_append) and validates the code.
+// One thread per 16-byte chunk of a record (per node when nothing is copied);
+// the chunk-0 thread also links the parent (as in trie_append) and validates
+// the code.
 __global__ __launch_bounds__(256) void append_codes_kernel(CodeAP p) {
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= p.total) return;
-  const long long rowi = idx / p.cpr;            // r * n_new + j
-  const int ch = (int)(idx % p.cpr);
+  const long long rowi = idx / p.cpt;            // r * n_new + j
+  const int ch = (int)(idx % p.cpt);
   const int r = (int)(rowi / p.n_new), j = (int)(rowi % p.n_new);
   int t = p.token[rowi];
   const bool bad_code = t < 0 || t >= p.V;
   if (bad_code) t = 0;
   const uint4 *src = p.table + (size_t)t * 3 * p.cpr;
   const long long dst = ((long long)r * p.cap + p.base + j) * p.cpr + ch;
-  if (p.q_out) p.q_out[idx] = src[ch];
+  if (p.q_out) p.q_out[rowi * p.cpr + ch] = src[ch];
   if (p.rec_row == nullptr) {
     p.ak[dst] = src[p.cpr + ch];
     p.av[dst] = src[2 * p.cpr + ch];
@@ -179,7 +180,8 @@ hipError_t launch_append_codes(const AppendCodesArgs &a, hipStream_t s) {
   p.token = a.token; p.parent_beam = a.parent_beam; p.prev_nodes = a.prev_nodes;
   p.node_out = a.node_out; p.dev_err = a.dev_err;
   p.cpr = a.H * a.hd * a.elem_bytes / 16;
-  p.total = (long long)a.R * a.n_new * p.cpr;
+  p.cpt = a.rec_row != nullptr && a.q_out == nullptr ? 1 : p.cpr;
+  p.total = (long long)a.R * a.n_new * p.cpt;
   p.cap = a.cap; p.base = a.base; p.n_new = a.n_new; p.n_prev = a.n_prev; p.V = a.V;
   p.rec_row = a.rec_row; p.row_n = a.row_n; p.row0 = a.row0;
   const long long blocks = (p.total + 255) / 256;

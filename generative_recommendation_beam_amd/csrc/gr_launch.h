@@ -23,13 +23,14 @@ struct AttnArgs {
   int32_t *dev_err;
   int R, H, hd, Lp, Lw, nb, cap, max_depth;
   float scale;
-  // Records read from code tables instead of the arena (whole-ID generation,
-  // bf16, arenas of at most kLdsChainNodes nodes): node n's key and value are
-  // row rec_row[r][n] of rec_tab ([rows][3][H][hd]: q, k, v), for the nodes
-  // n < rec_rows <= cap that chains reach.  Null: the arena.
+  // Records and queries read from code tables instead of the arena and q
+  // (whole-ID generation, bf16, arenas of at most kLdsChainNodes nodes): node
+  // n's key and value, and the query of a beam at node n, are row
+  // rec_row[r][n] of rec_tab ([rec_tab_rows][3][H][hd]: q, k, v), for the
+  // nodes n < rec_rows <= cap that chains reach.  Null: the arena and q.
   const void *rec_tab = nullptr;
   const int32_t *rec_row = nullptr;   // [R][rec_rows]
-  int rec_rows = 0;
+  int rec_rows = 0, rec_tab_rows = 0;
 };
 hipError_t launch_attn(const AttnArgs &a, hipStream_t s);
 
@@ -140,7 +141,8 @@ struct AppendCodesArgs {
   int R, H, hd, cap, base, n_new, n_prev, V;
   // Records left in the code tables: node n's table row (row0 + its code) is
   // written to rec_row[r][n] ([R][row_n], n < row_n) and ak / av are not
-  // touched.  Null: the rows are copied into the arena.
+  // touched (q_out may then be null too).  Null: the rows are copied into the
+  // arena.
   int32_t *rec_row = nullptr;
   int row_n = 0, row0 = 0;
 };

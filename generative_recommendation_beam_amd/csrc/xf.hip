@@ -16,8 +16,9 @@
 // and to its own key; after the last layer a final LayerNorm and a linear
 // head give the score.
 //
-// Layout of a wave's tokens.  A wave owns 32 tokens (candidates, or user
-// tokens) and keeps everything about them in registers: the residual stream
+// Layout of a wave's tokens (the user pass; the candidate kernel uses the
+// 16-wide form of the same scheme, described at its section).  A wave owns
+// 32 tokens and keeps everything about them in registers: the residual stream
 // x in fp32, and each product's output, in the accumulator layout of
 // v_mfma_f32_32x32x16_bf16 transposed (features x tokens: lane (c, g) holds
 // token c).  The A operand of every product is a weight (or user key /
@@ -43,8 +44,8 @@
 // a request; launch l finishes layer l-1 (attention over the user keys of
 // l-1, output projection, FFN) and forms layer l's queries, keys and values,
 // its four waves splitting every product by head or by output features.
-// xf_cand_kernel: all layers for 4 x 32 candidates per workgroup, then the
-// final LayerNorm and the score.
+// xf_cand16_kernel: all layers for 10 x 16 candidates per workgroup, then the
+// final LayerNorm and the score (16-wide products; see its section).
 
 #include "gr_device.h"
 #include "gr_launch.h"
@@ -167,41 +168,6 @@ __device__ __forceinline__ void layer_norm_b(const Acc (&x)[4], const float *gai
     }
 }
 
-// x[ot] += W_o[32 ot + pi(c)][head h's 32 columns] . o_h: the head's column
-// block of W_o in LDS, 128 rows of 64 bytes (chunk ^ (row >> 2) & 3).
-__device__ __forceinline__ void oproj_head(Acc (&x)[4], const unsigned char *wo, int c, int g, const bf16x8 (&ob)[2]) {
-  const int cf = fresh(c), gf = fresh(g);
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-#pragma unroll
-    for (int ot = 0; ot < 4; ++ot) {
-      const int row = 32 * ot + xpi(cf);
-      const bf16x8 a = *(const bf16x8 *)(wo + row * 64 + 16 * ((2 * s + gf) ^ ((row >> 2) & 3)));
-      x[ot] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ob[s], x[ot], 0, 0, 0);
-    }
-  }
-}
-
-// acc[t] += W[rows row0 + 32 t + pi(c)] . h for t < NT (K = 128): the
-// k-steps outermost, so that the NT accumulation chains interleave on the
-// MFMA pipe instead of each waiting for its previous step.
-template <int NT>
-__device__ __forceinline__ void gemm_tiles(Acc (&acc)[NT], const unsigned char *w, int row0, int c, int g,
-                                           const bf16x8 (&h)[4][2]) {
-  const int cf = fresh(c), gf = fresh(g);
-  const int r0 = row0 + xpi(cf);
-  const int sw = r0 & 15;
-#pragma unroll
-  for (int ft = 0; ft < 4; ++ft)
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const bf16x8 a = *(const bf16x8 *)(w + (r0 + 32 * t) * 256 + 16 * ((4 * ft + 2 * s + gf) ^ sw));
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, h[ft][s], acc[t], 0, 0, 0);
-      }
-}
-
 __device__ __forceinline__ void zero(Acc &a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) a[i] = 0.f;
@@ -305,31 +271,243 @@ struct XfCandP {
   float sl2;                // log2(e) / sqrt(32)
 };
 
-constexpr int kXCandWaves = 4;
+// ---- candidate kernel, 16-candidate waves ------------------------------------
+// The same computation on v_mfma_f32_16x16x32_bf16, with half the tokens per
+// wave: 40 000 candidates are then 2500 half-size waves, and ten-wave
+// workgroups (160 candidates, one per CU) leave at most three of them on a
+// SIMD, against two full waves on the busiest SIMDs of the 32-wide form.
+// Lane (c, q) = (lane & 15, lane >> 4) holds token c and, of every
+// 32-feature block b, the features 32 b + 8 q + 4 e + i in t[e][i]: the
+// output tile e of a product takes its A rows in the order
+// rho(m, e) = 8 (m >> 2) + 4 e + (m & 3), so the lane's eight features of a
+// block are the eight k-values it supplies as the B operand of the next
+// product.  A token's statistics are in-lane sums plus the exchanges with
+// the lanes 16 and 32 apart.  Weights and user keys / values use the LDS
+// layouts of the 32-wide kernel.
+__device__ __forceinline__ int xrho(int m, int e) { return 8 * (m >> 2) + 4 * e + (m & 3); }
 
-__global__ __launch_bounds__(kXCandWaves * 64, 2) void xf_cand_kernel(XfCandP p) {
-  constexpr int NW = kXCandWaves;
+// Combine x of lane l with x of lane l^16 (one v_permlane16_swap: the two
+// results hold the values of the even and of the odd 16-lane row of each
+// pair of rows).
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float tok_sum(float x) { return xor32_sum(xor16_sum(x)); }
+__device__ __forceinline__ float tok_max(float x) { return xor32_max(xor16_max(x)); }
+
+struct Blk {
+  f32x4 t[2];
+};
+__device__ __forceinline__ void bzero(Blk &b) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b.t[0][i] = b.t[1][i] = 0.f;
+}
+__device__ __forceinline__ bf16x8 bpack(const Blk &b) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = (__bf16)b.t[0][i];
+    r[4 + i] = (__bf16)b.t[1][i];
+  }
+  return r;
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void layer_norm16(const Blk (&x)[4], const float *gain, const float *bias, int q,
+                                             bf16x8 (&h)[4]) {
+  q = fresh(q);
+  float s = 0.f;
+#pragma unroll
+  for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s += x[ft].t[0][i] + x[ft].t[1][i];
+  const float mean = tok_sum(s) * (1.f / kXD);
+  float v = 0.f;
+#pragma unroll
+  for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float d = x[ft].t[e][i] - mean;
+        v = fmaf(d, d, v);
+      }
+  const float rstd = 1.f / sqrtf(tok_sum(v) * (1.f / kXD) + 1e-5f);
+#pragma unroll
+  for (int ft = 0; ft < 4; ++ft) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int f0 = 32 * ft + 8 * q + 4 * e;
+      const float4 gg = *(const float4 *)(gain + f0), bb = *(const float4 *)(bias + f0);
+      r[4 * e + 0] = (__bf16)fmaf((x[ft].t[e][0] - mean) * rstd, gg.x, bb.x);
+      r[4 * e + 1] = (__bf16)fmaf((x[ft].t[e][1] - mean) * rstd, gg.y, bb.y);
+      r[4 * e + 2] = (__bf16)fmaf((x[ft].t[e][2] - mean) * rstd, gg.z, bb.z);
+      r[4 * e + 3] = (__bf16)fmaf((x[ft].t[e][3] - mean) * rstd, gg.w, bb.w);
+    }
+    h[ft] = r;
+  }
+}
+
+// x[ot] += W_o[32 ot + rho(c, e)][head h's 32 columns] . o_h: one k-step per
+// output tile (the W_o column block layout of the 32-wide kernel)
+__device__ __forceinline__ void oproj16(Blk (&x)[4], const unsigned char *wo, int c, int q, bf16x8 ob) {
+  const int cf = fresh(c), qf = fresh(q);
+#pragma unroll
+  for (int ot = 0; ot < 4; ++ot)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int row = 32 * ot + xrho(cf, e);
+      const bf16x8 a = *(const bf16x8 *)(wo + row * 64 + 16 * (qf ^ ((row >> 2) & 3)));
+      x[ot].t[e] = mfma16(a, ob, x[ot].t[e]);
+    }
+}
+
+// acc[t] += W[rows row0 + 32 t + rho(c, e)] . h for t < NT (K = 128, four
+// k-steps outermost so that the 2 NT chains interleave on the MFMA pipe)
+template <int NT>
+__device__ __forceinline__ void gemm16(Blk (&acc)[NT], const unsigned char *w, int row0, int c, int q,
+                                       const bf16x8 (&h)[4]) {
+  const int cf = fresh(c), qf = fresh(q);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int row = row0 + 32 * t + xrho(cf, e);
+        const bf16x8 a = *(const bf16x8 *)(w + row * 256 + 16 * ((4 * ks + qf) ^ (row & 15)));
+        acc[t].t[e] = mfma16(a, h[ks], acc[t].t[e]);
+      }
+}
+
+// add the bias of features f0 + 8 q + 4 e + i (b points at f0)
+__device__ __forceinline__ void add_bias16(Blk &a, const float *b, int q) {
+  q = fresh(q);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const float4 v = *(const float4 *)(b + 8 * q + 4 * e);
+    a.t[e][0] += v.x; a.t[e][1] += v.y; a.t[e][2] += v.z; a.t[e][3] += v.w;
+  }
+}
+
+struct HeadState16 {
+  Blk o;          // output dims of the head, unnormalised
+  float m, l;     // running max (log2 units, the same in the token's four lanes) and this lane's partial sum
+};
+
+// S^T for the 16 keys 32 kt + rho(c', e) of a key tile: one MFMA over the
+// head's 32 dims (K layout [key][32], chunk ^ (key >> 2) & 3)
+__device__ __forceinline__ f32x4 scores16(const unsigned char *kp, int kt, int e, int c, int q, bf16x8 qb) {
+  const int key = 32 * kt + xrho(c, e);
+  const bf16x8 a = *(const bf16x8 *)(kp + key * 64 + 16 * (q ^ ((key >> 2) & 3)));
+  f32x4 z;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) z[i] = 0.f;
+  return mfma16(a, qb, z);
+}
+// O^T += V^T P^T over the 32 keys of tile kt; p holds the weights of keys
+// 32 kt + 8 q .. + 7 (V^T layout [32][key], chunk ^ dim & 15)
+__device__ __forceinline__ void values16(Blk &o, const unsigned char *vp, int kt, int c, int q, bf16x8 p) {
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int dim = xrho(c, e), ch = 4 * kt + q;
+    const bf16x8 a = *(const bf16x8 *)(vp + dim * 512 + 16 * (ch ^ (dim & 15)));
+    o.t[e] = mfma16(a, p, o.t[e]);
+  }
+}
+// one piece of user keys / values (n_kt tiles of 32 keys), two tiles a round
+__device__ __forceinline__ void attend_piece16(HeadState16 &st, const unsigned char *piece, int n_kt, int c, int q,
+                                               bf16x8 qb, float sl2) {
+  const unsigned char *kp = piece, *vp = piece + 16384;
+  c = fresh(c);
+  q = fresh(q);
+  Blk o2;                                  // the second tile's chain, summed at the end
+  bzero(o2);
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    const bool two = kt + 1 < n_kt;
+    f32x4 s0[2], s1[2];
+    s0[0] = scores16(kp, kt, 0, c, q, qb);
+    s0[1] = scores16(kp, kt, 1, c, q, qb);
+    if (two) {
+      s1[0] = scores16(kp, kt + 1, 0, c, q, qb);
+      s1[1] = scores16(kp, kt + 1, 1, c, q, qb);
+    }
+    float mx = s0[0][0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s0[i >> 2][i & 3]);
+    if (two) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, s1[i >> 2][i & 3]);
+    }
+    const float m_new = fmaxf(st.m, tok_max(mx) * sl2);
+    const float corr = fast_exp2(st.m - m_new);
+    st.l *= corr;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        st.o.t[e][i] *= corr;
+        o2.t[e][i] *= corr;
+      }
+    st.m = m_new;
+    bf16x8 p0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float v = fast_exp2(fmaf(s0[i >> 2][i & 3], sl2, -m_new));
+      st.l += v;
+      p0[i] = (__bf16)v;
+    }
+    values16(st.o, vp, kt, c, q, p0);
+    if (two) {
+      bf16x8 p1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = fast_exp2(fmaf(s1[i >> 2][i & 3], sl2, -m_new));
+        st.l += v;
+        p1[i] = (__bf16)v;
+      }
+      values16(o2, vp, kt + 1, c, q, p1);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.o.t[e][i] += o2.t[e][i];
+}
+
+constexpr int kXCand16Waves = 10;
+
+__global__ __launch_bounds__(kXCand16Waves * 64, 1) void xf_cand16_kernel(XfCandP p) {
+  constexpr int NW = kXCand16Waves;
   __shared__ __attribute__((aligned(1024))) XfSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5, c = lane & 31;
-  const int tiles = (p.N + 32 * NW - 1) / (32 * NW);
+  const int q = lane >> 4, c = lane & 15;
+  const int tiles = (p.N + 16 * NW - 1) / (16 * NW);
   const int r = blockIdx.x / tiles, tb = blockIdx.x % tiles;
-  const int n = (tb * NW + wave) * 32 + c;
+  const int n = (tb * NW + wave) * 16 + c;
   const int nl = min(n, p.N - 1);
-
-  // the residual stream of this lane's token, features 32 ft + 16 s + 8 g + t
-  Acc x[4];
+  // the residual stream of this lane's token, features 32 ft + 8 q + 4 e + i
+  Blk x[4];
   {
-    const uint16_t *src = p.cand + ((size_t)r * p.N + nl) * kXD + 8 * g;
+    const uint16_t *src = p.cand + ((size_t)r * p.N + nl) * kXD + 8 * q;
 #pragma unroll
-    for (int ft = 0; ft < 4; ++ft)
+    for (int ft = 0; ft < 4; ++ft) {
+      const bf16x8 v = *(const bf16x8 *)(src + 32 * ft);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 v = *(const bf16x8 *)(src + 32 * ft + 16 * s);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) x[ft][8 * s + t] = (float)v[t];
+      for (int i = 0; i < 4; ++i) {
+        x[ft].t[0][i] = (float)v[i];
+        x[ft].t[1][i] = (float)v[4 + i];
       }
+    }
   }
 
   // Pieces of a layer: per head h, its q, k, v weight rows (24 KB) with
@@ -385,75 +563,79 @@ __global__ __launch_bounds__(kXCandWaves * 64, 2) void xf_cand_kernel(XfCandP p)
 
   issue(0);
   int pc = 0;
-  bf16x8 hB[4][2];
+  bf16x8 hB[4];
   for (int l = 0; l < p.L; ++l) {
-    bf16x8 ob[2];                                      // the previous head's output
+    bf16x8 ob;                                         // the previous head's output
     for (int h = 0; h < kXHeads; ++h) {
       const unsigned char *w = step(pc++);
       if (h == 0) {
-        layer_norm_b(x, sm.vec + kVln1g, sm.vec + kVln1b, g, hB);
+        layer_norm16(x, sm.vec + kVln1g, sm.vec + kVln1b, q, hB);
       } else {
-        oproj_head(x, w + 24576, c, g, ob);
+        oproj16(x, w + 24576, c, q, ob);
         if (h == 1) {
 #pragma unroll
-          for (int ot = 0; ot < 4; ++ot) add_bias(x[ot], sm.vec + kVbO + 32 * ot, g);
+          for (int ot = 0; ot < 4; ++ot) add_bias16(x[ot], sm.vec + kVbO + 32 * ot, q);
         }
       }
-      Acc qkv[3];
-      zero(qkv[0]); zero(qkv[1]); zero(qkv[2]);
-      gemm_tiles<3>(qkv, w, 0, c, g, hB);
-      add_bias(qkv[0], sm.vec + kVbQKV + 32 * h, g);
-      add_bias(qkv[1], sm.vec + kVbQKV + kXD + 32 * h, g);
-      add_bias(qkv[2], sm.vec + kVbQKV + 2 * kXD + 32 * h, g);
+      Blk qkv[3];
+      bzero(qkv[0]); bzero(qkv[1]); bzero(qkv[2]);
+      gemm16<3>(qkv, w, 0, c, q, hB);
+      add_bias16(qkv[0], sm.vec + kVbQKV + 32 * h, q);
+      add_bias16(qkv[1], sm.vec + kVbQKV + kXD + 32 * h, q);
+      add_bias16(qkv[2], sm.vec + kVbQKV + 2 * kXD + 32 * h, q);
       float ss = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ss = fmaf(qkv[0][i], qkv[1][i], ss);
-      const float s_self = xor32_sum(ss) * p.sl2;     // own key, log2 units
-      const bf16x8 qb[2] = {pack8(qkv[0], 0), pack8(qkv[0], 1)};
-      const Acc va = qkv[2];
-      HeadState st;
-      zero(st.o);
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss = fmaf(qkv[0].t[e][i], qkv[1].t[e][i], ss);
+      const float s_self = tok_sum(ss) * p.sl2;       // own key, log2 units
+      const bf16x8 qb = bpack(qkv[0]);
+      const Blk va = qkv[2];
+      HeadState16 st;
+      bzero(st.o);
       st.m = s_self;                                   // the own key starts the running max
       st.l = 0.f;
       for (int j = 0; j < p.n_kc; ++j) {
         const unsigned char *kv = step(pc++);
-        attend_piece(st, kv, min(8, (p.Lu - 256 * j) >> 5), c, g, qb, p.sl2);
+        attend_piece16(st, kv, min(8, (p.Lu - 256 * j) >> 5), c, q, qb, p.sl2);
       }
       // own key: p_self = exp2(s_self - m), counted once in the sum
       const float p_self = fast_exp2(s_self - st.m);
-      const float inv = 1.f / (xor32_sum(st.l) + p_self);
+      const float inv = 1.f / (tok_sum(st.l) + p_self);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) st.o[i] = (st.o[i] + p_self * va[i]) * inv;
-      ob[0] = pack8(st.o, 0);
-      ob[1] = pack8(st.o, 1);
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.o.t[e][i] = (st.o.t[e][i] + p_self * va.t[e][i]) * inv;
+      ob = bpack(st.o);
     }
     {
       const unsigned char *w = step(pc++);
-      oproj_head(x, w, c, g, ob);
-      layer_norm_b(x, sm.vec + kVln2g, sm.vec + kVln2b, g, hB);
+      oproj16(x, w, c, q, ob);
+      layer_norm16(x, sm.vec + kVln2g, sm.vec + kVln2b, q, hB);
     }
     for (int fh = 0; fh < 2; ++fh) {
-      bf16x8 uB[4][2];
+      bf16x8 uB[4];
       {
         const unsigned char *w = step(pc++);
-        Acc a[4];
+        Blk a[4];
 #pragma unroll
-        for (int ot = 0; ot < 4; ++ot) zero(a[ot]);
-        gemm_tiles<4>(a, w, 0, c, g, hB);
+        for (int ot = 0; ot < 4; ++ot) bzero(a[ot]);
+        gemm16<4>(a, w, 0, c, q, hB);
 #pragma unroll
         for (int ot = 0; ot < 4; ++ot) {
-          add_bias(a[ot], sm.vec + kVb1 + 128 * fh + 32 * ot, g);
+          add_bias16(a[ot], sm.vec + kVb1 + 128 * fh + 32 * ot, q);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) a[ot][i] = fmaxf(a[ot][i], 0.f);
-          uB[ot][0] = pack8(a[ot], 0);
-          uB[ot][1] = pack8(a[ot], 1);
+          for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[ot].t[e][i] = fmaxf(a[ot].t[e][i], 0.f);
+          uB[ot] = bpack(a[ot]);
         }
       }
       const unsigned char *w = step(pc++);
-      gemm_tiles<4>(x, w, 0, c, g, uB);
+      gemm16<4>(x, w, 0, c, q, uB);
       if (fh == 0) {
 #pragma unroll
-        for (int ot = 0; ot < 4; ++ot) add_bias(x[ot], sm.vec + kVb2 + 32 * ot, g);
+        for (int ot = 0; ot < 4; ++ot) add_bias16(x[ot], sm.vec + kVb2 + 32 * ot, q);
       }
     }
   }
@@ -465,27 +647,32 @@ __global__ __launch_bounds__(kXCandWaves * 64, 2) void xf_cand_kernel(XfCandP p)
 #pragma unroll
     for (int ft = 0; ft < 4; ++ft)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s += x[ft][i];
-    const float mean = xor32_sum(s) * (1.f / kXD);
+      for (int i = 0; i < 4; ++i) s += x[ft].t[0][i] + x[ft].t[1][i];
+    const float mean = tok_sum(s) * (1.f / kXD);
     float v = 0.f;
 #pragma unroll
     for (int ft = 0; ft < 4; ++ft)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float d = x[ft][i] - mean;
-        v = fmaf(d, d, v);
-      }
-    const float rstd = 1.f / sqrtf(xor32_sum(v) * (1.f / kXD) + 1e-5f);
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float d = x[ft].t[e][i] - mean;
+          v = fmaf(d, d, v);
+        }
+    const float rstd = 1.f / sqrtf(tok_sum(v) * (1.f / kXD) + 1e-5f);
+    const int qf = fresh(q);
     float dot = 0.f;
 #pragma unroll
     for (int ft = 0; ft < 4; ++ft)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int f = 32 * ft + 16 * (i >> 3) + 8 * g + (i & 7);
-        dot = fmaf(fmaf((x[ft][i] - mean) * rstd, gain[f], bias[f]), w[f], dot);
-      }
-    dot = xor32_sum(dot) + sm.vec[3 * kXD];
-    if (g == 0 && n < p.N) p.score[(size_t)r * p.N + n] = dot;
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int f = 32 * ft + 8 * qf + 4 * e + i;
+          dot = fmaf(fmaf((x[ft].t[e][i] - mean) * rstd, gain[f], bias[f]), w[f], dot);
+        }
+    dot = tok_sum(dot) + sm.vec[3 * kXD];
+    if (q == 0 && n < p.N) p.score[(size_t)r * p.N + n] = dot;
   }
 }
 
@@ -785,8 +972,8 @@ hipError_t launch_xf_scores(const XfArgs &a, hipStream_t s) {
   c.score = a.score;
   c.R = a.R; c.N = a.N; c.L = a.L; c.n_kc = n_kc; c.Lu = a.Lu;
   c.sl2 = u.sl2;
-  const int tiles = (a.N + 32 * kXCandWaves - 1) / (32 * kXCandWaves);
-  hipLaunchKernelGGL(xf_cand_kernel, dim3((unsigned)(a.R * tiles)), dim3(kXCandWaves * 64), 0, s, c);
+  const int tiles = (a.N + 16 * kXCand16Waves - 1) / (16 * kXCand16Waves);
+  hipLaunchKernelGGL(xf_cand16_kernel, dim3((unsigned)(a.R * tiles)), dim3(kXCand16Waves * 64), 0, s, c);
   return hipGetLastError();
 }
 
